@@ -1,0 +1,363 @@
+"""Plain fp64 CPU oracle for the NSA forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the benchmark's CPU-baseline leg
+may import this module.  It shares no code with the HIP library and does not import it; the only
+module both sides use is the seeded input generator (`workloads`), which holds none of the
+method's arithmetic.
+
+Every function is written from the pages' statement of the method, in the plainest form: explicit
+loops over query rows and blocks, numpy for the small per-row vector products, float64 throughout
+(inputs are first widened exactly from their float32 / bfloat16 values).
+
+Sources (cited by page title and section; no page prints code or worked numbers):
+  [LSRM-cn]  hyper.ai summary of "LSRM" (arXiv 2604.05182), section 方法 (Method):
+             gated self/cross attention (eq. o^x, o^y and the Sigmoid gates), block partition,
+             compression eq. k^cmp / v^cmp = AvgPool(ResBlock(.)), compressed + selected branches,
+             3D-aware block routing (voxel centre / surface point, distance to block centres),
+             window (local) attention inside a block.
+  [LSRM-ko]  gist.science Korean technical summary of LSRM, section 2.2: geometric routing and
+             block-aware locality.
+  [Speed3R]  gist.science summary of "Speed3R" (arXiv 2603.08055), section 2.1 Global Sparse
+             Attention: pooled Q/K/V compression branch, top-K selection from the compressed score
+             matrix, learned gate combining the branches.
+
+Readings where the pages are silent (each is listed with its reason in the design notes):
+  * softmax scale is a parameter (callers pass 1/sqrt(D)); attention is non-causal;
+  * ResBlock before AvgPool is the identity, so compression is the mean over a block's valid tokens;
+  * padded slots are neither keys nor queries; padded outputs are 0, padded routing rows are -1;
+  * geometric routing ranks blocks by the exact integer squared distance between the query point
+    and the block centroid on a 2^-12 lattice (u = rint(4096 p) + 4096), ties by ascending blk_key;
+  * GQA score routing sums the group's softmax probabilities against the compressed keys;
+  * each gate channel is an independent sigmoid; an empty key set contributes 0.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+CMP, SEL, LOC = 0, 1, 2
+BRANCH_NAMES = {"cmp": CMP, "sel": SEL, "loc": LOC}
+
+
+# ----------------------------------------------------------------------------------------------
+# basic pieces
+# ----------------------------------------------------------------------------------------------
+
+def sigmoid(x):
+    """Logistic gate of [LSRM-cn] eq. w = Sigmoid(Linear_gate(.)); exact 0 and 1 at -inf / +inf."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def valid_mask(blk_cnt, cap):
+    """Slot s (in block s // cap) holds a token iff s % cap < cnt[s // cap]."""
+    blk_cnt = np.asarray(blk_cnt)
+    slot = np.arange(blk_cnt.shape[0] * cap)
+    return (slot % cap) < blk_cnt[slot // cap]
+
+
+def block_slots(blk_cnt, cap, b):
+    """The storage slots of block b's valid tokens."""
+    return np.arange(b * cap, b * cap + int(blk_cnt[b]))
+
+
+def attend(qrow, keys, vals, scale, return_weights=False):
+    """Softmax attention of one query row against an explicit key set.
+
+    qrow [Hq, D]; keys, vals [n, Hkv, D]; query head h reads KV head h // (Hq // Hkv) (grouped-query
+    attention, [LSRM-cn] dense transformer paragraph).  For each head:
+        s_i = scale * <q_h, k_i>,  a_i = exp(s_i - max s) / sum_j exp(s_j - max s),  o_h = sum_i a_i v_i
+    Returns (o [Hq, D], lse [Hq]) with lse = max s + log(sum exp(s - max s)); an empty key set gives
+    o = 0 and lse = -inf.
+    """
+    qrow = np.asarray(qrow, dtype=np.float64)
+    Hq, D = qrow.shape
+    n = keys.shape[0]
+    if n == 0:
+        o = np.zeros((Hq, D))
+        lse = np.full(Hq, -np.inf)
+        return (o, lse, np.zeros((Hq, 0))) if return_weights else (o, lse)
+    Hkv = keys.shape[1]
+    G = Hq // Hkv
+    o = np.zeros((Hq, D))
+    lse = np.zeros(Hq)
+    weights = np.zeros((Hq, n))
+    for h in range(Hq):
+        j = h // G
+        s = scale * (keys[:, j, :].astype(np.float64) @ qrow[h])
+        m = s.max()
+        e = np.exp(s - m)
+        z = e.sum()
+        a = e / z
+        o[h] = a @ vals[:, j, :].astype(np.float64)
+        lse[h] = m + math.log(z)
+        weights[h] = a
+    return (o, lse, weights) if return_weights else (o, lse)
+
+
+# ----------------------------------------------------------------------------------------------
+# A1: block compression
+# ----------------------------------------------------------------------------------------------
+
+def pool_blocks(x, blk_cnt, cap):
+    """Compressed block features, [LSRM-cn] eq. k^cmp = AvgPool(ResBlock(k_t)) with the ResBlock
+    taken as the identity, and the 4x4 average pooling of Q/K/V in [Speed3R] 2.1: the mean of the
+    block's valid tokens.  x [S, H, D] -> [n_blk, H, D] (float64)."""
+    blk_cnt = np.asarray(blk_cnt)
+    n_blk = blk_cnt.shape[0]
+    out = np.zeros((n_blk,) + x.shape[1:])
+    for b in range(n_blk):
+        rows = x[block_slots(blk_cnt, cap, b)].astype(np.float64)
+        out[b] = rows.sum(axis=0) / rows.shape[0]
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# A2: 3D-aware geometric routing
+# ----------------------------------------------------------------------------------------------
+
+def lattice_coords(pts):
+    """Query points on the 2^-12 lattice: u = rint(4096 p) + 4096 per axis, p in [-1, 1] -> [0, 8192]."""
+    return (np.rint(4096.0 * np.asarray(pts, dtype=np.float64)) + 4096.0).astype(np.int64)
+
+
+def block_centroids(pts, blk_cnt, cap):
+    """Centroid of each block's member points on the lattice, rounded half-up:
+    c_b = floor((2 * sum_t u_t + cnt_b) / (2 * cnt_b)) per axis (all quantities non-negative)."""
+    u = lattice_coords(pts)
+    blk_cnt = np.asarray(blk_cnt)
+    c = np.zeros((blk_cnt.shape[0], 3), dtype=np.int64)
+    for b in range(blk_cnt.shape[0]):
+        tot = u[block_slots(blk_cnt, cap, b)].sum(axis=0)
+        n = int(blk_cnt[b])
+        c[b] = (2 * tot + n) // (2 * n)
+    return c
+
+
+def route_geometric(pts, blk_cnt, blk_key, cap, top_k, rows=None):
+    """3D-aware block routing ([LSRM-cn] routing paragraph; [LSRM-ko] 2.2): each query token keeps
+    the blocks whose centres are nearest to its 3D point.  The metric is the exact squared distance
+    d2(t, b) = |u_t - c_b|^2 (an integer < 2^28); blocks are taken in ascending (d2, blk_key) order.
+
+    Returns sel int32 [len(rows), top_k] (storage block indices, best first) and d2 uint32 of the
+    same shape.  Padding rows and positions beyond n_blk hold -1 / 0xFFFFFFFF.
+    rows defaults to every slot.
+    """
+    blk_cnt = np.asarray(blk_cnt)
+    blk_key = np.asarray(blk_key, dtype=np.int64)
+    S = blk_cnt.shape[0] * cap
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    valid = valid_mask(blk_cnt, cap)
+    cen = block_centroids(pts, blk_cnt, cap)
+    u = lattice_coords(pts)
+    sel = np.full((rows.shape[0], top_k), -1, dtype=np.int32)
+    dd = np.full((rows.shape[0], top_k), 0xFFFFFFFF, dtype=np.uint32)
+    kk = min(top_k, blk_cnt.shape[0])
+    for i, r in enumerate(rows):
+        if not valid[r]:
+            continue
+        d2 = ((u[r][None, :] - cen) ** 2).sum(axis=1)
+        order = np.lexsort((blk_key, d2))[:kk]
+        sel[i, :kk] = order
+        dd[i, :kk] = d2[order]
+    return sel, dd
+
+
+# ----------------------------------------------------------------------------------------------
+# A3: score routing against the compressed keys
+# ----------------------------------------------------------------------------------------------
+
+def route_scores(q_rows, k_cmp, blk_key, scale, top_k, lse=None, row_valid=None):
+    """Top-k block selection from compressed attention scores.
+
+    [Speed3R] 2.1 selection branch / [LSRM-cn] ("standard NSA selects KV blocks by attention score
+    against the compressed keys").  q_rows [R, Hq, D], k_cmp [n_blk, Hkv, D].
+      * Hq == Hkv (one query head per KV head): block b's importance for (row r, head h) is the
+        compressed score <q_rh, k_cmp[b, h]> (same order as its softmax probability);
+      * Hq > Hkv: importance for (row r, KV group j) is sum over the group's heads h of
+        exp(scale * <q_rh, k_cmp[b, j]> - lse[r, h]), i.e. the group's summed softmax probability.
+    Blocks are ranked by descending importance, ties by ascending blk_key.
+    Returns sel int32 [R, Hkv, top_k] (rows where row_valid is False hold -1) and the importance of
+    every block, float64 [R, Hkv, n_blk].
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k_cmp = np.asarray(k_cmp, dtype=np.float64)
+    blk_key = np.asarray(blk_key, dtype=np.int64)
+    R, Hq, D = q_rows.shape
+    n_blk, Hkv, _ = k_cmp.shape
+    G = Hq // Hkv
+    if G > 1 and lse is None:
+        raise ValueError("grouped score routing needs the compressed branch's lse")
+    kk = min(top_k, n_blk)
+    sel = np.full((R, Hkv, top_k), -1, dtype=np.int32)
+    imp_all = np.zeros((R, Hkv, n_blk))
+    for r in range(R):
+        if row_valid is not None and not row_valid[r]:
+            continue
+        for j in range(Hkv):
+            if G == 1:
+                imp = k_cmp[:, j, :] @ q_rows[r, j]
+            else:
+                imp = np.zeros(n_blk)
+                for h in range(j * G, (j + 1) * G):
+                    imp += np.exp(scale * (k_cmp[:, j, :] @ q_rows[r, h]) - lse[r, h])
+            imp_all[r, j] = imp
+            order = np.lexsort((blk_key, -imp))[:kk]
+            sel[r, j, :kk] = order
+    return sel, imp_all
+
+
+# ----------------------------------------------------------------------------------------------
+# A4-A6: the three attention branches
+# ----------------------------------------------------------------------------------------------
+
+def attn_branch(branch, q, k, v, blk_cnt, cap, scale, sel=None, q_gran="token", rows=None):
+    """One NSA branch for the query rows `rows` (storage slots; default all).
+
+    branch CMP ([LSRM-cn] compressed branch; [Speed3R] compression branch): keys/values are the
+      pooled arrays k, v [n_blk, Hkv, D].  q_gran 'token': every valid token's own query attends all
+      blocks.  q_gran 'block': q is pooled [n_blk, Hq, D]; block b's pooled query attends all blocks
+      and its output is given to each valid token of block b.
+    branch LOC ([LSRM-cn] window attention): the valid tokens of the query's own block.
+    branch SEL ([LSRM-cn] selected blocks; [Speed3R] selection branch): the valid tokens of the
+      blocks listed in sel (a set; -1 entries skipped).  sel is [S, top_k] (one list per token,
+      shared by all heads), [S, Hkv, top_k] (one list per token and KV group), or with q_gran
+      'block' [n_blk, top_k] / [n_blk, Hkv, top_k] (one list per query block).
+    Returns o [len(rows), Hq, D] and lse [len(rows), Hq] (padding rows: 0 and -inf).
+    """
+    blk_cnt = np.asarray(blk_cnt)
+    n_blk = blk_cnt.shape[0]
+    S = n_blk * cap
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    valid = valid_mask(blk_cnt, cap)
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    o = np.zeros((rows.shape[0], Hq, D))
+    lse = np.full((rows.shape[0], Hq), -np.inf)
+    cache = {}
+    for i, r in enumerate(rows):
+        if not valid[r]:
+            continue
+        b = r // cap
+        if branch == CMP:
+            if q_gran == "block":
+                if b not in cache:
+                    cache[b] = attend(q[b], k, v, scale)
+                o[i], lse[i] = cache[b]
+            else:
+                o[i], lse[i] = attend(q[r], k, v, scale)
+        elif branch == LOC:
+            ks = block_slots(blk_cnt, cap, b)
+            o[i], lse[i] = attend(q[r], k[ks], v[ks], scale)
+        elif branch == SEL:
+            lst = sel[b] if q_gran == "block" else sel[r]
+            lst = np.asarray(lst)
+            if lst.ndim == 1:
+                blocks = sorted(set(int(x) for x in lst if x >= 0))
+                ks = np.concatenate([block_slots(blk_cnt, cap, x) for x in blocks]) if blocks else np.zeros(0, int)
+                o[i], lse[i] = attend(q[r], k[ks], v[ks], scale)
+            else:
+                for j in range(Hkv):
+                    blocks = sorted(set(int(x) for x in lst[j] if x >= 0))
+                    ks = np.concatenate([block_slots(blk_cnt, cap, x) for x in blocks]) if blocks else np.zeros(0, int)
+                    hs = slice(j * G, (j + 1) * G)
+                    oj, lj = attend(q[r, hs], k[ks][:, j:j + 1], v[ks][:, j:j + 1], scale)
+                    o[i, hs], lse[i, hs] = oj, lj
+        else:
+            raise ValueError(branch)
+    return o, lse
+
+
+# ----------------------------------------------------------------------------------------------
+# A7: gate
+# ----------------------------------------------------------------------------------------------
+
+def gate_combine(outs, gate_logits):
+    """o = sum_c sigmoid(g_c) * o_c per (row, query head): [LSRM-cn] Sigmoid gates; [Speed3R] 2.1
+    gated aggregation of the branch outputs.  outs: list of [R, Hq, D]; gate_logits [R, Hq, n]."""
+    g = sigmoid(np.asarray(gate_logits, dtype=np.float64))
+    o = np.zeros(np.asarray(outs[0]).shape)
+    for c, oc in enumerate(outs):
+        o += g[:, :, c:c + 1] * np.asarray(oc, dtype=np.float64)
+    return o
+
+
+# ----------------------------------------------------------------------------------------------
+# A8: stage-1 dense gated self/cross attention
+# ----------------------------------------------------------------------------------------------
+
+def dense_gated_xattn(q, k, v, n_x, gate_logits, scale, rows=None):
+    """[LSRM-cn] eq. o^x = w^{x-self} CrossAttn(x, x) + w^{x-cross} CrossAttn(x, y) and the same for
+    y: tokens [0, n_x) are volume tokens x, the rest image tokens y.  One q, k, v per token serves
+    both terms; gate channel 0 is the self gate, channel 1 the cross gate.  An empty key set adds 0."""
+    N = q.shape[0]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    g = sigmoid(np.asarray(gate_logits, dtype=np.float64))
+    xs = np.arange(0, n_x)
+    ys = np.arange(n_x, N)
+    o = np.zeros((rows.shape[0], q.shape[1], q.shape[2]))
+    for i, t in enumerate(rows):
+        own, other = (xs, ys) if t < n_x else (ys, xs)
+        o_self, _ = attend(q[t], k[own], v[own], scale)
+        o_cross, _ = attend(q[t], k[other], v[other], scale)
+        o[i] = g[t, :, 0:1] * o_self + g[t, :, 1:2] * o_cross
+    return o
+
+
+# ----------------------------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------------------------
+
+def nsa_forward(w, rows=None, return_parts=False):
+    """One NSA layer on a block-major workload `w` (see workloads.Workload):
+    compress K and V (and Q for block-granular queries), route, run the branches listed in
+    w.branches and combine them with the sigmoid gates (channel c = c-th listed branch).
+    Geometric routing ([LSRM-cn]) is per token and shared by all heads; score routing ([Speed3R])
+    with one query head per KV head is per (query block, head) from the pooled queries."""
+    cap = w.blk_cap
+    S = w.n_slots
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    k_cmp = pool_blocks(w.k, w.blk_cnt, cap)
+    v_cmp = pool_blocks(w.v, w.blk_cnt, cap)
+    parts = {"k_cmp": k_cmp, "v_cmp": v_cmp}
+    if w.q_gran == "block":
+        q_cmp = pool_blocks(w.q, w.blk_cnt, cap)
+        parts["q_cmp"] = q_cmp
+    if w.routing == "geometric":
+        sel_rows, _ = route_geometric(w.pts, w.blk_cnt, w.blk_key, cap, w.top_k, rows=rows)
+        sel = np.full((S, w.top_k), -1, dtype=np.int32)
+        sel[rows] = sel_rows
+        q_gran_sel = "token"
+    else:
+        if w.n_qh != w.n_kvh:
+            raise NotImplementedError("whole-layer score routing is defined here for Hq == Hkv")
+        sel, _ = route_scores(parts["q_cmp"], k_cmp, w.blk_key, w.scale, w.top_k)
+        q_gran_sel = "block"
+    parts["sel"] = sel
+    outs = []
+    for name in w.branches:
+        br = BRANCH_NAMES[name]
+        if br == CMP:
+            if w.q_gran == "block":
+                oc, lc = attn_branch(CMP, parts["q_cmp"], k_cmp, v_cmp, w.blk_cnt, cap, w.scale,
+                                     q_gran="block", rows=rows)
+            else:
+                oc, lc = attn_branch(CMP, w.q, k_cmp, v_cmp, w.blk_cnt, cap, w.scale, rows=rows)
+        elif br == SEL:
+            oc, lc = attn_branch(SEL, w.q, w.k, w.v, w.blk_cnt, cap, w.scale, sel=sel,
+                                 q_gran=q_gran_sel, rows=rows)
+        else:
+            oc, lc = attn_branch(LOC, w.q, w.k, w.v, w.blk_cnt, cap, w.scale, rows=rows)
+        parts["o_" + name] = oc
+        parts["lse_" + name] = lc
+        outs.append(oc)
+    o = gate_combine(outs, w.gates[rows])
+    o[~valid_mask(w.blk_cnt, cap)[rows]] = 0.0
+    return (o, parts) if return_parts else o

@@ -1,0 +1,358 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against something independent: a hand-worked fixture, a closed form,
+a textbook library routine (torch's scaled-dot-product attention in float64 on the CPU), brute
+force on tiny inputs, or an invariant of the definition (row sums, storage-order invariance).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def sdpa(q, k, v, scale):
+    """Library attention: q [n, Hq, D], k/v [m, Hkv, D] -> [n, Hq, D] (torch, float64, CPU)."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    tq = torch.from_numpy(np.asarray(q, dtype=np.float64)).permute(1, 0, 2)
+    tk = torch.from_numpy(np.asarray(k, dtype=np.float64)).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    tv = torch.from_numpy(np.asarray(v, dtype=np.float64)).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+    return o.permute(1, 0, 2).numpy()
+
+
+def small(seed=1, cnt=(5, 8, 1, 3, 8, 6), cap=8, Hq=4, Hkv=2, D=8, top_k=3, dtype="f32"):
+    return W.custom_block_workload(seed, list(cnt), cap, Hq, Hkv, D, dtype, top_k)
+
+
+# ---------------------------------------------------------------------------------------------
+# hand-worked fixtures
+# ---------------------------------------------------------------------------------------------
+
+def test_attend_hand_fixture():
+    fx = json.load(open(os.path.join(GOLDEN, "attend_hand.json")))
+    o, lse, wts = O.attend(np.array(fx["q"]), np.array(fx["k"]), np.array(fx["v"]), fx["scale"],
+                           return_weights=True)
+    np.testing.assert_allclose(o, fx["o"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, fx["lse"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(wts, fx["weights"], rtol=0, atol=1e-15)
+
+
+def test_route_hand_fixture():
+    fx = json.load(open(os.path.join(GOLDEN, "route_hand.json")))
+    for case in fx["cases"]:
+        sel, d2 = O.route_geometric(np.array(case["pts"], dtype=np.float32), np.array(case["blk_cnt"]),
+                                    np.array(case["blk_key"], dtype=np.uint32), case["cap"], case["top_k"])
+        assert sel.tolist() == case["sel"], case["name"]
+        assert d2.tolist() == case["d2"], case["name"]
+
+
+def test_sigmoid_closed_forms():
+    g = O.sigmoid(np.array([0.0, math.log(3.0), -math.log(3.0), np.inf, -np.inf, 800.0, -800.0]))
+    np.testing.assert_allclose(g, [0.5, 0.75, 0.25, 1.0, 0.0, 1.0, 0.0], rtol=0, atol=1e-15)
+    assert g[3] == 1.0 and g[4] == 0.0
+
+
+# ---------------------------------------------------------------------------------------------
+# attention branches against library attention
+# ---------------------------------------------------------------------------------------------
+
+def test_attend_matches_library_and_rows_sum_to_one():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((6, 8))
+    k = rng.standard_normal((11, 2, 8))
+    v = rng.standard_normal((11, 2, 8))
+    o, lse, wts = O.attend(q, k, v, 0.3, return_weights=True)
+    ref = sdpa(q[None], k, v, 0.3)[0]
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(wts.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+    assert (wts >= 0).all()
+    # lse is the log of the partition function
+    G = 3
+    for h in range(6):
+        s = 0.3 * k[:, h // G, :] @ q[h]
+        assert abs(lse[h] - math.log(np.exp(s).sum())) < 1e-12
+
+
+@pytest.mark.parametrize("name", ["tiny", "custom"])
+def test_dense_equivalence(name):
+    """top_k = n_blk with only the selected branch gated on reproduces dense attention."""
+    w = W.make("tiny") if name == "tiny" else small()
+    w.top_k = w.n_blk
+    w.gates = np.zeros_like(w.gates)
+    w.gates[..., 0] = -np.inf
+    w.gates[..., 1] = np.inf
+    w.gates[..., 2] = -np.inf
+    o = O.nsa_forward(w)
+    vs = w.valid_slots()
+    ref = sdpa(w.q[vs], w.k[vs], w.v[vs], w.scale)
+    np.testing.assert_allclose(o[vs], ref, rtol=0, atol=1e-12)
+    assert np.all(o[~w.valid_mask()] == 0)
+
+
+def test_local_branch_is_blockwise_attention():
+    w = small(seed=3)
+    o, lse = O.attn_branch(O.LOC, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale)
+    for b in range(w.n_blk):
+        s = O.block_slots(w.blk_cnt, w.blk_cap, b)
+        np.testing.assert_allclose(o[s], sdpa(w.q[s], w.k[s], w.v[s], w.scale), rtol=0, atol=1e-13)
+
+
+def test_compressed_branch_against_library_pooling():
+    w = small(seed=4)
+    kc = O.pool_blocks(w.k, w.blk_cnt, w.blk_cap)
+    vc = O.pool_blocks(w.v, w.blk_cnt, w.blk_cap)
+    # pooling against a scatter-mean from torch
+    vs = w.valid_slots()
+    seg = torch.from_numpy(vs // w.blk_cap)
+    for x, xc in ((w.k, kc), (w.v, vc)):
+        acc = torch.zeros((w.n_blk,) + x.shape[1:], dtype=torch.float64)
+        acc.index_add_(0, seg, torch.from_numpy(x[vs].astype(np.float64)))
+        cnt = torch.bincount(seg, minlength=w.n_blk).to(torch.float64)
+        np.testing.assert_allclose(xc, (acc / cnt[:, None, None]).numpy(), rtol=0, atol=1e-14)
+    o, _ = O.attn_branch(O.CMP, w.q, kc, vc, w.blk_cnt, w.blk_cap, w.scale)
+    np.testing.assert_allclose(o[vs], sdpa(w.q[vs], kc, vc, w.scale), rtol=0, atol=1e-13)
+
+
+def test_selected_branch_per_group_lists():
+    """Per-KV-group selection lists: each group attends exactly its own blocks."""
+    w = small(seed=5)
+    rng = np.random.default_rng(9)
+    S = w.n_slots
+    sel = np.full((S, 2, 3), -1, dtype=np.int32)
+    for r in range(S):
+        for j in range(2):
+            sel[r, j, :2] = rng.choice(w.n_blk, 2, replace=False)
+    o, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel)
+    for r in w.valid_slots()[:10]:
+        for j in range(2):
+            ks = np.concatenate([O.block_slots(w.blk_cnt, w.blk_cap, b) for b in sorted(sel[r, j, :2])])
+            ref = sdpa(w.q[r:r + 1, 2 * j:2 * j + 2], w.k[ks][:, j:j + 1], w.v[ks][:, j:j + 1], w.scale)
+            np.testing.assert_allclose(o[r, 2 * j:2 * j + 2], ref[0], rtol=0, atol=1e-13)
+
+
+def test_single_block_closed_forms():
+    w = small(seed=6, cnt=(7,), top_k=1)
+    vs = w.valid_slots()
+    kc = O.pool_blocks(w.k, w.blk_cnt, w.blk_cap)
+    vc = O.pool_blocks(w.v, w.blk_cnt, w.blk_cap)
+    o_cmp, _ = O.attn_branch(O.CMP, w.q, kc, vc, w.blk_cnt, w.blk_cap, w.scale)
+    # a one-key softmax has weight 1: the compressed branch returns the block mean of v
+    for r in vs:
+        np.testing.assert_allclose(o_cmp[r], np.repeat(w.v[vs].astype(np.float64).mean(0), 2, axis=0),
+                                   rtol=0, atol=1e-14)
+    sel = np.zeros((w.n_slots, 1), dtype=np.int32)
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel)
+    o_loc, _ = O.attn_branch(O.LOC, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale)
+    ref = sdpa(w.q[vs], w.k[vs], w.v[vs], w.scale)
+    np.testing.assert_allclose(o_sel[vs], ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(o_loc[vs], ref, rtol=0, atol=1e-13)
+
+
+def test_constant_values_closed_form():
+    w = small(seed=7)
+    w.v[:] = 0.0
+    vs = w.valid_slots()
+    w.v[vs] = np.array([0.5, -1.25, 2.0, 0.0, 3.5, -0.75, 1.0, 4.0], dtype=np.float32)
+    o = O.nsa_forward(w)
+    gsum = O.sigmoid(w.gates[vs]).sum(axis=2)          # [n, Hq]
+    ref = gsum[:, :, None] * w.v[vs][:, :1, :].astype(np.float64)
+    np.testing.assert_allclose(o[vs], ref, rtol=0, atol=1e-13)
+
+
+def test_gate_combine_selects_single_branch():
+    rng = np.random.default_rng(1)
+    outs = [rng.standard_normal((5, 4, 3)) for _ in range(3)]
+    for c in range(3):
+        g = np.full((5, 4, 3), -np.inf)
+        g[..., c] = np.inf
+        np.testing.assert_array_equal(O.gate_combine(outs, g), outs[c])
+    g = np.zeros((5, 4, 3))
+    np.testing.assert_allclose(O.gate_combine(outs, g), 0.5 * (outs[0] + outs[1] + outs[2]), atol=1e-15)
+
+
+# ---------------------------------------------------------------------------------------------
+# storage-order invariance of the whole layer
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_storage_permutation_invariance(seed):
+    w = W.make("tiny") if seed == 0 else small(seed=11)
+    o1, p1 = O.nsa_forward(w, return_parts=True)
+    w2, smap = W.permute_storage(w, seed=100 + seed)
+    o2, p2 = O.nsa_forward(w2, return_parts=True)
+    new = np.nonzero(smap >= 0)[0]
+    np.testing.assert_allclose(o2[new], o1[smap[new]], rtol=0, atol=1e-12)
+    # routed blocks, named by blk_key, are identical
+    keys1 = np.where(p1["sel"] >= 0, w.blk_key[p1["sel"]], 0)
+    keys2 = np.where(p2["sel"] >= 0, w2.blk_key[p2["sel"]], 0)
+    np.testing.assert_array_equal(keys2[new], keys1[smap[new]])
+
+
+# ---------------------------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------------------------
+
+def brute_route(pts, blk_cnt, blk_key, cap, k):
+    """Pure-Python brute force over real-valued points: quantise, average, sort tuples."""
+    n_blk = len(blk_cnt)
+    members = [[b * cap + i for i in range(blk_cnt[b])] for b in range(n_blk)]
+    lat = lambda x: int(round(4096 * float(x))) + 4096  # noqa: E731  (exact: 4096*x is a float64)
+    cents = []
+    for b in range(n_blk):
+        c = []
+        for ax in range(3):
+            tot = sum(lat(pts[s][ax]) for s in members[b])
+            n = blk_cnt[b]
+            c.append((2 * tot + n) // (2 * n))
+        cents.append(c)
+    out = {}
+    for b in range(n_blk):
+        for s in members[b]:
+            u = [lat(pts[s][ax]) for ax in range(3)]
+            cand = sorted((sum((u[a] - cents[c][a]) ** 2 for a in range(3)), int(blk_key[c]), c)
+                          for c in range(n_blk))
+            out[s] = [c for _, _, c in cand[:k]]
+    return out
+
+
+@pytest.mark.parametrize("mode", ["random", "lattice"])
+def test_geometric_routing_brute_force(mode):
+    if mode == "random":
+        w = W.custom_block_workload(21, [5, 8, 1, 3, 8, 6, 2, 7, 8], 8, 4, 2, 8, "f32", 4, pts_mode=mode)
+    else:
+        # one token per block on a coarse lattice: centroids coincide with lattice points
+        w = W.custom_block_workload(21, [1] * 40, 1, 4, 2, 8, "f32", 6, pts_mode=mode)
+    sel, d2 = O.route_geometric(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k)
+    ref = brute_route(w.pts.tolist(), w.blk_cnt.tolist(), w.blk_key, w.blk_cap, w.top_k)
+    for s in range(w.n_slots):
+        if s in ref:
+            assert sel[s].tolist() == ref[s]
+        else:
+            assert (sel[s] == -1).all()
+    if mode == "lattice":
+        # the lattice inputs do create exact distance ties among the top candidates
+        assert any(len(set(row[:4].tolist())) < 4 for row in d2[w.valid_mask()])
+
+
+def test_geometric_routing_own_block_first_in_full_grid():
+    """In a full voxel grid partitioned into 4^3 cells the centroids form a cubic lattice, so every
+    voxel's nearest centroid is its own cell's (Voronoi cell of a cubic lattice)."""
+    side = 16
+    g = np.arange(side)
+    zz, yy, xx = np.meshgrid(g, g, g, indexing="ij")
+    vox = np.stack([xx.ravel(), yy.ravel(), zz.ravel()], axis=1)
+    cell = W.morton3(vox[:, 0] // 4, vox[:, 1] // 4, vox[:, 2] // 4)
+    order = np.lexsort((W.morton3(vox[:, 0], vox[:, 1], vox[:, 2]), cell))
+    pts = (-1.0 + (2.0 * vox[order] + 1.0) / side).astype(np.float32)
+    n_blk = (side // 4) ** 3
+    blk_cnt = np.full(n_blk, 64, dtype=np.int32)
+    blk_key = np.arange(n_blk, dtype=np.uint32)
+    sel, d2 = O.route_geometric(pts, blk_cnt, blk_key, 64, 1)
+    np.testing.assert_array_equal(sel[:, 0], np.arange(n_blk * 64) // 64)
+
+
+def test_geometric_routing_k_beyond_blocks():
+    w = small(seed=8)
+    sel, d2 = O.route_geometric(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.n_blk + 3)
+    vm = w.valid_mask()
+    assert (sel[vm][:, w.n_blk:] == -1).all()
+    assert (d2[vm][:, w.n_blk:] == 0xFFFFFFFF).all()
+    for row in sel[vm]:
+        assert sorted(row[:w.n_blk].tolist()) == list(range(w.n_blk))
+
+
+def test_score_routing_exact_on_integer_inputs():
+    """One query head per KV head: integer-valued inputs make every score exact; compare with a
+    pure-Python sort of (-score, key)."""
+    rng = np.random.default_rng(3)
+    R, H, D, n_blk, k = 7, 3, 4, 12, 5
+    q = rng.integers(-3, 4, size=(R, H, D)).astype(np.float64)
+    kc = rng.integers(-3, 4, size=(n_blk, H, D)).astype(np.float64)
+    key = rng.permutation(n_blk).astype(np.uint32) + 100
+    sel, imp = O.route_scores(q, kc, key, 0.5, k)
+    for r in range(R):
+        for h in range(H):
+            sc = [(-int(sum(q[r, h, d] * kc[b, h, d] for d in range(D))), int(key[b]), b) for b in range(n_blk)]
+            assert sel[r, h].tolist() == [b for _, _, b in sorted(sc)[:k]]
+
+
+def test_grouped_score_routing_importance_sums_to_group_size():
+    """With lse from the compressed branch, each head's probabilities over all blocks sum to one, so a
+    group's summed importance over all blocks equals the group size."""
+    w = small(seed=12)
+    kc = O.pool_blocks(w.k, w.blk_cnt, w.blk_cap)
+    vc = O.pool_blocks(w.v, w.blk_cnt, w.blk_cap)
+    vs = w.valid_slots()
+    _, lse = O.attn_branch(O.CMP, w.q, kc, vc, w.blk_cnt, w.blk_cap, w.scale, rows=vs)
+    sel, imp = O.route_scores(w.q[vs], kc, w.blk_key, w.scale, 3, lse=lse)
+    np.testing.assert_allclose(imp.sum(axis=2), 2.0, rtol=0, atol=1e-12)
+    # the selection holds the largest importances
+    for r in range(len(vs)):
+        for j in range(2):
+            kth = np.sort(imp[r, j])[::-1][2]
+            assert (imp[r, j, sel[r, j]] >= kth).all()
+
+
+# ---------------------------------------------------------------------------------------------
+# stage-1 dense gated self/cross attention
+# ---------------------------------------------------------------------------------------------
+
+def test_dense_gated_reduces_to_library_attention():
+    w = W.make("dense_small", dtype="f32")
+    N, nx = w.n_tok, w.n_x
+    rows = np.array([0, 1, nx - 1, nx, nx + 5, N - 1])
+    g = np.zeros_like(w.gates)
+    g[..., 0], g[..., 1] = np.inf, -np.inf
+    o = O.dense_gated_xattn(w.q, w.k, w.v, nx, g, w.scale, rows=rows)
+    for i, t in enumerate(rows):
+        own = slice(0, nx) if t < nx else slice(nx, N)
+        np.testing.assert_allclose(o[i], sdpa(w.q[t:t + 1], w.k[own], w.v[own], w.scale)[0], atol=1e-13)
+    g[..., 0], g[..., 1] = -np.inf, np.inf
+    o = O.dense_gated_xattn(w.q, w.k, w.v, nx, g, w.scale, rows=rows)
+    for i, t in enumerate(rows):
+        oth = slice(nx, N) if t < nx else slice(0, nx)
+        np.testing.assert_allclose(o[i], sdpa(w.q[t:t + 1], w.k[oth], w.v[oth], w.scale)[0], atol=1e-13)
+    # all tokens of one type: the cross term is empty and contributes nothing
+    g = w.gates.copy()
+    o = O.dense_gated_xattn(w.q, w.k, w.v, N, g, w.scale, rows=rows)
+    ref = O.sigmoid(g[rows][..., 0:1]) * sdpa(w.q[rows], w.k, w.v, w.scale)
+    np.testing.assert_allclose(o, ref, atol=1e-13)
+
+
+def test_dense_gated_swap_symmetry():
+    w = W.make("dense_small", dtype="f32")
+    N, nx = w.n_tok, w.n_x
+    perm = np.concatenate([np.arange(nx, N), np.arange(0, nx)])     # image tokens first
+    rows = np.array([0, 7, nx, N - 1])
+    o1 = O.dense_gated_xattn(w.q, w.k, w.v, nx, w.gates, w.scale, rows=rows)
+    inv = np.argsort(perm)
+    o2 = O.dense_gated_xattn(w.q[perm], w.k[perm], w.v[perm], N - nx, w.gates[perm], w.scale,
+                             rows=inv[rows])
+    np.testing.assert_allclose(o2, o1, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------------
+# pooling
+# ---------------------------------------------------------------------------------------------
+
+def test_pool_identity_linearity_constant():
+    rng = np.random.default_rng(2)
+    cnt = np.array([1, 4, 2, 1])
+    x = rng.standard_normal((16, 3, 5))
+    y = rng.standard_normal((16, 3, 5))
+    p = O.pool_blocks(x, cnt, 4)
+    np.testing.assert_array_equal(p[0], x[0])
+    np.testing.assert_array_equal(p[3], x[12])
+    np.testing.assert_allclose(O.pool_blocks(2 * x - 3 * y, cnt, 4), 2 * p - 3 * O.pool_blocks(y, cnt, 4),
+                               atol=1e-14)
+    c = np.full((16, 3, 5), 1.75)
+    np.testing.assert_array_equal(O.pool_blocks(c, cnt, 4), np.full((4, 3, 5), 1.75))
