@@ -1,0 +1,181 @@
+/*
+ * libnsa — Native Sparse Attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a DEVICE pointer unless it is marked "host".  Every call only
+ * validates its arguments on the host and enqueues kernels on the caller's stream: NSA_OK means
+ * "enqueued", not "finished".  The library never allocates, frees or synchronises, keeps no
+ * per-call state, and is safe to call from several host threads.  The caller owns every buffer.
+ *
+ * Status convention for every call:
+ *   NSA_ERR_INVALID      a null pointer, a non-positive size, inconsistent sizes (e.g. n_qh not a
+ *                        multiple of n_kvh) or a value outside the documented range; nothing is
+ *                        launched and no output is touched;
+ *   NSA_ERR_UNSUPPORTED  a valid request outside the compiled kernel set (see each call);
+ *                        nothing is launched;
+ *   NSA_ERR_HIP          a HIP launch error; outputs are unspecified.
+ * nsa_last_error() returns a thread-local, human-readable reason for the last non-OK status.
+ *
+ * Token storage is BLOCK-MAJOR (the spatial block partition of the LSRM pages: hyper.ai summary
+ * of arXiv 2604.05182, section 方法, block paragraph): block b owns the slots
+ * [b*blk_cap, b*blk_cap + blk_cnt[b]); the other slots of the block are padding.  S = n_blk*blk_cap.
+ * Tensors are row-major and contiguous:  q [S][n_qh][D],  k, v [S][n_kvh][D],
+ * pooled x_cmp [n_blk][H][D],  gate logits [rows][n_qh][channels],  points [S][3].
+ * Query head h reads KV head h / (n_qh / n_kvh) (grouped-query attention of the LSRM pages,
+ * dense-transformer paragraph: 32 query heads share 2 KV heads).
+ * Padding slots are never read as keys or queries; every output row of a padding slot is written
+ * as 0 (attention, gate), -1 (routing indices) or -inf (lse).
+ * Device-side preconditions (not checked on the host): 1 <= blk_cnt[b] <= blk_cap; blk_key values
+ * are unique; points lie in [-1, 1]; routing indices are -1 or in [0, n_blk).
+ */
+#ifndef NSA_H
+#define NSA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NSA_OK = 0,
+  NSA_ERR_INVALID = -1,
+  NSA_ERR_UNSUPPORTED = -2,
+  NSA_ERR_HIP = -3
+} nsa_status;
+
+typedef enum { NSA_F32 = 0, NSA_BF16 = 1 } nsa_dtype;   /* element type of q, k, v, o, gates */
+
+/* Branch bits for nsa_attn_fwd. */
+enum {
+  NSA_BR_CMP = 1,   /* compressed branch: all pooled blocks                              */
+  NSA_BR_SEL = 2,   /* selected branch: the blocks of the routing table                  */
+  NSA_BR_LOC = 4    /* local (window) branch: the query's own block                      */
+};
+
+typedef enum {
+  NSA_Q_TOKEN = 0,  /* routing rows and compressed-branch queries are per token           */
+  NSA_Q_BLOCK = 1   /* per block: pooled queries for the compressed branch (output given  */
+                    /* to every valid token of the block), one routing row per block      */
+} nsa_qgran;
+
+/* Host struct describing the block-major layout.  blk_cnt and blk_key are DEVICE arrays. */
+typedef struct {
+  int32_t n_blk;            /* >= 1                                                          */
+  int32_t blk_cap;          /* 1..64                                                         */
+  int32_t n_qh, n_kvh;      /* n_qh % n_kvh == 0                                             */
+  int32_t head_dim;         /* D                                                             */
+  float scale;              /* softmax scale, callers pass 1/sqrt(D); > 0                    */
+  const int32_t* blk_cnt;   /* [n_blk] valid tokens per block, 1..blk_cap                    */
+  const uint32_t* blk_key;  /* [n_blk] unique logical block ids; the routing tie-break order */
+} nsa_layout;
+
+/*
+ * Block compression.  LSRM pages, section 方法, eq. k^cmp = AvgPool(ResBlock(k_t)) (ResBlock taken
+ * as the identity); Speed3R page (arXiv 2603.08055 summary), section 2.1, 4x4 average pooling of
+ * Q/K/V.  x_cmp[b][h][:] = mean of x[s][h][:] over the valid slots s of block b, accumulated in
+ * fp32 and rounded to `dtype`.
+ *   x      [S][n_heads][head_dim]      x_cmp  [n_blk][n_heads][head_dim]
+ * n_heads * head_dim <= 1024.
+ */
+nsa_status nsa_pool_blocks(const nsa_layout* layout, nsa_dtype dtype, int32_t n_heads,
+                           const void* x, void* x_cmp, hipStream_t stream);
+
+/*
+ * 3D-aware geometric routing.  LSRM pages, section 方法, routing paragraph (and the Korean summary,
+ * section 2.2): each query token keeps the blocks whose centres lie nearest to its 3D point.
+ * Exact integer form: u = rint(4096*p) + 4096 per axis; block centroid
+ * c_b = floor((2*sum u + cnt_b) / (2*cnt_b)); d2 = |u_t - c_b|^2 (< 2^28).  Each valid token gets
+ * the top_k blocks in ascending (d2, blk_key) order, best first.  One list per token, shared by all
+ * heads.
+ *   pts        [S][3] float32 in [-1, 1]
+ *   centroids  [n_blk][4] int32 workspace and output: (cx, cy, cz, blk_key bits)
+ *   sel        [S][top_k] int32 storage block indices; -1 on padding rows and beyond n_blk
+ *   sel_d2     [S][top_k] uint32 or NULL; 0xFFFFFFFF where sel is -1
+ * 1 <= top_k <= 64.
+ */
+nsa_status nsa_route_geometric(const nsa_layout* layout, const float* pts, int32_t top_k,
+                               int32_t* centroids, int32_t* sel, uint32_t* sel_d2,
+                               hipStream_t stream);
+
+/*
+ * Score routing against the compressed keys ("standard NSA" selection the LSRM pages compare
+ * with; Speed3R page, section 2.1, top-K from the compressed score matrix), without storing the
+ * score matrix.
+ *   G = n_qh/n_kvh > 1: importance of block b for (row r, group j) is
+ *       sum over the group's heads h of exp(scale*<q[r][h], k_cmp[b][j]> - lse[r][h]);
+ *   G == 1: importance of block b for (row r, head h) is <q[r][h], k_cmp[b][h]>.
+ * Blocks are ranked by descending importance, ties by ascending blk_key.
+ *   q_gran NSA_Q_TOKEN: rows = S, q [S][n_qh][D] (padding rows get -1)
+ *   q_gran NSA_Q_BLOCK: rows = n_blk, q is the pooled query [n_blk][n_qh][D]
+ *   k_cmp [n_blk][n_kvh][D];  lse [rows][n_qh] float32 natural-log partition function of the
+ *   compressed branch (required iff G > 1);  sel [rows][n_kvh][top_k] int32.
+ * Supported: (D, G) = (32, 16) with q_gran TOKEN; 1 <= top_k <= 64; n_blk <= 65536.
+ */
+nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_qgran q_gran,
+                                 const void* q, const void* k_cmp, const float* lse,
+                                 int32_t top_k, int32_t* sel, hipStream_t stream);
+
+/*
+ * NSA attention branches, optionally gated and fused.  LSRM pages, section 方法: compressed block
+ * features give global coarse context, selected blocks give fine detail, window attention runs
+ * inside a block; Speed3R page, section 2.1: a learned gate combines the branches.
+ * For query row r, head h and the key set K of a branch:
+ *     o_h = sum_{i in K} softmax_i(scale * <q_h, k_i>) v_i        (empty K gives o_h = 0)
+ *   CMP: K = every pooled block (k_cmp, v_cmp); queries are q (NSA_Q_TOKEN) or the block's pooled
+ *        query q_cmp (NSA_Q_BLOCK, result given to each valid token of the block);
+ *   SEL: K = valid tokens of the blocks in the routing row (duplicates count once, -1 skipped);
+ *        rows are per token (NSA_Q_TOKEN) or per block (NSA_Q_BLOCK);
+ *        sel_groups == 1: sel [rows][top_k] shared by all heads;
+ *        sel_groups == n_kvh: sel [rows][n_kvh][top_k], head h uses group h / (n_qh/n_kvh);
+ *   LOC: K = valid tokens of the query's own block.
+ * `branches` is a non-empty OR of NSA_BR_* bits.  If gate_logits is NULL, exactly one branch must
+ * be named and o receives it.  Otherwise o = sum over the named branches c of
+ * sigmoid(gate_logits[s][h][ch(c)]) * o_c, where ch(c) is c's rank among the named branches in the
+ * order CMP, SEL, LOC and gate_logits is [S][n_qh][popcount(branches)] in `dtype`.
+ *   q [S][n_qh][D]; k, v [S][n_kvh][D] (SEL, LOC); q_cmp [n_blk][n_qh][D] (CMP with NSA_Q_BLOCK);
+ *   k_cmp, v_cmp [n_blk][n_kvh][D] (CMP); unused pointers may be NULL.  o [S][n_qh][D].
+ *   lse: NULL, or (single branch only) float32 [rows][n_qh] natural-log partition function,
+ *        rows = n_blk for CMP with NSA_Q_BLOCK, else S; -inf on padding rows and empty key sets.
+ * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16; NSA_Q_TOKEN; top_k <= 64; n_blk <= 65536
+ * when SEL is named.  Accumulation is fp32; bf16 probabilities feed the value product.
+ */
+nsa_status nsa_attn_fwd(const nsa_layout* layout, nsa_dtype dtype, uint32_t branches,
+                        nsa_qgran q_gran, const void* q, const void* k, const void* v,
+                        const void* q_cmp, const void* k_cmp, const void* v_cmp,
+                        const int32_t* sel, int32_t top_k, int32_t sel_groups,
+                        const void* gate_logits, void* o, float* lse, hipStream_t stream);
+
+/*
+ * Sigmoid-gated sum of branch outputs (LSRM pages, section 方法, Sigmoid gates; Speed3R page,
+ * section 2.1, gated aggregation), as a standalone pass:
+ *     o[r][h][:] = sum_c sigmoid(gate_logits[r][h][c]) * o_branch[c][r][h][:]
+ *   o_branch   host array of n_branch device pointers, each [n_rows][n_qh][head_dim]
+ *   gate_logits [n_rows][n_qh][n_branch];  o [n_rows][n_qh][head_dim];  1 <= n_branch <= 8.
+ */
+nsa_status nsa_gate_combine(nsa_dtype dtype, int32_t n_rows, int32_t n_qh, int32_t head_dim,
+                            int32_t n_branch, const void* const* o_branch,
+                            const void* gate_logits, void* o, hipStream_t stream);
+
+/*
+ * Stage-1 dense gated self/cross attention (LSRM pages, section 方法, eq. o^x and o^y):
+ * tokens [0, n_x) are volume tokens x, [n_x, n_tok) image tokens y, and
+ *     o_t = sigmoid(g[t][h][0]) * Attn(q_t; keys of t's own type)
+ *         + sigmoid(g[t][h][1]) * Attn(q_t; keys of the other type),
+ * an empty key set contributing 0.  q [n_tok][n_qh][D]; k, v [n_tok][n_kvh][D];
+ * gate_logits [n_tok][n_qh][2]; o [n_tok][n_qh][D].  0 <= n_x <= n_tok.
+ * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16.
+ */
+nsa_status dense_gated_xattn_fwd(nsa_dtype dtype, int32_t n_tok, int32_t n_x, int32_t n_qh,
+                                 int32_t n_kvh, int32_t head_dim, float scale, const void* q,
+                                 const void* k, const void* v, const void* gate_logits, void* o,
+                                 hipStream_t stream);
+
+/* Thread-local description of the last non-OK status returned on this thread (host string). */
+const char* nsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_H */

@@ -1,0 +1,199 @@
+"""Python binding of libnsa (NSA forward pass for MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of libnsa.so.  Tensors are torch
+tensors on the GPU (PyTorch provides device memory and the current stream); each function checks
+shapes, dtypes and contiguity, then calls the C ABI declared in include/nsa.h with raw pointers.
+There is no CPU fallback: importing this package fails if the library has not been built, and any
+call with tensors that are not on a GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnsa.so")
+
+NSA_OK, NSA_ERR_INVALID, NSA_ERR_UNSUPPORTED, NSA_ERR_HIP = 0, -1, -2, -3
+NSA_F32, NSA_BF16 = 0, 1
+BR_CMP, BR_SEL, BR_LOC = 1, 2, 4
+Q_TOKEN, Q_BLOCK = 0, 1
+EXPORTS = ("nsa_pool_blocks", "nsa_route_geometric", "nsa_route_scores_topk", "nsa_attn_fwd",
+           "nsa_gate_combine", "dense_gated_xattn_fwd", "nsa_last_error")
+
+
+class NsaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("libnsa status %d: %s" % (status, msg))
+        self.status = status
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("n_blk", ctypes.c_int32), ("blk_cap", ctypes.c_int32), ("n_qh", ctypes.c_int32),
+                ("n_kvh", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("blk_cnt", ctypes.c_void_p), ("blk_key", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libnsa.so is not built; run `python __graft_entry__.py` or "
+                          "`python sparse_attention_feed_amd/build.py` first (%s)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, U, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
+    LP = ctypes.POINTER(Layout)
+    sig = {
+        "nsa_pool_blocks": [LP, I, I, P, P, P],
+        "nsa_route_geometric": [LP, P, I, P, P, P, P],
+        "nsa_route_scores_topk": [LP, I, I, P, P, P, I, P, P],
+        "nsa_attn_fwd": [LP, I, U, I, P, P, P, P, P, P, P, I, I, P, P, P, P],
+        "nsa_gate_combine": [I, I, I, I, I, ctypes.POINTER(ctypes.c_void_p), P, P, P],
+        "dense_gated_xattn_fwd": [I, I, I, I, I, I, F, P, P, P, P, P, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.nsa_last_error.argtypes = []
+    lib.nsa_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != NSA_OK:
+        raise NsaError(status, lib.nsa_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libnsa needs GPU tensors")
+    if not t.is_contiguous():
+        raise ValueError("libnsa needs contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return NSA_BF16
+    if t.dtype == torch.float32:
+        return NSA_F32
+    raise ValueError("unsupported dtype %s" % t.dtype)
+
+
+class BlockLayout:
+    """Block-major token layout: blk_cnt / blk_key device tensors plus the head shape."""
+
+    def __init__(self, blk_cnt, blk_key, blk_cap, n_qh, n_kvh, head_dim, scale=None):
+        self.blk_cnt = blk_cnt
+        self.blk_key = blk_key
+        self.blk_cap = int(blk_cap)
+        self.n_blk = int(blk_cnt.shape[0])
+        self.n_qh, self.n_kvh, self.head_dim = int(n_qh), int(n_kvh), int(head_dim)
+        self.scale = float(scale) if scale is not None else 1.0 / math.sqrt(head_dim)
+        if blk_cnt.dtype != torch.int32:
+            raise ValueError("blk_cnt must be int32")
+        if blk_key is not None and blk_key.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("blk_key must be 32-bit")
+        self._c = Layout(self.n_blk, self.blk_cap, self.n_qh, self.n_kvh, self.head_dim, self.scale,
+                         _ptr(blk_cnt), _ptr(blk_key) if blk_key is not None else None)
+
+    @property
+    def n_slots(self):
+        return self.n_blk * self.blk_cap
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def pool_blocks(layout: BlockLayout, x, out=None):
+    """Mean of each block's valid token rows: x [S, H, D] -> [n_blk, H, D]."""
+    S, H, D = x.shape
+    assert S == layout.n_slots and D == layout.head_dim
+    if out is None:
+        out = torch.empty((layout.n_blk, H, D), dtype=x.dtype, device=x.device)
+    _check(lib.nsa_pool_blocks(layout.c, _dtype(x), H, _ptr(x), _ptr(out), _stream()))
+    return out
+
+
+def route_geometric(layout: BlockLayout, pts, top_k, sel=None, sel_d2=None, centroids=None, want_d2=True):
+    """Top-k nearest blocks per token on the integer lattice; returns (sel, sel_d2, centroids)."""
+    S = layout.n_slots
+    assert pts.shape == (S, 3) and pts.dtype == torch.float32
+    dev = pts.device
+    if sel is None:
+        sel = torch.empty((S, top_k), dtype=torch.int32, device=dev)
+    if want_d2 and sel_d2 is None:
+        sel_d2 = torch.empty((S, top_k), dtype=torch.int32, device=dev)
+    if centroids is None:
+        centroids = torch.empty((layout.n_blk, 4), dtype=torch.int32, device=dev)
+    _check(lib.nsa_route_geometric(layout.c, _ptr(pts), int(top_k), _ptr(centroids), _ptr(sel),
+                                   _ptr(sel_d2) if want_d2 else None, _stream()))
+    return sel, sel_d2, centroids
+
+
+def route_scores_topk(layout: BlockLayout, q, k_cmp, lse, top_k, q_gran=Q_TOKEN, sel=None):
+    rows = layout.n_slots if q_gran == Q_TOKEN else layout.n_blk
+    if sel is None:
+        sel = torch.empty((rows, layout.n_kvh, top_k), dtype=torch.int32, device=q.device)
+    _check(lib.nsa_route_scores_topk(layout.c, _dtype(q), int(q_gran), _ptr(q), _ptr(k_cmp),
+                                     _ptr(lse), int(top_k), _ptr(sel), _stream()))
+    return sel
+
+
+def attn_fwd(layout: BlockLayout, branches, q, k=None, v=None, q_cmp=None, k_cmp=None, v_cmp=None,
+             sel=None, top_k=0, sel_groups=1, gates=None, out=None, lse=None, q_gran=Q_TOKEN):
+    """NSA branches (bitmask of BR_CMP | BR_SEL | BR_LOC), gated and fused when gates is given."""
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.nsa_attn_fwd(layout.c, _dtype(q), int(branches), int(q_gran), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(q_cmp), _ptr(k_cmp), _ptr(v_cmp), _ptr(sel), int(top_k), int(sel_groups),
+                            _ptr(gates), _ptr(out), _ptr(lse), _stream()))
+    return out
+
+
+def gate_combine(outs, gates, out=None):
+    n_rows, n_qh, D = outs[0].shape
+    if out is None:
+        out = torch.empty_like(outs[0])
+    arr = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
+    _check(lib.nsa_gate_combine(_dtype(outs[0]), n_rows, n_qh, D, len(outs), arr, _ptr(gates), _ptr(out),
+                                _stream()))
+    return out
+
+
+def dense_gated_xattn(q, k, v, n_x, gates, scale=None, out=None):
+    n_tok, n_qh, D = q.shape
+    n_kvh = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.dense_gated_xattn_fwd(_dtype(q), n_tok, int(n_x), n_qh, n_kvh, D, float(scale), _ptr(q),
+                                     _ptr(k), _ptr(v), _ptr(gates), _ptr(out), _stream()))
+    return out
+
+
+def nsa_layer(layout: BlockLayout, q, k, v, pts, gates, top_k, ws=None):
+    """One geometric-routed NSA layer: pool K and V, route, then the fused three-branch attention
+    with the sigmoid gate.  `ws` may hold preallocated k_cmp, v_cmp, sel, centroids and out."""
+    ws = {} if ws is None else ws
+    k_cmp = pool_blocks(layout, k, ws.get("k_cmp"))
+    v_cmp = pool_blocks(layout, v, ws.get("v_cmp"))
+    sel, _, cent = route_geometric(layout, pts, top_k, sel=ws.get("sel"), centroids=ws.get("centroids"),
+                                   want_d2=False)
+    o = attn_fwd(layout, BR_CMP | BR_SEL | BR_LOC, q, k, v, k_cmp=k_cmp, v_cmp=v_cmp, sel=sel, top_k=top_k,
+                 sel_groups=1, gates=gates, out=ws.get("out"))
+    ws.update(k_cmp=k_cmp, v_cmp=v_cmp, sel=sel, centroids=cent, out=o)
+    return o

@@ -1,0 +1,234 @@
+// C ABI of libnsa: host-side argument validation and kernel dispatch (see include/nsa.h).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/nsa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+nsa_status fail(nsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+// A launch failure can be forced from the host (NSA_FORCE_HIP_ERROR=1) to test error handling
+// without any device work.
+bool forced_hip_error() {
+  const char* e = getenv("NSA_FORCE_HIP_ERROR");
+  return e != nullptr && e[0] == '1';
+}
+
+nsa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(NSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return NSA_OK;
+}
+
+// Every entry point calls this after validation and before any HIP call.
+#define NSA_FORCED_FAILURE(fn)                                                                 \
+  do {                                                                                         \
+    if (forced_hip_error()) return fail(NSA_ERR_HIP, "%s: launch failure forced by NSA_FORCE_HIP_ERROR", fn); \
+  } while (0)
+
+nsa_status check_layout(const nsa_layout* L, const char* fn) {
+  if (L == nullptr) return fail(NSA_ERR_INVALID, "%s: layout is NULL", fn);
+  if (L->n_blk < 1) return fail(NSA_ERR_INVALID, "%s: n_blk must be >= 1 (got %d)", fn, L->n_blk);
+  if (L->blk_cap < 1 || L->blk_cap > 64)
+    return fail(NSA_ERR_INVALID, "%s: blk_cap must be in 1..64 (got %d)", fn, L->blk_cap);
+  if (L->n_qh < 1 || L->n_kvh < 1 || L->n_qh % L->n_kvh != 0)
+    return fail(NSA_ERR_INVALID, "%s: n_qh (%d) must be a positive multiple of n_kvh (%d)", fn, L->n_qh, L->n_kvh);
+  if (L->head_dim < 1) return fail(NSA_ERR_INVALID, "%s: head_dim must be >= 1", fn);
+  if (!(L->scale > 0.f) || L->scale > 1e30f) return fail(NSA_ERR_INVALID, "%s: scale must be a positive finite value", fn);
+  if (L->blk_cnt == nullptr) return fail(NSA_ERR_INVALID, "%s: blk_cnt is NULL", fn);
+  if ((long long)L->n_blk * L->blk_cap > 0x7FFFFFFFLL) return fail(NSA_ERR_INVALID, "%s: too many slots", fn);
+  return NSA_OK;
+}
+
+bool dtype_ok(nsa_dtype d) { return d == NSA_F32 || d == NSA_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* nsa_last_error(void) { return g_err; }
+
+nsa_status nsa_pool_blocks(const nsa_layout* L, nsa_dtype dtype, int32_t n_heads, const void* x,
+                           void* x_cmp, hipStream_t stream) {
+  nsa_status st = check_layout(L, "nsa_pool_blocks");
+  if (st != NSA_OK) return st;
+  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "nsa_pool_blocks: unknown dtype %d", (int)dtype);
+  if (x == nullptr || x_cmp == nullptr) return fail(NSA_ERR_INVALID, "nsa_pool_blocks: x or x_cmp is NULL");
+  if (n_heads < 1) return fail(NSA_ERR_INVALID, "nsa_pool_blocks: n_heads must be >= 1");
+  if ((long long)n_heads * L->head_dim > 1024)
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_pool_blocks: n_heads * head_dim must be <= 1024");
+  NSA_FORCED_FAILURE("nsa_pool_blocks");
+  return hip_status(nsa::launch_pool(dtype == NSA_BF16, x, x_cmp, L->blk_cnt, L->n_blk, L->blk_cap, n_heads,
+                                     L->head_dim, stream),
+                    "nsa_pool_blocks");
+}
+
+nsa_status nsa_route_geometric(const nsa_layout* L, const float* pts, int32_t top_k, int32_t* centroids,
+                               int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
+  nsa_status st = check_layout(L, "nsa_route_geometric");
+  if (st != NSA_OK) return st;
+  if (pts == nullptr || centroids == nullptr || sel == nullptr || L->blk_key == nullptr)
+    return fail(NSA_ERR_INVALID, "nsa_route_geometric: pts, centroids, sel and blk_key must be non-NULL");
+  if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "nsa_route_geometric: top_k must be in 1..64 (got %d)", top_k);
+  NSA_FORCED_FAILURE("nsa_route_geometric");
+  nsa::RouteArgs a;
+  a.pts = pts;
+  a.blk_cnt = L->blk_cnt;
+  a.blk_key = L->blk_key;
+  a.cent = centroids;
+  a.sel = sel;
+  a.sel_d2 = sel_d2;
+  a.n_blk = L->n_blk;
+  a.cap = L->blk_cap;
+  a.top_k = top_k;
+  return hip_status(nsa::launch_route_geometric(a, stream), "nsa_route_geometric");
+}
+
+nsa_status nsa_route_scores_topk(const nsa_layout* L, nsa_dtype dtype, nsa_qgran q_gran, const void* q,
+                                 const void* k_cmp, const float* lse, int32_t top_k, int32_t* sel,
+                                 hipStream_t stream) {
+  nsa_status st = check_layout(L, "nsa_route_scores_topk");
+  if (st != NSA_OK) return st;
+  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "nsa_route_scores_topk: unknown dtype");
+  if (q_gran != NSA_Q_TOKEN && q_gran != NSA_Q_BLOCK) return fail(NSA_ERR_INVALID, "nsa_route_scores_topk: bad q_gran");
+  if (q == nullptr || k_cmp == nullptr || sel == nullptr || L->blk_key == nullptr)
+    return fail(NSA_ERR_INVALID, "nsa_route_scores_topk: q, k_cmp, sel and blk_key must be non-NULL");
+  if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "nsa_route_scores_topk: top_k must be in 1..64");
+  const int G = L->n_qh / L->n_kvh;
+  if (G > 1 && lse == nullptr) return fail(NSA_ERR_INVALID, "nsa_route_scores_topk: lse is required when n_qh > n_kvh");
+  if (L->head_dim != 32 || G != 16 || q_gran != NSA_Q_TOKEN)
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: compiled for head_dim 32, 16 query heads per KV head, per-token rows");
+  if (L->n_blk > 65536) return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: n_blk must be <= 65536");
+  NSA_FORCED_FAILURE("nsa_route_scores_topk");
+  nsa::ScoreRouteArgs a;
+  a.q = q;
+  a.k_cmp = k_cmp;
+  a.lse = lse;
+  a.blk_cnt = L->blk_cnt;
+  a.blk_key = L->blk_key;
+  a.sel = sel;
+  a.n_rows = L->n_blk * L->blk_cap;
+  a.n_blk = L->n_blk;
+  a.cap = L->blk_cap;
+  a.n_qh = L->n_qh;
+  a.n_kvh = L->n_kvh;
+  a.top_k = top_k;
+  a.scale = L->scale;
+  return hip_status(nsa::launch_route_scores(dtype == NSA_BF16, a, stream), "nsa_route_scores_topk");
+}
+
+nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches, nsa_qgran q_gran,
+                        const void* q, const void* k, const void* v, const void* q_cmp, const void* k_cmp,
+                        const void* v_cmp, const int32_t* sel, int32_t top_k, int32_t sel_groups,
+                        const void* gate_logits, void* o, float* lse, hipStream_t stream) {
+  nsa_status st = check_layout(L, "nsa_attn_fwd");
+  if (st != NSA_OK) return st;
+  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: unknown dtype");
+  if (branches == 0 || (branches & ~7u) != 0) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: branches must be a non-empty OR of NSA_BR_* bits");
+  if (q_gran != NSA_Q_TOKEN && q_gran != NSA_Q_BLOCK) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: bad q_gran");
+  const int n_named = __builtin_popcount(branches);
+  if (gate_logits == nullptr && n_named != 1)
+    return fail(NSA_ERR_INVALID, "nsa_attn_fwd: several branches need gate_logits to be combined");
+  if (lse != nullptr && n_named != 1) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: lse needs exactly one branch");
+  if (o == nullptr || q == nullptr) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: q and o must be non-NULL");
+  if ((branches & (NSA_BR_SEL | NSA_BR_LOC)) && (k == nullptr || v == nullptr))
+    return fail(NSA_ERR_INVALID, "nsa_attn_fwd: SEL and LOC need k and v");
+  if ((branches & NSA_BR_CMP) && (k_cmp == nullptr || v_cmp == nullptr))
+    return fail(NSA_ERR_INVALID, "nsa_attn_fwd: CMP needs k_cmp and v_cmp");
+  if ((branches & NSA_BR_CMP) && q_gran == NSA_Q_BLOCK && q_cmp == nullptr)
+    return fail(NSA_ERR_INVALID, "nsa_attn_fwd: CMP with NSA_Q_BLOCK needs q_cmp");
+  if (branches & NSA_BR_SEL) {
+    if (sel == nullptr) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: SEL needs sel");
+    if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: top_k must be in 1..64 (got %d)", top_k);
+    if (sel_groups != 1 && sel_groups != L->n_kvh)
+      return fail(NSA_ERR_INVALID, "nsa_attn_fwd: sel_groups must be 1 or n_kvh");
+    if (L->n_blk > 65536) return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: SEL supports n_blk <= 65536");
+  }
+  if (L->head_dim != 32 || L->n_qh / L->n_kvh != 16 || q_gran != NSA_Q_TOKEN)
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: compiled for head_dim 32, 16 query heads per KV head, NSA_Q_TOKEN");
+  nsa::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_cmp = k_cmp;
+  a.v_cmp = v_cmp;
+  a.sel = sel;
+  a.blk_cnt = L->blk_cnt;
+  a.gates = gate_logits;
+  a.o = o;
+  a.lse = lse;
+  a.n_blk = L->n_blk;
+  a.cap = L->blk_cap;
+  a.n_qh = L->n_qh;
+  a.n_kvh = L->n_kvh;
+  a.top_k = (branches & NSA_BR_SEL) ? top_k : 0;
+  a.sel_groups = sel_groups < 1 ? 1 : sel_groups;
+  a.n_gch = n_named;
+  a.scale = L->scale;
+  a.branches = branches;
+  a.n_words = (L->n_blk + 31) / 32;
+  {
+    long long u = (long long)L->blk_cap * (a.top_k > 0 ? a.top_k : 1);
+    a.u_cap = (int)(u < L->n_blk ? u : L->n_blk);
+  }
+  const size_t lds = nsa::attn_lds_bytes(dtype == NSA_BF16, a);
+  if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: LDS need %zu bytes exceeds 160 KiB", lds);
+  NSA_FORCED_FAILURE("nsa_attn_fwd");
+  return hip_status(nsa::launch_attn(dtype == NSA_BF16, a, stream), "nsa_attn_fwd");
+}
+
+nsa_status nsa_gate_combine(nsa_dtype dtype, int32_t n_rows, int32_t n_qh, int32_t head_dim, int32_t n_branch,
+                            const void* const* o_branch, const void* gate_logits, void* o, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "nsa_gate_combine: unknown dtype");
+  if (n_rows < 1 || n_qh < 1 || head_dim < 1) return fail(NSA_ERR_INVALID, "nsa_gate_combine: sizes must be >= 1");
+  if (n_branch < 1 || n_branch > 8) return fail(NSA_ERR_INVALID, "nsa_gate_combine: n_branch must be in 1..8");
+  if (o_branch == nullptr || gate_logits == nullptr || o == nullptr)
+    return fail(NSA_ERR_INVALID, "nsa_gate_combine: NULL pointer");
+  for (int c = 0; c < n_branch; ++c)
+    if (o_branch[c] == nullptr) return fail(NSA_ERR_INVALID, "nsa_gate_combine: o_branch[%d] is NULL", c);
+  if (head_dim % 4 != 0) return fail(NSA_ERR_UNSUPPORTED, "nsa_gate_combine: head_dim must be a multiple of 4");
+  NSA_FORCED_FAILURE("nsa_gate_combine");
+  return hip_status(nsa::launch_gate(dtype == NSA_BF16, n_rows, n_qh, head_dim, n_branch, o_branch, gate_logits, o,
+                                     stream),
+                    "nsa_gate_combine");
+}
+
+nsa_status dense_gated_xattn_fwd(nsa_dtype dtype, int32_t n_tok, int32_t n_x, int32_t n_qh, int32_t n_kvh,
+                                 int32_t head_dim, float scale, const void* q, const void* k, const void* v,
+                                 const void* gate_logits, void* o, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "dense_gated_xattn_fwd: unknown dtype");
+  if (n_tok < 1 || n_x < 0 || n_x > n_tok) return fail(NSA_ERR_INVALID, "dense_gated_xattn_fwd: need n_tok >= 1 and 0 <= n_x <= n_tok");
+  if (n_qh < 1 || n_kvh < 1 || n_qh % n_kvh != 0 || head_dim < 1)
+    return fail(NSA_ERR_INVALID, "dense_gated_xattn_fwd: bad head counts");
+  if (!(scale > 0.f) || scale > 1e30f) return fail(NSA_ERR_INVALID, "dense_gated_xattn_fwd: bad scale");
+  if (q == nullptr || k == nullptr || v == nullptr || gate_logits == nullptr || o == nullptr)
+    return fail(NSA_ERR_INVALID, "dense_gated_xattn_fwd: NULL pointer");
+  if (head_dim != 32 || n_qh / n_kvh != 16)
+    return fail(NSA_ERR_UNSUPPORTED, "dense_gated_xattn_fwd: compiled for head_dim 32, 16 query heads per KV head");
+  NSA_FORCED_FAILURE("dense_gated_xattn_fwd");
+  nsa::DenseArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gates = gate_logits;
+  a.o = o;
+  a.n_tok = n_tok;
+  a.n_x = n_x;
+  a.n_qh = n_qh;
+  a.n_kvh = n_kvh;
+  a.scale = scale;
+  return hip_status(nsa::launch_dense(dtype == NSA_BF16, a, stream), "dense_gated_xattn_fwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,568 @@
+// NSA attention branches (compressed / selected / local) with a fused sigmoid-gate epilogue, and the
+// stage-1 dense gated self/cross attention, for gfx950.
+//
+// Math (LSRM pages, hyper.ai summary of arXiv 2604.05182, section 方法; Speed3R page, section 2.1):
+// per query row and head, o = softmax(scale * q K^T) V over a branch's key set, then
+// o = sum_c sigmoid(g_c) o_c over the branches.
+//
+// Work decomposition.  One workgroup owns one storage block (up to 64 query slots) and one KV
+// head j.  The 16 query heads of group j that share KV head j form the N = 16 columns of every MFMA,
+// so a K/V tile staged once in LDS serves all 16 heads of every token of the block.
+//
+// Per 64-key tile and token (all in registers, transposed so no cross-lane moves are needed):
+//   S^T[key][head] = K Q^T     4 x v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the token's q)
+//   lane (l) then holds head l%16 and keys 16*kt + 4*(l/16) + i, i.e. one head per lane;
+//   online softmax in base 2 (running max, rescale factor, row sum) per lane;
+//   O^T[d][head] += V^T P^T    4 MFMAs, B = P straight from the S^T registers (bf16), A = V^T from
+//   LDS, where V is stored transposed with the key order permuted so that each lane's eight
+//   probabilities line up with eight contiguous V^T elements.
+// The f32 variant issues eight v_mfma_f32_16x16x4f32 per step on the same lane data.
+#include "common.h"
+#include "kernels.h"
+
+namespace nsa {
+namespace {
+
+constexpr int TILE = 64;     // keys per LDS tile
+constexpr int HD = 32;       // head dim of the compiled kernels
+constexpr int GRP = 16;      // query heads per KV head of the compiled kernels
+
+template <typename T> struct Pad;
+template <> struct Pad<bf16> { static constexpr int K = 40, V = 72; };   // LDS row strides (elements)
+template <> struct Pad<float> { static constexpr int K = 36, V = 68; };
+
+template <typename T> struct TileBuf {
+  T k[TILE][Pad<T>::K];
+  T vt[HD][Pad<T>::V];
+};
+
+// Column of V^T (LDS) holding key `key` of the tile: lane group g of an MFMA step over keys
+// [32c, 32c+32) reads probabilities of keys {32c+4g+i, 32c+16+4g+i}, i<4, as k-slots 8g..8g+7.
+__device__ __forceinline__ int vt_pos(int key) {
+  int c = key >> 5, r = key & 31;
+  int hi = r >> 4, rr = r & 15;
+  return 32 * c + 8 * (rr >> 2) + 4 * hi + (rr & 3);
+}
+
+template <typename T, int NT> struct Stager {
+  static constexpr int E = 16 / sizeof(T);        // elements per 16-byte chunk
+  static constexpr int CPR = HD / E;               // chunks per key row
+  static constexpr int CH = TILE * CPR;            // chunks per tensor per tile
+  static constexpr int PER = (2 * CH + NT - 1) / NT;
+  uint4 r[PER];
+
+  __device__ __forceinline__ void load(const T* kb, const T* vb, int stride, int nk) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int c = threadIdx.x + i * NT;
+      if (c < 2 * CH) {
+        bool isv = c >= CH;
+        int cc = isv ? c - CH : c;
+        int key = cc / CPR, part = cc % CPR;
+        if (key < nk)
+          r[i] = *reinterpret_cast<const uint4*>((isv ? vb : kb) + (size_t)key * stride + part * E);
+        else
+          r[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(TileBuf<T>& b) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int c = threadIdx.x + i * NT;
+      if (c < 2 * CH) {
+        bool isv = c >= CH;
+        int cc = isv ? c - CH : c;
+        int key = cc / CPR, part = cc % CPR;
+        if (!isv) {
+          *reinterpret_cast<uint4*>(&b.k[key][part * E]) = r[i];
+        } else {
+          const T* e = reinterpret_cast<const T*>(&r[i]);
+          int pos = vt_pos(key);
+#pragma unroll
+          for (int x = 0; x < E; ++x) b.vt[part * E + x][pos] = e[x];
+        }
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ Frag8<bf16> lds_frag(const bf16* p) {
+  Frag8<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag8<float> lds_frag(const float* p) {
+  Frag8<float> f;
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  f.v = (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
+}
+__device__ __forceinline__ Frag8<bf16> glb_frag(const bf16* p) { return lds_frag(p); }
+__device__ __forceinline__ Frag8<float> glb_frag(const float* p) { return lds_frag(p); }
+
+template <typename T> __device__ __forceinline__ void set_elem(Frag8<T>& f, int e, float x) {
+  f.v[e] = from_f32<T>(x);
+}
+
+// Online-softmax state of one token (16 heads of one KV group) held by one wave.
+struct TokState {
+  f32x4 acc[2];   // O^T: lane holds d = 16*dt + 4*(lane/16) + i for head lane%16
+  float m;        // running max of raw scores for head lane%16 (replicated over lane groups)
+  float l;        // this lane group's share of the running sum
+};
+
+__device__ __forceinline__ void tok_init(TokState& s) {
+  s.acc[0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  s.acc[1] = s.acc[0];
+  s.m = -INFINITY;
+  s.l = 0.f;
+}
+
+template <typename T>
+__device__ __forceinline__ void tok_tile(TokState& st, const Frag8<T>& qf, const Frag8<T> (&kf)[4],
+                                         const Frag8<T> (&vf)[2][2], int nk, float c2) {
+  const int g = lane_id() >> 4;
+  f32x4 s[4];
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) s[kt] = mma16(kf[kt], qf, z);
+  if (nk < TILE) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * kt + 4 * g + i >= nk) s[kt][i] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                       fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+  mx = wave_max_across_rows(mx);
+  const float mnew = fmaxf(st.m, mx);
+  const float alpha = __builtin_amdgcn_exp2f((st.m - mnew) * c2);
+  const float mc = mnew * c2;
+  Frag8<T> pf[2];
+  float psum = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kt = 2 * h + (e >> 2), i = e & 3;
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -mc));
+      set_elem(pf[h], e, p);
+      psum += to_f32(pf[h].v[e]);
+    }
+  st.l = st.l * alpha + psum;
+  st.m = mnew;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+    st.acc[dt] *= alpha;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) st.acc[dt] = mma16(vf[dt][h], pf[h], st.acc[dt]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_tile_frags(const TileBuf<T>& b, Frag8<T> (&kf)[4], Frag8<T> (&vf)[2][2]) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) kf[kt] = lds_frag(&b.k[16 * kt + r][8 * g]);
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vf[dt][h] = lds_frag(&b.vt[16 * dt + r][32 * h + 8 * g]);
+}
+
+// Finish one branch for one token: normalise, optionally write lse, and fold into the output.
+__device__ __forceinline__ void tok_finish(const TokState& st, f32x4 (&out)[2], float wgt, bool first,
+                                           float scale, float* lse_out) {
+  const float l = wave_sum_across_rows(st.l);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+    f32x4 o = st.acc[dt] * (inv * wgt);
+    out[dt] = first ? o : out[dt] + o;
+  }
+  if (lse_out != nullptr && (lane_id() >> 4) == 0)
+    *lse_out = l > 0.f ? st.m * scale + __logf(l) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------------------------
+// generic tile loop: double-buffered LDS staging shared by the workgroup
+// ---------------------------------------------------------------------------------------------
+
+template <typename T, int NT, int TPW, class Src, class Part>
+__device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int ntiles, const Part& part,
+                                          TokState (&st)[TPW], const Frag8<T> (&qf)[TPW], float c2) {
+  Stager<T, NT> sg;
+  if (ntiles <= 0) return;
+  sg.load(src.kptr(0), src.vptr(0), src.stride, src.nk(0));
+  sg.store(buf[0]);
+  __syncthreads();
+  for (int u = 0; u < ntiles; ++u) {
+    const bool more = u + 1 < ntiles;
+    if (more) sg.load(src.kptr(u + 1), src.vptr(u + 1), src.stride, src.nk(u + 1));
+    const TileBuf<T>& b = buf[u & 1];
+    const int nk = src.nk(u);
+    const uint32_t pm = part.wave_mask(u);
+    if (pm) {
+      Frag8<T> kf[4], vf[2][2];
+      load_tile_frags(b, kf, vf);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        if (pm & (1u << t)) tok_tile<T>(st[t], qf[t], kf, vf, nk, c2);
+    }
+    if (more) sg.store(buf[(u + 1) & 1]);
+    __syncthreads();
+  }
+}
+
+// Key tile sources ------------------------------------------------------------------------------
+
+template <typename T> struct RangeSrc {     // tiles of 64 consecutive rows [lo, hi) of [rows][n_kvh][D]
+  const T* base;   // &x[0][j][0]
+  int stride, lo, hi;
+  __device__ const T* kptr(int u) const { return base + (size_t)(lo + TILE * u) * stride; }
+  __device__ const T* vptr(int u) const { return vbase + (size_t)(lo + TILE * u) * stride; }
+  __device__ int nk(int u) const { int r = hi - lo - TILE * u; return r < TILE ? r : TILE; }
+  const T* vbase;
+};
+
+template <typename T> struct UnionSrc {     // one tile per block in the selection union
+  const T* kb;     // &k[0][j][0]
+  const T* vb;
+  int stride;      // n_kvh * D
+  int cap;
+  const int* ulist;        // LDS
+  const int32_t* blk_cnt;  // global
+  __device__ const T* kptr(int u) const { return kb + (size_t)ulist[u] * cap * stride; }
+  __device__ const T* vptr(int u) const { return vb + (size_t)ulist[u] * cap * stride; }
+  __device__ int nk(int u) const { return blk_cnt[ulist[u]]; }
+};
+
+struct AllPart {                 // every valid token of the wave takes part
+  uint32_t m;
+  __device__ uint32_t wave_mask(int) const { return m; }
+};
+struct UnionPart {               // tokens whose routing row holds the tile's block
+  const unsigned long long* umask;  // LDS
+  int shift;                        // first slot of this wave
+  uint32_t valid;
+  __device__ uint32_t wave_mask(int u) const { return (uint32_t)(umask[u] >> shift) & valid; }
+};
+
+// ---------------------------------------------------------------------------------------------
+// block-wide helpers for the selection union
+// ---------------------------------------------------------------------------------------------
+
+template <int NT>
+__device__ int block_exclusive_scan(int x, int* scratch /* NT/64 + 1 ints */) {
+  const int l = lane_id(), w = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(inc, o, 64);
+    if (l >= o) inc += y;
+  }
+  if (l == 63) scratch[w] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int s = 0;
+    for (int i = 0; i < NT / 64; ++i) { int t = scratch[i]; scratch[i] = s; s += t; }
+    scratch[NT / 64] = s;
+  }
+  __syncthreads();
+  return scratch[w] + inc - x;
+}
+
+// ---------------------------------------------------------------------------------------------
+// the NSA kernel
+// ---------------------------------------------------------------------------------------------
+
+template <typename T, int WAVES, int TPW>
+__global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
+  constexpr int NT = WAVES * 64;
+  static_assert(WAVES * TPW == 64, "a workgroup covers 64 query slots");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  TileBuf<T>* buf = reinterpret_cast<TileBuf<T>*>(smem);
+  unsigned char* extra = smem + 2 * sizeof(TileBuf<T>);
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = wg / a.n_kvh, j = wg % a.n_kvh;
+  const int cap = a.cap, cnt = a.blk_cnt[b];
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  const int hh = j * GRP + r;                  // query head of this lane
+  const int kvs = a.n_kvh * HD;                // key row stride (elements)
+  const float c2 = a.scale * kLog2e;
+  const T* q = reinterpret_cast<const T*>(a.q);
+
+  // queries of this wave's tokens
+  Frag8<T> qf[TPW];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int slot = w * TPW + t;
+    if (slot < cnt) {
+      valid |= 1u << t;
+      qf[t] = glb_frag(q + ((size_t)(b * cap + slot) * a.n_qh + hh) * HD + 8 * g);
+    } else {
+      qf[t] = glb_frag(q + 0);   // unused
+    }
+  }
+
+  f32x4 out[TPW][2];
+  TokState st[TPW];
+  int phase = 0;
+  const int n_named = __builtin_popcount(a.branches);
+  (void)n_named;
+
+  auto finish_all = [&](int ch) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      if (!(valid & (1u << t))) continue;
+      const size_t row = (size_t)(b * cap + w * TPW + t);
+      float wgt = 1.f;
+      if (a.gates) {
+        const T* gp = reinterpret_cast<const T*>(a.gates);
+        wgt = sigmoidf_(to_f32(gp[(row * a.n_qh + hh) * a.n_gch + ch]));
+      }
+      float* lp = a.lse ? a.lse + row * a.n_qh + hh : nullptr;
+      tok_finish(st[t], out[t], wgt, phase == 0, a.scale, lp);
+    }
+    ++phase;
+  };
+
+  // ---- compressed branch: every pooled block ----
+  if (a.branches & 1) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) tok_init(st[t]);
+    RangeSrc<T> src;
+    src.base = reinterpret_cast<const T*>(a.k_cmp) + j * HD;
+    src.vbase = reinterpret_cast<const T*>(a.v_cmp) + j * HD;
+    src.stride = kvs;
+    src.lo = 0;
+    src.hi = a.n_blk;
+    AllPart part{valid};
+    run_tiles<T, NT, TPW>(buf, src, (a.n_blk + TILE - 1) / TILE, part, st, qf, c2);
+    finish_all(phase);
+  }
+
+  // ---- selected branch: union of the block's routing rows, streamed once ----
+  if (a.branches & 2) {
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(extra);
+    int* wpre = reinterpret_cast<int*>(bitmap + a.n_words);
+    int* ulist = wpre + a.n_words;
+    int* scratch = ulist + a.u_cap;
+    unsigned long long* umask = reinterpret_cast<unsigned long long*>(
+        (reinterpret_cast<uintptr_t>(scratch + NT / 64 + 1) + 7) & ~uintptr_t(7));
+    const int grp = a.sel_groups == 1 ? 0 : j;
+    const int kk = a.top_k;
+    for (int i = threadIdx.x; i < a.n_words; i += NT) bitmap[i] = 0u;
+    __syncthreads();
+    for (int e = threadIdx.x; e < cnt * kk; e += NT) {
+      const int t = e / kk, s = e % kk;
+      const int blk = a.sel[((size_t)(b * cap + t) * a.sel_groups + grp) * kk + s];
+      if (blk >= 0 && blk < a.n_blk) atomicOr(&bitmap[blk >> 5], 1u << (blk & 31));
+    }
+    __syncthreads();
+    // exclusive prefix of popcounts over the bitmap words (contiguous ranges per thread)
+    const int per = (a.n_words + NT - 1) / NT;
+    const int w0 = threadIdx.x * per;
+    int mine = 0;
+    for (int i = 0; i < per; ++i)
+      if (w0 + i < a.n_words) mine += __builtin_popcount(bitmap[w0 + i]);
+    int base = block_exclusive_scan<NT>(mine, scratch);
+    const int n_union = scratch[NT / 64];
+    for (int i = 0; i < per; ++i) {
+      const int wi = w0 + i;
+      if (wi < a.n_words) {
+        wpre[wi] = base;
+        uint32_t bits = bitmap[wi];
+        while (bits) {
+          const int bit = __builtin_ctz(bits);
+          bits &= bits - 1;
+          ulist[base++] = 32 * wi + bit;
+        }
+      }
+    }
+    for (int i = threadIdx.x; i < n_union; i += NT) umask[i] = 0ull;
+    __syncthreads();
+    for (int e = threadIdx.x; e < cnt * kk; e += NT) {
+      const int t = e / kk, s = e % kk;
+      const int blk = a.sel[((size_t)(b * cap + t) * a.sel_groups + grp) * kk + s];
+      if (blk >= 0 && blk < a.n_blk) {
+        const int wi = blk >> 5;
+        const int u = wpre[wi] + __builtin_popcount(bitmap[wi] & ((1u << (blk & 31)) - 1u));
+        atomicOr(&umask[u], 1ull << t);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) tok_init(st[t]);
+    UnionSrc<T> src;
+    src.kb = reinterpret_cast<const T*>(a.k) + j * HD;
+    src.vb = reinterpret_cast<const T*>(a.v) + j * HD;
+    src.stride = kvs;
+    src.cap = cap;
+    src.ulist = ulist;
+    src.blk_cnt = a.blk_cnt;
+    UnionPart part{umask, w * TPW, valid};
+    run_tiles<T, NT, TPW>(buf, src, n_union, part, st, qf, c2);
+    finish_all(phase);
+  }
+
+  // ---- local branch: the query's own block ----
+  if (a.branches & 4) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) tok_init(st[t]);
+    RangeSrc<T> src;
+    src.base = reinterpret_cast<const T*>(a.k) + j * HD;
+    src.vbase = reinterpret_cast<const T*>(a.v) + j * HD;
+    src.stride = kvs;
+    src.lo = b * cap;
+    src.hi = b * cap + cnt;
+    AllPart part{valid};
+    run_tiles<T, NT, TPW>(buf, src, 1, part, st, qf, c2);
+    finish_all(phase);
+  }
+
+  // ---- store: valid slots get the (gated) sum, padding slots of the block get zeros ----
+  T* o = reinterpret_cast<T*>(a.o);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int slot = w * TPW + t;
+    if (slot >= cap) continue;
+    const size_t row = (size_t)(b * cap + slot);
+    const bool v = slot < cnt;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      T* dst = o + (row * a.n_qh + hh) * HD + 16 * dt + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(v ? out[t][dt][i] : 0.f);
+    }
+    if (!v && a.lse && g == 0) a.lse[row * a.n_qh + hh] = -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// stage-1 dense gated self/cross attention
+// ---------------------------------------------------------------------------------------------
+
+template <typename T, int WAVES, int TPW>
+__global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
+  constexpr int NT = WAVES * 64;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  TileBuf<T>* buf = reinterpret_cast<TileBuf<T>*>(smem);
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int qb = wg / a.n_kvh, j = wg % a.n_kvh;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  const int hh = j * GRP + r;
+  const int kvs = a.n_kvh * HD;
+  const float c2 = a.scale * kLog2e;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* gp = reinterpret_cast<const T*>(a.gates);
+
+  Frag8<T> qf[TPW];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tok = qb * 64 + w * TPW + t;
+    if (tok < a.n_tok) {
+      valid |= 1u << t;
+      qf[t] = glb_frag(q + ((size_t)tok * a.n_qh + hh) * HD + 8 * g);
+    } else {
+      qf[t] = glb_frag(q + 0);
+    }
+  }
+  f32x4 out[TPW][2];
+  TokState st[TPW];
+  for (int ph = 0; ph < 2; ++ph) {
+    const int lo = ph == 0 ? 0 : a.n_x, hi = ph == 0 ? a.n_x : a.n_tok;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) tok_init(st[t]);
+    RangeSrc<T> src;
+    src.base = reinterpret_cast<const T*>(a.k) + j * HD;
+    src.vbase = reinterpret_cast<const T*>(a.v) + j * HD;
+    src.stride = kvs;
+    src.lo = lo;
+    src.hi = hi;
+    AllPart part{valid};
+    run_tiles<T, NT, TPW>(buf, src, (hi - lo + TILE - 1) / TILE, part, st, qf, c2);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tok = qb * 64 + w * TPW + t;
+      if (!(valid & (1u << t))) continue;
+      // phase 0 holds x keys: self for x tokens, cross for y tokens
+      const int ch = ((tok < a.n_x) == (ph == 0)) ? 0 : 1;
+      const float wgt = sigmoidf_(to_f32(gp[((size_t)tok * a.n_qh + hh) * 2 + ch]));
+      tok_finish(st[t], out[t], wgt, ph == 0, a.scale, nullptr);
+    }
+  }
+  T* o = reinterpret_cast<T*>(a.o);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (!(valid & (1u << t))) continue;
+    const int tok = qb * 64 + w * TPW + t;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      T* dst = o + ((size_t)tok * a.n_qh + hh) * HD + 16 * dt + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(out[t][dt][i]);
+    }
+  }
+}
+
+template <typename T> struct Shape;
+template <> struct Shape<bf16> { static constexpr int WAVES = 8, TPW = 8; };
+template <> struct Shape<float> { static constexpr int WAVES = 16, TPW = 4; };
+
+template <typename T>
+hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
+  constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
+  size_t lds = 2 * sizeof(TileBuf<T>);
+  if (a.branches & 2) {
+    lds += (size_t)a.n_words * 8 + (size_t)a.u_cap * 4 + (NT / 64 + 1) * 4 + 8 + (size_t)a.u_cap * 8;
+  }
+  const int nwg = a.n_blk * a.n_kvh;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nsa_attn_kernel<T, WAVES, TPW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((nsa_attn_kernel<T, WAVES, TPW>), dim3(nwg), dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dense_t(const DenseArgs& a, hipStream_t s) {
+  constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
+  const size_t lds = 2 * sizeof(TileBuf<T>);
+  const int nwg = ((a.n_tok + 63) / 64) * a.n_kvh;
+  hipLaunchKernelGGL((dense_xattn_kernel<T, WAVES, TPW>), dim3(nwg), dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_lds_bytes(int is_bf16, const AttnArgs& a) {
+  const int NT = is_bf16 ? 512 : 1024;
+  size_t lds = 2 * (is_bf16 ? sizeof(TileBuf<bf16>) : sizeof(TileBuf<float>));
+  if (a.branches & 2)
+    lds += (size_t)a.n_words * 8 + (size_t)a.u_cap * 4 + (NT / 64 + 1) * 4 + 8 + (size_t)a.u_cap * 8;
+  return lds;
+}
+
+hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s) {
+  return is_bf16 ? launch_attn_t<bf16>(a, s) : launch_attn_t<float>(a, s);
+}
+
+hipError_t launch_dense(int is_bf16, const DenseArgs& a, hipStream_t s) {
+  return is_bf16 ? launch_dense_t<bf16>(a, s) : launch_dense_t<float>(a, s);
+}
+
+}  // namespace nsa

@@ -1,0 +1,79 @@
+// HBM-bound passes: block mean pooling and the standalone sigmoid-gated combine.
+#include "common.h"
+#include "kernels.h"
+
+namespace nsa {
+namespace {
+
+// Block compression (LSRM pages, section 方法, eq. k^cmp = AvgPool(ResBlock(k)), ResBlock = identity;
+// Speed3R page, section 2.1, average pooling).  One workgroup per block; thread = (head, dim), so
+// each token row of the block is one coalesced read.  fp32 accumulation in token order.
+template <typename T>
+__global__ void pool_kernel(const T* __restrict__ x, T* __restrict__ xc, const int32_t* __restrict__ blk_cnt,
+                            int cap, int row) {
+  const int b = blockIdx.x;
+  const int e = threadIdx.x;
+  if (e >= row) return;
+  const int cnt = blk_cnt[b];
+  const T* src = x + (size_t)b * cap * row + e;
+  float s = 0.f;
+  for (int t = 0; t < cnt; ++t) s += to_f32(src[(size_t)t * row]);
+  xc[(size_t)b * row + e] = from_f32<T>(s / (float)cnt);
+}
+
+struct BranchPtrs {
+  const void* p[8];
+};
+
+// o = sum_c sigmoid(g_c) o_c (LSRM pages, Sigmoid gates; Speed3R page, gated aggregation).
+// One thread per (row, head, 4 consecutive dims).
+template <typename T>
+__global__ void gate_kernel(BranchPtrs br, int n_branch, const T* __restrict__ gates, T* __restrict__ o,
+                            long long n_vec, int n_qh, int head_dim) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_vec) return;
+  const long long e0 = i * 4;
+  const long long rh = e0 / head_dim;          // row * n_qh + head
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < n_branch; ++c) {
+    const float wgt = sigmoidf_(to_f32(gates[rh * n_branch + c]));
+    const T* oc = reinterpret_cast<const T*>(br.p[c]) + e0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc[x] += wgt * to_f32(oc[x]);
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) o[e0 + x] = from_f32<T>(acc[x]);
+}
+
+}  // namespace
+
+hipError_t launch_pool(int is_bf16, const void* x, void* x_cmp, const int32_t* blk_cnt, int n_blk,
+                       int cap, int n_heads, int head_dim, hipStream_t s) {
+  const int row = n_heads * head_dim;
+  const int nt = ((row + 63) / 64) * 64;
+  if (is_bf16)
+    hipLaunchKernelGGL(pool_kernel<bf16>, dim3(n_blk), dim3(nt), 0, s, (const bf16*)x, (bf16*)x_cmp,
+                       blk_cnt, cap, row);
+  else
+    hipLaunchKernelGGL(pool_kernel<float>, dim3(n_blk), dim3(nt), 0, s, (const float*)x, (float*)x_cmp,
+                       blk_cnt, cap, row);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate(int is_bf16, int n_rows, int n_qh, int head_dim, int n_branch,
+                       const void* const* o_branch, const void* gates, void* o, hipStream_t s) {
+  BranchPtrs br;
+  for (int c = 0; c < 8; ++c) br.p[c] = c < n_branch ? o_branch[c] : nullptr;
+  const long long n_vec = (long long)n_rows * n_qh * head_dim / 4;
+  const int nt = 256;
+  const unsigned nb = (unsigned)((n_vec + nt - 1) / nt);
+  if (is_bf16)
+    hipLaunchKernelGGL(gate_kernel<bf16>, dim3(nb), dim3(nt), 0, s, br, n_branch, (const bf16*)gates,
+                       (bf16*)o, n_vec, n_qh, head_dim);
+  else
+    hipLaunchKernelGGL(gate_kernel<float>, dim3(nb), dim3(nt), 0, s, br, n_branch, (const float*)gates,
+                       (float*)o, n_vec, n_qh, head_dim);
+  return hipGetLastError();
+}
+
+}  // namespace nsa

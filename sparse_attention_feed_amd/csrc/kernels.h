@@ -1,0 +1,69 @@
+// Internal interface between the C ABI (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nsa {
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k_cmp;
+  const void* v_cmp;
+  const int32_t* sel;
+  const int32_t* blk_cnt;
+  const void* gates;   // nullable
+  void* o;
+  float* lse;          // nullable
+  int n_blk, cap, n_qh, n_kvh, top_k, sel_groups, n_gch;
+  float scale;
+  uint32_t branches;
+  int n_words;         // ceil(n_blk / 32): selection bitmap words
+  int u_cap;           // bound on the number of distinct selected blocks of one query block
+};
+
+struct DenseArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* gates;
+  void* o;
+  int n_tok, n_x, n_qh, n_kvh;
+  float scale;
+};
+
+struct RouteArgs {
+  const float* pts;
+  const int32_t* blk_cnt;
+  const uint32_t* blk_key;
+  int32_t* cent;        // [n_blk][4]
+  int32_t* sel;
+  uint32_t* sel_d2;     // nullable
+  int n_blk, cap, top_k;
+};
+
+struct ScoreRouteArgs {
+  const void* q;
+  const void* k_cmp;
+  const float* lse;
+  const int32_t* blk_cnt;
+  const uint32_t* blk_key;
+  int32_t* sel;
+  int n_rows, n_blk, cap, n_qh, n_kvh, top_k;
+  float scale;
+};
+
+size_t attn_lds_bytes(int is_bf16, const AttnArgs& a);
+hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s);
+hipError_t launch_dense(int is_bf16, const DenseArgs& a, hipStream_t s);
+hipError_t launch_pool(int is_bf16, const void* x, void* x_cmp, const int32_t* blk_cnt, int n_blk,
+                       int cap, int n_heads, int head_dim, hipStream_t s);
+hipError_t launch_route_geometric(const RouteArgs& a, hipStream_t s);
+hipError_t launch_route_scores(int is_bf16, const ScoreRouteArgs& a, hipStream_t s);
+hipError_t launch_gate(int is_bf16, int n_rows, int n_qh, int head_dim, int n_branch,
+                       const void* const* o_branch, const void* gates, void* o, hipStream_t s);
+
+}  // namespace nsa

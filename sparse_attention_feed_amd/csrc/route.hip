@@ -1,0 +1,303 @@
+// Block routing for the selected branch, without materialising a score or distance matrix.
+//
+// Geometric routing (LSRM pages, hyper.ai summary of arXiv 2604.05182, section 方法, routing
+// paragraph; Korean summary, section 2.2): a query keeps the blocks whose centres are nearest to its
+// 3D point.  The metric is made exact and reproducible on an integer lattice: u = rint(4096 p) + 4096
+// per axis, block centroid rounded half-up, squared distance < 2^28 in 32-bit integers; ranking is
+// the total order (d2, blk_key).
+//
+// Score routing ("standard NSA" selection the LSRM pages compare with; Speed3R page, section 2.1):
+// importance of a pooled block for a query token and KV group = the group's summed softmax
+// probability against the compressed keys, computed tile by tile with MFMA and reduced to a top-k
+// per lane, then merged across the wave.
+#include "common.h"
+#include "kernels.h"
+
+namespace nsa {
+namespace {
+
+__device__ __forceinline__ int lattice(float p) { return (int)rintf(4096.0f * p) + 4096; }
+
+// One wave per block: integer centroid of the block's valid points plus its key.
+__global__ __launch_bounds__(64) void centroid_kernel(const float* __restrict__ pts, const int32_t* __restrict__ blk_cnt,
+                                                      const uint32_t* __restrict__ blk_key, int32_t* __restrict__ cent,
+                                                      int cap) {
+  const int b = blockIdx.x, l = threadIdx.x;
+  const int cnt = blk_cnt[b];
+  int sx = 0, sy = 0, sz = 0;
+  for (int t = l; t < cnt; t += 64) {
+    const float* p = pts + (size_t)(b * cap + t) * 3;
+    sx += lattice(p[0]);
+    sy += lattice(p[1]);
+    sz += lattice(p[2]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sx += __shfl_xor(sx, o, 64);
+    sy += __shfl_xor(sy, o, 64);
+    sz += __shfl_xor(sz, o, 64);
+  }
+  if (l == 0) {
+    int4 c;
+    c.x = (2 * sx + cnt) / (2 * cnt);
+    c.y = (2 * sy + cnt) / (2 * cnt);
+    c.z = (2 * sz + cnt) / (2 * cnt);
+    c.w = (int)blk_key[b];
+    reinterpret_cast<int4*>(cent)[b] = c;
+  }
+}
+
+__device__ __forceinline__ bool before(uint32_t d, uint32_t k, uint32_t d2, uint32_t k2) {
+  return d < d2 || (d == d2 && k < k2);
+}
+
+constexpr int RCH = 1024;   // centroids per LDS chunk
+
+// One thread per query slot; a sorted top-K list (d2, key, index) lives in registers.
+template <int K>
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+  __shared__ int4 cs[RCH];
+  const int S = a.n_blk * a.cap;
+  const int slot = blockIdx.x * 256 + threadIdx.x;
+  bool valid = false;
+  int ux = 0, uy = 0, uz = 0;
+  if (slot < S) {
+    valid = (slot % a.cap) < a.blk_cnt[slot / a.cap];
+    if (valid) {
+      const float* p = a.pts + (size_t)slot * 3;
+      ux = lattice(p[0]);
+      uy = lattice(p[1]);
+      uz = lattice(p[2]);
+    }
+  }
+  uint32_t bd[K], bk[K];
+  int bi[K];
+#pragma unroll
+  for (int x = 0; x < K; ++x) {
+    bd[x] = 0xFFFFFFFFu;
+    bk[x] = 0xFFFFFFFFu;
+    bi[x] = -1;
+  }
+  const int nch = (a.n_blk + RCH - 1) / RCH;
+  const int first_blk = min(a.n_blk - 1, (blockIdx.x * 256) / a.cap);
+  const int c0 = first_blk / RCH;       // start near this workgroup's own blocks
+  const int4* cent = reinterpret_cast<const int4*>(a.cent);
+  for (int ci = 0; ci < nch; ++ci) {
+    const int c = (c0 + ci) % nch;
+    const int base = c * RCH;
+    const int n = min(RCH, a.n_blk - base);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) cs[i] = cent[base + i];
+    __syncthreads();
+    if (valid) {
+      for (int i = 0; i < n; ++i) {
+        const int4 e = cs[i];
+        const int dx = ux - e.x, dy = uy - e.y, dz = uz - e.z;
+        const uint32_t d = (uint32_t)(__mul24(dx, dx) + __mul24(dy, dy) + __mul24(dz, dz));
+        const uint32_t key = (uint32_t)e.w;
+        if (before(d, key, bd[K - 1], bk[K - 1])) {
+          const int idx = base + i;
+#pragma unroll
+          for (int x = K - 1; x > 0; --x) {
+            const bool bp = before(d, key, bd[x - 1], bk[x - 1]);
+            const bool bc = before(d, key, bd[x], bk[x]);
+            if (bp) {
+              bd[x] = bd[x - 1];
+              bk[x] = bk[x - 1];
+              bi[x] = bi[x - 1];
+            } else if (bc) {
+              bd[x] = d;
+              bk[x] = key;
+              bi[x] = idx;
+            }
+          }
+          if (before(d, key, bd[0], bk[0])) {
+            bd[0] = d;
+            bk[0] = key;
+            bi[0] = idx;
+          }
+        }
+      }
+    }
+  }
+  if (slot < S) {
+    int32_t* so = a.sel + (size_t)slot * a.top_k;
+    uint32_t* dout = a.sel_d2 ? a.sel_d2 + (size_t)slot * a.top_k : nullptr;
+#pragma unroll
+    for (int x = 0; x < K; ++x) {
+      if (x < a.top_k) {
+        so[x] = valid ? bi[x] : -1;
+        if (dout) dout[x] = valid ? bd[x] : 0xFFFFFFFFu;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// score routing, grouped-query form (16 query heads per KV head, head dim 32)
+// ---------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ bool better(float v, uint32_t k, float v2, uint32_t k2) {
+  return v > v2 || (v == v2 && k < k2);
+}
+
+template <typename T, int K>
+__global__ __launch_bounds__(256) void score_route_kernel(ScoreRouteArgs a) {
+  constexpr int HD = 32, GRP = 16;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const int row = wave / a.n_kvh, j = wave % a.n_kvh;
+  if (row >= a.n_rows) return;
+  int32_t* so = a.sel + ((size_t)row * a.n_kvh + j) * a.top_k;
+  const bool valid = (row % a.cap) < a.blk_cnt[row / a.cap];
+  if (!valid) {
+    for (int x = l; x < a.top_k; x += 64) so[x] = -1;
+    return;
+  }
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* kc = reinterpret_cast<const T*>(a.k_cmp);
+  Frag8<T> qf;
+  {
+    const T* qp = q + ((size_t)row * a.n_qh + j * GRP + r) * HD + 8 * g;
+    qf.v = *reinterpret_cast<const decltype(qf.v)*>(qp);
+  }
+  const float c2 = a.scale * kLog2e;
+  const float lse2 = a.lse[(size_t)row * a.n_qh + j * GRP + r] * kLog2e;
+  float bv[K];
+  uint32_t bk[K];
+  int bi[K];
+#pragma unroll
+  for (int x = 0; x < K; ++x) {
+    bv[x] = -INFINITY;
+    bk[x] = 0xFFFFFFFFu;
+    bi[x] = -1;
+  }
+  const int kstride = a.n_kvh * HD;
+  const int own_kt = r >> 2, own_i = r & 3;   // the key of each 64-key step this lane ranks
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.n_blk; k0 += 64) {
+    float red[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = k0 + 16 * kt + r;
+      Frag8<T> kf;
+      if (key < a.n_blk)
+        kf.v = *reinterpret_cast<const decltype(kf.v)*>(kc + (size_t)key * kstride + j * HD + 8 * g);
+      else
+        kf.v = decltype(kf.v){};
+      f32x4 s = mma16(kf, qf, z);      // lane: head r, keys k0 + 16kt + 4g + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2));
+        // sum over the 16 heads of the group = the 16 lanes of this row
+        p += __shfl_xor(p, 1, 64);
+        p += __shfl_xor(p, 2, 64);
+        p += __shfl_xor(p, 4, 64);
+        p += __shfl_xor(p, 8, 64);
+        red[kt][i] = p;
+      }
+    }
+    float val = red[0][0];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kt == own_kt && i == own_i) val = red[kt][i];
+    const int idx = k0 + 16 * own_kt + 4 * g + own_i;
+    if (idx < a.n_blk) {
+      const uint32_t key = a.blk_key[idx];
+      if (better(val, key, bv[K - 1], bk[K - 1])) {
+#pragma unroll
+        for (int x = K - 1; x > 0; --x) {
+          const bool bp = better(val, key, bv[x - 1], bk[x - 1]);
+          const bool bc = better(val, key, bv[x], bk[x]);
+          if (bp) {
+            bv[x] = bv[x - 1];
+            bk[x] = bk[x - 1];
+            bi[x] = bi[x - 1];
+          } else if (bc) {
+            bv[x] = val;
+            bk[x] = key;
+            bi[x] = idx;
+          }
+        }
+        if (better(val, key, bv[0], bk[0])) {
+          bv[0] = val;
+          bk[0] = key;
+          bi[0] = idx;
+        }
+      }
+    }
+  }
+  // merge the 64 per-lane lists: top_k rounds of a wave arg-best over the list heads
+  for (int x = 0; x < a.top_k; ++x) {
+    float v = bv[0];
+    uint32_t k = bk[0];
+    int src = l;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(v, o, 64);
+      const uint32_t k2 = __shfl_xor(k, o, 64);
+      const int s2 = __shfl_xor(src, o, 64);
+      if (better(v2, k2, v, k)) {
+        v = v2;
+        k = k2;
+        src = s2;
+      }
+    }
+    const int win = __shfl(bi[0], src, 64);
+    if (l == 0) so[x] = (v == -INFINITY) ? -1 : win;
+    if (l == src) {
+#pragma unroll
+      for (int y = 0; y < K - 1; ++y) {
+        bv[y] = bv[y + 1];
+        bk[y] = bk[y + 1];
+        bi[y] = bi[y + 1];
+      }
+      bv[K - 1] = -INFINITY;
+      bk[K - 1] = 0xFFFFFFFFu;
+      bi[K - 1] = -1;
+    }
+  }
+}
+
+template <int K>
+hipError_t launch_route_k(const RouteArgs& a, hipStream_t s) {
+  const int S = a.n_blk * a.cap;
+  hipLaunchKernelGGL(route_kernel<K>, dim3((S + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int K>
+hipError_t launch_score_k(const ScoreRouteArgs& a, hipStream_t s) {
+  const long long waves = (long long)a.n_rows * a.n_kvh;
+  hipLaunchKernelGGL((score_route_kernel<T, K>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_score_t(const ScoreRouteArgs& a, hipStream_t s) {
+  if (a.top_k <= 8) return launch_score_k<T, 8>(a, s);
+  if (a.top_k <= 16) return launch_score_k<T, 16>(a, s);
+  if (a.top_k <= 32) return launch_score_k<T, 32>(a, s);
+  return launch_score_k<T, 64>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_route_geometric(const RouteArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(centroid_kernel, dim3(a.n_blk), dim3(64), 0, s, a.pts, a.blk_cnt, a.blk_key, a.cent, a.cap);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.top_k <= 4) return launch_route_k<4>(a, s);
+  if (a.top_k <= 8) return launch_route_k<8>(a, s);
+  if (a.top_k <= 16) return launch_route_k<16>(a, s);
+  if (a.top_k <= 32) return launch_route_k<32>(a, s);
+  return launch_route_k<64>(a, s);
+}
+
+hipError_t launch_route_scores(int is_bf16, const ScoreRouteArgs& a, hipStream_t s) {
+  return is_bf16 ? launch_score_t<bf16>(a, s) : launch_score_t<float>(a, s);
+}
+
+}  // namespace nsa

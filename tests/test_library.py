@@ -1,0 +1,143 @@
+"""Host-side tests of libnsa that need no GPU: the library loads, exports every symbol declared in
+include/nsa.h, and rejects invalid arguments (or reports a forced launch failure) before any HIP
+call is made."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsa.h")
+LIB = os.path.join(ROOT, "sparse_attention_feed_amd", "libnsa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libnsa.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:nsa_status|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 7
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_binding_names_match_header():
+    import sparse_attention_feed_amd as S
+    assert sorted(S.EXPORTS) == declared_functions()
+
+
+@pytest.fixture()
+def S():
+    import sparse_attention_feed_amd as mod
+    return mod
+
+
+def layout(S, **kw):
+    d = dict(n_blk=4, blk_cap=64, n_qh=32, n_kvh=2, head_dim=32, scale=0.17677669, blk_cnt=0x1000, blk_key=0x2000)
+    d.update(kw)
+    return S.Layout(d["n_blk"], d["blk_cap"], d["n_qh"], d["n_kvh"], d["head_dim"], d["scale"], d["blk_cnt"],
+                    d["blk_key"])
+
+
+FAKE = 0x10000   # never dereferenced: validation returns before any device work
+
+
+def attn(S, L, **kw):
+    a = dict(dtype=1, branches=7, q_gran=0, q=FAKE, k=FAKE, v=FAKE, q_cmp=None, k_cmp=FAKE, v_cmp=FAKE,
+             sel=FAKE, top_k=4, sel_groups=1, gates=FAKE, o=FAKE, lse=None)
+    a.update(kw)
+    return S.lib.nsa_attn_fwd(ctypes.byref(L), a["dtype"], a["branches"], a["q_gran"], a["q"], a["k"], a["v"],
+                              a["q_cmp"], a["k_cmp"], a["v_cmp"], a["sel"], a["top_k"], a["sel_groups"],
+                              a["gates"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_blk=0), -1), (dict(blk_cap=65), -1), (dict(blk_cap=0), -1), (dict(n_qh=31), -1),
+    (dict(scale=0.0), -1), (dict(scale=float("nan")), -1), (dict(blk_cnt=None), -1),
+    (dict(head_dim=64), -2), (dict(n_qh=16, n_kvh=16), -2),
+])
+def test_attn_layout_validation(S, kw, status):
+    assert attn(S, layout(S, **kw)) == status
+    assert S.lib.nsa_last_error().decode().startswith("nsa_attn_fwd")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(branches=0), dict(branches=8), dict(gates=None), dict(lse=FAKE), dict(q=None), dict(o=None),
+    dict(k=None), dict(v_cmp=None), dict(sel=None), dict(top_k=0), dict(top_k=65), dict(sel_groups=3),
+    dict(dtype=7), dict(q_gran=5), dict(branches=1, q_gran=1, q_cmp=None),
+])
+def test_attn_argument_validation(S, kw):
+    assert attn(S, layout(S), **kw) == -1
+
+
+def test_attn_single_branch_needs_no_gate(S, monkeypatch):
+    # a single branch without gates is valid: with a forced launch failure it reaches the launch
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    assert attn(S, layout(S), branches=4, gates=None, sel=None) == -3
+    assert "forced" in S.lib.nsa_last_error().decode()
+
+
+def test_other_calls_validate(S, monkeypatch):
+    L = layout(S)
+    lib = S.lib
+    assert lib.nsa_pool_blocks(ctypes.byref(L), 1, 2, None, FAKE, None) == -1
+    assert lib.nsa_pool_blocks(ctypes.byref(L), 1, 64, FAKE, FAKE, None) == -2       # 64*32 > 1024
+    assert lib.nsa_route_geometric(ctypes.byref(L), FAKE, 0, FAKE, FAKE, None, None) == -1
+    assert lib.nsa_route_geometric(ctypes.byref(L), FAKE, 65, FAKE, FAKE, None, None) == -1
+    assert lib.nsa_route_geometric(ctypes.byref(L), None, 4, FAKE, FAKE, None, None) == -1
+    assert lib.nsa_route_geometric(ctypes.byref(layout(S, blk_key=None)), FAKE, 4, FAKE, FAKE, None, None) == -1
+    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE, None, 4, FAKE, None) == -1  # lse needed
+    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 1, FAKE, FAKE, FAKE, 4, FAKE, None) == -2
+    arr = (ctypes.c_void_p * 2)(FAKE, None)
+    assert lib.nsa_gate_combine(1, 10, 32, 32, 2, arr, FAKE, FAKE, None) == -1
+    assert lib.nsa_gate_combine(1, 10, 32, 32, 9, arr, FAKE, FAKE, None) == -1
+    assert lib.dense_gated_xattn_fwd(1, 100, 101, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.dense_gated_xattn_fwd(1, 100, -1, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.dense_gated_xattn_fwd(1, 100, 50, 32, 2, 64, 0.125, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    assert lib.nsa_pool_blocks(ctypes.byref(L), 1, 2, FAKE, FAKE, None) == -3
+    assert lib.nsa_route_geometric(ctypes.byref(L), FAKE, 4, FAKE, FAKE, None, None) == -3
+    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE, FAKE, 4, FAKE, None) == -3
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert lib.nsa_gate_combine(1, 10, 32, 32, 2, arr, FAKE, FAKE, None) == -3
+    assert lib.dense_gated_xattn_fwd(1, 100, 50, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert attn(S, L) == -3
+
+
+def test_error_message_is_thread_local(S):
+    import threading
+    assert attn(S, layout(S, n_blk=0)) == -1
+    msgs = []
+
+    def other():
+        msgs.append(S.lib.nsa_last_error().decode())
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert msgs == [""]
+    assert "n_blk" in S.lib.nsa_last_error().decode()
+
+
+def test_binding_refuses_cpu_tensors(S):
+    import torch
+    with pytest.raises(ValueError):
+        S._ptr(torch.zeros(3))
+
+
+def test_build_is_hip_only():
+    """The package has no CPU fallback: it exposes only the library wrappers."""
+    src = open(os.path.join(ROOT, "sparse_attention_feed_amd", "__init__.py")).read()
+    assert "import oracle" not in src and "from oracle" not in src
