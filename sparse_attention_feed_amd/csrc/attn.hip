@@ -106,62 +106,98 @@ template <typename T> __device__ __forceinline__ void set_elem(Frag8<T>& f, int 
   f.v[e] = from_f32<T>(x);
 }
 
-// Online-softmax state of one token (16 heads of one KV group) held by one wave.
+// Online-softmax state of one token (16 heads of one KV group) held by one wave.  The running
+// maximum is kept in base-2 logit units (mc = max * scale * log2 e) and is allowed to go stale:
+// a tile is exponentiated against the current mc, and only if some probability could exceed
+// kStaleLimit (a lane's partial sum exceeds it, or is inf/NaN because no maximum exists yet) does
+// the wave take the exact path that raises mc and rescales.  Results equal the textbook online
+// softmax up to rounding; every probability stays <= kStaleLimit, far inside fp32/bf16 range.
 struct TokState {
   f32x4 acc[2];   // O^T: lane holds d = 16*dt + 4*(lane/16) + i for head lane%16
-  float m;        // running max of raw scores for head lane%16 (replicated over lane groups)
-  float l;        // this lane group's share of the running sum
+  float mc;       // running max (base-2 units) for head lane%16, identical across lane groups
+  float l;        // this lane group's share of the running sum of probabilities
 };
+
+constexpr float kStaleLimit = 65536.0f;
 
 __device__ __forceinline__ void tok_init(TokState& s) {
   s.acc[0] = (f32x4){0.f, 0.f, 0.f, 0.f};
   s.acc[1] = s.acc[0];
-  s.m = -INFINITY;
+  s.mc = -INFINITY;
   s.l = 0.f;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// p = exp2(s*c2 - mc) for the lane's 16 scores, packed as the two B operands of the PV product;
+// returns the lane's sum of the probabilities as rounded for that product.
 template <typename T>
-__device__ __forceinline__ void tok_tile(TokState& st, const Frag8<T>& qf, const Frag8<T> (&kf)[4],
-                                         const Frag8<T> (&vf)[2][2], int nk, float c2) {
-  const int g = lane_id() >> 4;
-  f32x4 s[4];
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ float exp_pack(const f32x4 (&s)[4], float c2, float mc, Frag8<T> (&pf)[2]);
+
+template <>
+__device__ __forceinline__ float exp_pack<bf16>(const f32x4 (&s)[4], float c2, float mc, Frag8<bf16> (&pf)[2]) {
+  float lt = 0.f;
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) s[kt] = mma16(kf[kt], qf, z);
-  if (nk < TILE) {
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (16 * kt + 4 * g + i >= nk) s[kt][i] = -INFINITY;
-  }
-  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
-                       fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
-  mx = wave_max_across_rows(mx);
-  const float mnew = fmaxf(st.m, mx);
-  const float alpha = __builtin_amdgcn_exp2f((st.m - mnew) * c2);
-  const float mc = mnew * c2;
-  Frag8<T> pf[2];
-  float psum = 0.f;
+    for (int e = 0; e < 8; e += 2) {
+      const int kt = 2 * h + (e >> 2), i = e & 3;
+      f32x2 x;
+      x[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -mc));
+      x[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i + 1], c2, -mc));
+      const bf16x2 pb = __builtin_convertvector(x, bf16x2);
+      pf[h].v[e] = pb[0];
+      pf[h].v[e + 1] = pb[1];
+      lt = __builtin_amdgcn_fdot2_f32_bf16(pb, one, lt, false);
+    }
+  return lt;
+}
+
+template <>
+__device__ __forceinline__ float exp_pack<float>(const f32x4 (&s)[4], float c2, float mc, Frag8<float> (&pf)[2]) {
+  float lt = 0.f;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int kt = 2 * h + (e >> 2), i = e & 3;
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -mc));
-      set_elem(pf[h], e, p);
-      psum += to_f32(pf[h].v[e]);
+      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -mc));
+      pf[h].v[e] = x;
+      lt += x;
     }
-  st.l = st.l * alpha + psum;
-  st.m = mnew;
+  return lt;
+}
+
+template <typename T>
+__device__ __forceinline__ void tok_tile(TokState& st, const Frag8<T>& qf, const Frag8<T> (&kf)[4],
+                                         const Frag8<T> (&vf)[2][2], const f32x4 (&cmask)[4], float c2) {
+  f32x4 s[4];
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt) {
-    st.acc[dt] *= alpha;
+  for (int kt = 0; kt < 4; ++kt) s[kt] = mma16(kf[kt], qf, cmask[kt]);   // padding keys -> -inf
+  Frag8<T> pf[2];
+  float lt = exp_pack<T>(s, c2, st.mc, pf);
+  if (__builtin_amdgcn_ballot_w64(!(lt <= kStaleLimit)) != 0) {
+    // exact path: new running max for every head of the token, rescale, redo the probabilities
+    float mx = fmaxf(fmaxf(__builtin_fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                         fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+    mx = wave_max_across_rows(mx) * c2;
+    const float mcn = fmaxf(st.mc, mx);
+    const float alpha = st.mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.mc - mcn);
+    st.l *= alpha;
+    st.acc[0] *= alpha;
+    st.acc[1] *= alpha;
+    st.mc = mcn;
+    lt = exp_pack<T>(s, c2, mcn, pf);
+  }
+  st.l += lt;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int h = 0; h < 2; ++h) st.acc[dt] = mma16(vf[dt][h], pf[h], st.acc[dt]);
-  }
 }
 
 template <typename T>
@@ -176,9 +212,19 @@ __device__ __forceinline__ void load_tile_frags(const TileBuf<T>& b, Frag8<T> (&
     for (int h = 0; h < 2; ++h) vf[dt][h] = lds_frag(&b.vt[16 * dt + r][32 * h + 8 * g]);
 }
 
+// MFMA accumulator seed that masks the keys of a tile at or beyond nk (-inf) and leaves the rest.
+__device__ __forceinline__ void tile_mask(int nk, f32x4 (&cm)[4]) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cm[kt][i] = (16 * kt + 4 * g + i < nk) ? 0.f : -INFINITY;
+}
+
 // Finish one branch for one token: normalise, optionally write lse, and fold into the output.
 __device__ __forceinline__ void tok_finish(const TokState& st, f32x4 (&out)[2], float wgt, bool first,
                                            float scale, float* lse_out) {
+  (void)scale;
   const float l = wave_sum_across_rows(st.l);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
@@ -187,7 +233,7 @@ __device__ __forceinline__ void tok_finish(const TokState& st, f32x4 (&out)[2], 
     out[dt] = first ? o : out[dt] + o;
   }
   if (lse_out != nullptr && (lane_id() >> 4) == 0)
-    *lse_out = l > 0.f ? st.m * scale + __logf(l) : -INFINITY;
+    *lse_out = l > 0.f ? (st.mc + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -210,10 +256,12 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
     const uint32_t pm = part.wave_mask(u);
     if (pm) {
       Frag8<T> kf[4], vf[2][2];
+      f32x4 cm[4];
       load_tile_frags(b, kf, vf);
+      tile_mask(nk, cm);
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
-        if (pm & (1u << t)) tok_tile<T>(st[t], qf[t], kf, vf, nk, c2);
+        if (pm & (1u << t)) tok_tile<T>(st[t], qf[t], kf, vf, cm, c2);
     }
     if (more) sg.store(buf[(u + 1) & 1]);
     __syncthreads();
@@ -282,13 +330,22 @@ __device__ int block_exclusive_scan(int x, int* scratch /* NT/64 + 1 ints */) {
 // the NSA kernel
 // ---------------------------------------------------------------------------------------------
 
+// Where the gated sum of finished branches lives between branch phases: registers for f32 (the
+// small fp32 path), LDS (fp32, 64 slots x 16 heads x 32 dims = 128 KiB) for bf16, which keeps the
+// bf16 kernel within 256 VGPRs per lane.
+template <typename T> struct OutInLds { static constexpr bool value = sizeof(T) == 2; };
+
 template <typename T, int WAVES, int TPW>
 __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   constexpr int NT = WAVES * 64;
+  constexpr bool kOutLds = OutInLds<T>::value;
   static_assert(WAVES * TPW == 64, "a workgroup covers 64 query slots");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   TileBuf<T>* buf = reinterpret_cast<TileBuf<T>*>(smem);
+  // region after the tiles: the selection-union tables during the SEL phase, then (bf16, several
+  // gated branches) the fp32 running gated sum; SEL runs first so the two never overlap in time
   unsigned char* extra = smem + 2 * sizeof(TileBuf<T>);
+  float* out_lds = reinterpret_cast<float*>(extra);
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int b = wg / a.n_kvh, j = wg % a.n_kvh;
@@ -299,6 +356,8 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   const int kvs = a.n_kvh * HD;                // key row stride (elements)
   const float c2 = a.scale * kLog2e;
   const T* q = reinterpret_cast<const T*>(a.q);
+  const int n_named = __builtin_popcount(a.branches);
+  const bool multi = n_named > 1;              // gated sum over several branches
 
   // queries of this wave's tokens
   Frag8<T> qf[TPW];
@@ -314,42 +373,49 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     }
   }
 
-  f32x4 out[TPW][2];
+  f32x4 out_reg[kOutLds ? 1 : TPW][2];
   TokState st[TPW];
-  int phase = 0;
-  const int n_named = __builtin_popcount(a.branches);
-  (void)n_named;
+  T* o = reinterpret_cast<T*>(a.o);
+  int done = 0;   // branches finished so far
 
+  // Close a branch: normalise, gate, and either store (last branch) or fold into the running sum.
   auto finish_all = [&](int ch) {
+    const bool first = done == 0, last = done == n_named - 1;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
+      const int slot = w * TPW + t;
       if (!(valid & (1u << t))) continue;
-      const size_t row = (size_t)(b * cap + w * TPW + t);
+      const size_t row = (size_t)(b * cap + slot);
       float wgt = 1.f;
       if (a.gates) {
         const T* gp = reinterpret_cast<const T*>(a.gates);
         wgt = sigmoidf_(to_f32(gp[(row * a.n_qh + hh) * a.n_gch + ch]));
       }
       float* lp = a.lse ? a.lse + row * a.n_qh + hh : nullptr;
-      tok_finish(st[t], out[t], wgt, phase == 0, a.scale, lp);
-    }
-    ++phase;
-  };
-
-  // ---- compressed branch: every pooled block ----
-  if (a.branches & 1) {
+      f32x4 res[2];
+      tok_finish(st[t], res, wgt, true, a.scale, lp);
+      float* ol = out_lds + ((size_t)slot * GRP + r) * HD + 4 * g;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) tok_init(st[t]);
-    RangeSrc<T> src;
-    src.base = reinterpret_cast<const T*>(a.k_cmp) + j * HD;
-    src.vbase = reinterpret_cast<const T*>(a.v_cmp) + j * HD;
-    src.stride = kvs;
-    src.lo = 0;
-    src.hi = a.n_blk;
-    AllPart part{valid};
-    run_tiles<T, NT, TPW>(buf, src, (a.n_blk + TILE - 1) / TILE, part, st, qf, c2);
-    finish_all(phase);
-  }
+      for (int dt = 0; dt < 2; ++dt) {
+        f32x4 acc = res[dt];
+        if (!first) {
+          if constexpr (kOutLds) acc += *reinterpret_cast<const f32x4*>(ol + 16 * dt);
+          else acc += out_reg[kOutLds ? 0 : t][dt];
+        }
+        if (last) {
+          T* dst = o + (row * a.n_qh + hh) * HD + 16 * dt + 4 * g;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(acc[i]);
+        } else if constexpr (kOutLds) {
+          *reinterpret_cast<f32x4*>(ol + 16 * dt) = acc;
+        } else {
+          out_reg[kOutLds ? 0 : t][dt] = acc;
+        }
+      }
+    }
+    ++done;
+  };
+  (void)multi;
 
   // ---- selected branch: union of the block's routing rows, streamed once ----
   if (a.branches & 2) {
@@ -411,8 +477,8 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.ulist = ulist;
     src.blk_cnt = a.blk_cnt;
     UnionPart part{umask, w * TPW, valid};
-    run_tiles<T, NT, TPW>(buf, src, n_union, part, st, qf, c2);
-    finish_all(phase);
+    run_tiles<T, NT, TPW>(buf, src, n_union, part, st, qf, c2);   // ends with a barrier
+    finish_all((a.branches & 1) ? 1 : 0);
   }
 
   // ---- local branch: the query's own block ----
@@ -427,24 +493,37 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.hi = b * cap + cnt;
     AllPart part{valid};
     run_tiles<T, NT, TPW>(buf, src, 1, part, st, qf, c2);
-    finish_all(phase);
+    finish_all(n_named - 1);
   }
 
-  // ---- store: valid slots get the (gated) sum, padding slots of the block get zeros ----
-  T* o = reinterpret_cast<T*>(a.o);
+  // ---- compressed branch: every pooled block ----
+  if (a.branches & 1) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) tok_init(st[t]);
+    RangeSrc<T> src;
+    src.base = reinterpret_cast<const T*>(a.k_cmp) + j * HD;
+    src.vbase = reinterpret_cast<const T*>(a.v_cmp) + j * HD;
+    src.stride = kvs;
+    src.lo = 0;
+    src.hi = a.n_blk;
+    AllPart part{valid};
+    run_tiles<T, NT, TPW>(buf, src, (a.n_blk + TILE - 1) / TILE, part, st, qf, c2);
+    finish_all(0);
+  }
+
+  // ---- padding slots of the block: zero output (and -inf lse) ----
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int slot = w * TPW + t;
-    if (slot >= cap) continue;
+    if (slot >= cap || slot < cnt) continue;
     const size_t row = (size_t)(b * cap + slot);
-    const bool v = slot < cnt;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       T* dst = o + (row * a.n_qh + hh) * HD + 16 * dt + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(v ? out[t][dt][i] : 0.f);
+      for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(0.f);
     }
-    if (!v && a.lse && g == 0) a.lse[row * a.n_qh + hh] = -INFINITY;
+    if (a.lse && g == 0) a.lse[row * a.n_qh + hh] = -INFINITY;
   }
 }
 
@@ -455,8 +534,10 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
 template <typename T, int WAVES, int TPW>
 __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
   constexpr int NT = WAVES * 64;
+  constexpr bool kOutLds = OutInLds<T>::value;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   TileBuf<T>* buf = reinterpret_cast<TileBuf<T>*>(smem);
+  float* out_lds = reinterpret_cast<float*>(smem + 2 * sizeof(TileBuf<T>));
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int qb = wg / a.n_kvh, j = wg % a.n_kvh;
   const int w = threadIdx.x >> 6, l = lane_id();
@@ -479,8 +560,9 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
       qf[t] = glb_frag(q + 0);
     }
   }
-  f32x4 out[TPW][2];
+  f32x4 out_reg[kOutLds ? 1 : TPW][2];
   TokState st[TPW];
+  T* o = reinterpret_cast<T*>(a.o);
   for (int ph = 0; ph < 2; ++ph) {
     const int lo = ph == 0 ? 0 : a.n_x, hi = ph == 0 ? a.n_x : a.n_tok;
 #pragma unroll
@@ -495,24 +577,29 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
     run_tiles<T, NT, TPW>(buf, src, (hi - lo + TILE - 1) / TILE, part, st, qf, c2);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const int tok = qb * 64 + w * TPW + t;
+      const int slot = w * TPW + t;
+      const int tok = qb * 64 + slot;
       if (!(valid & (1u << t))) continue;
       // phase 0 holds x keys: self for x tokens, cross for y tokens
       const int ch = ((tok < a.n_x) == (ph == 0)) ? 0 : 1;
       const float wgt = sigmoidf_(to_f32(gp[((size_t)tok * a.n_qh + hh) * 2 + ch]));
-      tok_finish(st[t], out[t], wgt, ph == 0, a.scale, nullptr);
-    }
-  }
-  T* o = reinterpret_cast<T*>(a.o);
+      f32x4 res[2];
+      tok_finish(st[t], res, wgt, true, a.scale, nullptr);
+      float* ol = out_lds + ((size_t)slot * GRP + r) * HD + 4 * g;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    if (!(valid & (1u << t))) continue;
-    const int tok = qb * 64 + w * TPW + t;
+      for (int dt = 0; dt < 2; ++dt) {
+        if (ph == 0) {
+          if constexpr (kOutLds) *reinterpret_cast<f32x4*>(ol + 16 * dt) = res[dt];
+          else out_reg[kOutLds ? 0 : t][dt] = res[dt];
+        } else {
+          f32x4 acc = res[dt];
+          if constexpr (kOutLds) acc += *reinterpret_cast<const f32x4*>(ol + 16 * dt);
+          else acc += out_reg[kOutLds ? 0 : t][dt];
+          T* dst = o + ((size_t)tok * a.n_qh + hh) * HD + 16 * dt + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      T* dst = o + ((size_t)tok * a.n_qh + hh) * HD + 16 * dt + 4 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(out[t][dt][i]);
+          for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(acc[i]);
+        }
+      }
     }
   }
 }
@@ -522,12 +609,22 @@ template <> struct Shape<bf16> { static constexpr int WAVES = 8, TPW = 8; };
 template <> struct Shape<float> { static constexpr int WAVES = 16, TPW = 4; };
 
 template <typename T>
+size_t attn_lds_t(const AttnArgs& a) {
+  constexpr int NT = Shape<T>::WAVES * 64;
+  size_t extra = 0;
+  if (a.branches & 2)
+    extra = (size_t)a.n_words * 8 + (size_t)a.u_cap * 4 + (NT / 64 + 1) * 4 + 8 + (size_t)a.u_cap * 8;
+  if (OutInLds<T>::value && __builtin_popcount(a.branches) > 1) {
+    const size_t out_bytes = (size_t)64 * GRP * HD * sizeof(float);
+    if (out_bytes > extra) extra = out_bytes;
+  }
+  return 2 * sizeof(TileBuf<T>) + extra;
+}
+
+template <typename T>
 hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
-  size_t lds = 2 * sizeof(TileBuf<T>);
-  if (a.branches & 2) {
-    lds += (size_t)a.n_words * 8 + (size_t)a.u_cap * 4 + (NT / 64 + 1) * 4 + 8 + (size_t)a.u_cap * 8;
-  }
+  const size_t lds = attn_lds_t<T>(a);
   const int nwg = a.n_blk * a.n_kvh;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nsa_attn_kernel<T, WAVES, TPW>),
@@ -541,8 +638,13 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
 template <typename T>
 hipError_t launch_dense_t(const DenseArgs& a, hipStream_t s) {
   constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
-  const size_t lds = 2 * sizeof(TileBuf<T>);
+  const size_t lds = 2 * sizeof(TileBuf<T>) + (OutInLds<T>::value ? (size_t)64 * GRP * HD * sizeof(float) : 0);
   const int nwg = ((a.n_tok + 63) / 64) * a.n_kvh;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_xattn_kernel<T, WAVES, TPW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((dense_xattn_kernel<T, WAVES, TPW>), dim3(nwg), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
@@ -550,11 +652,7 @@ hipError_t launch_dense_t(const DenseArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t attn_lds_bytes(int is_bf16, const AttnArgs& a) {
-  const int NT = is_bf16 ? 512 : 1024;
-  size_t lds = 2 * (is_bf16 ? sizeof(TileBuf<bf16>) : sizeof(TileBuf<float>));
-  if (a.branches & 2)
-    lds += (size_t)a.n_words * 8 + (size_t)a.u_cap * 4 + (NT / 64 + 1) * 4 + 8 + (size_t)a.u_cap * 8;
-  return lds;
+  return is_bf16 ? attn_lds_t<bf16>(a) : attn_lds_t<float>(a);
 }
 
 hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s) {
