@@ -106,37 +106,70 @@ template <typename T> __device__ __forceinline__ void set_elem(Frag8<T>& f, int 
   f.v[e] = from_f32<T>(x);
 }
 
-// Online-softmax state of one token (16 heads of one KV group) held by one wave.  The running
-// maximum is kept in base-2 logit units (mc = max * scale * log2 e) and is allowed to go stale:
-// a tile is exponentiated against the current mc, and only if some probability could exceed
-// kStaleLimit (a lane's partial sum exceeds it, or is inf/NaN because no maximum exists yet) does
-// the wave take the exact path that raises mc and rescales.  Results equal the textbook online
-// softmax up to rounding; every probability stays <= kStaleLimit, far inside fp32/bf16 range.
+// Online-softmax state of one token (16 heads of one KV group) held by one wave.
+//
+// Queries are pre-scaled by c2 = scale * log2(e) in fp32 and rounded once to the storage type, so
+// S^T comes out in base-2 logit units (for bf16 this adds one rounding of relative size <= 2^-9
+// per query element, the same order as the bf16 rounding of the probabilities).  The running
+// maximum mc (base-2 units) starts at 0 and is allowed to go stale: it enters the QK^T product as
+// the MFMA accumulator seed (-mc, together with -inf for padding keys), so exp2 reads the MFMA
+// output directly.  The wave takes an exact path only when a lane's probability sum could exceed
+// kStaleLimit (or is not finite), or when a head has no probability mass yet and the tile's sum is
+// tiny; that path moves mc to the tile maximum and rescales.  Results equal the textbook online
+// softmax up to rounding, every probability stays <= kStaleLimit, and no row underflows.
 struct TokState {
   f32x4 acc[2];   // O^T: lane holds d = 16*dt + 4*(lane/16) + i for head lane%16
-  float mc;       // running max (base-2 units) for head lane%16, identical across lane groups
+  float mc;       // running reference max (base-2 units) for head lane%16, same in all lane groups
   float l;        // this lane group's share of the running sum of probabilities
 };
 
 constexpr float kStaleLimit = 65536.0f;
+constexpr float kTinyMass = 1.0e-30f;
 
 __device__ __forceinline__ void tok_init(TokState& s) {
   s.acc[0] = (f32x4){0.f, 0.f, 0.f, 0.f};
   s.acc[1] = s.acc[0];
-  s.mc = -INFINITY;
+  s.mc = 0.f;
   s.l = 0.f;
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// p = exp2(s*c2 - mc) for the lane's 16 scores, packed as the two B operands of the PV product;
+// Pre-scaled query fragment of one token: the MFMA B operand of S^T = K Q^T.
+template <typename T> struct QF { Frag8<T> hi; };
+
+__device__ __forceinline__ QF<bf16> make_qf(const bf16* p, float c2) {
+  const bf16x8 raw = *reinterpret_cast<const bf16x8*>(p);
+  QF<bf16> q;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q.hi.v[e] = (bf16)((float)raw[e] * c2);
+  return q;
+}
+__device__ __forceinline__ QF<float> make_qf(const float* p, float c2) {
+  QF<float> q;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    q.hi.v[e] = a[e] * c2;
+    q.hi.v[e + 4] = b[e] * c2;
+  }
+  return q;
+}
+template <typename T> __device__ __forceinline__ QF<T> zero_qf() {
+  QF<T> q;
+  q.hi.v = decltype(q.hi.v){};
+  return q;
+}
+
+// p = exp2(x) for the lane's 16 base-2 logits, packed as the two B operands of the PV product;
 // returns the lane's sum of the probabilities as rounded for that product.
 template <typename T>
-__device__ __forceinline__ float exp_pack(const f32x4 (&s)[4], float c2, float mc, Frag8<T> (&pf)[2]);
+__device__ __forceinline__ float exp_pack(const f32x4 (&x)[4], Frag8<T> (&pf)[2]);
 
 template <>
-__device__ __forceinline__ float exp_pack<bf16>(const f32x4 (&s)[4], float c2, float mc, Frag8<bf16> (&pf)[2]) {
+__device__ __forceinline__ float exp_pack<bf16>(const f32x4 (&x)[4], Frag8<bf16> (&pf)[2]) {
   float lt = 0.f;
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
@@ -144,10 +177,10 @@ __device__ __forceinline__ float exp_pack<bf16>(const f32x4 (&s)[4], float c2, f
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const int kt = 2 * h + (e >> 2), i = e & 3;
-      f32x2 x;
-      x[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -mc));
-      x[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i + 1], c2, -mc));
-      const bf16x2 pb = __builtin_convertvector(x, bf16x2);
+      f32x2 p;
+      p[0] = __builtin_amdgcn_exp2f(x[kt][i]);
+      p[1] = __builtin_amdgcn_exp2f(x[kt][i + 1]);
+      const bf16x2 pb = __builtin_convertvector(p, bf16x2);
       pf[h].v[e] = pb[0];
       pf[h].v[e + 1] = pb[1];
       lt = __builtin_amdgcn_fdot2_f32_bf16(pb, one, lt, false);
@@ -156,48 +189,102 @@ __device__ __forceinline__ float exp_pack<bf16>(const f32x4 (&s)[4], float c2, f
 }
 
 template <>
-__device__ __forceinline__ float exp_pack<float>(const f32x4 (&s)[4], float c2, float mc, Frag8<float> (&pf)[2]) {
+__device__ __forceinline__ float exp_pack<float>(const f32x4 (&x)[4], Frag8<float> (&pf)[2]) {
   float lt = 0.f;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int kt = 2 * h + (e >> 2), i = e & 3;
-      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -mc));
-      pf[h].v[e] = x;
-      lt += x;
+      const float p = __builtin_amdgcn_exp2f(x[kt][i]);
+      pf[h].v[e] = p;
+      lt += p;
     }
   return lt;
 }
 
-template <typename T>
-__device__ __forceinline__ void tok_tile(TokState& st, const Frag8<T>& qf, const Frag8<T> (&kf)[4],
-                                         const Frag8<T> (&vf)[2][2], const f32x4 (&cmask)[4], float c2) {
-  f32x4 s[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) s[kt] = mma16(kf[kt], qf, cmask[kt]);   // padding keys -> -inf
-  Frag8<T> pf[2];
-  float lt = exp_pack<T>(s, c2, st.mc, pf);
-  if (__builtin_amdgcn_ballot_w64(!(lt <= kStaleLimit)) != 0) {
-    // exact path: new running max for every head of the token, rescale, redo the probabilities
-    float mx = fmaxf(fmaxf(__builtin_fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+__device__ __forceinline__ float lane_max16(const f32x4 (&s)[4]) {
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  return fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
                          fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
-    mx = wave_max_across_rows(mx) * c2;
-    const float mcn = fmaxf(st.mc, mx);
-    const float alpha = st.mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.mc - mcn);
-    st.l *= alpha;
-    st.acc[0] *= alpha;
-    st.acc[1] *= alpha;
-    st.mc = mcn;
-    lt = exp_pack<T>(s, c2, mcn, pf);
+}
+
+// Logits of one token against the tile, relative to its reference max: S^T = K Q^T + seed with
+// seed = -mc on keys below nk and -inf on padding keys (cm holds 0 / -inf).
+template <typename T>
+__device__ __forceinline__ void tok_qk(const TokState& st, const QF<T>& qf, const Frag8<T> (&kf)[4],
+                                       const f32x4 (&cm)[4], bool full, f32x4 (&x)[4]) {
+  if (full) {
+    const f32x4 seed = {-st.mc, -st.mc, -st.mc, -st.mc};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) x[kt] = mma16(kf[kt], qf.hi, seed);
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) x[kt] = mma16(kf[kt], qf.hi, cm[kt] - st.mc);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void tok_softmax_pv(TokState& st, f32x4 (&x)[4], const Frag8<T> (&vf)[2][2]) {
+  Frag8<T> pf[2];
+  float lt = exp_pack<T>(x, pf);
+  if (__builtin_amdgcn_ballot_w64(!(lt <= kStaleLimit) || !(st.l + lt >= kTinyMass)) != 0) {
+    // exact path for every head of the token: move the reference max to the tile's maximum if it
+    // is larger, or to it outright while the head has no mass yet; rescale and redo
+    const float xm = wave_max_across_rows(lane_max16(x));
+    const float lh = wave_sum_across_rows(st.l);
+    float shift = lh > 0.f ? fmaxf(xm, 0.f) : xm;
+    if (!(shift > -INFINITY)) shift = 0.f;         // no valid key for this lane's head
+    if (lh > 0.f && shift > 0.f) {
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      st.l *= alpha;
+      st.acc[0] *= alpha;
+      st.acc[1] *= alpha;
+    }
+    st.mc += shift;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) x[kt] -= shift;
+    lt = exp_pack<T>(x, pf);
   }
   st.l += lt;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int h = 0; h < 2; ++h) st.acc[dt] = mma16(vf[dt][h], pf[h], st.acc[dt]);
+}
+
+// Tokens t < n (a prefix of the wave's tokens) against one tile, software-pipelined: the QK^T
+// product of token t+1 is issued before the softmax of token t.
+template <typename T, int TPW>
+__device__ __forceinline__ void tile_prefix(TokState (&st)[TPW], const QF<T> (&qf)[TPW], int n, const Frag8<T> (&kf)[4],
+                                            const Frag8<T> (&vf)[2][2], const f32x4 (&cm)[4], bool full) {
+  f32x4 x[4], xn[4];
+  tok_qk<T>(st[0], qf[0], kf, cm, full, x);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (t < n) {
+      if (t + 1 < TPW && t + 1 < n) tok_qk<T>(st[t + 1], qf[t + 1], kf, cm, full, xn);
+      tok_softmax_pv<T>(st[t], x, vf);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) x[kt] = xn[kt];
+    }
+  }
+}
+
+// Tokens named by a mask (selected branch).
+template <typename T, int TPW>
+__device__ __forceinline__ void tile_masked(TokState (&st)[TPW], const QF<T> (&qf)[TPW], uint32_t pm,
+                                            const Frag8<T> (&kf)[4], const Frag8<T> (&vf)[2][2],
+                                            const f32x4 (&cm)[4], bool full) {
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (pm & (1u << t)) {
+      f32x4 x[4];
+      tok_qk<T>(st[t], qf[t], kf, cm, full, x);
+      tok_softmax_pv<T>(st[t], x, vf);
+    }
+  }
 }
 
 template <typename T>
@@ -221,17 +308,12 @@ __device__ __forceinline__ void tile_mask(int nk, f32x4 (&cm)[4]) {
     for (int i = 0; i < 4; ++i) cm[kt][i] = (16 * kt + 4 * g + i < nk) ? 0.f : -INFINITY;
 }
 
-// Finish one branch for one token: normalise, optionally write lse, and fold into the output.
-__device__ __forceinline__ void tok_finish(const TokState& st, f32x4 (&out)[2], float wgt, bool first,
-                                           float scale, float* lse_out) {
-  (void)scale;
+// Finish one branch for one token: normalise and gate; optionally write lse (natural log).
+__device__ __forceinline__ void tok_finish(const TokState& st, f32x4 (&res)[2], float wgt, float* lse_out) {
   const float l = wave_sum_across_rows(st.l);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt) {
-    f32x4 o = st.acc[dt] * (inv * wgt);
-    out[dt] = first ? o : out[dt] + o;
-  }
+  for (int dt = 0; dt < 2; ++dt) res[dt] = st.acc[dt] * (inv * wgt);
   if (lse_out != nullptr && (lane_id() >> 4) == 0)
     *lse_out = l > 0.f ? (st.mc + __log2f(l)) * kLn2 : -INFINITY;
 }
@@ -240,9 +322,11 @@ __device__ __forceinline__ void tok_finish(const TokState& st, f32x4 (&out)[2], 
 // generic tile loop: double-buffered LDS staging shared by the workgroup
 // ---------------------------------------------------------------------------------------------
 
+// Part::kAll: every wave's participating tokens are the prefix t < n_valid (compressed, local and
+// dense phases); otherwise a per-tile mask (selected phase).
 template <typename T, int NT, int TPW, class Src, class Part>
 __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int ntiles, const Part& part,
-                                          TokState (&st)[TPW], const Frag8<T> (&qf)[TPW], float c2) {
+                                          TokState (&st)[TPW], const QF<T> (&qf)[TPW]) {
   Stager<T, NT> sg;
   if (ntiles <= 0) return;
   sg.load(src.kptr(0), src.vptr(0), src.stride, src.nk(0));
@@ -253,15 +337,14 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
     if (more) sg.load(src.kptr(u + 1), src.vptr(u + 1), src.stride, src.nk(u + 1));
     const TileBuf<T>& b = buf[u & 1];
     const int nk = src.nk(u);
-    const uint32_t pm = part.wave_mask(u);
-    if (pm) {
+    const uint32_t pm = Part::kAll ? 0u : part.wave_mask(u);
+    if (Part::kAll ? part.n > 0 : pm != 0u) {
       Frag8<T> kf[4], vf[2][2];
       f32x4 cm[4];
       load_tile_frags(b, kf, vf);
       tile_mask(nk, cm);
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-        if (pm & (1u << t)) tok_tile<T>(st[t], qf[t], kf, vf, cm, c2);
+      if constexpr (Part::kAll) tile_prefix<T, TPW>(st, qf, part.n, kf, vf, cm, nk == TILE);
+      else tile_masked<T, TPW>(st, qf, pm, kf, vf, cm, nk == TILE);
     }
     if (more) sg.store(buf[(u + 1) & 1]);
     __syncthreads();
@@ -291,15 +374,24 @@ template <typename T> struct UnionSrc {     // one tile per block in the selecti
   __device__ int nk(int u) const { return blk_cnt[ulist[u]]; }
 };
 
-struct AllPart {                 // every valid token of the wave takes part
-  uint32_t m;
-  __device__ uint32_t wave_mask(int) const { return m; }
+struct AllPart {                 // the wave's valid tokens (a prefix) take part in every tile
+  static constexpr bool kAll = true;
+  int n;
+  __device__ uint32_t wave_mask(int) const { return (1u << n) - 1u; }
 };
+template <int WAVES, int TPW>
 struct UnionPart {               // tokens whose routing row holds the tile's block
-  const unsigned long long* umask;  // LDS
-  int shift;                        // first slot of this wave
-  uint32_t valid;
-  __device__ uint32_t wave_mask(int u) const { return (uint32_t)(umask[u] >> shift) & valid; }
+  static constexpr bool kAll = false;
+  const unsigned long long* umask;  // LDS, bit s = block slot s
+  int w;                            // wave index; its token t is slot t * WAVES + w
+  int n = 0;                        // unused
+  __device__ uint32_t wave_mask(int u) const {
+    const unsigned long long m = umask[u] >> w;
+    uint32_t r = 0;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) r |= (uint32_t)((m >> (t * WAVES)) & 1ull) << t;
+    return r;
+  }
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -359,18 +451,16 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   const int n_named = __builtin_popcount(a.branches);
   const bool multi = n_named > 1;              // gated sum over several branches
 
-  // queries of this wave's tokens
-  Frag8<T> qf[TPW];
-  uint32_t valid = 0;
+  // queries of this wave's tokens: token t of wave w is block slot t * WAVES + w, so the valid
+  // slots [0, cnt) spread evenly over the waves and each wave's valid tokens are a prefix
+  QF<T> qf[TPW];
+  const int n_valid = cnt > w ? min(TPW, (cnt - w + WAVES - 1) / WAVES) : 0;
+  const uint32_t valid = (1u << n_valid) - 1u;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int slot = w * TPW + t;
-    if (slot < cnt) {
-      valid |= 1u << t;
-      qf[t] = glb_frag(q + ((size_t)(b * cap + slot) * a.n_qh + hh) * HD + 8 * g);
-    } else {
-      qf[t] = glb_frag(q + 0);   // unused
-    }
+    const int slot = t * WAVES + w;
+    if (t < n_valid) qf[t] = make_qf(q + ((size_t)(b * cap + slot) * a.n_qh + hh) * HD + 8 * g, c2);
+    else qf[t] = zero_qf<T>();
   }
 
   f32x4 out_reg[kOutLds ? 1 : TPW][2];
@@ -383,7 +473,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     const bool first = done == 0, last = done == n_named - 1;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const int slot = w * TPW + t;
+      const int slot = t * WAVES + w;
       if (!(valid & (1u << t))) continue;
       const size_t row = (size_t)(b * cap + slot);
       float wgt = 1.f;
@@ -393,7 +483,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
       }
       float* lp = a.lse ? a.lse + row * a.n_qh + hh : nullptr;
       f32x4 res[2];
-      tok_finish(st[t], res, wgt, true, a.scale, lp);
+      tok_finish(st[t], res, wgt, lp);
       float* ol = out_lds + ((size_t)slot * GRP + r) * HD + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
@@ -476,8 +566,8 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.cap = cap;
     src.ulist = ulist;
     src.blk_cnt = a.blk_cnt;
-    UnionPart part{umask, w * TPW, valid};
-    run_tiles<T, NT, TPW>(buf, src, n_union, part, st, qf, c2);   // ends with a barrier
+    UnionPart<WAVES, TPW> part{umask, w};
+    run_tiles<T, NT, TPW>(buf, src, n_union, part, st, qf);   // ends with a barrier
     finish_all((a.branches & 1) ? 1 : 0);
   }
 
@@ -491,8 +581,8 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.stride = kvs;
     src.lo = b * cap;
     src.hi = b * cap + cnt;
-    AllPart part{valid};
-    run_tiles<T, NT, TPW>(buf, src, 1, part, st, qf, c2);
+    AllPart part{n_valid};
+    run_tiles<T, NT, TPW>(buf, src, 1, part, st, qf);
     finish_all(n_named - 1);
   }
 
@@ -506,15 +596,15 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.stride = kvs;
     src.lo = 0;
     src.hi = a.n_blk;
-    AllPart part{valid};
-    run_tiles<T, NT, TPW>(buf, src, (a.n_blk + TILE - 1) / TILE, part, st, qf, c2);
+    AllPart part{n_valid};
+    run_tiles<T, NT, TPW>(buf, src, (a.n_blk + TILE - 1) / TILE, part, st, qf);
     finish_all(0);
   }
 
   // ---- padding slots of the block: zero output (and -inf lse) ----
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int slot = w * TPW + t;
+    const int slot = t * WAVES + w;
     if (slot >= cap || slot < cnt) continue;
     const size_t row = (size_t)(b * cap + slot);
 #pragma unroll
@@ -548,17 +638,15 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
   const T* q = reinterpret_cast<const T*>(a.q);
   const T* gp = reinterpret_cast<const T*>(a.gates);
 
-  Frag8<T> qf[TPW];
-  uint32_t valid = 0;
+  QF<T> qf[TPW];
+  const int rem = a.n_tok - qb * 64;            // tokens of this workgroup: slots [0, rem)
+  const int n_valid = rem > w ? min(TPW, (rem - w + WAVES - 1) / WAVES) : 0;
+  const uint32_t valid = (1u << n_valid) - 1u;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int tok = qb * 64 + w * TPW + t;
-    if (tok < a.n_tok) {
-      valid |= 1u << t;
-      qf[t] = glb_frag(q + ((size_t)tok * a.n_qh + hh) * HD + 8 * g);
-    } else {
-      qf[t] = glb_frag(q + 0);
-    }
+    const int tok = qb * 64 + t * WAVES + w;
+    if (t < n_valid) qf[t] = make_qf(q + ((size_t)tok * a.n_qh + hh) * HD + 8 * g, c2);
+    else qf[t] = zero_qf<T>();
   }
   f32x4 out_reg[kOutLds ? 1 : TPW][2];
   TokState st[TPW];
@@ -573,18 +661,18 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
     src.stride = kvs;
     src.lo = lo;
     src.hi = hi;
-    AllPart part{valid};
-    run_tiles<T, NT, TPW>(buf, src, (hi - lo + TILE - 1) / TILE, part, st, qf, c2);
+    AllPart part{n_valid};
+    run_tiles<T, NT, TPW>(buf, src, (hi - lo + TILE - 1) / TILE, part, st, qf);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const int slot = w * TPW + t;
+      const int slot = t * WAVES + w;
       const int tok = qb * 64 + slot;
       if (!(valid & (1u << t))) continue;
       // phase 0 holds x keys: self for x tokens, cross for y tokens
       const int ch = ((tok < a.n_x) == (ph == 0)) ? 0 : 1;
       const float wgt = sigmoidf_(to_f32(gp[((size_t)tok * a.n_qh + hh) * 2 + ch]));
       f32x4 res[2];
-      tok_finish(st[t], res, wgt, true, a.scale, nullptr);
+      tok_finish(st[t], res, wgt, nullptr);
       float* ol = out_lds + ((size_t)slot * GRP + r) * HD + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
