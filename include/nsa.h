@@ -110,7 +110,8 @@ nsa_status nsa_route_geometric(const nsa_layout* layout, const float* pts, int32
  *   q_gran NSA_Q_BLOCK: rows = n_blk, q is the pooled query [n_blk][n_qh][D]
  *   k_cmp [n_blk][n_kvh][D];  lse [rows][n_qh] float32 natural-log partition function of the
  *   compressed branch (required iff G > 1);  sel [rows][n_kvh][top_k] int32.
- * Supported: (D, G) = (32, 16) with q_gran TOKEN; 1 <= top_k <= 64; n_blk <= 65536.
+ * Supported: (D, G) = (32, 16) with q_gran TOKEN (bf16 or f32, n_blk <= 65536), and (64, 1) with
+ * q_gran BLOCK (bf16); 1 <= top_k <= 64.
  */
 nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_qgran q_gran,
                                  const void* q, const void* k_cmp, const float* lse,
@@ -137,8 +138,10 @@ nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_
  *   k_cmp, v_cmp [n_blk][n_kvh][D] (CMP); unused pointers may be NULL.  o [S][n_qh][D].
  *   lse: NULL, or (single branch only) float32 [rows][n_qh] natural-log partition function,
  *        rows = n_blk for CMP with NSA_Q_BLOCK, else S; -inf on padding rows and empty key sets.
- * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16; NSA_Q_TOKEN; top_k <= 64; n_blk <= 65536
- * when SEL is named.  Accumulation is fp32; bf16 probabilities feed the value product.
+ * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16 with NSA_Q_TOKEN (n_blk <= 65536 when SEL
+ * is named); and (D, G) = (64, 1) for NSA_BF16 with NSA_Q_BLOCK, branches CMP and SEL, blk_cap in
+ * {1, 2, 4, 8, 16} (the compressed branch's gated result is written to o in bf16 and the selected
+ * branch adds to it).  top_k <= 64.  Accumulation is fp32; bf16 probabilities feed the value product.
  */
 nsa_status nsa_attn_fwd(const nsa_layout* layout, nsa_dtype dtype, uint32_t branches,
                         nsa_qgran q_gran, const void* q, const void* k, const void* v,

@@ -144,6 +144,8 @@ def route_geometric(layout: BlockLayout, pts, top_k, sel=None, sel_d2=None, cent
 
 
 def route_scores_topk(layout: BlockLayout, q, k_cmp, lse, top_k, q_gran=Q_TOKEN, sel=None):
+    """Top-k blocks by compressed score (GQA: summed group probability, needs lse; one query head
+    per KV head: raw score).  Returns sel [rows, n_kvh, top_k]."""
     rows = layout.n_slots if q_gran == Q_TOKEN else layout.n_blk
     if sel is None:
         sel = torch.empty((rows, layout.n_kvh, top_k), dtype=torch.int32, device=q.device)

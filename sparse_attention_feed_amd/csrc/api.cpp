@@ -107,6 +107,26 @@ nsa_status nsa_route_scores_topk(const nsa_layout* L, nsa_dtype dtype, nsa_qgran
   if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "nsa_route_scores_topk: top_k must be in 1..64");
   const int G = L->n_qh / L->n_kvh;
   if (G > 1 && lse == nullptr) return fail(NSA_ERR_INVALID, "nsa_route_scores_topk: lse is required when n_qh > n_kvh");
+  if (G == 1) {
+    if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK || dtype != NSA_BF16)
+      return fail(NSA_ERR_UNSUPPORTED,
+                  "nsa_route_scores_topk: with one query head per KV head the compiled kernel takes head_dim 64, "
+                  "NSA_Q_BLOCK rows and bf16");
+    NSA_FORCED_FAILURE("nsa_route_scores_topk");
+    nsa::G1Args g{};
+    g.q_cmp = q;
+    g.k_cmp = k_cmp;
+    g.sel = sel;
+    g.blk_cnt = L->blk_cnt;
+    g.blk_key = L->blk_key;
+    g.n_blk = L->n_blk;
+    g.cap = L->blk_cap;
+    g.n_qh = L->n_qh;
+    g.n_kvh = L->n_kvh;
+    g.top_k = top_k;
+    g.scale = L->scale;
+    return hip_status(nsa::launch_route_g1(g, stream), "nsa_route_scores_topk");
+  }
   if (L->head_dim != 32 || G != 16 || q_gran != NSA_Q_TOKEN)
     return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: compiled for head_dim 32, 16 query heads per KV head, per-token rows");
   if (L->n_blk > 65536) return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: n_blk must be <= 65536");
@@ -155,8 +175,43 @@ nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches,
       return fail(NSA_ERR_INVALID, "nsa_attn_fwd: sel_groups must be 1 or n_kvh");
     if (L->n_blk > 65536) return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: SEL supports n_blk <= 65536");
   }
+  if (L->n_qh == L->n_kvh) {
+    // one query head per KV head (score-routed, block-granular layout)
+    if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK || dtype != NSA_BF16 || (branches & NSA_BR_LOC) ||
+        L->blk_cap > 16 || 64 % L->blk_cap != 0)
+      return fail(NSA_ERR_UNSUPPORTED,
+                  "nsa_attn_fwd: with one query head per KV head the compiled kernels take head_dim 64, NSA_Q_BLOCK, "
+                  "bf16, the CMP and SEL branches and blk_cap in {1, 2, 4, 8, 16}");
+    NSA_FORCED_FAILURE("nsa_attn_fwd");
+    nsa::G1Args g{};
+    g.q = q;
+    g.k = k;
+    g.v = v;
+    g.q_cmp = q_cmp;
+    g.k_cmp = k_cmp;
+    g.v_cmp = v_cmp;
+    g.sel = sel;
+    g.blk_cnt = L->blk_cnt;
+    g.blk_key = L->blk_key;
+    g.gates = gate_logits;
+    g.o = o;
+    g.lse = lse;
+    g.n_blk = L->n_blk;
+    g.cap = L->blk_cap;
+    g.n_qh = L->n_qh;
+    g.n_kvh = L->n_kvh;
+    g.top_k = (branches & NSA_BR_SEL) ? top_k : 0;
+    g.sel_groups = sel_groups < 1 ? 1 : sel_groups;
+    g.n_gch = n_named;
+    g.ch_cmp = 0;
+    g.ch_sel = (branches & NSA_BR_CMP) ? 1 : 0;
+    g.scale = L->scale;
+    g.branches = branches;
+    return hip_status(nsa::launch_attn_g1(g, stream), "nsa_attn_fwd");
+  }
   if (L->head_dim != 32 || L->n_qh / L->n_kvh != 16 || q_gran != NSA_Q_TOKEN)
-    return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: compiled for head_dim 32, 16 query heads per KV head, NSA_Q_TOKEN");
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: compiled for head_dim 32, 16 query heads per KV head, NSA_Q_TOKEN "
+                                     "(or head_dim 64, one query head per KV head, NSA_Q_BLOCK)");
   nsa::AttnArgs a;
   a.q = q;
   a.k = k;

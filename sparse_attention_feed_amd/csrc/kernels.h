@@ -56,6 +56,28 @@ struct ScoreRouteArgs {
   float scale;
 };
 
+// One query head per KV head, head dim 64, block-granular queries and routing rows (bf16).
+struct G1Args {
+  const void* q;        // [S][n_qh][64] token queries (selected branch)
+  const void* k;        // [S][n_kvh][64]
+  const void* v;
+  const void* q_cmp;    // [n_blk][n_qh][64] pooled queries
+  const void* k_cmp;    // [n_blk][n_kvh][64]
+  const void* v_cmp;
+  const int32_t* sel;   // routing rows [n_blk][sel_groups][top_k] (attention input, routing output)
+  const int32_t* blk_cnt;
+  const uint32_t* blk_key;
+  const void* gates;    // nullable
+  void* o;
+  float* lse;           // nullable
+  int n_blk, cap, n_qh, n_kvh, top_k, sel_groups, n_gch, ch_cmp, ch_sel;
+  float scale;
+  uint32_t branches;
+  int accumulate;       // selected branch adds to o (the compressed branch wrote it first)
+};
+hipError_t launch_route_g1(const G1Args& a, hipStream_t s);
+hipError_t launch_attn_g1(const G1Args& a, hipStream_t s);
+
 size_t attn_lds_bytes(int is_bf16, const AttnArgs& a);
 hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s);
 hipError_t launch_dense(int is_bf16, const DenseArgs& a, hipStream_t s);

@@ -1,0 +1,175 @@
+"""GPU parity of the score-routed, block-granular path (one query head per KV head, head dim 64):
+score routing, the compressed branch with pooled queries, the selected branch with per-block
+routing rows, and the gated combination, against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import host, max_err, rounded, say, to_dev
+
+pytestmark = pytest.mark.gpu
+_cache = {}
+
+
+def wl(name):
+    if name not in _cache:
+        _cache[name] = W.make(name)
+    return _cache[name]
+
+
+def pooled(w):
+    return [rounded(O.pool_blocks(x, w.blk_cnt, w.blk_cap), "bf16") for x in (w.q, w.k, w.v)]
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
+
+
+def check_eps_ties(got, ref_sel, imp, k, eps_rel):
+    exact = 0
+    R, H = ref_sel.shape[:2]
+    for r in range(R):
+        for h in range(H):
+            g_row, r_row = got[r, h], ref_sel[r, h]
+            assert len(set(g_row.tolist())) == k and g_row.min() >= 0
+            if np.array_equal(g_row, r_row):
+                exact += 1
+                continue
+            kth = np.sort(imp[r, h])[::-1][k - 1]
+            for b in set(g_row.tolist()) ^ set(r_row.tolist()):
+                assert abs(imp[r, h, b] - kth) <= eps_rel * abs(kth) + 1e-3, (r, h, b)
+    return exact / (R * H)
+
+
+def test_score_routing_block_rows_eps_ties():
+    import sparse_attention_feed_amd as S
+    w = wl("speed3r_small")
+    d = to_dev(w)
+    qc, kc, _ = pooled(w)
+    say("route_g1 speed3r_small")
+    sel = S.route_scores_topk(d["layout"], dev(qc), dev(kc), None, w.top_k, q_gran=S.Q_BLOCK)
+    torch.cuda.synchronize()
+    ref_sel, imp = O.route_scores(qc, kc, w.blk_key, w.scale, w.top_k)
+    frac = check_eps_ties(host(sel), ref_sel, imp, w.top_k, 1e-2)
+    assert frac >= 0.9, frac
+
+
+def test_score_routing_exact_on_integer_inputs():
+    """Small-integer pooled queries and keys make every score exact in fp32: ranking is bit-exact,
+    ties included (resolved by blk_key)."""
+    import sparse_attention_feed_amd as S
+    w = wl("speed3r_small")
+    d = to_dev(w)
+    rng = np.random.default_rng(5)
+    qc = rng.integers(-2, 3, size=(w.n_blk, w.n_qh, w.head_dim)).astype(np.float32)
+    kc = rng.integers(-2, 3, size=(w.n_blk, w.n_kvh, w.head_dim)).astype(np.float32)
+    for k in (16, 5, 32):
+        say("route_g1 exact k", k)
+        sel = S.route_scores_topk(d["layout"], dev(qc), dev(kc), None, k, q_gran=S.Q_BLOCK)
+        torch.cuda.synchronize()
+        ref_sel, _ = O.route_scores(qc, kc, w.blk_key, w.scale, k)
+        np.testing.assert_array_equal(host(sel), ref_sel)
+
+
+@pytest.mark.parametrize("branch", ["cmp", "sel"])
+def test_single_branch_block_rows(branch):
+    import sparse_attention_feed_amd as S
+    w = wl("speed3r_small")
+    d = to_dev(w)
+    qc, kc, vc = pooled(w)
+    sel, _ = O.route_scores(qc, kc, w.blk_key, w.scale, w.top_k)
+    rows = w.n_blk if branch == "cmp" else w.n_slots
+    lse = torch.empty((rows, w.n_qh), dtype=torch.float32, device="cuda")
+    say("attn_g1", branch)
+    bit = S.BR_CMP if branch == "cmp" else S.BR_SEL
+    o = S.attn_fwd(d["layout"], bit, d["q"], d["k"], d["v"], q_cmp=dev(qc), k_cmp=dev(kc), v_cmp=dev(vc),
+                   sel=torch.from_numpy(sel).cuda(), top_k=w.top_k, sel_groups=w.n_kvh, lse=lse, q_gran=S.Q_BLOCK)
+    torch.cuda.synchronize()
+    if branch == "cmp":
+        ref, ref_lse = O.attn_branch(O.CMP, qc.astype(np.float64), kc.astype(np.float64), vc.astype(np.float64),
+                                     w.blk_cnt, w.blk_cap, w.scale, q_gran="block")
+        # lse of the compressed branch is per pooled row
+        ref_lse_rows = np.zeros((w.n_blk, w.n_qh))
+        for b in range(w.n_blk):
+            ref_lse_rows[b] = O.attend(qc[b], kc, vc, w.scale)[1]
+        gl = host(lse)
+        assert max_err(gl, ref_lse_rows) <= 5e-3
+    else:
+        ref, ref_lse = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel,
+                                     q_gran="block")
+        vm = w.valid_mask()
+        gl = host(lse)
+        assert np.all(np.isneginf(gl[~vm]))
+        assert max_err(gl[vm], ref_lse[vm]) <= 5e-3
+    vm = w.valid_mask()
+    err = max_err(host(o), ref)
+    assert err <= 2e-2, err
+    assert np.all(host(o)[~vm] == 0)
+
+
+def test_fused_layer_block_rows():
+    """Pool Q/K/V, score routing, then the gated compressed + selected branches: the whole layer."""
+    import sparse_attention_feed_amd as S
+    w = wl("speed3r_small")
+    d = to_dev(w)
+    say("speed3r layer small")
+    L = d["layout"]
+    qc = S.pool_blocks(L, d["q"])
+    kc = S.pool_blocks(L, d["k"])
+    vc = S.pool_blocks(L, d["v"])
+    sel = S.route_scores_topk(L, qc, kc, None, w.top_k, q_gran=S.Q_BLOCK)
+    o = S.attn_fwd(L, S.BR_CMP | S.BR_SEL, d["q"], d["k"], d["v"], q_cmp=qc, k_cmp=kc, v_cmp=vc, sel=sel,
+                   top_k=w.top_k, sel_groups=w.n_kvh, gates=d["gates"], q_gran=S.Q_BLOCK)
+    torch.cuda.synchronize()
+    # reference: the oracle's steps with the pooled values rounded to bf16 where the layer stores them
+    qc_r, kc_r, vc_r = pooled(w)
+    ref_sel, _ = O.route_scores(qc_r, kc_r, w.blk_key, w.scale, w.top_k)
+    o_cmp, _ = O.attn_branch(O.CMP, qc_r, kc_r, vc_r, w.blk_cnt, w.blk_cap, w.scale, q_gran="block")
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=ref_sel, q_gran="block")
+    ref = O.gate_combine([o_cmp, o_sel], w.gates)
+    # where fp32 scores order near-tied blocks differently the routing rows differ; compare outputs
+    # where the rows agree (the routing itself is checked against epsilon ties above)
+    same = np.all(host(sel) == ref_sel, axis=2)                      # [n_blk, H]
+    assert same.mean() > 0.9, same.mean()
+    blk = np.arange(w.n_slots) // w.blk_cap
+    vm = w.valid_mask()
+    got = host(o)
+    agree = same[blk] & vm[:, None]                                 # [S, H]
+    diff = np.abs(got - ref).max(axis=2)                            # [S, H]
+    assert diff[agree].max() <= 2e-2
+    assert np.all(got[~vm] == 0)
+
+
+def test_full_size_sampled():
+    import sparse_attention_feed_amd as S
+    say("generate speed3r")
+    w = wl("speed3r")
+    d = to_dev(w)
+    L = d["layout"]
+    say("speed3r layer full", w.n_valid, w.n_blk)
+    qc = S.pool_blocks(L, d["q"])
+    kc = S.pool_blocks(L, d["k"])
+    vc = S.pool_blocks(L, d["v"])
+    sel = S.route_scores_topk(L, qc, kc, None, w.top_k, q_gran=S.Q_BLOCK)
+    o = S.attn_fwd(L, S.BR_CMP | S.BR_SEL, d["q"], d["k"], d["v"], q_cmp=qc, k_cmp=kc, v_cmp=vc, sel=sel,
+                   top_k=w.top_k, sel_groups=w.n_kvh, gates=d["gates"], q_gran=S.Q_BLOCK)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    # routing: sampled block rows against the oracle on the GPU's own pooled values (rounded bf16)
+    qch, kch = host(qc), host(kc)
+    rows = np.sort(rng.choice(w.n_blk, 24, replace=False))
+    ref_sel, imp = O.route_scores(qch[rows], kch, w.blk_key, w.scale, w.top_k)
+    frac = check_eps_ties(host(sel)[rows], ref_sel, imp, w.top_k, 1e-2)
+    assert frac >= 0.8, frac
+    # attention on sampled tokens, using the GPU routing rows (an input of the attention call)
+    vs = w.valid_slots()
+    toks = np.sort(rng.choice(vs, 64, replace=False))
+    vch = host(vc)
+    selh = host(sel)
+    o_cmp, _ = O.attn_branch(O.CMP, qch, kch, vch, w.blk_cnt, w.blk_cap, w.scale, q_gran="block", rows=toks)
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=selh, q_gran="block",
+                             rows=toks)
+    ref = O.gate_combine([o_cmp, o_sel], w.gates[toks])
+    assert max_err(host(o)[toks], ref) <= 2e-2
