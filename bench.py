@@ -51,21 +51,118 @@ def cpu_baseline(w, budget_s):
     from threadpoolctl import threadpool_limits
     import oracle as O
     rng = np.random.default_rng(123)
-    vs = w.valid_slots()
+    if hasattr(w, "n_x"):
+        vs = np.arange(w.n_tok)
+        run = lambda rows: O.dense_gated_xattn(w.q, w.k, w.v, w.n_x, w.gates, w.scale, rows=rows)  # noqa: E731
+    else:
+        vs = w.valid_slots()
+        run = lambda rows: O.nsa_forward(w, rows=rows)  # noqa: E731
     with threadpool_limits(limits=1):
         rows = np.sort(rng.choice(vs, 16, replace=False))
         t0 = time.perf_counter()
-        O.nsa_forward(w, rows=rows)
+        run(rows)
         t1 = time.perf_counter() - t0
         n2 = int(min(4096, max(16, (budget_s - t1) / (t1 / 16))))
         rows = np.sort(rng.choice(vs, n2, replace=False))
         t0 = time.perf_counter()
-        O.nsa_forward(w, rows=rows)
+        run(rows)
         t2 = time.perf_counter() - t0
     n = 16 + n2
     return {"value": round(n / (t1 + t2), 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": "%d random query tokens of the same workload in two calls, %.1f s; every call also "
                       "pools all blocks and computes all block centroids" % (n, t1 + t2)}
+
+
+def setup_geometric(w, S, torch, dev):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, g = (torch.from_numpy(getattr(w, n)).to(dev).to(dt).contiguous() for n in ("q", "k", "v", "gates"))
+    pts = torch.from_numpy(w.pts).to(dev)
+    L = S.BlockLayout(torch.from_numpy(w.blk_cnt).to(dev), torch.from_numpy(w.blk_key.view(np.int32)).to(dev),
+                      w.blk_cap, w.n_qh, w.n_kvh, w.head_dim)
+    ws = {
+        "k_cmp": torch.empty((w.n_blk, w.n_kvh, w.head_dim), dtype=dt, device=dev),
+        "v_cmp": torch.empty((w.n_blk, w.n_kvh, w.head_dim), dtype=dt, device=dev),
+        "sel": torch.empty((w.n_slots, w.top_k), dtype=torch.int32, device=dev),
+        "centroids": torch.empty((w.n_blk, 4), dtype=torch.int32, device=dev),
+        "out": torch.empty_like(q),
+    }
+
+    def stages():
+        return [
+            ("pool_kv", lambda: (S.pool_blocks(L, k, ws["k_cmp"]), S.pool_blocks(L, v, ws["v_cmp"]))),
+            ("route_geometric", lambda: S.route_geometric(L, pts, w.top_k, sel=ws["sel"],
+                                                         centroids=ws["centroids"], want_d2=False)),
+            ("attn_fused", lambda: S.attn_fwd(L, S.BR_CMP | S.BR_SEL | S.BR_LOC, q, k, v, k_cmp=ws["k_cmp"],
+                                              v_cmp=ws["v_cmp"], sel=ws["sel"], top_k=w.top_k, gates=g,
+                                              out=ws["out"])),
+        ]
+
+    def flops():
+        return algorithmic_flops(w, ws["sel"].cpu().numpy())
+
+    def branch(bits):
+        nb = bin(bits).count("1")
+        gg = g[:, :, :nb].contiguous() if nb > 1 else None
+        return lambda: S.attn_fwd(L, bits, q, k, v, k_cmp=ws["k_cmp"], v_cmp=ws["v_cmp"], sel=ws["sel"],
+                                  top_k=w.top_k, gates=gg, out=ws["out"])
+
+    combos = {"cmp": S.BR_CMP, "sel": S.BR_SEL, "loc": S.BR_LOC, "sel+loc": S.BR_SEL | S.BR_LOC}
+    return stages, flops, {n: branch(b) for n, b in combos.items()}, "attn_fused"
+
+
+def setup_speed3r(w, S, torch, dev):
+    dt = torch.bfloat16
+    q, k, v, g = (torch.from_numpy(getattr(w, n)).to(dev).to(dt).contiguous() for n in ("q", "k", "v", "gates"))
+    L = S.BlockLayout(torch.from_numpy(w.blk_cnt).to(dev), torch.from_numpy(w.blk_key.view(np.int32)).to(dev),
+                      w.blk_cap, w.n_qh, w.n_kvh, w.head_dim)
+    shp = (w.n_blk, w.n_kvh, w.head_dim)
+    ws = {n: torch.empty(shp, dtype=dt, device=dev) for n in ("q_cmp", "k_cmp", "v_cmp")}
+    ws["sel"] = torch.empty((w.n_blk, w.n_kvh, w.top_k), dtype=torch.int32, device=dev)
+    ws["out"] = torch.empty_like(q)
+
+    def stages():
+        return [
+            ("pool_qkv", lambda: (S.pool_blocks(L, q, ws["q_cmp"]), S.pool_blocks(L, k, ws["k_cmp"]),
+                                  S.pool_blocks(L, v, ws["v_cmp"]))),
+            ("route_scores", lambda: S.route_scores_topk(L, ws["q_cmp"], ws["k_cmp"], None, w.top_k,
+                                                          q_gran=S.Q_BLOCK, sel=ws["sel"])),
+            ("attn_fused", lambda: S.attn_fwd(L, S.BR_CMP | S.BR_SEL, q, k, v, q_cmp=ws["q_cmp"], k_cmp=ws["k_cmp"],
+                                              v_cmp=ws["v_cmp"], sel=ws["sel"], top_k=w.top_k, sel_groups=w.n_kvh,
+                                              gates=g, out=ws["out"], q_gran=S.Q_BLOCK)),
+        ]
+
+    def flops():
+        cnt = w.blk_cnt.astype(np.int64)
+        per = 4 * w.head_dim
+        sel = ws["sel"].cpu().numpy()                       # [n_blk, H, k]
+        sel_cnt = np.where(sel >= 0, cnt[np.clip(sel, 0, None)], 0).sum(axis=2)   # [n_blk, H]
+        return {"cmp": per * w.n_blk * w.n_blk * w.n_qh,
+                "sel": per * int((sel_cnt * cnt[:, None]).sum()),
+                "route": per // 2 * w.n_blk * w.n_blk * w.n_qh}
+
+    def branch(bits):
+        nb = bin(bits).count("1")
+        gg = g[:, :, :nb].contiguous() if nb > 1 else None
+        return lambda: S.attn_fwd(L, bits, q, k, v, q_cmp=ws["q_cmp"], k_cmp=ws["k_cmp"], v_cmp=ws["v_cmp"],
+                                  sel=ws["sel"], top_k=w.top_k, sel_groups=w.n_kvh, gates=gg, out=ws["out"],
+                                  q_gran=S.Q_BLOCK)
+
+    return stages, flops, {"cmp": branch(S.BR_CMP), "sel": branch(S.BR_SEL)}, "attn_fused"
+
+
+def setup_dense(w, S, torch, dev):
+    dt = torch.bfloat16
+    t = {n: torch.from_numpy(getattr(w, n)).to(dev).to(dt).contiguous() for n in ("q", "k", "v", "gates")}
+    out = torch.empty_like(t["q"])
+
+    def stages():
+        return [("dense_gated_xattn", lambda: S.dense_gated_xattn(t["q"], t["k"], t["v"], w.n_x, t["gates"],
+                                                                  out=out))]
+
+    def flops():
+        return {"dense": 4 * w.head_dim * w.n_qh * w.n_tok * w.n_tok}
+
+    return stages, flops, {}, "dense_gated_xattn"
 
 
 def main():
@@ -89,42 +186,31 @@ def main():
 
     t0 = time.time()
     w = W.make(args.config)
-    log("workload %s: %d valid tokens, %d blocks, cap %d, top_k %d (%.1fs)" %
-        (args.config, w.n_valid, w.n_blk, w.blk_cap, w.top_k, time.time() - t0))
+    dense = isinstance(w, W.DenseWorkload)
+    n_tok = w.n_tok if dense else w.n_valid
+    log("workload %s: %d tokens (%.1fs)" % (args.config, n_tok, time.time() - t0))
     dev = "cuda:0"
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    q, k, v, g = (torch.from_numpy(getattr(w, n)).to(dev).to(dt).contiguous() for n in ("q", "k", "v", "gates"))
-    pts = torch.from_numpy(w.pts).to(dev)
-    L = S.BlockLayout(torch.from_numpy(w.blk_cnt).to(dev), torch.from_numpy(w.blk_key.view(np.int32)).to(dev),
-                      w.blk_cap, w.n_qh, w.n_kvh, w.head_dim)
-    ws = {
-        "k_cmp": torch.empty((w.n_blk, w.n_kvh, w.head_dim), dtype=dt, device=dev),
-        "v_cmp": torch.empty((w.n_blk, w.n_kvh, w.head_dim), dtype=dt, device=dev),
-        "sel": torch.empty((w.n_slots, w.top_k), dtype=torch.int32, device=dev),
-        "centroids": torch.empty((w.n_blk, 4), dtype=torch.int32, device=dev),
-        "out": torch.empty_like(q),
-    }
+    if dense:
+        stages_fn, flops_fn, branches, dominant = setup_dense(w, S, torch, dev)
+    elif w.routing == "scores":
+        stages_fn, flops_fn, branches, dominant = setup_speed3r(w, S, torch, dev)
+    else:
+        stages_fn, flops_fn, branches, dominant = setup_geometric(w, S, torch, dev)
+    stages = stages_fn()
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        for i, (_, fn) in enumerate(stages):
+            if ev is not None:
+                ev[i].record(stream)
+            fn()
         if ev is not None:
-            ev[0].record(stream)
-        S.pool_blocks(L, k, ws["k_cmp"])
-        S.pool_blocks(L, v, ws["v_cmp"])
-        if ev is not None:
-            ev[1].record(stream)
-        S.route_geometric(L, pts, w.top_k, sel=ws["sel"], centroids=ws["centroids"], want_d2=False)
-        if ev is not None:
-            ev[2].record(stream)
-        S.attn_fwd(L, S.BR_CMP | S.BR_SEL | S.BR_LOC, q, k, v, k_cmp=ws["k_cmp"], v_cmp=ws["v_cmp"],
-                   sel=ws["sel"], top_k=w.top_k, gates=g, out=ws["out"])
-        if ev is not None:
-            ev[3].record(stream)
+            ev[len(stages)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -135,41 +221,32 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    pool_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    route_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    value = w.n_valid / (ms_step * 1e-3)
+    kern_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, (name, _) in enumerate(stages)}
+    value = n_tok / (ms_step * 1e-3)
 
-    sel = ws["sel"].cpu().numpy()
-    fl = algorithmic_flops(w, sel)
-    attn_flops = fl["cmp"] + fl["sel"] + fl["loc"]
-    achieved = attn_flops / (attn_ms * 1e-3) / 1e12
-    log("step %.3f ms: pool %.3f, route %.3f, attn %.3f ms; attention %.1f TFLOP/s" %
-        (ms_step, pool_ms, route_ms, attn_ms, achieved))
+    fl = flops_fn()
+    dom_flops = sum(v for kk, v in fl.items() if kk != "route")
+    achieved = dom_flops / (kern_ms[dominant] * 1e-3) / 1e12
+    log("step %.3f ms; %s; %s %.1f TFLOP/s" % (ms_step, ", ".join("%s %.3f" % kv for kv in kern_ms.items()),
+                                              dominant, achieved))
 
     breakdown = None
-    if not args.no_breakdown:
+    if branches and not args.no_breakdown:
         breakdown = {}
-        combos = {"cmp": S.BR_CMP, "sel": S.BR_SEL, "loc": S.BR_LOC, "sel+loc": S.BR_SEL | S.BR_LOC}
-        for name, bits in combos.items():
-            nb = bin(bits).count("1")
-            gg = g[:, :, :nb].contiguous() if nb > 1 else None
+        for name, fn in branches.items():
             for _ in range(2):
-                S.attn_fwd(L, bits, q, k, v, k_cmp=ws["k_cmp"], v_cmp=ws["v_cmp"], sel=ws["sel"], top_k=w.top_k,
-                           gates=gg, out=ws["out"])
+                fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = 5
             e0.record(stream)
             for _ in range(reps):
-                S.attn_fwd(L, bits, q, k, v, k_cmp=ws["k_cmp"], v_cmp=ws["v_cmp"], sel=ws["sel"], top_k=w.top_k,
-                           gates=gg, out=ws["out"])
+                fn()
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
             f = sum(fl[p] for p in name.split("+"))
             breakdown[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 1),
                                "mfma_frac": round(f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        # restore the step's output
         step()
         torch.cuda.synchronize()
 
@@ -178,6 +255,19 @@ def main():
         log("timing the fp64 oracle on a bounded sample (~%.0f s)" % args.cpu_seconds)
         cpu = cpu_baseline(w, args.cpu_seconds)
 
+    if args.config == "large":
+        desc = ("large: 128^3 volume (%d active surface voxels) + 16 views x 128^2 at 50%% foreground (%d), "
+                "32q/2kv heads, D=32, 64-token blocks, top-%d geometric routing + local + compressed, "
+                "3-way sigmoid gate" % (w.n_vol_tokens, w.n_img_tokens, w.top_k))
+    elif dense:
+        desc = "%s: stage-1 dense gated self/cross attention, %d tokens (%d volume), 32q/2kv, D=32" % (
+            args.config, w.n_tok, w.n_x)
+    else:
+        desc = "%s: %d tokens, %d blocks of %d, %dq/%dkv heads, D=%d, top-%d %s routing" % (
+            args.config, w.n_valid, w.n_blk, w.blk_cap, w.n_qh, w.n_kvh, w.head_dim, w.top_k, w.routing)
+    cfg = {"workload": desc, "n_tokens": n_tok, "n_qh": w.n_qh, "n_kvh": w.n_kvh, "head_dim": w.head_dim}
+    if not dense:
+        cfg.update(n_blk=w.n_blk, blk_cap=w.blk_cap, top_k=w.top_k)
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -190,17 +280,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; shapes of the LSRM sparse stage)",
-        "config": {
-            "workload": "%s: 128^3 volume (%d active surface voxels) + 16 views x 128^2 at 50%% fg (%d), "
-                        "32q/2kv heads, D=32, 64-token blocks, top-%d geometric routing + local + "
-                        "compressed, 3-way sigmoid gate" % (args.config, w.n_vol_tokens, w.n_img_tokens, w.top_k)
-            if args.config == "large" else args.config,
-            "n_valid_tokens": w.n_valid, "n_blk": w.n_blk, "blk_cap": w.blk_cap, "top_k": w.top_k,
-            "n_qh": w.n_qh, "n_kvh": w.n_kvh, "head_dim": w.head_dim,
-        },
+        "data": "synthetic (seeded; token geometry and head shapes of the pages' workloads)",
+        "config": cfg,
         "roofline": {
-            "kernel": "nsa_attn_kernel (fused CMP+SEL+LOC+gate)",
+            "kernel": dominant,
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -208,8 +291,7 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": None,
         },
-        "kernels_ms": {"pool_kv": round(pool_ms, 4), "route_geometric": round(route_ms, 4),
-                       "attn_fused": round(attn_ms, 4)},
+        "kernels_ms": {kk: round(vv, 4) for kk, vv in kern_ms.items()},
         "algorithmic_gflop": {kk: round(vv / 1e9, 2) for kk, vv in fl.items()},
         "branch_breakdown": breakdown,
         "cpu_baseline": cpu,

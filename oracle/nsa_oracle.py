@@ -338,7 +338,10 @@ def nsa_forward(w, rows=None, return_parts=False):
     else:
         if w.n_qh != w.n_kvh:
             raise NotImplementedError("whole-layer score routing is defined here for Hq == Hkv")
-        sel, _ = route_scores(parts["q_cmp"], k_cmp, w.blk_key, w.scale, w.top_k)
+        # routing rows are per query block; only the blocks holding the requested rows are needed
+        need = np.unique(rows // cap)
+        sel = np.full((w.n_blk, w.n_kvh, w.top_k), -1, dtype=np.int32)
+        sel[need], _ = route_scores(parts["q_cmp"][need], k_cmp, w.blk_key, w.scale, w.top_k)
         q_gran_sel = "block"
     parts["sel"] = sel
     outs = []
