@@ -45,6 +45,35 @@ def algorithmic_flops(w, sel):
     return {"cmp": per * cmp_pairs, "sel": per * sel_pairs, "loc": per * loc_pairs}
 
 
+def _source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "sparse_attention_feed_amd", "csrc"))):
+        with open(os.path.join(ROOT, "sparse_attention_feed_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, config):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary, if
+    that summary was taken on the current kernel sources (same digest); otherwise None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.md" % (kernel, config))
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                kk, vv = line[2:].split(": ", 1)
+                vals[kk.strip()] = vv.strip().strip("`")
+    if vals.get("source digest") != _source_digest():
+        return None
+    try:
+        return float(vals["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, budget_s):
     """fp64 oracle on a bounded sample of query rows of the same workload, one thread: a probe call
     of 16 rows sizes a second call that fills the time budget."""
@@ -174,6 +203,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed region, copy 1 GiB device to device twice: the reference kernel "
+                         "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the NSA layer would "
@@ -250,6 +282,14 @@ def main():
         step()
         torch.cuda.synchronize()
 
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu:
         log("timing the fp64 oracle on a bounded sample (~%.0f s)" % args.cpu_seconds)
@@ -289,7 +329,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dominant, args.config),
         },
         "kernels_ms": {kk: round(vv, 4) for kk, vv in kern_ms.items()},
         "algorithmic_gflop": {kk: round(vv / 1e9, 2) for kk, vv in fl.items()},
