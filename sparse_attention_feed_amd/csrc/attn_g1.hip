@@ -263,128 +263,192 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
 // ---------------------------------------------------------------------------------------------
 // routing: top-k blocks per (query block, head) by compressed score, no score matrix stored
 // ---------------------------------------------------------------------------------------------
+//
+// Each wave scores CG column groups (16 query rows each) against a staged 64-key tile with MFMA.
+// Lane (r, g) sees a quarter of every row's keys and keeps a sorted list of its best K.  Candidates
+// are filtered first against a row-level bound of the row's current k-th best (the lists of the
+// four lanes of a row give one): after the first tiles almost no score passes, so the sorted
+// insertions run for few lanes and few steps.  The tile's scores go to wave-private LDS so that
+// each lane can walk only its own candidates.  Ranking key: (score, then smaller blk_key) packed
+// into 64 bits so that one unsigned compare orders both.
 
-constexpr int RW = 8;       // waves per workgroup; one column group (16 query rows) per wave
+constexpr int RW = 8;       // waves per workgroup
 
-__device__ __forceinline__ bool rbetter(float v, uint32_t k, float v2, uint32_t k2) {
-  return v > v2 || (v == v2 && k < k2);
+__device__ __forceinline__ uint32_t ord_f32(float v) {
+  uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);      // -0 ranks with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord_f32(uint32_t o) {
+  if (o == 0u) return -INFINITY;                         // empty list slot: everything passes
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint64_t rank_key(float v, uint32_t blk_key) {
+  return ((uint64_t)ord_f32(v) << 32) | (uint64_t)(~blk_key);
 }
 
 template <int K>
+struct TopList {
+  uint64_t key[K];          // descending; 0 = empty
+  int idx[K];
+};
+
+template <int K>
+__device__ __forceinline__ void toplist_init(TopList<K>& t) {
+#pragma unroll
+  for (int x = 0; x < K; ++x) {
+    t.key[x] = 0ull;
+    t.idx[x] = -1;
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void toplist_insert(TopList<K>& t, uint64_t ck, int ci) {
+  if (ck <= t.key[K - 1]) return;
+#pragma unroll
+  for (int x = K - 1; x > 0; --x) {
+    const bool gp = ck > t.key[x - 1];
+    const bool gc = ck > t.key[x];
+    t.key[x] = gp ? t.key[x - 1] : (gc ? ck : t.key[x]);
+    t.idx[x] = gp ? t.idx[x - 1] : (gc ? ci : t.idx[x]);
+  }
+  if (ck > t.key[0]) {
+    t.key[0] = ck;
+    t.idx[0] = ci;
+  }
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Lower bound on the row's K-th best key: each lane list holds K distinct keys >= its last entry,
+// and the four lists together hold K distinct keys >= the smallest of their (K/4)-th entries.
+template <int K>
+__device__ __forceinline__ float row_threshold(const TopList<K>& t) {
+  uint64_t hi = t.key[K - 1], lo = t.key[K / 4 - 1];
+#pragma unroll
+  for (int m = 16; m <= 32; m <<= 1) {
+    const uint64_t h2 = shfl_xor_u64(hi, m), l2 = shfl_xor_u64(lo, m);
+    hi = h2 > hi ? h2 : hi;
+    lo = l2 < lo ? l2 : lo;
+  }
+  const uint64_t b = hi > lo ? hi : lo;
+  return unord_f32((uint32_t)(b >> 32));
+}
+
+template <int K, int CG>
 __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
-  __shared__ TileG1 tb[2];
-  __shared__ int rows_lds[2][KT];
+  __shared__ bf16 kt_lds[2][KT][KP];
   __shared__ uint32_t keys_lds[2][KT];
-  const int nt = RW * 64;
-  const int n_rowgrp = (a.n_blk + RW * 16 - 1) / (RW * 16);
+  __shared__ f32x4 sc_lds[RW][4][64];      // one column group's tile scores per wave, slot-major
+  const int rows_per_wg = RW * CG * 16;
+  const int n_rowgrp = (a.n_blk + rows_per_wg - 1) / rows_per_wg;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int h = wg / n_rowgrp, rg = wg % n_rowgrp;
-  const int w = threadIdx.x >> 6, l = lane_id(), r = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), r = l & 15, g = l >> 4;
   const int stride = a.n_kvh * DG;
   const bf16* qc = reinterpret_cast<const bf16*>(a.q_cmp);
   const bf16* kb = reinterpret_cast<const bf16*>(a.k_cmp) + h * DG;
-  const int row = (rg * RW + w) * 16 + r;
-  const QG1 q = load_q_row(qc + ((size_t)row * a.n_qh + h) * DG, row < a.n_blk);
 
-  float bv[K];
-  uint32_t bk[K];
-  int bi[K];
+  QG1 q[CG];
+  TopList<K> lst[CG];
+  float thr[CG];
+  int row_of[CG];
 #pragma unroll
-  for (int x = 0; x < K; ++x) {
-    bv[x] = -INFINITY;
-    bk[x] = 0xFFFFFFFFu;
-    bi[x] = -1;
+  for (int c = 0; c < CG; ++c) {
+    row_of[c] = rg * rows_per_wg + (w * CG + c) * 16 + r;
+    q[c] = load_q_row(qc + ((size_t)row_of[c] * a.n_qh + h) * DG, row_of[c] < a.n_blk);
+    toplist_init(lst[c]);
+    thr[c] = -INFINITY;
   }
   const int ntiles = (a.n_blk + KT - 1) / KT;
-  for (int i = threadIdx.x; i < KT; i += nt) {
-    rows_lds[0][i] = i < a.n_blk ? i : -1;
-    keys_lds[0][i] = i < a.n_blk ? a.blk_key[i] : 0u;
-  }
-  __syncthreads();
-  stage_rows_g1(tb[0], kb, kb, stride, rows_lds[0], threadIdx.x, nt);   // V part unused
+  // staging: thread t copies 16 bytes (key t / 8, piece t % 8) of the K tile; threads < 64 the keys
+  const int s_key = tid >> 3, s_part = tid & 7;
+  auto fetch = [&](int u, uint4& kv, uint32_t& bkey) {
+    const int key = u * KT + s_key;
+    kv = make_uint4(0u, 0u, 0u, 0u);
+    if (key < a.n_blk) kv = *reinterpret_cast<const uint4*>(kb + (size_t)key * stride + s_part * 8);
+    const int kk = u * KT + tid;
+    bkey = (tid < KT && kk < a.n_blk) ? a.blk_key[kk] : 0u;
+  };
+  auto store = [&](int buf, const uint4& kv, uint32_t bkey) {
+    *reinterpret_cast<uint4*>(&kt_lds[buf][s_key][s_part * 8]) = kv;
+    if (tid < KT) keys_lds[buf][tid] = bkey;
+  };
+  uint4 kv;
+  uint32_t bkey;
+  fetch(0, kv, bkey);
+  store(0, kv, bkey);
   __syncthreads();
   for (int u = 0; u < ntiles; ++u) {
     const int cur = u & 1;
-    if (u + 1 < ntiles) {
-      for (int i = threadIdx.x; i < KT; i += nt) {
-        const int key = (u + 1) * KT + i;
-        rows_lds[cur ^ 1][i] = key < a.n_blk ? key : -1;
-        keys_lds[cur ^ 1][i] = key < a.n_blk ? a.blk_key[key] : 0u;
-      }
-    }
-    TileFragsG1 f;
-    load_frags_g1(tb[cur], f);
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 zs[4] = {z, z, z, z};
-    f32x4 s[4];
-    scores_g1(f, q, zs, s);
-    const int nk = min(KT, a.n_blk - u * KT);
+    if (u + 1 < ntiles) fetch(u + 1, kv, bkey);
+    Frag8<bf16> kf[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * kt + 4 * g + i;
-        if (key >= nk) continue;
-        const float v = s[kt][i];
-        const uint32_t kk = keys_lds[cur][key];
-        if (rbetter(v, kk, bv[K - 1], bk[K - 1])) {
-          const int idx = u * KT + key;
+      for (int hh = 0; hh < 2; ++hh) kf[kt][hh] = ld8(&kt_lds[cur][16 * kt + r][32 * hh + 8 * g]);
+    const int nk = min(KT, a.n_blk - u * KT);
+    uint32_t vmask = 0xFFFFu;                 // slot j = 4*kt + i holds key 16*kt + 4*g + i
+    if (nk < KT) {
+      vmask = 0u;
 #pragma unroll
-          for (int x = K - 1; x > 0; --x) {
-            const bool bp = rbetter(v, kk, bv[x - 1], bk[x - 1]);
-            const bool bc = rbetter(v, kk, bv[x], bk[x]);
-            if (bp) {
-              bv[x] = bv[x - 1];
-              bk[x] = bk[x - 1];
-              bi[x] = bi[x - 1];
-            } else if (bc) {
-              bv[x] = v;
-              bk[x] = kk;
-              bi[x] = idx;
-            }
-          }
-          if (rbetter(v, kk, bv[0], bk[0])) {
-            bv[0] = v;
-            bk[0] = kk;
-            bi[0] = idx;
-          }
-        }
+      for (int j = 0; j < 16; ++j) vmask |= (16 * (j >> 2) + 4 * g + (j & 3) < nk) ? (1u << j) : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      f32x4 s[4];
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[kt] = mma16(kf[kt][1], q[c].h[1], mma16(kf[kt][0], q[c].h[0], z));
+      uint32_t m = 0u;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m |= (s[j >> 2][j & 3] >= thr[c]) ? (1u << j) : 0u;
+      m &= vmask;
+      if (__builtin_amdgcn_ballot_w64(m != 0u) == 0ull) continue;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sc_lds[w][kt][l] = s[kt];
+      while (m != 0u) {
+        const int j = __builtin_ctz(m);
+        m &= m - 1u;
+        const float v = reinterpret_cast<const float*>(&sc_lds[w][j >> 2][l])[j & 3];
+        const int key = 16 * (j >> 2) + 4 * g + (j & 3);
+        toplist_insert(lst[c], rank_key(v, keys_lds[cur][key]), u * KT + key);
       }
-    __syncthreads();
-    if (u + 1 < ntiles) stage_rows_g1(tb[cur ^ 1], kb, kb, stride, rows_lds[cur ^ 1], threadIdx.x, nt);
+      thr[c] = row_threshold(lst[c]);
+    }
+    // every wave finished tile u - 1 (the previous barrier), so buffer cur ^ 1 is free
+    if (u + 1 < ntiles) store(cur ^ 1, kv, bkey);
     __syncthreads();
   }
-  // merge the four lane groups' lists of each row (lanes r, r+16, r+32, r+48): top_k rounds of an
-  // arg-best over the four list heads
-  if (row < a.n_blk) {
+  // merge the four lane lists of each row: top_k rounds of arg-best over the list heads
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const int row = row_of[c];
     int32_t* so = const_cast<int32_t*>(a.sel) + ((size_t)row * a.n_kvh + h) * a.top_k;
     for (int x = 0; x < a.top_k; ++x) {
-      float v = bv[0];
-      uint32_t kk = bk[0];
+      uint64_t best = lst[c].key[0];
       int src = g;
 #pragma unroll
       for (int o = 16; o <= 32; o <<= 1) {
-        const float v2 = __shfl_xor(v, o, 64);
-        const uint32_t k2 = __shfl_xor(kk, o, 64);
+        const uint64_t b2 = shfl_xor_u64(best, o);
         const int s2 = __shfl_xor(src, o, 64);
-        if (rbetter(v2, k2, v, kk)) {
-          v = v2;
-          kk = k2;
+        if (b2 > best) {
+          best = b2;
           src = s2;
         }
       }
-      const int win = __shfl(bi[0], r + 16 * src, 64);
-      if (g == 0) so[x] = (v == -INFINITY) ? -1 : win;
+      const int win = __shfl(lst[c].idx[0], r + 16 * src, 64);
+      if (g == 0 && row < a.n_blk) so[x] = best == 0ull ? -1 : win;
       if (g == src) {
 #pragma unroll
         for (int y = 0; y < K - 1; ++y) {
-          bv[y] = bv[y + 1];
-          bk[y] = bk[y + 1];
-          bi[y] = bi[y + 1];
+          lst[c].key[y] = lst[c].key[y + 1];
+          lst[c].idx[y] = lst[c].idx[y + 1];
         }
-        bv[K - 1] = -INFINITY;
-        bk[K - 1] = 0xFFFFFFFFu;
-        bi[K - 1] = -1;
+        lst[c].key[K - 1] = 0ull;
+        lst[c].idx[K - 1] = -1;
       }
     }
   }
@@ -477,20 +541,20 @@ __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
   }
 }
 
-template <int K>
+template <int K, int CG>
 hipError_t launch_route_g1_k(const G1Args& a, hipStream_t s) {
-  const int n_rowgrp = (a.n_blk + RW * 16 - 1) / (RW * 16);
-  hipLaunchKernelGGL(route_g1_kernel<K>, dim3(n_rowgrp * a.n_kvh), dim3(RW * 64), 0, s, a);
+  const int n_rowgrp = (a.n_blk + RW * CG * 16 - 1) / (RW * CG * 16);
+  hipLaunchKernelGGL((route_g1_kernel<K, CG>), dim3(n_rowgrp * a.n_kvh), dim3(RW * 64), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_route_g1(const G1Args& a, hipStream_t s) {
-  if (a.top_k <= 8) return launch_route_g1_k<8>(a, s);
-  if (a.top_k <= 16) return launch_route_g1_k<16>(a, s);
-  if (a.top_k <= 32) return launch_route_g1_k<32>(a, s);
-  return launch_route_g1_k<64>(a, s);
+  if (a.top_k <= 8) return launch_route_g1_k<8, 2>(a, s);
+  if (a.top_k <= 16) return launch_route_g1_k<16, 2>(a, s);
+  if (a.top_k <= 32) return launch_route_g1_k<32, 1>(a, s);
+  return launch_route_g1_k<64, 1>(a, s);
 }
 
 hipError_t launch_attn_g1(const G1Args& a0, hipStream_t s) {

@@ -65,12 +65,30 @@ def test_score_routing_exact_on_integer_inputs():
     rng = np.random.default_rng(5)
     qc = rng.integers(-2, 3, size=(w.n_blk, w.n_qh, w.head_dim)).astype(np.float32)
     kc = rng.integers(-2, 3, size=(w.n_blk, w.n_kvh, w.head_dim)).astype(np.float32)
-    for k in (16, 5, 32):
+    for k in (16, 5, 32, 40):
         say("route_g1 exact k", k)
         sel = S.route_scores_topk(d["layout"], dev(qc), dev(kc), None, k, q_gran=S.Q_BLOCK)
         torch.cuda.synchronize()
         ref_sel, _ = O.route_scores(qc, kc, w.blk_key, w.scale, k)
         np.testing.assert_array_equal(host(sel), ref_sel)
+
+
+@pytest.mark.parametrize("n_blk,k", [(10, 16), (1, 8), (77, 16), (130, 5)])
+def test_score_routing_edge_sizes(n_blk, k):
+    """Fewer blocks than k (tail of -1), a single block, and ragged last key tiles, with shuffled
+    blk_key order and exact integer scores: bit-exact against the oracle, ties included."""
+    import sparse_attention_feed_amd as S
+    w = W.custom_block_workload(40 + n_blk, np.full(n_blk, 16), 16, 16, 16, 64, "bf16", k, routing="scores",
+                                q_gran="block", branches=("cmp", "sel"))
+    d = to_dev(w)
+    rng = np.random.default_rng(n_blk)
+    qc = rng.integers(-1, 2, size=(n_blk, 16, 64)).astype(np.float32)
+    kc = rng.integers(-1, 2, size=(n_blk, 16, 64)).astype(np.float32)
+    say("route_g1 edge", n_blk, k)
+    sel = S.route_scores_topk(d["layout"], dev(qc), dev(kc), None, k, q_gran=S.Q_BLOCK)
+    torch.cuda.synchronize()
+    ref_sel, _ = O.route_scores(qc, kc, w.blk_key, w.scale, k)
+    np.testing.assert_array_equal(host(sel), ref_sel)
 
 
 @pytest.mark.parametrize("branch", ["cmp", "sel"])
