@@ -254,20 +254,19 @@ __device__ __forceinline__ void tok_softmax_pv(TokState& st, f32x4 (&x)[4], cons
     for (int h = 0; h < 2; ++h) st.acc[dt] = mma16(vf[dt][h], pf[h], st.acc[dt]);
 }
 
-// Tokens t < n (a prefix of the wave's tokens) against one tile, software-pipelined: the QK^T
-// product of token t+1 is issued before the softmax of token t.
+// Tokens t < n (a prefix of the wave's tokens) against one tile, one token at a time (the other
+// wave on the SIMD covers the wait for each token's QK^T results; a software pipeline across
+// tokens costs more in register copies than it saves at this register budget).
 template <typename T, int TPW>
 __device__ __forceinline__ void tile_prefix(TokState (&st)[TPW], const QF<T> (&qf)[TPW], int n, const Frag8<T> (&kf)[4],
                                             const Frag8<T> (&vf)[2][2], const f32x4 (&cm)[4], bool full) {
-  f32x4 x[4], xn[4];
-  tok_qk<T>(st[0], qf[0], kf, cm, full, x);
+  n = __builtin_amdgcn_readfirstlane(n);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     if (t < n) {
-      if (t + 1 < TPW && t + 1 < n) tok_qk<T>(st[t + 1], qf[t + 1], kf, cm, full, xn);
+      f32x4 x[4];
+      tok_qk<T>(st[t], qf[t], kf, cm, full, x);
       tok_softmax_pv<T>(st[t], x, vf);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) x[kt] = xn[kt];
     }
   }
 }
@@ -342,7 +341,7 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
       Frag8<T> kf[4], vf[2][2];
       f32x4 cm[4];
       load_tile_frags(b, kf, vf);
-      tile_mask(nk, cm);
+      if (nk < TILE) tile_mask(nk, cm);
       if constexpr (Part::kAll) tile_prefix<T, TPW>(st, qf, part.n, kf, vf, cm, nk == TILE);
       else tile_masked<T, TPW>(st, qf, pm, kf, vf, cm, nk == TILE);
     }
