@@ -326,14 +326,15 @@ __device__ __forceinline__ void tok_finish(const TokState& st, f32x4 (&res)[2], 
 template <typename T, int NT, int TPW, class Src, class Part>
 __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int ntiles, const Part& part,
                                           TokState (&st)[TPW], const QF<T> (&qf)[TPW]) {
-  Stager<T, NT> sg;
+  // Global loads run two tiles ahead of the compute (two register sets), LDS holds two tiles.
+  Stager<T, NT> next, after;
   if (ntiles <= 0) return;
-  sg.load(src.kptr(0), src.vptr(0), src.stride, src.nk(0));
-  sg.store(buf[0]);
+  next.load(src.kptr(0), src.vptr(0), src.stride, src.nk(0));
+  next.store(buf[0]);
+  if (ntiles > 1) next.load(src.kptr(1), src.vptr(1), src.stride, src.nk(1));
   __syncthreads();
   for (int u = 0; u < ntiles; ++u) {
-    const bool more = u + 1 < ntiles;
-    if (more) sg.load(src.kptr(u + 1), src.vptr(u + 1), src.stride, src.nk(u + 1));
+    if (u + 2 < ntiles) after.load(src.kptr(u + 2), src.vptr(u + 2), src.stride, src.nk(u + 2));
     const TileBuf<T>& b = buf[u & 1];
     const int nk = src.nk(u);
     const uint32_t pm = Part::kAll ? 0u : part.wave_mask(u);
@@ -345,7 +346,8 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
       if constexpr (Part::kAll) tile_prefix<T, TPW>(st, qf, part.n, kf, vf, cm, nk == TILE);
       else tile_masked<T, TPW>(st, qf, pm, kf, vf, cm, nk == TILE);
     }
-    if (more) sg.store(buf[(u + 1) & 1]);
+    if (u + 1 < ntiles) next.store(buf[(u + 1) & 1]);
+    next = after;
     __syncthreads();
   }
 }
@@ -381,15 +383,11 @@ struct AllPart {                 // the wave's valid tokens (a prefix) take part
 template <int WAVES, int TPW>
 struct UnionPart {               // tokens whose routing row holds the tile's block
   static constexpr bool kAll = false;
-  const unsigned long long* umask;  // LDS, bit s = block slot s
+  const unsigned long long* umask;  // LDS: bits [TPW w, TPW w + TPW) of umask[u] = wave w's tokens that selected union block u
   int w;                            // wave index; its token t is slot t * WAVES + w
   int n = 0;                        // unused
   __device__ uint32_t wave_mask(int u) const {
-    const unsigned long long m = umask[u] >> w;
-    uint32_t r = 0;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) r |= (uint32_t)((m >> (t * WAVES)) & 1ull) << t;
-    return r;
+    return __builtin_amdgcn_readfirstlane((uint32_t)(umask[u] >> (TPW * w)) & ((1u << TPW) - 1u));
   }
 };
 
@@ -552,7 +550,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
       if (blk >= 0 && blk < a.n_blk) {
         const int wi = blk >> 5;
         const int u = wpre[wi] + __builtin_popcount(bitmap[wi] & ((1u << (blk & 31)) - 1u));
-        atomicOr(&umask[u], 1ull << t);
+        atomicOr(&umask[u], 1ull << (TPW * (t % WAVES) + t / WAVES));   // wave t % WAVES, its token t / WAVES
       }
     }
     __syncthreads();
