@@ -53,6 +53,26 @@ __device__ __forceinline__ bool before(uint32_t d, uint32_t k, uint32_t d2, uint
 
 constexpr int RCH = 1024;   // centroids per LDS chunk
 
+// Sorted insertion of (d, key, idx) into the lane's ascending top-K list, if it ranks within it.
+template <int K>
+__device__ __forceinline__ void topk_insert(uint32_t (&bd)[K], uint32_t (&bk)[K], int (&bi)[K], uint32_t d,
+                                            uint32_t key, int idx) {
+  if (!before(d, key, bd[K - 1], bk[K - 1])) return;
+#pragma unroll
+  for (int x = K - 1; x > 0; --x) {
+    const bool bp = before(d, key, bd[x - 1], bk[x - 1]);
+    const bool bc = before(d, key, bd[x], bk[x]);
+    bd[x] = bp ? bd[x - 1] : (bc ? d : bd[x]);
+    bk[x] = bp ? bk[x - 1] : (bc ? key : bk[x]);
+    bi[x] = bp ? bi[x - 1] : (bc ? idx : bi[x]);
+  }
+  if (before(d, key, bd[0], bk[0])) {
+    bd[0] = d;
+    bk[0] = key;
+    bi[0] = idx;
+  }
+}
+
 // One thread per query slot; a sorted top-K list (d2, key, index) lives in registers.
 template <int K>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
@@ -90,33 +110,29 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     for (int i = threadIdx.x; i < n; i += 256) cs[i] = cent[base + i];
     __syncthreads();
     if (valid) {
-      for (int i = 0; i < n; ++i) {
+      // filter on d2 alone (a superset of the candidates: d2 equal to the current K-th may still
+      // win on blk_key), four centroids at a time; the sorted insertion runs only for candidates
+      int i = 0;
+      for (; i + 4 <= n; i += 4) {
+        uint32_t d[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int4 e = cs[i + x];
+          const int dx = ux - e.x, dy = uy - e.y, dz = uz - e.z;
+          d[x] = (uint32_t)(__mul24(dx, dx) + __mul24(dy, dy) + __mul24(dz, dz));
+        }
+        const uint32_t thr = bd[K - 1];
+        if ((d[0] <= thr) | (d[1] <= thr) | (d[2] <= thr) | (d[3] <= thr)) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            topk_insert<K>(bd, bk, bi, d[x], (uint32_t)cs[i + x].w, base + i + x);
+        }
+      }
+      for (; i < n; ++i) {
         const int4 e = cs[i];
         const int dx = ux - e.x, dy = uy - e.y, dz = uz - e.z;
         const uint32_t d = (uint32_t)(__mul24(dx, dx) + __mul24(dy, dy) + __mul24(dz, dz));
-        const uint32_t key = (uint32_t)e.w;
-        if (before(d, key, bd[K - 1], bk[K - 1])) {
-          const int idx = base + i;
-#pragma unroll
-          for (int x = K - 1; x > 0; --x) {
-            const bool bp = before(d, key, bd[x - 1], bk[x - 1]);
-            const bool bc = before(d, key, bd[x], bk[x]);
-            if (bp) {
-              bd[x] = bd[x - 1];
-              bk[x] = bk[x - 1];
-              bi[x] = bi[x - 1];
-            } else if (bc) {
-              bd[x] = d;
-              bk[x] = key;
-              bi[x] = idx;
-            }
-          }
-          if (before(d, key, bd[0], bk[0])) {
-            bd[0] = d;
-            bk[0] = key;
-            bi[0] = idx;
-          }
-        }
+        topk_insert<K>(bd, bk, bi, d, (uint32_t)e.w, base + i);
       }
     }
   }
