@@ -111,21 +111,29 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     __syncthreads();
     if (valid) {
       // filter on d2 alone (a superset of the candidates: d2 equal to the current K-th may still
-      // win on blk_key), four centroids at a time; the sorted insertion runs only for candidates
+      // win on blk_key), eight centroids at a time; each lane then walks only its own candidates,
+      // so a group costs the wave one insertion per candidate of its busiest lane
+      constexpr int GR = 8;
       int i = 0;
-      for (; i + 4 <= n; i += 4) {
-        uint32_t d[4];
+      for (; i + GR <= n; i += GR) {
+        uint32_t d[GR];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
+        for (int x = 0; x < GR; ++x) {
           const int4 e = cs[i + x];
           const int dx = ux - e.x, dy = uy - e.y, dz = uz - e.z;
           d[x] = (uint32_t)(__mul24(dx, dx) + __mul24(dy, dy) + __mul24(dz, dz));
         }
         const uint32_t thr = bd[K - 1];
-        if ((d[0] <= thr) | (d[1] <= thr) | (d[2] <= thr) | (d[3] <= thr)) {
+        uint32_t m = 0u;
 #pragma unroll
-          for (int x = 0; x < 4; ++x)
-            topk_insert<K>(bd, bk, bi, d[x], (uint32_t)cs[i + x].w, base + i + x);
+        for (int x = 0; x < GR; ++x) m |= (d[x] <= thr) ? (1u << x) : 0u;
+        while (m != 0u) {
+          const int x = __builtin_ctz(m);
+          m &= m - 1u;
+          uint32_t dd = d[0];
+#pragma unroll
+          for (int y = 1; y < GR; ++y) dd = x == y ? d[y] : dd;
+          topk_insert<K>(bd, bk, bi, dd, (uint32_t)cs[i + x].w, base + i + x);
         }
       }
       for (; i < n; ++i) {
