@@ -74,19 +74,30 @@ __device__ __forceinline__ void topk_insert(uint32_t (&bd)[K], uint32_t (&bk)[K]
 }
 
 // One thread per query slot; a sorted top-K list (d2, key, index) lives in registers.
+typedef short short2v __attribute__((ext_vector_type(2)));
+
+// Squared lattice distance: x and y as packed 16-bit differences through one dot2, z in 24 bits
+// (|difference| <= 8192 per axis, so every product and the sum are exact).
+__device__ __forceinline__ uint32_t dist2(uint32_t uxy, int uz, int2 c) {
+  const short2v d = __builtin_bit_cast(short2v, uxy) - __builtin_bit_cast(short2v, c.x);
+  const int dz = uz - c.y;
+  return (uint32_t)__builtin_amdgcn_sdot2(d, d, __mul24(dz, dz), false);
+}
+
 template <int K>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-  __shared__ int4 cs[RCH];
+  __shared__ int2 cs[RCH];        // (x | y << 16, z) of the chunk's centroids
+  __shared__ uint32_t ck[RCH];    // their blk_key
   const int S = a.n_blk * a.cap;
   const int slot = blockIdx.x * 256 + threadIdx.x;
   bool valid = false;
-  int ux = 0, uy = 0, uz = 0;
+  uint32_t uxy = 0u;
+  int uz = 0;
   if (slot < S) {
     valid = (slot % a.cap) < a.blk_cnt[slot / a.cap];
     if (valid) {
       const float* p = a.pts + (size_t)slot * 3;
-      ux = lattice(p[0]);
-      uy = lattice(p[1]);
+      uxy = (uint32_t)lattice(p[0]) | ((uint32_t)lattice(p[1]) << 16);
       uz = lattice(p[2]);
     }
   }
@@ -107,7 +118,11 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     const int base = c * RCH;
     const int n = min(RCH, a.n_blk - base);
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 256) cs[i] = cent[base + i];
+    for (int i = threadIdx.x; i < n; i += 256) {
+      const int4 e = cent[base + i];
+      cs[i] = make_int2(e.x | (e.y << 16), e.z);
+      ck[i] = (uint32_t)e.w;
+    }
     __syncthreads();
     if (valid) {
       // filter on d2 alone (a superset of the candidates: d2 equal to the current K-th may still
@@ -118,11 +133,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
       for (; i + GR <= n; i += GR) {
         uint32_t d[GR];
 #pragma unroll
-        for (int x = 0; x < GR; ++x) {
-          const int4 e = cs[i + x];
-          const int dx = ux - e.x, dy = uy - e.y, dz = uz - e.z;
-          d[x] = (uint32_t)(__mul24(dx, dx) + __mul24(dy, dy) + __mul24(dz, dz));
-        }
+        for (int x = 0; x < GR; ++x) d[x] = dist2(uxy, uz, cs[i + x]);
         const uint32_t thr = bd[K - 1];
         uint32_t m = 0u;
 #pragma unroll
@@ -133,15 +144,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
           uint32_t dd = d[0];
 #pragma unroll
           for (int y = 1; y < GR; ++y) dd = x == y ? d[y] : dd;
-          topk_insert<K>(bd, bk, bi, dd, (uint32_t)cs[i + x].w, base + i + x);
+          topk_insert<K>(bd, bk, bi, dd, ck[i + x], base + i + x);
         }
       }
-      for (; i < n; ++i) {
-        const int4 e = cs[i];
-        const int dx = ux - e.x, dy = uy - e.y, dz = uz - e.z;
-        const uint32_t d = (uint32_t)(__mul24(dx, dx) + __mul24(dy, dy) + __mul24(dz, dz));
-        topk_insert<K>(bd, bk, bi, d, (uint32_t)e.w, base + i);
-      }
+      for (; i < n; ++i) topk_insert<K>(bd, bk, bi, dist2(uxy, uz, cs[i]), ck[i], base + i);
     }
   }
   if (slot < S) {
