@@ -252,9 +252,8 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
       if (t < cnt) wgt = gp ? sigmoidf_((float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_cmp]) * inv : inv;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        bf16* dst = o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = (bf16)(st[c].acc[dt][i] * wgt);
+        bf16x4* dst = reinterpret_cast<bf16x4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
+        *dst = __builtin_convertvector(st[c].acc[dt] * wgt, bf16x4);
       }
     }
   }
@@ -460,10 +459,7 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
 
 __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
   __shared__ TileG1 tb;
-  __shared__ int rows_lds[KT];
-  __shared__ bool kvalid[KT];
-  __shared__ int blist[64];
-  __shared__ int nlist;
+  __shared__ int keys_lds[64 * 16 + KT];   // source rows of the selected valid tokens, packed
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int b = wg / a.n_kvh, h = wg % a.n_kvh;
   const int l = lane_id(), r = l & 15, g = l >> 4;
@@ -473,47 +469,38 @@ __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
   const bf16* kb = reinterpret_cast<const bf16*>(a.k) + h * DG;
   const bf16* vb = reinterpret_cast<const bf16*>(a.v) + h * DG;
   const float c2 = a.scale * kLog2e;
-  // this block's selected blocks for head h, duplicates and -1 removed (order kept)
+  // lane x < top_k holds entry x of this block's routing row for head h; -1, out-of-range and
+  // repeated entries count no keys; the valid tokens of the rest are packed one after another
   const int grp = a.sel_groups == 1 ? 0 : h;
   const int32_t* srow = a.sel + ((size_t)b * a.sel_groups + grp) * a.top_k;
-  if (l == 0) {
-    int n = 0;
-    for (int x = 0; x < a.top_k; ++x) {
-      const int s = srow[x];
-      if (s < 0 || s >= a.n_blk) continue;
-      bool dup = false;
-      for (int y = 0; y < n; ++y) dup |= blist[y] == s;
-      if (!dup) blist[n++] = s;
-    }
-    nlist = n;
+  const int sb = l < a.top_k ? srow[l] : -1;
+  bool keep = sb >= 0 && sb < a.n_blk;
+  for (int y = 0; y < a.top_k; ++y) {
+    const int sy = __builtin_amdgcn_readlane(sb, y);
+    keep = keep && !(y < l && sy == sb);
   }
+  const int c = keep ? a.blk_cnt[sb] : 0;
+  int inc = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (l >= o) inc += y;
+  }
+  const int total = __builtin_amdgcn_readlane(inc, 63);
+  for (int t = 0; t < c; ++t) keys_lds[inc - c + t] = sb * cap + t;
+  const int ntiles = (total + KT - 1) / KT;
+  for (int i = total + l; i < ntiles * KT; i += 64) keys_lds[i] = -1;
   __syncthreads();
-  const int nb = nlist;
-  const int per = KT / cap;                       // blocks per 64-key tile
-  const int ntiles = (nb + per - 1) / per;
   StateG1 st;
   state_init(st);
   const QG1 qq = load_q_row(q + ((size_t)(b * cap + r) * a.n_qh + h) * DG, r < cnt);
   for (int u = 0; u < ntiles; ++u) {
-    // key slot i of the tile: block blist[u*per + i/cap], token i%cap
-    {
-      const int i = l;
-      const int bi = u * per + i / cap, tk = i % cap;
-      int src = -1;
-      if (i < per * cap && bi < nb) {
-        const int blk = blist[bi];
-        if (tk < a.blk_cnt[blk]) src = blk * cap + tk;
-      }
-      rows_lds[i] = src;
-      kvalid[i] = src >= 0;
-    }
-    __syncthreads();
-    stage_rows_g1(tb, kb, vb, stride, rows_lds, l, 64);
+    stage_rows_g1(tb, kb, vb, stride, keys_lds + u * KT, l, 64);
     __syncthreads();
     TileFragsG1 f;
     load_frags_g1(tb, f);
     f32x4 seed[4];
-    mask_seed(KT, kvalid, seed);
+    mask_seed(min(KT, total - u * KT), nullptr, seed);
     f32x4 s[4];
     scores_g1(f, qq, seed, s);
     softmax_pv_g1(st, s, f, c2);
@@ -530,13 +517,14 @@ __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
     const float wgt = valid ? (gp ? sigmoidf_((float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_sel]) * inv : inv) : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      bf16* dst = o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g;
+      bf16x4* dst = reinterpret_cast<bf16x4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
+      f32x4 v = st.acc[dt] * wgt;
+      if (a.accumulate && valid) {
+        const bf16x4 prev = *dst;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = st.acc[dt][i] * wgt;
-        if (a.accumulate && valid) v += (float)dst[i];
-        dst[i] = (bf16)v;
+        for (int i = 0; i < 4; ++i) v[i] += (float)prev[i];
       }
+      *dst = __builtin_convertvector(v, bf16x4);
     }
   }
 }

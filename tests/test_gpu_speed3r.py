@@ -127,6 +127,28 @@ def test_single_branch_block_rows(branch):
     assert np.all(host(o)[~vm] == 0)
 
 
+@pytest.mark.parametrize("k", [16, 40])
+def test_selected_rows_with_repeats_and_gaps(k):
+    """Block routing rows holding repeated entries and -1, over blocks of ragged counts: the selected
+    branch attends the set of named blocks (k = 40 spans several 64-key tiles of packed tokens)."""
+    import sparse_attention_feed_amd as S
+    rng = np.random.default_rng(7)
+    n_blk = 90
+    cnt = rng.integers(1, 17, size=n_blk)
+    w = W.custom_block_workload(77, cnt, 16, 16, 16, 64, "bf16", k, routing="scores", q_gran="block",
+                                branches=("cmp", "sel"))
+    d = to_dev(w)
+    sel = rng.integers(-1, n_blk, size=(n_blk, 16, k)).astype(np.int32)
+    sel[:, :, 1] = sel[:, :, 0]                       # a repeat in every row
+    sel[::7, :, :] = -1                               # some rows select nothing
+    say("sel_g1 repeats", k)
+    o = S.attn_fwd(d["layout"], S.BR_SEL, d["q"], d["k"], d["v"], sel=torch.from_numpy(sel).cuda(), top_k=k,
+                   sel_groups=16, q_gran=S.Q_BLOCK)
+    torch.cuda.synchronize()
+    ref, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel, q_gran="block")
+    assert max_err(host(o), ref) <= 2e-2
+
+
 def test_fused_layer_block_rows():
     """Pool Q/K/V, score routing, then the gated compressed + selected branches: the whole layer."""
     import sparse_attention_feed_amd as S
