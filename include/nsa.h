@@ -76,7 +76,8 @@ typedef struct {
  * Q/K/V.  x_cmp[b][h][:] = mean of x[s][h][:] over the valid slots s of block b, accumulated in
  * fp32 and rounded to `dtype`.
  *   x      [S][n_heads][head_dim]      x_cmp  [n_blk][n_heads][head_dim]
- * n_heads * head_dim <= 1024.
+ * n_heads * head_dim must be a multiple of 8 (bf16) or 4 (f32) and x, x_cmp 16-byte aligned
+ * (NSA_ERR_UNSUPPORTED otherwise): each row is read in 16-byte pieces.
  */
 nsa_status nsa_pool_blocks(const nsa_layout* layout, nsa_dtype dtype, int32_t n_heads,
                            const void* x, void* x_cmp, hipStream_t stream);

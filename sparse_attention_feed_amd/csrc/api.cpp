@@ -66,8 +66,11 @@ nsa_status nsa_pool_blocks(const nsa_layout* L, nsa_dtype dtype, int32_t n_heads
   if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "nsa_pool_blocks: unknown dtype %d", (int)dtype);
   if (x == nullptr || x_cmp == nullptr) return fail(NSA_ERR_INVALID, "nsa_pool_blocks: x or x_cmp is NULL");
   if (n_heads < 1) return fail(NSA_ERR_INVALID, "nsa_pool_blocks: n_heads must be >= 1");
-  if ((long long)n_heads * L->head_dim > 1024)
-    return fail(NSA_ERR_UNSUPPORTED, "nsa_pool_blocks: n_heads * head_dim must be <= 1024");
+  const int vec = dtype == NSA_BF16 ? 8 : 4;     // elements per 16-byte piece
+  if (((long long)n_heads * L->head_dim) % vec != 0)
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_pool_blocks: n_heads * head_dim must be a multiple of %d for this dtype", vec);
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(x_cmp)) % 16 != 0)
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_pool_blocks: x and x_cmp must be 16-byte aligned");
   NSA_FORCED_FAILURE("nsa_pool_blocks");
   return hip_status(nsa::launch_pool(dtype == NSA_BF16, x, x_cmp, L->blk_cnt, L->n_blk, L->blk_cap, n_heads,
                                      L->head_dim, stream),

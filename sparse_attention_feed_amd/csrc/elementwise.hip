@@ -6,19 +6,47 @@ namespace nsa {
 namespace {
 
 // Block compression (LSRM pages, section 方法, eq. k^cmp = AvgPool(ResBlock(k)), ResBlock = identity;
-// Speed3R page, section 2.1, average pooling).  One workgroup per block; thread = (head, dim), so
-// each token row of the block is one coalesced read.  fp32 accumulation in token order.
+// Speed3R page, section 2.1, average pooling).  One thread per (block, 16-byte piece of the row):
+// it reads that piece of each valid token (one coalesced 16-byte load per token, four in flight)
+// and accumulates in fp32 in token order.
 template <typename T>
-__global__ void pool_kernel(const T* __restrict__ x, T* __restrict__ xc, const int32_t* __restrict__ blk_cnt,
-                            int cap, int row) {
-  const int b = blockIdx.x;
-  const int e = threadIdx.x;
-  if (e >= row) return;
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, T* __restrict__ xc,
+                                                   const int32_t* __restrict__ blk_cnt, int n_blk, int cap,
+                                                   int row) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int pieces = row / VEC;
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)n_blk * pieces) return;
+  const int b = (int)(i / pieces), pc = (int)(i % pieces);
   const int cnt = blk_cnt[b];
-  const T* src = x + (size_t)b * cap * row + e;
-  float s = 0.f;
-  for (int t = 0; t < cnt; ++t) s += to_f32(src[(size_t)t * row]);
-  xc[(size_t)b * row + e] = from_f32<T>(s / (float)cnt);
+  const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)b * cap * row + pc * VEC);
+  const size_t step = (size_t)row / VEC;      // uint4 per token row
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  int t = 0;
+  for (; t + 4 <= cnt; t += 4) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = src[(size_t)(t + u) * step];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const T* e = reinterpret_cast<const T*>(&v[u]);
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) acc[k] += to_f32(e[k]);
+    }
+  }
+  for (; t < cnt; ++t) {
+    const uint4 v = src[(size_t)t * step];
+    const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[k] += to_f32(e[k]);
+  }
+  uint4 out;
+  T* oe = reinterpret_cast<T*>(&out);
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) oe[k] = from_f32<T>(acc[k] / (float)cnt);
+  *reinterpret_cast<uint4*>(xc + (size_t)b * row + pc * VEC) = out;
 }
 
 struct BranchPtrs {
@@ -50,13 +78,16 @@ __global__ void gate_kernel(BranchPtrs br, int n_branch, const T* __restrict__ g
 hipError_t launch_pool(int is_bf16, const void* x, void* x_cmp, const int32_t* blk_cnt, int n_blk,
                        int cap, int n_heads, int head_dim, hipStream_t s) {
   const int row = n_heads * head_dim;
-  const int nt = ((row + 63) / 64) * 64;
+  const int vec = is_bf16 ? 8 : 4;
+  if (row % vec != 0) return hipErrorInvalidValue;
+  const long long n = (long long)n_blk * (row / vec);
+  const unsigned nb = (unsigned)((n + 255) / 256);
   if (is_bf16)
-    hipLaunchKernelGGL(pool_kernel<bf16>, dim3(n_blk), dim3(nt), 0, s, (const bf16*)x, (bf16*)x_cmp,
-                       blk_cnt, cap, row);
+    hipLaunchKernelGGL(pool_kernel<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)x, (bf16*)x_cmp,
+                       blk_cnt, n_blk, cap, row);
   else
-    hipLaunchKernelGGL(pool_kernel<float>, dim3(n_blk), dim3(nt), 0, s, (const float*)x, (float*)x_cmp,
-                       blk_cnt, cap, row);
+    hipLaunchKernelGGL(pool_kernel<float>, dim3(nb), dim3(256), 0, s, (const float*)x, (float*)x_cmp,
+                       blk_cnt, n_blk, cap, row);
   return hipGetLastError();
 }
 

@@ -93,7 +93,10 @@ def test_other_calls_validate(S, monkeypatch):
     L = layout(S)
     lib = S.lib
     assert lib.nsa_pool_blocks(ctypes.byref(L), 1, 2, None, FAKE, None) == -1
-    assert lib.nsa_pool_blocks(ctypes.byref(L), 1, 64, FAKE, FAKE, None) == -2       # 64*32 > 1024
+    L3 = layout(S, head_dim=3)
+    assert lib.nsa_pool_blocks(ctypes.byref(L3), 1, 2, FAKE, FAKE, None) == -2      # row of 6 bf16
+    assert lib.nsa_pool_blocks(ctypes.byref(L3), 0, 1, FAKE, FAKE, None) == -2      # row of 3 f32
+    assert lib.nsa_pool_blocks(ctypes.byref(L), 1, 2, FAKE + 8, FAKE, None) == -2    # misaligned
     assert lib.nsa_route_geometric(ctypes.byref(L), FAKE, 0, FAKE, FAKE, None, None) == -1
     assert lib.nsa_route_geometric(ctypes.byref(L), FAKE, 65, FAKE, FAKE, None, None) == -1
     assert lib.nsa_route_geometric(ctypes.byref(L), None, 4, FAKE, FAKE, None, None) == -1
