@@ -40,15 +40,23 @@ __device__ __forceinline__ Frag8<bf16> ld8(const bf16* p) {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Query fragments (two d halves) of one row: B operand of S^T.
+// Query fragments (two d halves) of one row: B operand of S^T.  With c2 != 1 every element is
+// multiplied by c2 = scale * log2(e) in fp32 and rounded once to bf16, so S^T comes out in base-2
+// logit units (the routing kernel keeps the raw query: c2 = 1).
 struct QG1 { Frag8<bf16> h[2]; };
 
-__device__ __forceinline__ QG1 load_q_row(const bf16* row, bool valid) {
+__device__ __forceinline__ QG1 load_q_row(const bf16* row, bool valid, float c2 = 1.f) {
   QG1 q;
   const int g = lane_id() >> 4;
   if (valid) {
     q.h[0] = ld8(row + 8 * g);
     q.h[1] = ld8(row + 32 + 8 * g);
+    if (c2 != 1.f) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q.h[hh].v[e] = (bf16)((float)q.h[hh].v[e] * c2);
+    }
   } else {
     q.h[0].v = bf16x8{};
     q.h[1].v = bf16x8{};
@@ -102,17 +110,24 @@ __device__ __forceinline__ void stage_rows_g1(TileG1& t, const bf16* kb, const b
   }
 }
 
-// Online softmax state of one column group (16 rows of one head).
+// Online softmax state of one column group (16 rows of one head), base-2 units.  The reference
+// maximum mc starts at 0 and may go stale: it enters S^T as the MFMA accumulator seed (-mc), and
+// it moves (with a rescale) only when a lane's probability sum could exceed kStaleLimitG1 or is
+// not finite, or when a row has no mass yet and the tile's mass is tiny.  The result equals the
+// textbook online softmax up to rounding.
 struct StateG1 {
   f32x4 acc[4];             // O^T[d = 16*dt + 4*(lane/16) + i][row lane%16]
-  float m;                  // running max of raw scores for row lane%16 (identical across lane groups)
+  float mc;                 // reference max of row lane%16 (identical across lane groups)
   float l;                  // this lane group's share of the sum
 };
+
+constexpr float kStaleLimitG1 = 65536.0f;
+constexpr float kTinyMassG1 = 1.0e-30f;
 
 __device__ __forceinline__ void state_init(StateG1& s) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) s.acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  s.m = -INFINITY;
+  s.mc = 0.f;
   s.l = 0.f;
 }
 
@@ -125,20 +140,9 @@ __device__ __forceinline__ float rows_sum(float x) {
   return x + __shfl_xor(x, 32, 64);
 }
 
-// One tile: scores s (raw, padding keys already -inf), exact running max (the max costs little next
-// to the 16 MFMAs per tile at head dim 64), probabilities rounded to bf16 for the value product.
-__device__ __forceinline__ void softmax_pv_g1(StateG1& st, const f32x4 (&s)[4], const TileFragsG1& f, float c2) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][i]);
-  mx = rows_max(mx);
-  const float mn = fmaxf(st.m, mx);
-  // (mn stays -inf only if no key has been valid yet; every probability is then exactly 0)
-  const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - mn) * c2);
-  const float mcn = mn == -INFINITY ? 0.f : mn * c2;
-  Frag8<bf16> pf[2];
+// p = exp2(x) for the lane's 16 logits, packed as the two B operands of the value product;
+// returns the lane's sum of the probabilities as rounded for that product.
+__device__ __forceinline__ float exp_pack_g1(const f32x4 (&x)[4], Frag8<bf16> (&pf)[2]) {
   float lt = 0.f;
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
@@ -147,20 +151,58 @@ __device__ __forceinline__ void softmax_pv_g1(StateG1& st, const f32x4 (&s)[4], 
     for (int e = 0; e < 8; e += 2) {
       const int kt = 2 * h + (e >> 2), i = e & 3;
       f32x2 p;
-      p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -mcn));
-      p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i + 1], c2, -mcn));
+      p[0] = __builtin_amdgcn_exp2f(x[kt][i]);
+      p[1] = __builtin_amdgcn_exp2f(x[kt][i + 1]);
       const bf16x2 pb = __builtin_convertvector(p, bf16x2);
       pf[h].v[e] = pb[0];
       pf[h].v[e + 1] = pb[1];
       lt = __builtin_amdgcn_fdot2_f32_bf16(pb, one, lt, false);
     }
-  st.l = st.l * alpha + lt;
-  st.m = mn;
+  return lt;
+}
+
+// One tile: x = S^T - mc (padding keys -inf) from scores_g1; probabilities rounded to bf16 for the
+// value product.
+__device__ __forceinline__ void softmax_pv_g1(StateG1& st, f32x4 (&x)[4], const TileFragsG1& f) {
+  Frag8<bf16> pf[2];
+  float lt = exp_pack_g1(x, pf);
+  if (__builtin_amdgcn_ballot_w64(!(lt <= kStaleLimitG1) || !(st.l + lt >= kTinyMassG1)) != 0) {
+    float mx = -INFINITY;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    st.acc[dt] *= alpha;
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kt][i]);
+    const float xm = rows_max(mx);
+    const float lh = rows_sum(st.l);
+    float shift = lh > 0.f ? fmaxf(xm, 0.f) : xm;
+    if (!(shift > -INFINITY)) shift = 0.f;          // no valid key in this row
+    if (lh > 0.f && shift > 0.f) {
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      st.l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) st.acc[dt] *= alpha;
+    }
+    st.mc += shift;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) x[kt] -= shift;
+    lt = exp_pack_g1(x, pf);
+  }
+  st.l += lt;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int c = 0; c < 2; ++c) st.acc[dt] = mma16(f.v[dt][c], pf[c], st.acc[dt]);
+}
+
+// Seeds of S^T for a column group: -mc on valid keys, -inf on the keys of a partial tile.
+__device__ __forceinline__ void row_seed(const StateG1& st, bool full, const f32x4 (&cm)[4], f32x4 (&seed)[4]) {
+  if (full) {
+    const f32x4 m = {-st.mc, -st.mc, -st.mc, -st.mc};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) seed[kt] = m;
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) seed[kt] = cm[kt] - st.mc;
   }
 }
 
@@ -184,9 +226,8 @@ constexpr int CW = 8;       // waves per workgroup
 constexpr int CG = 2;       // column groups (16 rows each) per wave
 
 __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
+  static_assert(CW * 64 == KT * 8, "one 16-byte piece of K and of V per thread");
   __shared__ TileG1 tb[2];
-  __shared__ int rows_lds[2][KT];
-  const int nt = CW * 64;
   const int n_rowgrp = (a.n_blk + CW * CG * 16 - 1) / (CW * CG * 16);
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int h = wg / n_rowgrp, rg = wg % n_rowgrp;
@@ -204,35 +245,51 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
   for (int c = 0; c < CG; ++c) {
     row_of[c] = (rg * CW * CG + w * CG + c) * 16 + r;
     const bool ok = row_of[c] < a.n_blk;
-    q[c] = load_q_row(qc + ((size_t)row_of[c] * a.n_qh + h) * DG, ok);
+    q[c] = load_q_row(qc + ((size_t)row_of[c] * a.n_qh + h) * DG, ok, c2);
     state_init(st[c]);
   }
   const int ntiles = (a.n_blk + KT - 1) / KT;
-  for (int i = threadIdx.x; i < KT; i += nt) rows_lds[0][i] = i < a.n_blk ? i : -1;
-  __syncthreads();
-  stage_rows_g1(tb[0], kb, vb, stride, rows_lds[0], threadIdx.x, nt);
+  // staging: thread t copies the 16-byte piece (key t / 8, part t % 8) of both K and V; the next
+  // tile's loads are issued before the current tile's compute
+  const int s_key = threadIdx.x >> 3, s_part = threadIdx.x & 7;
+  auto fetch = [&](int u, uint4& kv, uint4& vv) {
+    const int key = u * KT + s_key;
+    kv = make_uint4(0u, 0u, 0u, 0u);
+    vv = kv;
+    if (key < a.n_blk) {
+      kv = *reinterpret_cast<const uint4*>(kb + (size_t)key * stride + s_part * 8);
+      vv = *reinterpret_cast<const uint4*>(vb + (size_t)key * stride + s_part * 8);
+    }
+  };
+  auto store = [&](TileG1& t, const uint4& kv, const uint4& vv) {
+    *reinterpret_cast<uint4*>(&t.k[s_key][s_part * 8]) = kv;
+    const bf16* e = reinterpret_cast<const bf16*>(&vv);
+    const int pos = vt_pos_g1(s_key);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) t.vt[s_part * 8 + x][pos] = e[x];
+  };
+  uint4 kv, vv;
+  fetch(0, kv, vv);
+  store(tb[0], kv, vv);
   __syncthreads();
   for (int u = 0; u < ntiles; ++u) {
     const int cur = u & 1;
-    if (u + 1 < ntiles) {
-      for (int i = threadIdx.x; i < KT; i += nt) {
-        const int key = (u + 1) * KT + i;
-        rows_lds[cur ^ 1][i] = key < a.n_blk ? key : -1;
-      }
-    }
+    if (u + 1 < ntiles) fetch(u + 1, kv, vv);
     TileFragsG1 f;
     load_frags_g1(tb[cur], f);
     const int nk = min(KT, a.n_blk - u * KT);
-    f32x4 seed[4];
-    mask_seed(nk, nullptr, seed);
+    const bool full = nk == KT;
+    f32x4 cm[4];
+    if (!full) mask_seed(nk, nullptr, cm);
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
-      f32x4 s[4];
-      scores_g1(f, q[c], seed, s);
-      softmax_pv_g1(st[c], s, f, c2);
+      f32x4 seed[4], x[4];
+      row_seed(st[c], full, cm, seed);
+      scores_g1(f, q[c], seed, x);
+      softmax_pv_g1(st[c], x, f);
     }
-    __syncthreads();
-    if (u + 1 < ntiles) stage_rows_g1(tb[cur ^ 1], kb, vb, stride, rows_lds[cur ^ 1], threadIdx.x, nt);
+    // every wave finished tile u - 1 (the previous barrier), so buffer cur ^ 1 is free
+    if (u + 1 < ntiles) store(tb[cur ^ 1], kv, vv);
     __syncthreads();
   }
   // finish: normalise, gate per token, give the block's pooled result to each of its tokens
@@ -244,7 +301,7 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
     const float lsum = rows_sum(st[c].l);
     if (b >= a.n_blk) continue;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    if (a.lse && g == 0) a.lse[(size_t)b * a.n_qh + h] = lsum > 0.f ? st[c].m * a.scale + __logf(lsum) : -INFINITY;
+    if (a.lse && g == 0) a.lse[(size_t)b * a.n_qh + h] = lsum > 0.f ? (st[c].mc + __log2f(lsum)) * kLn2 : -INFINITY;
     const int cnt = a.blk_cnt[b];
     for (int t = 0; t < a.cap; ++t) {
       const size_t row = (size_t)b * a.cap + t;
@@ -493,17 +550,18 @@ __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
   __syncthreads();
   StateG1 st;
   state_init(st);
-  const QG1 qq = load_q_row(q + ((size_t)(b * cap + r) * a.n_qh + h) * DG, r < cnt);
+  const QG1 qq = load_q_row(q + ((size_t)(b * cap + r) * a.n_qh + h) * DG, r < cnt, c2);
   for (int u = 0; u < ntiles; ++u) {
     stage_rows_g1(tb, kb, vb, stride, keys_lds + u * KT, l, 64);
     __syncthreads();
     TileFragsG1 f;
     load_frags_g1(tb, f);
-    f32x4 seed[4];
-    mask_seed(min(KT, total - u * KT), nullptr, seed);
-    f32x4 s[4];
-    scores_g1(f, qq, seed, s);
-    softmax_pv_g1(st, s, f, c2);
+    const int nk = min(KT, total - u * KT);
+    f32x4 cm[4], seed[4], x[4];
+    if (nk < KT) mask_seed(nk, nullptr, cm);
+    row_seed(st, nk == KT, cm, seed);
+    scores_g1(f, qq, seed, x);
+    softmax_pv_g1(st, x, f);
     __syncthreads();
   }
   const float lsum = rows_sum(st.l);
@@ -512,7 +570,7 @@ __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
   const bf16* gp = reinterpret_cast<const bf16*>(a.gates);
   if (r < cap) {
     const size_t row = (size_t)b * cap + r;
-    if (a.lse && g == 0) a.lse[row * a.n_qh + h] = (r < cnt && lsum > 0.f) ? st.m * a.scale + __logf(lsum) : -INFINITY;
+    if (a.lse && g == 0) a.lse[row * a.n_qh + h] = (r < cnt && lsum > 0.f) ? (st.mc + __log2f(lsum)) * kLn2 : -INFINITY;
     const bool valid = r < cnt;
     const float wgt = valid ? (gp ? sigmoidf_((float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_sel]) * inv : inv) : 0.f;
 #pragma unroll

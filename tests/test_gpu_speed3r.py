@@ -27,6 +27,15 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
 
 
+def lse_bound(w, q, k):
+    """lse bound from the arithmetic: bf16 probabilities (|d ln l| <= -ln(1 - 2^-9) ~= 1.96e-3),
+    queries scaled by scale*log2(e) and rounded once to bf16 (each logit moves by at most
+    2^-9 * scale * |q| * |k|, Cauchy-Schwarz), plus fp32 rounding."""
+    qn = np.linalg.norm(np.asarray(q, dtype=np.float64), axis=-1).max()
+    kn = np.linalg.norm(np.asarray(k, dtype=np.float64), axis=-1).max()
+    return 1.96e-3 + 2.0 ** -9 * w.scale * qn * kn + 1e-4
+
+
 def check_eps_ties(got, ref_sel, imp, k, eps_rel):
     exact = 0
     R, H = ref_sel.shape[:2]
@@ -113,14 +122,14 @@ def test_single_branch_block_rows(branch):
         for b in range(w.n_blk):
             ref_lse_rows[b] = O.attend(qc[b], kc, vc, w.scale)[1]
         gl = host(lse)
-        assert max_err(gl, ref_lse_rows) <= 5e-3
+        assert max_err(gl, ref_lse_rows) <= lse_bound(w, qc, kc)
     else:
         ref, ref_lse = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel,
                                      q_gran="block")
         vm = w.valid_mask()
         gl = host(lse)
         assert np.all(np.isneginf(gl[~vm]))
-        assert max_err(gl[vm], ref_lse[vm]) <= 5e-3
+        assert max_err(gl[vm], ref_lse[vm]) <= lse_bound(w, w.q, w.k)
     vm = w.valid_mask()
     err = max_err(host(o), ref)
     assert err <= 2e-2, err
