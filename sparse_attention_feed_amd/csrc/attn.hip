@@ -99,12 +99,7 @@ __device__ __forceinline__ Frag8<float> lds_frag(const float* p) {
   f.v = (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return f;
 }
-__device__ __forceinline__ Frag8<bf16> glb_frag(const bf16* p) { return lds_frag(p); }
-__device__ __forceinline__ Frag8<float> glb_frag(const float* p) { return lds_frag(p); }
 
-template <typename T> __device__ __forceinline__ void set_elem(Frag8<T>& f, int e, float x) {
-  f.v[e] = from_f32<T>(x);
-}
 
 // Online-softmax state of one token (16 heads of one KV group) held by one wave.
 //
@@ -446,7 +441,6 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   const float c2 = a.scale * kLog2e;
   const T* q = reinterpret_cast<const T*>(a.q);
   const int n_named = __builtin_popcount(a.branches);
-  const bool multi = n_named > 1;              // gated sum over several branches
 
   // queries of this wave's tokens: token t of wave w is block slot t * WAVES + w, so the valid
   // slots [0, cnt) spread evenly over the waves and each wave's valid tokens are a prefix
@@ -502,7 +496,6 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     }
     ++done;
   };
-  (void)multi;
 
   // ---- selected branch: union of the block's routing rows, streamed once ----
   if (a.branches & 2) {

@@ -206,16 +206,13 @@ __device__ __forceinline__ void row_seed(const StateG1& st, bool full, const f32
   }
 }
 
-__device__ __forceinline__ void mask_seed(int nk, const bool* kvalid /* LDS or null */, f32x4 (&seed)[4]) {
+// 0 on the keys of a tile below nk, -inf beyond (the lane's keys are 16*kt + 4*(lane/16) + i).
+__device__ __forceinline__ void mask_seed(int nk, f32x4 (&cm)[4]) {
   const int g = lane_id() >> 4;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 16 * kt + 4 * g + i;
-      const bool ok = key < nk && (kvalid == nullptr || kvalid[key]);
-      seed[kt][i] = ok ? 0.f : -INFINITY;
-    }
+    for (int i = 0; i < 4; ++i) cm[kt][i] = (16 * kt + 4 * g + i < nk) ? 0.f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -280,7 +277,7 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
     const int nk = min(KT, a.n_blk - u * KT);
     const bool full = nk == KT;
     f32x4 cm[4];
-    if (!full) mask_seed(nk, nullptr, cm);
+    if (!full) mask_seed(nk, cm);
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
       f32x4 seed[4], x[4];
@@ -558,7 +555,7 @@ __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
     load_frags_g1(tb, f);
     const int nk = min(KT, total - u * KT);
     f32x4 cm[4], seed[4], x[4];
-    if (nk < KT) mask_seed(nk, nullptr, cm);
+    if (nk < KT) mask_seed(nk, cm);
     row_seed(st, nk == KT, cm, seed);
     scores_g1(f, qq, seed, x);
     softmax_pv_g1(st, x, f);
