@@ -347,6 +347,75 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
   }
 }
 
+// Barrier-free tile ring for the selected branch.  R LDS buffers; tile t lives in buffer t % R.
+// Every wave stages its own share of each tile (the chunks its threads own) and then adds 1 to
+// ready[t % R]; it computes tile t once ready shows all WAVES shares of that use of the buffer, and
+// adds 1 to done[t % R] after its last read.  A wave stages tile t + R - 1 into the buffer of tile
+// t - 1 only after done shows that every wave has finished tile t - 1.  Each wait names a strictly
+// earlier event of other waves, so the ring cannot deadlock; it lets a wave run up to R - 2 tiles
+// ahead of the slowest, instead of meeting at a barrier after every tile (the work per wave and
+// tile varies with how many of its tokens selected the tile's block).  Waits are bounded: if a
+// count ever failed to arrive, the wave marks the workgroup broken and stops waiting (the output
+// would then be wrong, but the kernel would still end).
+constexpr int kRingSpinLimit = 1 << 16;
+
+__device__ __forceinline__ void ring_wait(const int* ctr, int target, int* broken) {
+  int spins = 0;
+  while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) <
+         target) {
+    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)))
+      break;
+    if (++spins > kRingSpinLimit) {
+      __hip_atomic_store(broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ __forceinline__ void ring_signal(int* ctr) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (lane_id() == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+template <typename T, int NT, int TPW, int R, class Src, class Part>
+__device__ __forceinline__ void run_tiles_ring(TileBuf<T>* const (&rb)[R], int* ready, int* done, int* broken,
+                                               const Src& src, int ntiles, const Part& part, TokState (&st)[TPW],
+                                               const QF<T> (&qf)[TPW]) {
+  constexpr int WAVES = NT / 64;
+  Stager<T, NT> sg;
+  for (int t = 0; t < R - 1 && t < ntiles; ++t) {
+    sg.load(src.kptr(t), src.vptr(t), src.stride, src.nk(t));
+    sg.store(*rb[t]);
+    ring_signal(&ready[t]);
+  }
+  for (int u = 0; u < ntiles; ++u) {
+    const int ahead = u + R - 1;                  // the tile this iteration stages
+    if (ahead < ntiles) sg.load(src.kptr(ahead), src.vptr(ahead), src.stride, src.nk(ahead));
+    const int bu = u % R;
+    ring_wait(&ready[bu], WAVES * (u / R + 1), broken);
+    const TileBuf<T>& b = *rb[bu];
+    const int nk = src.nk(u);
+    const uint32_t pm = part.wave_mask(u);
+    if (pm != 0u) {
+      Frag8<T> kf[4], vf[2][2];
+      f32x4 cm[4];
+      load_tile_frags(b, kf, vf);
+      if (nk < TILE) tile_mask(nk, cm);
+      tile_masked<T, TPW>(st, qf, pm, kf, vf, cm, nk == TILE);
+    }
+    ring_signal(&done[bu]);
+    if (ahead < ntiles) {
+      const int bp = (u + R - 1) % R;              // == (u - 1) % R, the buffer of tile u - 1
+      if (u >= 1) ring_wait(&done[bp], WAVES * ((u - 1) / R + 1), broken);
+      sg.store(*rb[bp]);
+      ring_signal(&ready[bp]);
+    }
+  }
+  __syncthreads();
+}
+
 // Key tile sources ------------------------------------------------------------------------------
 
 template <typename T> struct RangeSrc {     // tiles of 64 consecutive rows [lo, hi) of [rows][n_kvh][D]
@@ -363,11 +432,10 @@ template <typename T> struct UnionSrc {     // one tile per block in the selecti
   const T* vb;
   int stride;      // n_kvh * D
   int cap;
-  const int* ulist;        // LDS
-  const int32_t* blk_cnt;  // global
-  __device__ const T* kptr(int u) const { return kb + (size_t)ulist[u] * cap * stride; }
-  __device__ const T* vptr(int u) const { return vb + (size_t)ulist[u] * cap * stride; }
-  __device__ int nk(int u) const { return blk_cnt[ulist[u]]; }
+  const int* ulist;        // LDS: block index | valid-token count << 16
+  __device__ const T* kptr(int u) const { return kb + (size_t)(ulist[u] & 0xFFFF) * cap * stride; }
+  __device__ const T* vptr(int u) const { return vb + (size_t)(ulist[u] & 0xFFFF) * cap * stride; }
+  __device__ int nk(int u) const { return ulist[u] >> 16; }
 };
 
 struct AllPart {                 // the wave's valid tokens (a prefix) take part in every tile
@@ -499,15 +567,26 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
 
   // ---- selected branch: union of the block's routing rows, streamed once ----
   if (a.branches & 2) {
+    // byte offsets from `extra` (kept as offsets so the pointers stay LDS pointers): bitmap,
+    // per-word prefix, union list, scan scratch, per-wave token masks, ring buffers 2 and 3, and
+    // the ring counters ready[4], done[4], broken
+    const int off_wpre = a.n_words * 4;
+    const int off_ulist = off_wpre + a.n_words * 4;
+    const int off_scratch = off_ulist + a.u_cap * 4;
+    const int off_umask = (off_scratch + (NT / 64 + 1) * 4 + 7) & ~7;
+    const int off_ring = (off_umask + a.u_cap * 8 + 15) & ~15;
+    const int off_ctr = off_ring + 2 * (int)sizeof(TileBuf<T>);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(extra);
-    int* wpre = reinterpret_cast<int*>(bitmap + a.n_words);
-    int* ulist = wpre + a.n_words;
-    int* scratch = ulist + a.u_cap;
-    unsigned long long* umask = reinterpret_cast<unsigned long long*>(
-        (reinterpret_cast<uintptr_t>(scratch + NT / 64 + 1) + 7) & ~uintptr_t(7));
+    int* wpre = reinterpret_cast<int*>(extra + off_wpre);
+    int* ulist = reinterpret_cast<int*>(extra + off_ulist);
+    int* scratch = reinterpret_cast<int*>(extra + off_scratch);
+    unsigned long long* umask = reinterpret_cast<unsigned long long*>(extra + off_umask);
+    TileBuf<T>* ring_hi = reinterpret_cast<TileBuf<T>*>(extra + off_ring);
+    int* ring_ctr = reinterpret_cast<int*>(extra + off_ctr);
     const int grp = a.sel_groups == 1 ? 0 : j;
     const int kk = a.top_k;
     for (int i = threadIdx.x; i < a.n_words; i += NT) bitmap[i] = 0u;
+    if (threadIdx.x < 9) ring_ctr[threadIdx.x] = 0;
     __syncthreads();
     for (int e = threadIdx.x; e < cnt * kk; e += NT) {
       const int t = e / kk, s = e % kk;
@@ -531,7 +610,8 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
         while (bits) {
           const int bit = __builtin_ctz(bits);
           bits &= bits - 1;
-          ulist[base++] = 32 * wi + bit;
+          const int blk = 32 * wi + bit;
+          ulist[base++] = blk | (a.blk_cnt[blk] << 16);
         }
       }
     }
@@ -555,9 +635,9 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.stride = kvs;
     src.cap = cap;
     src.ulist = ulist;
-    src.blk_cnt = a.blk_cnt;
     UnionPart<WAVES, TPW> part{umask, w};
-    run_tiles<T, NT, TPW>(buf, src, n_union, part, st, qf);   // ends with a barrier
+    TileBuf<T>* const rb[4] = {buf, buf + 1, ring_hi, ring_hi + 1};
+    run_tiles_ring<T, NT, TPW, 4>(rb, ring_ctr, ring_ctr + 4, ring_ctr + 8, src, n_union, part, st, qf);  // ends with a barrier
     finish_all((a.branches & 1) ? 1 : 0);
   }
 
@@ -690,8 +770,9 @@ template <typename T>
 size_t attn_lds_t(const AttnArgs& a) {
   constexpr int NT = Shape<T>::WAVES * 64;
   size_t extra = 0;
-  if (a.branches & 2)
-    extra = (size_t)a.n_words * 8 + (size_t)a.u_cap * 4 + (NT / 64 + 1) * 4 + 8 + (size_t)a.u_cap * 8;
+  if (a.branches & 2)   // union tables, two more ring buffers, ring counters (with alignment slack)
+    extra = (size_t)a.n_words * 8 + (size_t)a.u_cap * 4 + (NT / 64 + 1) * 4 + 8 + (size_t)a.u_cap * 8 + 16 +
+            2 * sizeof(TileBuf<T>) + 9 * sizeof(int);
   if (OutInLds<T>::value && __builtin_popcount(a.branches) > 1) {
     const size_t out_bytes = (size_t)64 * GRP * HD * sizeof(float);
     if (out_bytes > extra) extra = out_bytes;
