@@ -240,6 +240,14 @@ nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches,
     long long u = (long long)L->blk_cap * (a.top_k > 0 ? a.top_k : 1);
     a.u_cap = (int)(u < L->n_blk ? u : L->n_blk);
   }
+  // Test hook (NSA_TEST_RING_STALL=1): the selected branch's tile ring waits for one count more
+  // than ever arrives, with a short bound, so the bounded-wait path runs (output NaN, no hang).
+  {
+    const char* e = getenv("NSA_TEST_RING_STALL");
+    const bool stall = e != nullptr && e[0] == '1';
+    a.ring_spins = stall ? 64 : (1 << 16);
+    a.ring_stall = stall ? 1 : 0;
+  }
   const size_t lds = nsa::attn_lds_bytes(dtype == NSA_BF16, a);
   if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: LDS need %zu bytes exceeds 160 KiB", lds);
   NSA_FORCED_FAILURE("nsa_attn_fwd");

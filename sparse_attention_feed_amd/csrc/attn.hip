@@ -355,17 +355,15 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
 // earlier event of other waves, so the ring cannot deadlock; it lets a wave run up to R - 2 tiles
 // ahead of the slowest, instead of meeting at a barrier after every tile (the work per wave and
 // tile varies with how many of its tokens selected the tile's block).  Waits are bounded: if a
-// count ever failed to arrive, the wave marks the workgroup broken and stops waiting (the output
-// would then be wrong, but the kernel would still end).
-constexpr int kRingSpinLimit = 1 << 16;
-
-__device__ __forceinline__ void ring_wait(const int* ctr, int target, int* broken) {
+// count ever failed to arrive, the wave marks the workgroup broken and stops waiting; the kernel
+// still ends and the branch's output is NaN.
+__device__ __forceinline__ void ring_wait(const int* ctr, int target, int* broken, int spin_limit) {
   int spins = 0;
   while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) <
          target) {
     if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)))
       break;
-    if (++spins > kRingSpinLimit) {
+    if (++spins > spin_limit) {
       __hip_atomic_store(broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       break;
     }
@@ -381,8 +379,8 @@ __device__ __forceinline__ void ring_signal(int* ctr) {
 
 template <typename T, int NT, int TPW, int R, class Src, class Part>
 __device__ __forceinline__ void run_tiles_ring(TileBuf<T>* const (&rb)[R], int* ready, int* done, int* broken,
-                                               const Src& src, int ntiles, const Part& part, TokState (&st)[TPW],
-                                               const QF<T> (&qf)[TPW]) {
+                                               int spin_limit, int stall, const Src& src, int ntiles,
+                                               const Part& part, TokState (&st)[TPW], const QF<T> (&qf)[TPW]) {
   constexpr int WAVES = NT / 64;
   Stager<T, NT> sg;
   for (int t = 0; t < R - 1 && t < ntiles; ++t) {
@@ -394,7 +392,7 @@ __device__ __forceinline__ void run_tiles_ring(TileBuf<T>* const (&rb)[R], int* 
     const int ahead = u + R - 1;                  // the tile this iteration stages
     if (ahead < ntiles) sg.load(src.kptr(ahead), src.vptr(ahead), src.stride, src.nk(ahead));
     const int bu = u % R;
-    ring_wait(&ready[bu], WAVES * (u / R + 1), broken);
+    ring_wait(&ready[bu], WAVES * (u / R + 1) + stall, broken, spin_limit);
     const TileBuf<T>& b = *rb[bu];
     const int nk = src.nk(u);
     const uint32_t pm = part.wave_mask(u);
@@ -408,12 +406,20 @@ __device__ __forceinline__ void run_tiles_ring(TileBuf<T>* const (&rb)[R], int* 
     ring_signal(&done[bu]);
     if (ahead < ntiles) {
       const int bp = (u + R - 1) % R;              // == (u - 1) % R, the buffer of tile u - 1
-      if (u >= 1) ring_wait(&done[bp], WAVES * ((u - 1) / R + 1), broken);
+      if (u >= 1) ring_wait(&done[bp], WAVES * ((u - 1) / R + 1), broken, spin_limit);
       sg.store(*rb[bp]);
       ring_signal(&ready[bp]);
     }
   }
   __syncthreads();
+  if (*broken) {
+    // a wait gave up: make the branch's output NaN rather than silently wrong
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      st[t].acc[0] = (f32x4){NAN, NAN, NAN, NAN};
+      st[t].acc[1] = st[t].acc[0];
+    }
+  }
 }
 
 // Key tile sources ------------------------------------------------------------------------------
@@ -637,7 +643,8 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.ulist = ulist;
     UnionPart<WAVES, TPW> part{umask, w};
     TileBuf<T>* const rb[4] = {buf, buf + 1, ring_hi, ring_hi + 1};
-    run_tiles_ring<T, NT, TPW, 4>(rb, ring_ctr, ring_ctr + 4, ring_ctr + 8, src, n_union, part, st, qf);  // ends with a barrier
+    run_tiles_ring<T, NT, TPW, 4>(rb, ring_ctr, ring_ctr + 4, ring_ctr + 8, a.ring_spins, a.ring_stall, src, n_union,
+                                  part, st, qf);   // ends with a barrier
     finish_all((a.branches & 1) ? 1 : 0);
   }
 

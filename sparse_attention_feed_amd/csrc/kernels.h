@@ -23,6 +23,8 @@ struct AttnArgs {
   uint32_t branches;
   int n_words;         // ceil(n_blk / 32): selection bitmap words
   int u_cap;           // bound on the number of distinct selected blocks of one query block
+  int ring_spins;      // bound on each wait of the selected branch's tile ring
+  int ring_stall;      // test hook: extra count the ring waits for (0 in normal use)
 };
 
 struct DenseArgs {

@@ -320,6 +320,29 @@ def test_full_size_dense_sampled():
 # reproducibility and storage-order invariance
 # ---------------------------------------------------------------------------------------------
 
+def test_ring_wait_bound_ends_with_nan(monkeypatch):
+    """The selected branch's tile ring waits only a bounded time.  A test hook makes it wait for a
+    count that never arrives: the kernel still completes and the branch output is NaN (no hang);
+    without the hook the same call matches the oracle."""
+    import sparse_attention_feed_amd as S
+    w = wl("stage2_small")
+    d = to_dev(w)
+    sel_ref, _ = O.route_geometric(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k)
+    sel = torch.from_numpy(sel_ref).cuda()
+    vm = w.valid_mask()
+    monkeypatch.setenv("NSA_TEST_RING_STALL", "1")
+    say("ring stall hook")
+    o = S.attn_fwd(d["layout"], S.BR_SEL, d["q"], d["k"], d["v"], sel=sel, top_k=w.top_k)
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(host(o)[vm]))
+    monkeypatch.delenv("NSA_TEST_RING_STALL")
+    say("ring normal")
+    o = S.attn_fwd(d["layout"], S.BR_SEL, d["q"], d["k"], d["v"], sel=sel, top_k=w.top_k)
+    torch.cuda.synchronize()
+    ref, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel_ref)
+    assert max_err(host(o), ref) <= tol(w)
+
+
 def test_repeat_runs_bit_identical():
     import sparse_attention_feed_amd as S
     w = wl("large_small")
