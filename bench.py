@@ -137,7 +137,13 @@ def setup_geometric(w, S, torch, dev):
                                   top_k=w.top_k, gates=gg, out=ws["out"])
 
     combos = {"cmp": S.BR_CMP, "sel": S.BR_SEL, "loc": S.BR_LOC, "sel+loc": S.BR_SEL | S.BR_LOC}
-    return stages, flops, {n: branch(b) for n, b in combos.items()}, "attn_fused"
+    fns = {n: branch(b) for n, b in combos.items()}
+    # the unfused alternative of the gate: a standalone combine of three branch outputs (HBM-bound);
+    # its inputs are any three [S, Hq, D] tensors of the right shape
+    extra = [q, torch.empty_like(q).copy_(q), torch.empty_like(q).copy_(q)]
+    gout = torch.empty_like(q)
+    fns["gate_combine_unfused"] = lambda: S.gate_combine(extra, g, out=gout)
+    return stages, flops, fns, "attn_fused"
 
 
 def setup_speed3r(w, S, torch, dev):
@@ -278,6 +284,13 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
+            if name == "gate_combine_unfused":
+                # bytes: three branch outputs and the gate logits read, the output written
+                esz = 2 if w.dtype == "bf16" else 4
+                nbytes = (4 * w.n_slots * w.n_qh * w.head_dim + w.n_slots * w.n_qh * 3) * esz
+                breakdown[name] = {"ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                   "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                continue
             f = sum(fl[p] for p in name.split("+"))
             breakdown[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 1),
                                "mfma_frac": round(f / (ms * 1e-3) / 1e12 / peak, 4)}

@@ -156,6 +156,8 @@ nsa_status nsa_attn_fwd(const nsa_layout* layout, nsa_dtype dtype, uint32_t bran
  *     o[r][h][:] = sum_c sigmoid(gate_logits[r][h][c]) * o_branch[c][r][h][:]
  *   o_branch   host array of n_branch device pointers, each [n_rows][n_qh][head_dim]
  *   gate_logits [n_rows][n_qh][n_branch];  o [n_rows][n_qh][head_dim];  1 <= n_branch <= 8.
+ * head_dim must be a multiple of 4 and o, o_branch[c] aligned to 4 elements (NSA_ERR_UNSUPPORTED
+ * otherwise): each thread moves four consecutive elements.
  */
 nsa_status nsa_gate_combine(nsa_dtype dtype, int32_t n_rows, int32_t n_qh, int32_t head_dim,
                             int32_t n_branch, const void* const* o_branch,

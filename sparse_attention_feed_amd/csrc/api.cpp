@@ -264,6 +264,13 @@ nsa_status nsa_gate_combine(nsa_dtype dtype, int32_t n_rows, int32_t n_qh, int32
   for (int c = 0; c < n_branch; ++c)
     if (o_branch[c] == nullptr) return fail(NSA_ERR_INVALID, "nsa_gate_combine: o_branch[%d] is NULL", c);
   if (head_dim % 4 != 0) return fail(NSA_ERR_UNSUPPORTED, "nsa_gate_combine: head_dim must be a multiple of 4");
+  {
+    const uintptr_t align = dtype == NSA_BF16 ? 8 : 16;     // four elements per vector access
+    uintptr_t bits = reinterpret_cast<uintptr_t>(o);
+    for (int c = 0; c < n_branch; ++c) bits |= reinterpret_cast<uintptr_t>(o_branch[c]);
+    if (bits % align != 0)
+      return fail(NSA_ERR_UNSUPPORTED, "nsa_gate_combine: o and o_branch must be %d-byte aligned", (int)align);
+  }
   NSA_FORCED_FAILURE("nsa_gate_combine");
   return hip_status(nsa::launch_gate(dtype == NSA_BF16, n_rows, n_qh, head_dim, n_branch, o_branch, gate_logits, o,
                                      stream),

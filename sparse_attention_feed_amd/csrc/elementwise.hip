@@ -54,23 +54,30 @@ struct BranchPtrs {
 };
 
 // o = sum_c sigmoid(g_c) o_c (LSRM pages, Sigmoid gates; Speed3R page, gated aggregation).
-// One thread per (row, head, 4 consecutive dims).
+// One thread per (row, head, 4 consecutive dims): one vector load per branch, one vector store.
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
+
 template <typename T>
 __global__ void gate_kernel(BranchPtrs br, int n_branch, const T* __restrict__ gates, T* __restrict__ o,
                             long long n_vec, int n_qh, int head_dim) {
+  typedef typename Vec4<T>::type V4;
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_vec) return;
   const long long e0 = i * 4;
   const long long rh = e0 / head_dim;          // row * n_qh + head
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int c = 0; c < n_branch; ++c) {
     const float wgt = sigmoidf_(to_f32(gates[rh * n_branch + c]));
-    const T* oc = reinterpret_cast<const T*>(br.p[c]) + e0;
+    const V4 v = reinterpret_cast<const V4*>(br.p[c])[i];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) acc[x] += wgt * to_f32(oc[x]);
+    for (int x = 0; x < 4; ++x) acc[x] += wgt * to_f32(v[x]);
   }
+  V4 out;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) o[e0 + x] = from_f32<T>(acc[x]);
+  for (int x = 0; x < 4; ++x) out[x] = from_f32<T>(acc[x]);
+  reinterpret_cast<V4*>(o)[i] = out;
 }
 
 }  // namespace

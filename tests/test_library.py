@@ -109,6 +109,8 @@ def test_other_calls_validate(S, monkeypatch):
     assert lib.dense_gated_xattn_fwd(1, 100, 101, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
     assert lib.dense_gated_xattn_fwd(1, 100, -1, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
     assert lib.dense_gated_xattn_fwd(1, 100, 50, 32, 2, 64, 0.125, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    mis = (ctypes.c_void_p * 2)(FAKE, FAKE + 2)
+    assert lib.nsa_gate_combine(1, 10, 32, 32, 2, mis, FAKE, FAKE, None) == -2         # misaligned branch
     monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
     assert lib.nsa_pool_blocks(ctypes.byref(L), 1, 2, FAKE, FAKE, None) == -3
     assert lib.nsa_route_geometric(ctypes.byref(L), FAKE, 4, FAKE, FAKE, None, None) == -3
