@@ -23,7 +23,8 @@ Sources (cited by page title and section; no page prints code or worked numbers)
 
 Readings where the pages are silent (each is listed with its reason in the design notes):
   * softmax scale is a parameter (callers pass 1/sqrt(D)); attention is non-causal;
-  * ResBlock before AvgPool is the identity, so compression is the mean over a block's valid tokens;
+  * ResBlock before AvgPool is the identity for the layer's compression (the mean over a block's
+    valid tokens); with seeded weights it is one residual MLP per head, x + W2 silu(W1 x + b1) + b2;
   * padded slots are neither keys nor queries; padded outputs are 0, padded routing rows are -1;
   * geometric routing ranks blocks by the exact integer squared distance between the query point
     and the block centroid on a 2^-12 lattice (u = rint(4096 p) + 4096), ties by ascending blk_key;
@@ -114,6 +115,41 @@ def pool_blocks(x, blk_cnt, cap):
     out = np.zeros((n_blk,) + x.shape[1:])
     for b in range(n_blk):
         rows = x[block_slots(blk_cnt, cap, b)].astype(np.float64)
+        out[b] = rows.sum(axis=0) / rows.shape[0]
+    return out
+
+
+def silu(x):
+    """x * sigmoid(x), the residual module's activation (a reading: the pages name no activation)."""
+    return np.asarray(x, dtype=np.float64) * sigmoid(x)
+
+
+def resblock(x, w1, b1, w2, b2):
+    """The residual module applied to token keys / values before pooling, [LSRM-cn] eq.
+    k^cmp = AvgPool(ResBlock(k_t)).  The pages do not define the module; the reading here is one
+    residual MLP per head with its own weights, hidden width D:
+        ResBlock(x) = x + W2 silu(W1 x + b1) + b2          (x a token's D-vector of head h)
+    x [..., H, D]; w1, w2 [H, D, D] (row j of w1[h] feeds hidden unit j; row d of w2[h] feeds
+    output d); b1, b2 [H, D]."""
+    x = np.asarray(x, dtype=np.float64)
+    w1 = np.asarray(w1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    b1 = np.asarray(b1, dtype=np.float64)
+    b2 = np.asarray(b2, dtype=np.float64)
+    out = np.empty_like(x)
+    for h in range(x.shape[-2]):
+        hidden = silu(x[..., h, :] @ w1[h].T + b1[h])
+        out[..., h, :] = x[..., h, :] + hidden @ w2[h].T + b2[h]
+    return out
+
+
+def pool_blocks_resblock(x, blk_cnt, cap, w1, b1, w2, b2):
+    """[LSRM-cn] eq. k^cmp = AvgPool(ResBlock(k_t)): the residual module on every valid token, then
+    the mean over the block's valid tokens.  x [S, H, D] -> [n_blk, H, D] (float64)."""
+    blk_cnt = np.asarray(blk_cnt)
+    out = np.zeros((blk_cnt.shape[0],) + x.shape[1:])
+    for b in range(blk_cnt.shape[0]):
+        rows = resblock(x[block_slots(blk_cnt, cap, b)], w1, b1, w2, b2)
         out[b] = rows.sum(axis=0) / rows.shape[0]
     return out
 

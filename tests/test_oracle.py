@@ -356,3 +356,43 @@ def test_pool_identity_linearity_constant():
                                atol=1e-14)
     c = np.full((16, 3, 5), 1.75)
     np.testing.assert_array_equal(O.pool_blocks(c, cnt, 4), np.full((4, 3, 5), 1.75))
+
+
+def test_resblock_pool_reduces_and_closed_forms():
+    """Pins of the residual module before pooling: zero weights give the plain block mean; a bias
+    b2 alone shifts every pooled row by b2; with W1 = W2 = I and zero biases a single-token block
+    gives x + silu(x) elementwise, silu written out as x / (1 + e^-x) (checked at a few points
+    against its closed values silu(0) = 0 and silu(ln 3) = 0.75 ln 3)."""
+    rng = np.random.default_rng(21)
+    cnt = np.array([1, 3, 4, 2])
+    H, D = 2, 3
+    x = rng.standard_normal((16, H, D))
+    z = np.zeros((H, D, D))
+    zb = np.zeros((H, D))
+    np.testing.assert_allclose(O.pool_blocks_resblock(x, cnt, 4, z, zb, z, zb), O.pool_blocks(x, cnt, 4),
+                               atol=1e-15)
+    b2 = rng.standard_normal((H, D))
+    np.testing.assert_allclose(O.pool_blocks_resblock(x, cnt, 4, z, zb, z, b2), O.pool_blocks(x, cnt, 4) + b2,
+                               atol=1e-14)
+    eye = np.broadcast_to(np.eye(D), (H, D, D))
+    got = O.pool_blocks_resblock(x, cnt, 4, eye, zb, eye, zb)[0]
+    np.testing.assert_allclose(got, x[0] + x[0] / (1.0 + np.exp(-x[0])), atol=1e-14)
+    assert O.silu(0.0) == 0.0
+    assert abs(O.silu(math.log(3.0)) - 0.75 * math.log(3.0)) < 1e-15
+
+
+def test_resblock_matches_a_dense_restatement():
+    """The per-head residual MLP equals a block-diagonal dense MLP over the whole token row."""
+    rng = np.random.default_rng(22)
+    H, D = 3, 4
+    x = rng.standard_normal((5, H, D))
+    w1 = rng.standard_normal((H, D, D)); w2 = rng.standard_normal((H, D, D))
+    b1 = rng.standard_normal((H, D)); b2 = rng.standard_normal((H, D))
+    W1 = np.zeros((H * D, H * D)); W2 = np.zeros((H * D, H * D))
+    for h in range(H):
+        W1[h * D:(h + 1) * D, h * D:(h + 1) * D] = w1[h]
+        W2[h * D:(h + 1) * D, h * D:(h + 1) * D] = w2[h]
+    flat = x.reshape(5, H * D)
+    pre = flat @ W1.T + b1.reshape(-1)
+    dense = flat + (pre * (0.5 + 0.5 * np.tanh(pre / 2))) @ W2.T + b2.reshape(-1)
+    np.testing.assert_allclose(O.resblock(x, w1, b1, w2, b2).reshape(5, H * D), dense, atol=1e-12)

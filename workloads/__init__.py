@@ -25,7 +25,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "DenseWorkload", "make", "CONFIGS", "bf16_round", "morton2", "morton3",
-    "permute_storage", "custom_block_workload",
+    "permute_storage", "custom_block_workload", "resblock_weights",
 ]
 
 
@@ -506,3 +506,14 @@ def permute_storage(w: Workload, seed: int) -> tuple:
                              blk_type=w.blk_type[perm_blk].copy(), pts=move(w.pts), q=move(w.q),
                              k=move(w.k), v=move(w.v), gates=move(w.gates))
     return w2, slot_map
+
+
+def resblock_weights(seed: int, n_heads: int, D: int):
+    """Seeded weights of the residual module applied before block pooling (one per head):
+    w1, w2 [H, D, D] ~ N(0, 1/D) and b1, b2 [H, D] ~ N(0, 0.1^2), float32."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    w1 = (rng.standard_normal((n_heads, D, D)) / np.sqrt(D)).astype(np.float32)
+    b1 = (0.1 * rng.standard_normal((n_heads, D))).astype(np.float32)
+    w2 = (rng.standard_normal((n_heads, D, D)) / np.sqrt(D)).astype(np.float32)
+    b2 = (0.1 * rng.standard_normal((n_heads, D))).astype(np.float32)
+    return w1, b1, w2, b2
