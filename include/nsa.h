@@ -83,6 +83,23 @@ nsa_status nsa_pool_blocks(const nsa_layout* layout, nsa_dtype dtype, int32_t n_
                            const void* x, void* x_cmp, hipStream_t stream);
 
 /*
+ * Block compression with the residual module: LSRM pages, section 方法, eq.
+ * k^cmp = AvgPool(ResBlock(k_t)), v^cmp = AvgPool(ResBlock(v_t)).  The pages do not define the
+ * module; this call takes one residual MLP per head,
+ *     ResBlock(x) = x + W2 silu(W1 x + b1) + b2,  silu(a) = a / (1 + e^-a),
+ * applied to each valid token's head vector, then the mean over the block's valid tokens,
+ * accumulated in fp32 and rounded to `dtype`.
+ *   x [S][n_heads][head_dim] (dtype);  x_cmp [n_blk][n_heads][head_dim] (dtype)
+ *   w1, w2 [n_heads][head_dim][head_dim] float32 (row j of w1[h] feeds hidden unit j, row d of
+ *   w2[h] feeds output d);  b1, b2 [n_heads][head_dim] float32.
+ * head_dim <= 64 (NSA_ERR_UNSUPPORTED otherwise).  Zero weights give nsa_pool_blocks.
+ */
+nsa_status nsa_pool_blocks_resblock(const nsa_layout* layout, nsa_dtype dtype, int32_t n_heads,
+                                    const void* x, const float* w1, const float* b1,
+                                    const float* w2, const float* b2, void* x_cmp,
+                                    hipStream_t stream);
+
+/*
  * 3D-aware geometric routing.  LSRM pages, section 方法, routing paragraph (and the Korean summary,
  * section 2.2): each query token keeps the blocks whose centres lie nearest to its 3D point.
  * Exact integer form: u = rint(4096*p) + 4096 per axis; block centroid

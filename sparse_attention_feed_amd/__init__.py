@@ -21,7 +21,7 @@ NSA_OK, NSA_ERR_INVALID, NSA_ERR_UNSUPPORTED, NSA_ERR_HIP = 0, -1, -2, -3
 NSA_F32, NSA_BF16 = 0, 1
 BR_CMP, BR_SEL, BR_LOC = 1, 2, 4
 Q_TOKEN, Q_BLOCK = 0, 1
-EXPORTS = ("nsa_pool_blocks", "nsa_route_geometric", "nsa_route_scores_topk", "nsa_attn_fwd",
+EXPORTS = ("nsa_pool_blocks", "nsa_pool_blocks_resblock", "nsa_route_geometric", "nsa_route_scores_topk", "nsa_attn_fwd",
            "nsa_gate_combine", "dense_gated_xattn_fwd", "nsa_last_error")
 
 
@@ -46,6 +46,7 @@ def _load():
     LP = ctypes.POINTER(Layout)
     sig = {
         "nsa_pool_blocks": [LP, I, I, P, P, P],
+        "nsa_pool_blocks_resblock": [LP, I, I, P, P, P, P, P, P, P],
         "nsa_route_geometric": [LP, P, I, P, P, P, P],
         "nsa_route_scores_topk": [LP, I, I, P, P, P, I, P, P],
         "nsa_attn_fwd": [LP, I, U, I, P, P, P, P, P, P, P, I, I, P, P, P, P],
@@ -124,6 +125,21 @@ def pool_blocks(layout: BlockLayout, x, out=None):
     if out is None:
         out = torch.empty((layout.n_blk, H, D), dtype=x.dtype, device=x.device)
     _check(lib.nsa_pool_blocks(layout.c, _dtype(x), H, _ptr(x), _ptr(out), _stream()))
+    return out
+
+
+def pool_blocks_resblock(layout: BlockLayout, x, w1, b1, w2, b2, out=None):
+    """Mean over each block's valid tokens of x + W2 silu(W1 x + b1) + b2 (one residual MLP per
+    head; weights float32 [H, D, D], biases [H, D]): x [S, H, D] -> [n_blk, H, D]."""
+    S, H, D = x.shape
+    assert S == layout.n_slots and D == layout.head_dim
+    for t, shape in ((w1, (H, D, D)), (w2, (H, D, D)), (b1, (H, D)), (b2, (H, D))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape:
+            raise ValueError("resblock weights must be float32 of shapes [H, D, D] / [H, D]")
+    if out is None:
+        out = torch.empty((layout.n_blk, H, D), dtype=x.dtype, device=x.device)
+    _check(lib.nsa_pool_blocks_resblock(layout.c, _dtype(x), H, _ptr(x), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                        _ptr(out), _stream()))
     return out
 
 

@@ -77,6 +77,26 @@ nsa_status nsa_pool_blocks(const nsa_layout* L, nsa_dtype dtype, int32_t n_heads
                     "nsa_pool_blocks");
 }
 
+nsa_status nsa_pool_blocks_resblock(const nsa_layout* L, nsa_dtype dtype, int32_t n_heads, const void* x,
+                                    const float* w1, const float* b1, const float* w2, const float* b2,
+                                    void* x_cmp, hipStream_t stream) {
+  nsa_status st = check_layout(L, "nsa_pool_blocks_resblock");
+  if (st != NSA_OK) return st;
+  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "nsa_pool_blocks_resblock: unknown dtype %d", (int)dtype);
+  if (x == nullptr || x_cmp == nullptr || w1 == nullptr || b1 == nullptr || w2 == nullptr || b2 == nullptr)
+    return fail(NSA_ERR_INVALID, "nsa_pool_blocks_resblock: NULL pointer");
+  if (n_heads < 1) return fail(NSA_ERR_INVALID, "nsa_pool_blocks_resblock: n_heads must be >= 1");
+  if (L->head_dim > 64) return fail(NSA_ERR_UNSUPPORTED, "nsa_pool_blocks_resblock: head_dim must be <= 64");
+  if (nsa::pool_resblock_lds_bytes(L->blk_cap, L->head_dim) > 160 * 1024)
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_pool_blocks_resblock: LDS need exceeds 160 KiB");
+  if ((long long)L->n_blk * n_heads > 0x7FFFFFFFLL)
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_pool_blocks_resblock: n_blk * n_heads too large");
+  NSA_FORCED_FAILURE("nsa_pool_blocks_resblock");
+  return hip_status(nsa::launch_pool_resblock(dtype == NSA_BF16, x, x_cmp, L->blk_cnt, w1, b1, w2, b2, L->n_blk,
+                                              L->blk_cap, n_heads, L->head_dim, stream),
+                    "nsa_pool_blocks_resblock");
+}
+
 nsa_status nsa_route_geometric(const nsa_layout* L, const float* pts, int32_t top_k, int32_t* centroids,
                                int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
   nsa_status st = check_layout(L, "nsa_route_geometric");

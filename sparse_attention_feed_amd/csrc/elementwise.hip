@@ -49,6 +49,59 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, T* _
   *reinterpret_cast<uint4*>(xc + (size_t)b * row + pc * VEC) = out;
 }
 
+// Block compression with the residual module (LSRM pages, section 方法, eq.
+// k^cmp = AvgPool(ResBlock(k_t))): ResBlock(x) = x + W2 silu(W1 x + b1) + b2 per head, then the mean
+// over the block's valid tokens.  One workgroup per (block, head): the head's weights and the
+// block's rows are staged in LDS as fp32 (rows padded to D + 1 floats against bank conflicts);
+// one thread per (token, unit) computes the hidden layer, then the output in place; the mean adds
+// the tokens in order.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_resblock_kernel(const T* __restrict__ x, T* __restrict__ xc,
+                                                            const int32_t* __restrict__ blk_cnt,
+                                                            const float* __restrict__ w1, const float* __restrict__ b1,
+                                                            const float* __restrict__ w2, const float* __restrict__ b2,
+                                                            int cap, int n_heads, int D) {
+  extern __shared__ float sm[];
+  const int Dp = D + 1;
+  float* W1 = sm;                 // [D][Dp]
+  float* W2 = W1 + D * Dp;        // [D][Dp]
+  float* X = W2 + D * Dp;         // [cap][Dp]: token rows, then the module's outputs
+  float* Hd = X + cap * Dp;       // [cap][Dp]: hidden layer
+  const int b = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int cnt = blk_cnt[b];
+  const float* w1h = w1 + (size_t)h * D * D;
+  const float* w2h = w2 + (size_t)h * D * D;
+  for (int i = tid; i < D * D; i += nt) {
+    W1[(i / D) * Dp + i % D] = w1h[i];
+    W2[(i / D) * Dp + i % D] = w2h[i];
+  }
+  for (int i = tid; i < cnt * D; i += nt) {
+    const int t = i / D, d = i % D;
+    X[t * Dp + d] = to_f32(x[((size_t)(b * cap + t) * n_heads + h) * D + d]);
+  }
+  __syncthreads();
+  for (int i = tid; i < cnt * D; i += nt) {
+    const int t = i / D, j = i % D;
+    float a = b1[h * D + j];
+    for (int k = 0; k < D; ++k) a += W1[j * Dp + k] * X[t * Dp + k];
+    Hd[t * Dp + j] = a / (1.f + __builtin_amdgcn_exp2f(-a * kLog2e));     // silu(a)
+  }
+  __syncthreads();
+  for (int i = tid; i < cnt * D; i += nt) {
+    const int t = i / D, d = i % D;
+    float y = X[t * Dp + d] + b2[h * D + d];
+    for (int j = 0; j < D; ++j) y += W2[d * Dp + j] * Hd[t * Dp + j];
+    X[t * Dp + d] = y;            // only this thread reads or writes element (t, d) in this pass
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += nt) {
+    float s = 0.f;
+    for (int t = 0; t < cnt; ++t) s += X[t * Dp + d];
+    xc[((size_t)b * n_heads + h) * D + d] = from_f32<T>(s / (float)cnt);
+  }
+}
+
 struct BranchPtrs {
   const void* p[8];
 };
@@ -95,6 +148,35 @@ hipError_t launch_pool(int is_bf16, const void* x, void* x_cmp, const int32_t* b
   else
     hipLaunchKernelGGL(pool_kernel<float>, dim3(nb), dim3(256), 0, s, (const float*)x, (float*)x_cmp,
                        blk_cnt, n_blk, cap, row);
+  return hipGetLastError();
+}
+
+size_t pool_resblock_lds_bytes(int cap, int head_dim) {
+  return (size_t)(2 * head_dim + 2 * cap) * (head_dim + 1) * sizeof(float);
+}
+
+hipError_t launch_pool_resblock(int is_bf16, const void* x, void* x_cmp, const int32_t* blk_cnt, const float* w1,
+                                const float* b1, const float* w2, const float* b2, int n_blk, int cap,
+                                int n_heads, int head_dim, hipStream_t s) {
+  const size_t lds = pool_resblock_lds_bytes(cap, head_dim);
+  const dim3 grid((unsigned)n_blk * (unsigned)n_heads);
+  if (is_bf16) {
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pool_resblock_kernel<bf16>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(pool_resblock_kernel<bf16>, grid, dim3(256), lds, s, (const bf16*)x, (bf16*)x_cmp, blk_cnt,
+                       w1, b1, w2, b2, cap, n_heads, head_dim);
+  } else {
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pool_resblock_kernel<float>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(pool_resblock_kernel<float>, grid, dim3(256), lds, s, (const float*)x, (float*)x_cmp,
+                       blk_cnt, w1, b1, w2, b2, cap, n_heads, head_dim);
+  }
   return hipGetLastError();
 }
 

@@ -63,6 +63,31 @@ def test_pool_blocks(name):
         assert err <= (1e-5 if w.dtype == "f32" else 8e-3), (key, err)
 
 
+@pytest.mark.parametrize("name", ["tiny", "stage2_small", "ragged_cap16", "cnt_one_blocks", "speed3r_small"])
+def test_pool_blocks_resblock(name):
+    """AvgPool(ResBlock(x)) with seeded weights against the oracle, and with zero weights exactly the
+    plain block mean of nsa_pool_blocks."""
+    import sparse_attention_feed_amd as S
+    w = get(name)
+    d = to_dev(w)
+    for key in ("k", "v"):
+        H = d[key].shape[1]
+        wts = W.resblock_weights(31 if key == "k" else 32, H, w.head_dim)
+        w1, b1, w2, b2 = (torch.from_numpy(a).cuda() for a in wts)
+        say("pool resblock", name, key)
+        got = host(S.pool_blocks_resblock(d["layout"], d[key], w1, b1, w2, b2))
+        torch.cuda.synchronize()
+        ref = O.pool_blocks_resblock(getattr(w, key), w.blk_cnt, w.blk_cap, *wts)
+        err = max_err(got, ref)
+        assert err <= (1e-4 if w.dtype == "f32" else 2e-2), (key, err)
+        z3 = torch.zeros_like(w1)
+        z2 = torch.zeros_like(b1)
+        plain = S.pool_blocks(d["layout"], d[key])
+        zero = S.pool_blocks_resblock(d["layout"], d[key], z3, z2, z3, z2)
+        torch.cuda.synchronize()
+        assert torch.equal(plain, zero)
+
+
 # ---------------------------------------------------------------------------------------------
 # geometric routing: bit-exact
 # ---------------------------------------------------------------------------------------------

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 7
+    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 8
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -93,6 +93,11 @@ def test_other_calls_validate(S, monkeypatch):
     L = layout(S)
     lib = S.lib
     assert lib.nsa_pool_blocks(ctypes.byref(L), 1, 2, None, FAKE, None) == -1
+    w = FAKE
+    assert lib.nsa_pool_blocks_resblock(ctypes.byref(L), 1, 2, FAKE, w, w, None, w, FAKE, None) == -1
+    assert lib.nsa_pool_blocks_resblock(ctypes.byref(L), 1, 0, FAKE, w, w, w, w, FAKE, None) == -1
+    assert lib.nsa_pool_blocks_resblock(ctypes.byref(layout(S, head_dim=128)), 1, 1, FAKE, w, w, w, w, FAKE,
+                                        None) == -2
     L3 = layout(S, head_dim=3)
     assert lib.nsa_pool_blocks(ctypes.byref(L3), 1, 2, FAKE, FAKE, None) == -2      # row of 6 bf16
     assert lib.nsa_pool_blocks(ctypes.byref(L3), 0, 1, FAKE, FAKE, None) == -2      # row of 3 f32
@@ -113,6 +118,7 @@ def test_other_calls_validate(S, monkeypatch):
     assert lib.nsa_gate_combine(1, 10, 32, 32, 2, mis, FAKE, FAKE, None) == -2         # misaligned branch
     monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
     assert lib.nsa_pool_blocks(ctypes.byref(L), 1, 2, FAKE, FAKE, None) == -3
+    assert lib.nsa_pool_blocks_resblock(ctypes.byref(L), 1, 2, FAKE, w, w, w, w, FAKE, None) == -3
     assert lib.nsa_route_geometric(ctypes.byref(L), FAKE, 4, FAKE, FAKE, None, None) == -3
     assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE, FAKE, 4, FAKE, None) == -3
     arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
