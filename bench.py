@@ -104,6 +104,7 @@ def cpu_baseline(w, budget_s):
 
 
 def setup_geometric(w, S, torch, dev):
+    import workloads as W
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v, g = (torch.from_numpy(getattr(w, n)).to(dev).to(dt).contiguous() for n in ("q", "k", "v", "gates"))
     pts = torch.from_numpy(w.pts).to(dev)
@@ -143,6 +144,10 @@ def setup_geometric(w, S, torch, dev):
     extra = [q, torch.empty_like(q).copy_(q), torch.empty_like(q).copy_(q)]
     gout = torch.empty_like(q)
     fns["gate_combine_unfused"] = lambda: S.gate_combine(extra, g, out=gout)
+    # compression through the residual module (seeded weights) in place of the plain block mean
+    rb = [tuple(torch.from_numpy(a).to(dev) for a in W.resblock_weights(s, w.n_kvh, w.head_dim)) for s in (31, 32)]
+    fns["pool_kv_resblock"] = lambda: (S.pool_blocks_resblock(L, k, *rb[0], out=ws["k_cmp"]),
+                                       S.pool_blocks_resblock(L, v, *rb[1], out=ws["v_cmp"]))
     return stages, flops, fns, "attn_fused"
 
 
@@ -284,6 +289,11 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
+            if name == "pool_kv_resblock":
+                # K and V: 4*D^2 FLOP per valid token and KV head (two D x D products)
+                f = 2 * 4 * w.head_dim * w.head_dim * w.n_kvh * int(w.blk_cnt.sum())
+                breakdown[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2)}
+                continue
             if name == "gate_combine_unfused":
                 # bytes: three branch outputs and the gate logits read, the output written
                 esz = 2 if w.dtype == "bf16" else 4
