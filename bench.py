@@ -220,8 +220,8 @@ def main():
                          "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the NSA layer would "
-              "shard by whole blocks with an all-gather of pooled K/V; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: libnsa has no multi-GPU path (the NSA layer would shard "
+              "whole blocks across GPUs and all-gather the pooled K/V).", file=sys.stderr)
         sys.exit(2)
 
     import torch

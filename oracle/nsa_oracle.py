@@ -21,7 +21,7 @@ Sources (cited by page title and section; no page prints code or worked numbers)
              Attention: pooled Q/K/V compression branch, top-K selection from the compressed score
              matrix, learned gate combining the branches.
 
-Readings where the pages are silent (each is listed with its reason in the design notes):
+Readings where the pages are silent:
   * softmax scale is a parameter (callers pass 1/sqrt(D)); attention is non-causal;
   * ResBlock before AvgPool is the identity for the layer's compression (the mean over a block's
     valid tokens); with seeded weights it is one residual MLP per head, x + W2 silu(W1 x + b1) + b2;

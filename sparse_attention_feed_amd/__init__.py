@@ -39,8 +39,8 @@ class Layout(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libnsa.so is not built; run `python __graft_entry__.py` or "
-                          "`python sparse_attention_feed_amd/build.py` first (%s)" % LIB_PATH)
+        raise ImportError("libnsa.so is not built; run `python sparse_attention_feed_amd/build.py` first (%s)"
+                          % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, I, U, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
     LP = ctypes.POINTER(Layout)
