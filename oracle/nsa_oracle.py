@@ -155,6 +155,80 @@ def pool_blocks_resblock(x, blk_cnt, cap, w1, b1, w2, b2):
 
 
 # ----------------------------------------------------------------------------------------------
+# A0 on the device: active-voxel selection and the volume block table
+# ----------------------------------------------------------------------------------------------
+
+def _morton3_u(x, y, z):
+    """Morton code with bits interleaved x (least significant), y, z, for coordinates < 2^10."""
+    code = np.zeros(np.broadcast(x, y, z).shape, dtype=np.int64)
+    for bit in range(10):
+        code |= ((np.asarray(x) >> bit) & 1) << (3 * bit)
+        code |= ((np.asarray(y) >> bit) & 1) << (3 * bit + 1)
+        code |= ((np.asarray(z) >> bit) & 1) << (3 * bit + 2)
+    return code
+
+
+def voxel_activity(sdf, N, tau):
+    """Active voxels of an N^3 grid over [-1, 1]^3, [LSRM-cn] eq. M^vol: voxel (i, j, k) is active iff
+    over its 4^3 sub-sample points min |s_t| <= tau or (min s_t) (max s_t) <= 0, with
+    s_t = Trilinear(sdf; p_t) (the dense stage's decoder taken as the identity on an SDF volume).
+
+    sdf [G][G][G] (z, y, x) holds values at the lattice points -1 + 2 g / (G - 1).  Sub-sample m of an
+    axis (m = 4 i + a) sits at grid coordinate u = (2m + 1)(G - 1) / (8N).  The decision is taken in
+    float32 in this order (the device's precision): u by one rounded division; cell g0 = floor(u)
+    (at most G - 2) and fraction f = u - g0; lerp(a, b, f) = a + f (b - a), rounded after every
+    operation, along x, then y, then z.  Returns bool [N][N][N] (z, y, x)."""
+    f32 = np.float32
+    sdf = np.asarray(sdf, dtype=f32)
+    G = sdf.shape[0]
+    m = np.arange(4 * N, dtype=np.int64)
+    u = ((2 * m + 1) * (G - 1)).astype(f32) / f32(8 * N)
+    g0 = np.minimum(np.floor(u).astype(np.int64), G - 2)
+    fr = (u - g0.astype(f32)).astype(f32)
+
+    def lerp(a, b, t):
+        return (a + (t * (b - a)).astype(f32)).astype(f32)
+
+    act = np.zeros((N, N, N), dtype=bool)
+    for k in range(N):                                 # one z-slab of voxels (4 sub-sample planes)
+        mz = np.arange(4 * k, 4 * k + 4)
+        zz, yy, xx = np.meshgrid(mz, np.arange(4 * N), np.arange(4 * N), indexing="ij")
+        x0, y0, z0 = g0[xx], g0[yy], g0[zz]
+        fx, fy, fz = fr[xx], fr[yy], fr[zz]
+        v = lambda a, b, c: sdf[z0 + c, y0 + b, x0 + a]     # noqa: E731
+        s = lerp(lerp(lerp(v(0, 0, 0), v(1, 0, 0), fx), lerp(v(0, 1, 0), v(1, 1, 0), fx), fy),
+                 lerp(lerp(v(0, 0, 1), v(1, 0, 1), fx), lerp(v(0, 1, 1), v(1, 1, 1), fx), fy), fz)
+        s = s.reshape(4, N, 4, N, 4).transpose(1, 3, 0, 2, 4).reshape(N, N, 64)   # [j][i][64 samples]
+        mn, mx = s.min(axis=2), s.max(axis=2)
+        act[k] = (np.abs(s).min(axis=2) <= f32(tau)) | ((mn * mx).astype(f32) <= 0)
+    return act
+
+
+def volume_block_table(sdf, N, tau):
+    """The volume block table built from the active voxels ([LSRM-cn] block paragraph: active tokens
+    grouped into spatial blocks that keep 3D locality): blocks are the 4^3-voxel cells holding at
+    least one active voxel, in ascending Morton order of the cell; inside a block the active voxels
+    follow ascending Morton order of their position in the cell; capacity 64.
+    Returns blk_cnt int32 [n_blk], blk_key uint32 [n_blk] (the cell's Morton code) and pts float32
+    [n_blk * 64, 3] (voxel centres ((2i + 1) - N) / N per axis, one rounded division; padding 0)."""
+    act = voxel_activity(sdf, N, tau)
+    kz, jy, ix = np.nonzero(act)
+    cell = _morton3_u(ix >> 2, jy >> 2, kz >> 2)
+    local = _morton3_u(ix & 3, jy & 3, kz & 3)
+    order = np.lexsort((local, cell))
+    kz, jy, ix, cell = kz[order], jy[order], ix[order], cell[order]
+    keys, start, cnt = np.unique(cell, return_index=True, return_counts=True)
+    n_blk = keys.shape[0]
+    pts = np.zeros((n_blk * 64, 3), dtype=np.float32)
+    f32 = np.float32
+    for b in range(n_blk):
+        sl = slice(start[b], start[b] + cnt[b])
+        for ax, c in enumerate((ix[sl], jy[sl], kz[sl])):
+            pts[b * 64: b * 64 + cnt[b], ax] = ((2 * c + 1).astype(f32) - f32(N)) / f32(N)
+    return cnt.astype(np.int32), keys.astype(np.uint32), pts
+
+
+# ----------------------------------------------------------------------------------------------
 # A2: 3D-aware geometric routing
 # ----------------------------------------------------------------------------------------------
 

@@ -396,3 +396,96 @@ def test_resblock_matches_a_dense_restatement():
     pre = flat @ W1.T + b1.reshape(-1)
     dense = flat + (pre * (0.5 + 0.5 * np.tanh(pre / 2))) @ W2.T + b2.reshape(-1)
     np.testing.assert_allclose(O.resblock(x, w1, b1, w2, b2).reshape(5, H * D), dense, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# active-voxel selection and the volume block table
+# ---------------------------------------------------------------------------------------------
+
+def test_volume_ramp_hand_fixture():
+    fx = json.load(open(os.path.join(GOLDEN, "volume_ramp.json"), encoding="utf-8"))
+    cnt, key, pts = O.volume_block_table(np.array(fx["sdf"], dtype=np.float32), fx["N"], fx["tau"])
+    assert cnt.tolist() == fx["blk_cnt"] and key.tolist() == fx["blk_key"]
+    np.testing.assert_array_equal(pts[:3], np.array(fx["first_points"], dtype=np.float32))
+    assert np.all(pts[32:] == 0)
+
+
+def test_volume_constant_sdf():
+    g = np.full((3, 3, 3), 0.3, dtype=np.float32)
+    assert not O.voxel_activity(g, 8, 0.2).any()
+    assert O.voxel_activity(g, 8, 0.3).all()
+    assert O.voxel_activity(np.zeros((3, 3, 3), np.float32), 8, 0.0).all()       # s = 0: min * max <= 0
+
+
+def _subsample_coords(N):
+    """Sub-sample positions of one axis in [-1, 1] (float64)."""
+    return -1.0 + (np.arange(4 * N) + 0.5) / (2.0 * N)
+
+
+def test_volume_linear_sdf_matches_closed_form():
+    """Trilinear interpolation reproduces a linear SDF, so activity follows from the analytic values
+    at the sub-samples (cases within 1e-5 of the threshold or of zero are not asserted)."""
+    G, N, tau = 5, 8, 0.07
+    a = np.array([0.6, -0.3, 0.2])
+    c0 = 0.013
+    g = np.linspace(-1.0, 1.0, G)
+    zz, yy, xx = np.meshgrid(g, g, g, indexing="ij")
+    sdf = (a[0] * xx + a[1] * yy + a[2] * zz + c0).astype(np.float32)
+    act = O.voxel_activity(sdf, N, tau)
+    x = _subsample_coords(N)
+    Z, Y, X = np.meshgrid(x, x, x, indexing="ij")
+    s = a[0] * X + a[1] * Y + a[2] * Z + c0
+    s = s.reshape(N, 4, N, 4, N, 4).transpose(0, 2, 4, 1, 3, 5).reshape(N, N, N, 64)
+    want = (np.abs(s).min(axis=3) <= tau) | (s.min(axis=3) * s.max(axis=3) <= 0)
+    margin = np.minimum(np.abs(np.abs(s).min(axis=3) - tau), np.abs(s).min(axis=3))
+    ok = margin > 1e-5
+    assert ok.mean() > 0.95
+    np.testing.assert_array_equal(act[ok], want[ok])
+
+
+def test_volume_sphere_sdf_bounds():
+    """A sphere SDF sampled on the lattice: voxels whose analytic sub-sample values all keep
+    |s| > tau + 0.02 (above the interpolation error) are inactive; voxels with a sub-sample within
+    tau - 0.02 of the surface, or cut by it with that margin, are active."""
+    G, N, r, tau = 33, 32, 0.55, 0.03
+    g = np.linspace(-1.0, 1.0, G)
+    zz, yy, xx = np.meshgrid(g, g, g, indexing="ij")
+    sdf = (np.sqrt(xx ** 2 + yy ** 2 + zz ** 2) - r).astype(np.float32)
+    act = O.voxel_activity(sdf, N, tau)
+    x = _subsample_coords(N)
+    Z, Y, X = np.meshgrid(x, x, x, indexing="ij")
+    s = (np.sqrt(X ** 2 + Y ** 2 + Z ** 2) - r).reshape(N, 4, N, 4, N, 4).transpose(0, 2, 4, 1, 3, 5)
+    s = s.reshape(N, N, N, 64)
+    mn, mx, mabs = s.min(axis=3), s.max(axis=3), np.abs(s).min(axis=3)
+    surely_off = (mabs > tau + 0.02) & ((mn > 0.02) | (mx < -0.02))
+    surely_on = (mabs < tau - 0.02) | ((mn < -0.02) & (mx > 0.02))
+    assert surely_on.sum() > 500 and surely_off.sum() > 20000
+    assert not act[surely_off].any()
+    assert act[surely_on].all()
+
+
+def test_volume_block_grouping_rules():
+    """Block table of a random SDF lattice: every block's points lie in one 4^3 cell whose Morton
+    code is its key, keys ascend, points inside a block ascend in local Morton order, counts add
+    up to the active voxels, padding points are zero."""
+    rng = np.random.default_rng(31)
+    N = 16
+    sdf = rng.standard_normal((7, 7, 7)).astype(np.float32)
+    act = O.voxel_activity(sdf, N, 0.05)
+    cnt, key, pts = O.volume_block_table(sdf, N, 0.05)
+    assert cnt.sum() == act.sum() and np.all(np.diff(key.astype(np.int64)) > 0)
+    for b in range(cnt.shape[0]):
+        p = pts[b * 64: b * 64 + cnt[b]].astype(np.float64)
+        idx = np.rint((p * N + N - 1) / 2).astype(np.int64)            # voxel indices back from centres
+        cx, cy, cz = idx[:, 0] >> 2, idx[:, 1] >> 2, idx[:, 2] >> 2
+        assert len(set(zip(cx, cy, cz))) == 1
+        code = 0
+        for bit in range(3):
+            code |= ((int(cx[0]) >> bit) & 1) << (3 * bit) | ((int(cy[0]) >> bit) & 1) << (3 * bit + 1) | \
+                    ((int(cz[0]) >> bit) & 1) << (3 * bit + 2)
+        assert code == key[b]
+        loc = [int(((x & 1) | ((y & 1) << 1) | ((z & 1) << 2) | ((x & 2) << 2) | ((y & 2) << 3) | ((z & 2) << 4)))
+               for x, y, z in zip(idx[:, 0] & 3, idx[:, 1] & 3, idx[:, 2] & 3)]
+        assert loc == sorted(loc) and len(set(loc)) == len(loc)
+        assert all(act[z, y, x] for x, y, z in idx)
+        assert np.all(pts[b * 64 + cnt[b]: (b + 1) * 64] == 0)
