@@ -148,6 +148,13 @@ def setup_geometric(w, S, torch, dev):
     rb = [tuple(torch.from_numpy(a).to(dev) for a in W.resblock_weights(s, w.n_kvh, w.head_dim)) for s in (31, 32)]
     fns["pool_kv_resblock"] = lambda: (S.pool_blocks_resblock(L, k, *rb[0], out=ws["k_cmp"]),
                                        S.pool_blocks_resblock(L, v, *rb[1], out=ws["v_cmp"]))
+    # the volume block table from the workload's SDF sampled on a (side + 1)^3 lattice
+    if "tau" in w.meta:
+        side = int(w.meta["vol_side"])
+        lat, tau = W.sdf_lattice(w, side + 1)
+        lat_d = torch.from_numpy(lat).to(dev)
+        vws = S.volume_workspace(side, device=dev)
+        fns["volume_blocks"] = lambda: S.build_volume_blocks(lat_d, side, tau, workspace=vws, sync=False)
     return stages, flops, fns, "attn_fused"
 
 
@@ -293,6 +300,13 @@ def main():
                 # K and V: 4*D^2 FLOP per valid token and KV head (two D x D products)
                 f = 2 * 4 * w.head_dim * w.head_dim * w.n_kvh * int(w.blk_cnt.sum())
                 breakdown[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2)}
+                continue
+            if name == "volume_blocks":
+                # 64 trilinear SDF samples per voxel of the side^3 grid
+                side = int(w.meta["vol_side"])
+                nb = int(fn()["n_blk"].item())
+                breakdown[name] = {"ms": round(ms, 4), "n_blk": nb,
+                                   "gvoxel_per_s": round(side ** 3 / (ms * 1e-3) / 1e9, 3)}
                 continue
             if name == "gate_combine_unfused":
                 # bytes: three branch outputs and the gate logits read, the output written

@@ -71,6 +71,34 @@ typedef struct {
 } nsa_layout;
 
 /*
+ * Volume token selection and the volume block table.  LSRM pages, section 方法: eq. M^vol marks a
+ * voxel active iff, over its 4^3 sub-sample points p_t, min |s_t| <= tau or
+ * (min s_t)(max s_t) <= 0; active tokens are grouped into spatial blocks.
+ *   sdf  [G][G][G] float32 (z, y, x): SDF values at the lattice points -1 + 2g/(G-1) of [-1, 1]^3;
+ *        s_t is its trilinear interpolation (the dense stage's SDF decoder taken as the identity).
+ *   Voxels: N^3 over [-1, 1]^3; sub-sample m = 4i + a of an axis lies at lattice coordinate
+ *   u = (2m + 1)(G - 1)/(8N).  The decision is taken in fp32 with every operation rounded in a
+ *   fixed order: u by one division; g0 = min(floor(u), G - 2), f = u - g0; lerp(a, b, f) =
+ *   a + f (b - a) along x, then y, then z (no fused multiply-adds).
+ *   Blocks: the 4^3-voxel cells with at least one active voxel, in ascending Morton order of the
+ *   cell (bits interleaved x, y, z from the least significant); inside a block the active voxels in
+ *   ascending Morton order of their position in the cell; capacity 64.
+ * Outputs: n_blk (device int32) = the number of blocks; for b < min(n_blk, max_blk):
+ *   blk_cnt[b] (1..64), blk_key[b] = the cell's Morton code, pts[b*64 + r][3] = the r-th token's
+ *   voxel centre ((2i + 1) - N)/N per axis (one rounded division), 0 on padding slots.  Blocks at
+ *   or beyond max_blk are not written (compare n_blk with max_blk after the call).
+ * Workspace: cell_mask [(N/4)^3] uint64 (active voxels of each cell) and cell_block [(N/4)^3]
+ * int32 (block index of each cell, -1 if empty), both indexed by the cell's Morton code and
+ * written.  N a positive multiple of 4 (else NSA_ERR_INVALID); N / 4 a power of two, N <= 512 and
+ * 8*N*G < 2^24 (else NSA_ERR_UNSUPPORTED); G >= 2 and tau finite and >= 0 (else NSA_ERR_INVALID).
+ * The device buffers are caller-owned; the call is asynchronous on `stream`.
+ */
+nsa_status nsa_build_volume_blocks(const float* sdf, int32_t G, int32_t N, float tau, int32_t max_blk,
+                                   uint64_t* cell_mask, int32_t* cell_block, int32_t* n_blk,
+                                   int32_t* blk_cnt, uint32_t* blk_key, float* pts,
+                                   hipStream_t stream);
+
+/*
  * Block compression.  LSRM pages, section 方法, eq. k^cmp = AvgPool(ResBlock(k_t)) (ResBlock taken
  * as the identity); Speed3R page (arXiv 2603.08055 summary), section 2.1, 4x4 average pooling of
  * Q/K/V.  x_cmp[b][h][:] = mean of x[s][h][:] over the valid slots s of block b, accumulated in

@@ -21,7 +21,7 @@ NSA_OK, NSA_ERR_INVALID, NSA_ERR_UNSUPPORTED, NSA_ERR_HIP = 0, -1, -2, -3
 NSA_F32, NSA_BF16 = 0, 1
 BR_CMP, BR_SEL, BR_LOC = 1, 2, 4
 Q_TOKEN, Q_BLOCK = 0, 1
-EXPORTS = ("nsa_pool_blocks", "nsa_pool_blocks_resblock", "nsa_route_geometric", "nsa_route_scores_topk", "nsa_attn_fwd",
+EXPORTS = ("nsa_build_volume_blocks", "nsa_pool_blocks", "nsa_pool_blocks_resblock", "nsa_route_geometric", "nsa_route_scores_topk", "nsa_attn_fwd",
            "nsa_gate_combine", "dense_gated_xattn_fwd", "nsa_last_error")
 
 
@@ -45,6 +45,7 @@ def _load():
     P, I, U, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
     LP = ctypes.POINTER(Layout)
     sig = {
+        "nsa_build_volume_blocks": [P, I, I, F, I, P, P, P, P, P, P, P],
         "nsa_pool_blocks": [LP, I, I, P, P, P],
         "nsa_pool_blocks_resblock": [LP, I, I, P, P, P, P, P, P, P],
         "nsa_route_geometric": [LP, P, I, P, P, P, P],
@@ -116,6 +117,45 @@ class BlockLayout:
     @property
     def c(self):
         return ctypes.byref(self._c)
+
+
+def volume_workspace(N, max_blk=None, device="cuda:0"):
+    """Device buffers for build_volume_blocks: cell_mask, cell_block, n_blk, blk_cnt, blk_key, pts."""
+    n_cells = (N // 4) ** 3
+    max_blk = n_cells if max_blk is None else int(max_blk)
+    m = max(max_blk, 1)
+    return {
+        "max_blk": max_blk,
+        "cell_mask": torch.empty(n_cells, dtype=torch.int64, device=device),
+        "cell_block": torch.empty(n_cells, dtype=torch.int32, device=device),
+        "n_blk": torch.zeros(1, dtype=torch.int32, device=device),
+        "blk_cnt": torch.empty(m, dtype=torch.int32, device=device),
+        "blk_key": torch.empty(m, dtype=torch.int32, device=device),
+        "pts": torch.empty((m * 64, 3), dtype=torch.float32, device=device),
+    }
+
+
+def build_volume_blocks(sdf, N, tau, max_blk=None, workspace=None, sync=True):
+    """Active voxels of an N^3 grid (eq. M^vol on the trilinear SDF lattice `sdf` [G, G, G]) grouped
+    into Morton-ordered 4^3-voxel blocks.  With sync (default) returns (n_blk, blk_cnt, blk_key, pts)
+    cut to n_blk and raises if n_blk exceeds max_blk (default: every cell); without, launches
+    asynchronously and returns the workspace (n_blk stays on the device)."""
+    G = int(sdf.shape[0])
+    if sdf.dtype != torch.float32 or tuple(sdf.shape) != (G, G, G):
+        raise ValueError("sdf must be a float32 [G, G, G] lattice")
+    ws = volume_workspace(N, max_blk, sdf.device) if workspace is None else workspace
+    if ws["cell_mask"].shape[0] != (N // 4) ** 3:
+        raise ValueError("workspace was made for another grid size")
+    mb = ws["max_blk"]
+    _check(lib.nsa_build_volume_blocks(_ptr(sdf), G, int(N), float(tau), mb, _ptr(ws["cell_mask"]),
+                                       _ptr(ws["cell_block"]), _ptr(ws["n_blk"]), _ptr(ws["blk_cnt"]),
+                                       _ptr(ws["blk_key"]), _ptr(ws["pts"]), _stream()))
+    if not sync:
+        return ws
+    nb = int(ws["n_blk"].item())
+    if nb > mb:
+        raise ValueError("%d blocks exceed max_blk = %d" % (nb, mb))
+    return nb, ws["blk_cnt"][:nb], ws["blk_key"][:nb], ws["pts"][:nb * 64]
 
 
 def pool_blocks(layout: BlockLayout, x, out=None):

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libnsa.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "attn.hip", "attn_g1.hip", "route.hip", "elementwise.hip"]
+SOURCES = ["api.cpp", "attn.hip", "attn_g1.hip", "route.hip", "elementwise.hip", "blocks.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,6 +1,7 @@
 // C ABI of libnsa: host-side argument validation and kernel dispatch (see include/nsa.h).
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
+#include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -95,6 +96,28 @@ nsa_status nsa_pool_blocks_resblock(const nsa_layout* L, nsa_dtype dtype, int32_
   return hip_status(nsa::launch_pool_resblock(dtype == NSA_BF16, x, x_cmp, L->blk_cnt, w1, b1, w2, b2, L->n_blk,
                                               L->blk_cap, n_heads, L->head_dim, stream),
                     "nsa_pool_blocks_resblock");
+}
+
+nsa_status nsa_build_volume_blocks(const float* sdf, int32_t G, int32_t N, float tau, int32_t max_blk,
+                                   uint64_t* cell_mask, int32_t* cell_block, int32_t* n_blk, int32_t* blk_cnt,
+                                   uint32_t* blk_key, float* pts, hipStream_t stream) {
+  if (sdf == nullptr || cell_mask == nullptr || cell_block == nullptr || n_blk == nullptr)
+    return fail(NSA_ERR_INVALID, "nsa_build_volume_blocks: NULL pointer");
+  if (max_blk > 0 && (blk_cnt == nullptr || blk_key == nullptr || pts == nullptr))
+    return fail(NSA_ERR_INVALID, "nsa_build_volume_blocks: NULL output with max_blk > 0");
+  if (G < 2) return fail(NSA_ERR_INVALID, "nsa_build_volume_blocks: G must be >= 2");
+  if (N < 4 || N % 4 != 0) return fail(NSA_ERR_INVALID, "nsa_build_volume_blocks: N must be a positive multiple of 4");
+  if (max_blk < 0) return fail(NSA_ERR_INVALID, "nsa_build_volume_blocks: max_blk must be >= 0");
+  if (!(tau >= 0.f) || tau == INFINITY) return fail(NSA_ERR_INVALID, "nsa_build_volume_blocks: tau must be finite, >= 0");
+  if (N > 512 || ((N / 4) & (N / 4 - 1)) != 0)
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_build_volume_blocks: N / 4 must be a power of two and N <= 512");
+  if ((long long)8 * N * G >= (1LL << 24))
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_build_volume_blocks: 8 * N * G must stay below 2^24 (exact fp32 coordinates)");
+  NSA_FORCED_FAILURE("nsa_build_volume_blocks");
+  return hip_status(nsa::launch_build_volume_blocks(sdf, G, N, tau, max_blk,
+                                                    reinterpret_cast<unsigned long long*>(cell_mask), cell_block,
+                                                    n_blk, blk_cnt, blk_key, pts, stream),
+                    "nsa_build_volume_blocks");
 }
 
 nsa_status nsa_route_geometric(const nsa_layout* L, const float* pts, int32_t top_k, int32_t* centroids,

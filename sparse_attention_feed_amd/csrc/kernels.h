@@ -89,6 +89,9 @@ size_t pool_resblock_lds_bytes(int cap, int head_dim);
 hipError_t launch_pool_resblock(int is_bf16, const void* x, void* x_cmp, const int32_t* blk_cnt, const float* w1,
                                 const float* b1, const float* w2, const float* b2, int n_blk, int cap,
                                 int n_heads, int head_dim, hipStream_t s);
+hipError_t launch_build_volume_blocks(const float* sdf, int G, int N, float tau, int max_blk,
+                                      unsigned long long* cell_mask, int* cell_block, int* n_blk, int32_t* blk_cnt,
+                                      uint32_t* blk_key, float* pts, hipStream_t s);
 hipError_t launch_route_geometric(const RouteArgs& a, hipStream_t s);
 hipError_t launch_route_scores(int is_bf16, const ScoreRouteArgs& a, hipStream_t s);
 hipError_t launch_gate(int is_bf16, int n_rows, int n_qh, int head_dim, int n_branch,

@@ -1,0 +1,153 @@
+"""GPU parity of the active-voxel selection and the volume block table (LSRM pages, section 方法,
+eq. M^vol and the block paragraph): counts, keys, token points and the block count bit-exact
+against the oracle, which takes the same fp32 decision in the same operation order."""
+import ctypes
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _gpu(sdf, N, tau, max_blk=None):
+    import sparse_attention_feed_amd as S
+    t = torch.from_numpy(np.ascontiguousarray(sdf, dtype=np.float32)).to("cuda:0")
+    nb, cnt, key, pts = S.build_volume_blocks(t, N, tau, max_blk)
+    torch.cuda.synchronize()
+    return nb, cnt.cpu().numpy(), key.cpu().numpy().view(np.uint32), pts.cpu().numpy()
+
+
+def _check(sdf, N, tau):
+    say("volume blocks", "G=%d" % sdf.shape[0], "N=%d" % N, "tau=%r" % tau)
+    cnt, key, pts = O.volume_block_table(sdf, N, tau)
+    nb, gc, gk, gp = _gpu(sdf, N, tau)
+    assert nb == cnt.shape[0]
+    np.testing.assert_array_equal(gc, cnt)
+    np.testing.assert_array_equal(gk, key)
+    np.testing.assert_array_equal(gp.view(np.uint32), pts.view(np.uint32))     # bit-exact, padding 0
+    return nb
+
+
+def _linear(G, a, c0):
+    g = np.linspace(-1.0, 1.0, G)
+    zz, yy, xx = np.meshgrid(g, g, g, indexing="ij")
+    return (a[0] * xx + a[1] * yy + a[2] * zz + c0).astype(np.float32)
+
+
+def _sphere(G, r, c=(0.0, 0.0, 0.0)):
+    g = np.linspace(-1.0, 1.0, G)
+    zz, yy, xx = np.meshgrid(g, g, g, indexing="ij")
+    return (np.sqrt((xx - c[0]) ** 2 + (yy - c[1]) ** 2 + (zz - c[2]) ** 2) - r).astype(np.float32)
+
+
+def test_volume_ramp_hand_fixture_gpu():
+    fx = json.load(open(os.path.join(GOLDEN, "volume_ramp.json"), encoding="utf-8"))
+    sdf = np.array(fx["sdf"], dtype=np.float32)
+    nb, gc, gk, gp = _gpu(sdf, fx["N"], fx["tau"])
+    assert nb == 1 and gc.tolist() == fx["blk_cnt"] and gk.tolist() == fx["blk_key"]
+    np.testing.assert_array_equal(gp[:3], np.array(fx["first_points"], dtype=np.float32))
+    assert np.all(gp[fx["blk_cnt"][0]:] == 0)
+    _check(sdf, fx["N"], fx["tau"])
+
+
+def test_volume_empty_and_full():
+    g = np.full((3, 3, 3), 0.3, dtype=np.float32)
+    assert _check(g, 8, 0.2) == 0                         # no active voxel: zero blocks
+    assert _check(g, 8, 0.3) == 8                         # every voxel active: 8 full blocks
+    assert _check(np.zeros((2, 2, 2), np.float32), 4, 0.0) == 1
+
+
+@pytest.mark.parametrize("case", ["linear", "random9", "random3_coarse", "sphere33", "sphere_offcentre",
+                                  "ties_at_tau"])
+def test_volume_blocks_bit_exact(case):
+    rng = np.random.default_rng(np.random.PCG64(77))
+    if case == "linear":
+        _check(_linear(5, (0.6, -0.3, 0.2), 0.013), 8, 0.07)
+    elif case == "random9":
+        _check(rng.standard_normal((9, 9, 9)).astype(np.float32), 16, 0.05)
+    elif case == "random3_coarse":                     # one lattice cell spans 16 voxels per axis
+        _check(rng.standard_normal((3, 3, 3)).astype(np.float32), 32, 0.02)
+    elif case == "sphere33":
+        _check(_sphere(33, 0.55), 32, 0.03)
+    elif case == "sphere_offcentre":
+        _check(_sphere(17, 0.4, (0.21, -0.13, 0.3)), 64, 0.011)
+    else:                                              # lattice values equal to tau and to -tau
+        sdf = np.round(rng.uniform(-4, 4, size=(5, 5, 5))).astype(np.float32) * np.float32(0.25)
+        _check(sdf, 16, 0.25)
+
+
+def test_volume_large_small_workload_lattice():
+    w = W.make("large_small")
+    lat, tau = W.sdf_lattice(w, 33)
+    nb = _check(lat, 32, tau)
+    assert nb > 50
+
+
+def test_volume_full_size_large_lattice():
+    """The 128^3 volume of the large sparse stage (SDF lattice 129^3): the whole table bit-exact."""
+    w = W.make("large")
+    lat, tau = W.sdf_lattice(w, 129)
+    nb = _check(lat, 128, tau)
+    assert nb > 5000
+
+
+def test_volume_max_blk_truncates_and_reports():
+    import sparse_attention_feed_amd as S
+    rng = np.random.default_rng(np.random.PCG64(78))
+    sdf = rng.standard_normal((9, 9, 9)).astype(np.float32)
+    N, tau = 16, 0.05
+    cnt, key, pts = O.volume_block_table(sdf, N, tau)
+    nb_all = cnt.shape[0]
+    cap = nb_all // 2
+    say("volume blocks max_blk", cap, "of", nb_all)
+    dev = "cuda:0"
+    t = torch.from_numpy(sdf).to(dev)
+    n_cells = (N // 4) ** 3
+    cell_mask = torch.empty(n_cells, dtype=torch.int64, device=dev)
+    cell_block = torch.empty(n_cells, dtype=torch.int32, device=dev)
+    n_blk = torch.zeros(1, dtype=torch.int32, device=dev)
+    sentinel = -7
+    blk_cnt = torch.full((cap + 1,), sentinel, dtype=torch.int32, device=dev)
+    blk_key = torch.full((cap + 1,), sentinel, dtype=torch.int32, device=dev)
+    out_pts = torch.full(((cap + 1) * 64, 3), -7.0, dtype=torch.float32, device=dev)
+    p = lambda x: ctypes.c_void_p(x.data_ptr())      # noqa: E731
+    rc = S.lib.nsa_build_volume_blocks(p(t), 9, N, tau, cap, p(cell_mask), p(cell_block), p(n_blk), p(blk_cnt),
+                                       p(blk_key), p(out_pts), None)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert int(n_blk.item()) == nb_all
+    np.testing.assert_array_equal(blk_cnt.cpu().numpy()[:cap], cnt[:cap])
+    np.testing.assert_array_equal(blk_key.cpu().numpy()[:cap].view(np.uint32), key[:cap])
+    np.testing.assert_array_equal(out_pts.cpu().numpy()[:cap * 64], pts[:cap * 64])
+    assert blk_cnt[cap].item() == sentinel and blk_key[cap].item() == sentinel    # nothing past max_blk
+    assert torch.all(out_pts[cap * 64:] == -7.0).item()
+    cb = cell_block.cpu().numpy()
+    assert sorted(cb[cb >= 0].tolist()) == list(range(nb_all))
+    with pytest.raises(ValueError):
+        S.build_volume_blocks(t, N, tau, cap)
+
+
+def test_volume_workspace_reuse():
+    """Two tables in a row through one workspace: the second call leaves nothing of the first."""
+    import sparse_attention_feed_amd as S
+    rng = np.random.default_rng(np.random.PCG64(79))
+    N = 16
+    ws = S.volume_workspace(N)
+    for G, tau in ((9, 0.3), (5, 0.01)):
+        sdf = rng.standard_normal((G, G, G)).astype(np.float32)
+        say("volume workspace reuse", G, tau)
+        cnt, key, pts = O.volume_block_table(sdf, N, tau)
+        nb, gc, gk, gp = S.build_volume_blocks(torch.from_numpy(sdf).to("cuda:0"), N, tau, workspace=ws)
+        assert nb == cnt.shape[0]
+        np.testing.assert_array_equal(gc.cpu().numpy(), cnt)
+        np.testing.assert_array_equal(gk.cpu().numpy().view(np.uint32), key)
+        np.testing.assert_array_equal(gp.cpu().numpy(), pts)

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 8
+    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 9
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -114,6 +114,19 @@ def test_other_calls_validate(S, monkeypatch):
     assert lib.dense_gated_xattn_fwd(1, 100, 101, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
     assert lib.dense_gated_xattn_fwd(1, 100, -1, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
     assert lib.dense_gated_xattn_fwd(1, 100, 50, 32, 2, 64, 0.125, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    vb = lib.nsa_build_volume_blocks
+    assert vb(None, 9, 16, 0.1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1           # no lattice
+    assert vb(FAKE, 9, 16, 0.1, 8, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == -1           # no counts
+    assert vb(FAKE, 1, 16, 0.1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1           # G < 2
+    assert vb(FAKE, 9, 14, 0.1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1           # N % 4
+    assert vb(FAKE, 9, 0, 0.1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert vb(FAKE, 9, 16, -0.1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1          # tau < 0
+    assert vb(FAKE, 9, 16, float("nan"), 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert vb(FAKE, 9, 16, float("inf"), 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert vb(FAKE, 9, 16, 0.1, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert vb(FAKE, 9, 24, 0.1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2           # N/4 = 6
+    assert vb(FAKE, 9, 1024, 0.1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert vb(FAKE, 8193, 256, 0.1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2       # 8NG >= 2^24
     mis = (ctypes.c_void_p * 2)(FAKE, FAKE + 2)
     assert lib.nsa_gate_combine(1, 10, 32, 32, 2, mis, FAKE, FAKE, None) == -2         # misaligned branch
     monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
@@ -124,6 +137,8 @@ def test_other_calls_validate(S, monkeypatch):
     arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
     assert lib.nsa_gate_combine(1, 10, 32, 32, 2, arr, FAKE, FAKE, None) == -3
     assert lib.dense_gated_xattn_fwd(1, 100, 50, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert lib.nsa_build_volume_blocks(FAKE, 9, 16, 0.1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert lib.nsa_build_volume_blocks(FAKE, 9, 16, 0.1, 0, FAKE, FAKE, FAKE, None, None, None, None) == -3
     assert attn(S, L) == -3
 
 

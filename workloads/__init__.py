@@ -25,7 +25,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "DenseWorkload", "make", "CONFIGS", "bf16_round", "morton2", "morton3",
-    "permute_storage", "custom_block_workload", "resblock_weights",
+    "permute_storage", "custom_block_workload", "resblock_weights", "sdf_lattice",
 ]
 
 
@@ -311,11 +311,49 @@ def _sphere_sdf(c, r):
     return lambda p: np.linalg.norm(p - c[None, :], axis=1) - r
 
 
+def _sphere_torus_sdf(side, ph):
+    """Noisy union of a sphere and a torus centred in a side^3 voxel grid; voxel-unit coordinates."""
+    half = side / 2.0
+    cen = np.full(3, half)
+    r_s, R_t, r_t = 0.62 * half, 0.55 * half, 0.18 * half
+    f = 2.0 * math.pi / (side / 4.0)
+
+    def sdf(p):
+        d = p - cen[None, :]
+        s1 = np.linalg.norm(d, axis=1) - r_s
+        q = np.sqrt(d[:, 0] ** 2 + d[:, 1] ** 2) - R_t
+        s2 = np.sqrt(q * q + d[:, 2] ** 2) - r_t
+        n = 1.5 * np.sin(f * p[:, 0] + ph[0]) * np.sin(f * p[:, 1] + ph[1]) * np.sin(f * p[:, 2] + ph[2])
+        return np.minimum(s1, s2) + n
+
+    return sdf
+
+
+def sdf_lattice(w, G):
+    """The SDF behind a geometric workload's volume, sampled at the (G)^3 lattice points
+    -1 + 2 g / (G - 1) of [-1, 1]^3 in normalised units (float32 [G][G][G], z, y, x), with its
+    activation threshold tau in the same units.  Returns (lattice, tau)."""
+    m = w.meta
+    side = int(m["vol_side"])
+    half = side / 2.0
+    if "sdf_phases" in m:
+        sdf = _sphere_torus_sdf(side, np.array(m["sdf_phases"]))
+    elif "sphere_centre" in m:
+        sdf = _sphere_sdf(np.array(m["sphere_centre"]), float(m["sphere_radius"]))
+    else:
+        raise ValueError("workload %s carries no volume SDF" % w.name)
+    g = np.linspace(-1.0, 1.0, G)
+    zz, yy, xx = np.meshgrid(g, g, g, indexing="ij")
+    p = (np.stack([xx.ravel(), yy.ravel(), zz.ravel()], axis=1) + 1.0) * half
+    lat = (sdf(p) / half).reshape(G, G, G).astype(np.float32)
+    return lat, float(m["tau"]) / half
+
+
 def _lsrm_geometric(name, seed, dtype, vol_side, vol_shape, vol_target, n_views, img_side, fg,
                     top_k, n_qh=32, n_kvh=2, D=32, cap=64, vol_all=False, img_all_sphere=False):
     rng = np.random.default_rng(np.random.PCG64(seed))
     half = vol_side / 2.0
-    meta = {}
+    meta = {"vol_side": vol_side}
     # --- geometry: volume ---
     if vol_all:
         g = np.arange(vol_side)
@@ -331,23 +369,11 @@ def _lsrm_geometric(name, seed, dtype, vol_side, vol_shape, vol_target, n_views,
         sph_r = rad / half
         meta.update(tau=tau, sphere_centre=cen.tolist(), sphere_radius=rad)
     elif vol_shape == "sphere_torus":
-        cen = np.full(3, half)
-        r_s, R_t, r_t = 0.62 * half, 0.55 * half, 0.18 * half
         ph = rng.uniform(0.0, 2.0 * math.pi, size=3)
-        f = 2.0 * math.pi / (vol_side / 4.0)
-
-        def sdf(p):
-            d = p - cen[None, :]
-            s1 = np.linalg.norm(d, axis=1) - r_s
-            q = np.sqrt(d[:, 0] ** 2 + d[:, 1] ** 2) - R_t
-            s2 = np.sqrt(q * q + d[:, 2] ** 2) - r_t
-            n = 1.5 * np.sin(f * p[:, 0] + ph[0]) * np.sin(f * p[:, 1] + ph[1]) * np.sin(f * p[:, 2] + ph[2])
-            return np.minimum(s1, s2) + n
-
-        vox, tau = _active_voxels(vol_side, sdf, vol_target, prefilter=16.0)
+        vox, tau = _active_voxels(vol_side, _sphere_torus_sdf(vol_side, ph), vol_target, prefilter=16.0)
         sph_c = np.zeros(3)
-        sph_r = r_s / half
-        meta.update(tau=tau)
+        sph_r = 0.62
+        meta.update(tau=tau, sdf_phases=ph.tolist())
     else:
         raise ValueError(vol_shape)
     vol_pts = _voxel_centres(vox, vol_side)
