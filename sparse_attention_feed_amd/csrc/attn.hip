@@ -324,6 +324,9 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
   // Global loads run two tiles ahead of the compute (two register sets), LDS holds two tiles.
   Stager<T, NT> next, after;
   if (ntiles <= 0) return;
+  // Settle every outstanding load of earlier phases here: the compiler's wait insertion would
+  // otherwise merge them with the prefetch in flight and wait for that prefetch inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
   next.load(src.kptr(0), src.vptr(0), src.stride, src.nk(0));
   next.store(buf[0]);
   if (ntiles > 1) next.load(src.kptr(1), src.vptr(1), src.stride, src.nk(1));
@@ -377,15 +380,29 @@ __device__ __forceinline__ void ring_signal(int* ctr) {
   if (lane_id() == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Buffers 0 and 1 of the ring are the workgroup's two staging tiles at the start of LDS; buffers 2
+// and 3 sit at byte offset hi_off.  The address is formed from the LDS base by integer offsets so
+// that every access stays an LDS (ds_*) access.
+template <typename T> struct RingBufs {
+  unsigned char* lds;
+  int hi_off;
+  __device__ __forceinline__ TileBuf<T>& operator[](int i) const {
+    const int off = i < 2 ? i * (int)sizeof(TileBuf<T>) : hi_off + (i - 2) * (int)sizeof(TileBuf<T>);
+    return *reinterpret_cast<TileBuf<T>*>(lds + off);
+  }
+};
+
 template <typename T, int NT, int TPW, int R, class Src, class Part>
-__device__ __forceinline__ void run_tiles_ring(TileBuf<T>* const (&rb)[R], int* ready, int* done, int* broken,
+__device__ __forceinline__ void run_tiles_ring(const RingBufs<T>& rb, int* ready, int* done, int* broken,
                                                int spin_limit, int stall, const Src& src, int ntiles,
                                                const Part& part, TokState (&st)[TPW], const QF<T> (&qf)[TPW]) {
+  static_assert(R == 4, "the ring has four buffers");
   constexpr int WAVES = NT / 64;
   Stager<T, NT> sg;
+  __builtin_amdgcn_s_waitcnt(0);   // as in run_tiles: no earlier load stays in flight into the loop
   for (int t = 0; t < R - 1 && t < ntiles; ++t) {
     sg.load(src.kptr(t), src.vptr(t), src.stride, src.nk(t));
-    sg.store(*rb[t]);
+    sg.store(rb[t]);
     ring_signal(&ready[t]);
   }
   for (int u = 0; u < ntiles; ++u) {
@@ -393,7 +410,7 @@ __device__ __forceinline__ void run_tiles_ring(TileBuf<T>* const (&rb)[R], int* 
     if (ahead < ntiles) sg.load(src.kptr(ahead), src.vptr(ahead), src.stride, src.nk(ahead));
     const int bu = u % R;
     ring_wait(&ready[bu], WAVES * (u / R + 1) + stall, broken, spin_limit);
-    const TileBuf<T>& b = *rb[bu];
+    const TileBuf<T>& b = rb[bu];
     const int nk = src.nk(u);
     const uint32_t pm = part.wave_mask(u);
     if (pm != 0u) {
@@ -407,7 +424,7 @@ __device__ __forceinline__ void run_tiles_ring(TileBuf<T>* const (&rb)[R], int* 
     if (ahead < ntiles) {
       const int bp = (u + R - 1) % R;              // == (u - 1) % R, the buffer of tile u - 1
       if (u >= 1) ring_wait(&done[bp], WAVES * ((u - 1) / R + 1), broken, spin_limit);
-      sg.store(*rb[bp]);
+      sg.store(rb[bp]);
       ring_signal(&ready[bp]);
     }
   }
@@ -587,7 +604,6 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     int* ulist = reinterpret_cast<int*>(extra + off_ulist);
     int* scratch = reinterpret_cast<int*>(extra + off_scratch);
     unsigned long long* umask = reinterpret_cast<unsigned long long*>(extra + off_umask);
-    TileBuf<T>* ring_hi = reinterpret_cast<TileBuf<T>*>(extra + off_ring);
     int* ring_ctr = reinterpret_cast<int*>(extra + off_ctr);
     const int grp = a.sel_groups == 1 ? 0 : j;
     const int kk = a.top_k;
@@ -642,7 +658,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.cap = cap;
     src.ulist = ulist;
     UnionPart<WAVES, TPW> part{umask, w};
-    TileBuf<T>* const rb[4] = {buf, buf + 1, ring_hi, ring_hi + 1};
+    const RingBufs<T> rb{smem, 2 * (int)sizeof(TileBuf<T>) + off_ring};
     run_tiles_ring<T, NT, TPW, 4>(rb, ring_ctr, ring_ctr + 4, ring_ctr + 8, a.ring_spins, a.ring_stall, src, n_union,
                                   part, st, qf);   // ends with a barrier
     finish_all((a.branches & 1) ? 1 : 0);
