@@ -47,9 +47,10 @@ def algorithmic_flops(w, sel):
 
 
 def _source_digest():
+    """Digest of the sources the fused attention kernel and its launch are built from."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "sparse_attention_feed_amd", "csrc"))):
+    for f in ("attn.hip", "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "sparse_attention_feed_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
