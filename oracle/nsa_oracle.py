@@ -29,7 +29,9 @@ Readings where the pages are silent:
   * geometric routing ranks blocks by the exact integer squared distance between the query point
     and the block centroid on a 2^-12 lattice (u = rint(4096 p) + 4096), ties by ascending blk_key;
   * GQA score routing sums the group's softmax probabilities against the compressed keys;
-  * each gate channel is an independent sigmoid; an empty key set contributes 0.
+  * each gate channel is an independent sigmoid; an empty key set contributes 0;
+  * the split self/cross form of stage 2 keeps stage 1's two sigmoid gates over an NSA per token
+    type, each NSA with its own branch gates (cross: compressed + selected, no local window).
 """
 from __future__ import annotations
 
@@ -474,3 +476,95 @@ def nsa_forward(w, rows=None, return_parts=False):
     o = gate_combine(outs, w.gates[rows])
     o[~valid_mask(w.blk_cnt, cap)[rows]] = 0.0
     return (o, parts) if return_parts else o
+
+
+# ----------------------------------------------------------------------------------------------
+# split self/cross NSA: stage 2 keeping stage 1's decoupled branches
+# ----------------------------------------------------------------------------------------------
+
+def route_geometric_range(pts, blk_cnt, blk_key, cap, top_k, q_blocks, kv_blocks):
+    """Geometric routing (the metric and order of route_geometric) for the query slots of the
+    blocks [q_lo, q_hi) with the candidates restricted to the blocks [kv_lo, kv_hi).
+    Returns sel int32 and d2 uint32 [(q_hi - q_lo) * cap, top_k] (storage block indices, best
+    first); padding rows and positions beyond the candidate count hold -1 / 0xFFFFFFFF."""
+    blk_cnt = np.asarray(blk_cnt)
+    blk_key = np.asarray(blk_key, dtype=np.int64)
+    q_lo, q_hi = q_blocks
+    kv_lo, kv_hi = kv_blocks
+    valid = valid_mask(blk_cnt, cap)
+    cen = block_centroids(pts, blk_cnt, cap)
+    u = lattice_coords(pts)
+    cand = np.arange(kv_lo, kv_hi)
+    rows = np.arange(q_lo * cap, q_hi * cap)
+    sel = np.full((rows.shape[0], top_k), -1, dtype=np.int32)
+    dd = np.full((rows.shape[0], top_k), 0xFFFFFFFF, dtype=np.uint32)
+    kk = min(top_k, cand.shape[0])
+    for i, r in enumerate(rows):
+        if not valid[r] or kk == 0:
+            continue
+        d2 = ((u[r][None, :] - cen[cand]) ** 2).sum(axis=1)
+        order = np.lexsort((blk_key[cand], d2))[:kk]
+        sel[i, :kk] = cand[order]
+        dd[i, :kk] = d2[order]
+    return sel, dd
+
+
+def _keys_of_blocks(blk_cnt, cap, blocks):
+    blocks = sorted(set(int(x) for x in blocks if x >= 0))
+    if not blocks:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate([block_slots(blk_cnt, cap, x) for x in blocks])
+
+
+def nsa_split_forward(w, n_x_blk, gates, rows=None, return_parts=False):
+    """Stage-2 NSA that keeps stage 1's decoupled self and cross branches ([LSRM-cn] eq. o^x, o^y
+    with Sigmoid gates, each dense attention replaced by NSA over the blocks of one token type).
+    Blocks [0, n_x_blk) hold volume tokens x, blocks [n_x_blk, n_blk) image tokens y.  For a token
+    whose own block lies in subset A (its type) with B the other subset:
+        o = s(g0) NSA_A + s(g1) NSA_B,   s = sigmoid,
+        NSA_A = s(g2) CMP_A + s(g3) SEL_A + s(g4) LOC,
+        NSA_B = s(g5) CMP_B + s(g6) SEL_B,
+    CMP_X attends the pooled blocks of X, SEL_X the valid tokens of the top-k blocks of X by
+    geometric routing (route_geometric_range), LOC the valid tokens of the own block.  gates is
+    [S, Hq, 7] in that channel order.  An empty subset contributes 0.  Returns o [len(rows), Hq, D]."""
+    cap = w.blk_cap
+    S = w.n_slots
+    n_blk = w.n_blk
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    valid = valid_mask(w.blk_cnt, cap)
+    k_cmp = pool_blocks(w.k, w.blk_cnt, cap)
+    v_cmp = pool_blocks(w.v, w.blk_cnt, cap)
+    g = sigmoid(np.asarray(gates, dtype=np.float64))
+    ranges = ((0, n_x_blk), (n_x_blk, n_blk))
+    sel_self = np.full((S, w.top_k), -1, dtype=np.int32)
+    sel_cross = np.full((S, w.top_k), -1, dtype=np.int32)
+    need = np.unique(rows // cap)
+    for qi, qr in enumerate(ranges):
+        blocks_here = need[(need >= qr[0]) & (need < qr[1])]
+        for b in blocks_here:
+            sl = slice(b * cap, (b + 1) * cap)
+            sel_self[sl], _ = route_geometric_range(w.pts, w.blk_cnt, w.blk_key, cap, w.top_k, (b, b + 1), qr)
+            sel_cross[sl], _ = route_geometric_range(w.pts, w.blk_cnt, w.blk_key, cap, w.top_k, (b, b + 1),
+                                                     ranges[1 - qi])
+    Hq, D = w.q.shape[1], w.q.shape[2]
+    o = np.zeros((rows.shape[0], Hq, D))
+    for i, r in enumerate(rows):
+        if not valid[r]:
+            continue
+        b = r // cap
+        own, other = (ranges[0], ranges[1]) if b < n_x_blk else (ranges[1], ranges[0])
+        cmp_a, _ = attend(w.q[r], k_cmp[own[0]:own[1]], v_cmp[own[0]:own[1]], w.scale)
+        cmp_b, _ = attend(w.q[r], k_cmp[other[0]:other[1]], v_cmp[other[0]:other[1]], w.scale)
+        ks = _keys_of_blocks(w.blk_cnt, cap, sel_self[r])
+        sel_a, _ = attend(w.q[r], w.k[ks], w.v[ks], w.scale)
+        ks = _keys_of_blocks(w.blk_cnt, cap, sel_cross[r])
+        sel_b, _ = attend(w.q[r], w.k[ks], w.v[ks], w.scale)
+        ks = block_slots(w.blk_cnt, cap, b)
+        loc, _ = attend(w.q[r], w.k[ks], w.v[ks], w.scale)
+        gr = g[r][:, :, None]
+        nsa_a = gr[:, 2] * cmp_a + gr[:, 3] * sel_a + gr[:, 4] * loc
+        nsa_b = gr[:, 5] * cmp_b + gr[:, 6] * sel_b
+        o[i] = gr[:, 0] * nsa_a + gr[:, 1] * nsa_b
+    if return_parts:
+        return o, {"k_cmp": k_cmp, "v_cmp": v_cmp, "sel_self": sel_self, "sel_cross": sel_cross}
+    return o

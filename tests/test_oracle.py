@@ -489,3 +489,97 @@ def test_volume_block_grouping_rules():
         assert loc == sorted(loc) and len(set(loc)) == len(loc)
         assert all(act[z, y, x] for x, y, z in idx)
         assert np.all(pts[b * 64 + cnt[b]: (b + 1) * 64] == 0)
+
+
+# ---------------------------------------------------------------------------------------------
+# split self/cross NSA
+# ---------------------------------------------------------------------------------------------
+
+def brute_route_range(pts, blk_cnt, blk_key, cap, k, q_blocks, kv_blocks):
+    """brute_route with the candidates restricted to the blocks kv_blocks, for the slots of q_blocks."""
+    full = {}
+    lat = lambda x: int(round(4096 * float(x))) + 4096  # noqa: E731
+    cents = {}
+    for b in range(len(blk_cnt)):
+        members = [b * cap + i for i in range(blk_cnt[b])]
+        n = blk_cnt[b]
+        cents[b] = [(2 * sum(lat(pts[s][ax]) for s in members) + n) // (2 * n) for ax in range(3)]
+    for b in range(*q_blocks):
+        for i in range(blk_cnt[b]):
+            s = b * cap + i
+            u = [lat(pts[s][ax]) for ax in range(3)]
+            cand = sorted((sum((u[a] - cents[c][a]) ** 2 for a in range(3)), int(blk_key[c]), c)
+                          for c in range(*kv_blocks))
+            full[s] = [c for _, _, c in cand[:k]]
+    return full
+
+
+@pytest.mark.parametrize("q_blocks,kv_blocks", [((0, 4), (0, 4)), ((0, 4), (4, 9)), ((4, 9), (0, 4)),
+                                                ((2, 7), (5, 6)), ((0, 9), (3, 3))])
+def test_route_range_brute_force(q_blocks, kv_blocks):
+    w = W.custom_block_workload(22, [5, 8, 1, 3, 8, 6, 2, 7, 8], 8, 4, 2, 8, "f32", 4)
+    sel, d2 = O.route_geometric_range(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k, q_blocks, kv_blocks)
+    ref = brute_route_range(w.pts.tolist(), w.blk_cnt.tolist(), w.blk_key, w.blk_cap, w.top_k, q_blocks, kv_blocks)
+    for i, s in enumerate(range(q_blocks[0] * w.blk_cap, q_blocks[1] * w.blk_cap)):
+        want = ref.get(s, [])
+        assert sel[i, :len(want)].tolist() == want
+        assert (sel[i, len(want):] == -1).all()
+    # with every block a candidate the range form is the plain routing
+    full, _ = O.route_geometric(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k)
+    rng_all, _ = O.route_geometric_range(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k, (0, 9), (0, 9))
+    np.testing.assert_array_equal(full, rng_all)
+
+
+def _split_case(seed=23, n_x_blk=4, dtype="f32"):
+    w = W.custom_block_workload(seed, [5, 8, 1, 3, 8, 6, 2, 7, 8], 8, 4, 2, 8, dtype, 3, n_gate=7)
+    return w, n_x_blk
+
+
+def test_split_reduces_to_dense_gated_self_cross():
+    """All blocks of a type routed and only the selected branches gated on: every token gets
+    s(g0) Attn(own-type tokens) + s(g1) Attn(other-type tokens), checked with library attention."""
+    w, nx = _split_case()
+    w.top_k = 5                               # at least the block count of either type
+    g = w.gates.copy()
+    g[..., 2] = g[..., 4] = g[..., 5] = -np.inf
+    g[..., 3] = g[..., 6] = np.inf
+    o = O.nsa_split_forward(w, nx, g)
+    vs = w.valid_slots()
+    xs = vs[vs // w.blk_cap < nx]
+    ys = vs[vs // w.blk_cap >= nx]
+    sg = 1.0 / (1.0 + np.exp(-g.astype(np.float64)))
+    for own, oth in ((xs, ys), (ys, xs)):
+        a = sdpa(w.q[own], w.k[own], w.v[own], w.scale)
+        c = sdpa(w.q[own], w.k[oth], w.v[oth], w.scale)
+        ref = sg[own][:, :, 0:1] * a + sg[own][:, :, 1:2] * c
+        np.testing.assert_allclose(o[own], ref, rtol=0, atol=1e-12)
+    assert np.all(o[~w.valid_mask()] == 0)
+
+
+@pytest.mark.parametrize("nx", [0, 9])
+def test_split_single_type_is_gated_nsa(nx):
+    """With one token type the cross term is empty and the layer is s(g0) times the three-branch
+    NSA layer whose gates are channels 2..4."""
+    w, _ = _split_case(seed=24)
+    o = O.nsa_split_forward(w, nx, w.gates)
+    w3 = W.custom_block_workload(24, [5, 8, 1, 3, 8, 6, 2, 7, 8], 8, 4, 2, 8, "f32", 3, n_gate=7)
+    w3.gates = w.gates[..., 2:5].copy()
+    ref = O.nsa_forward(w3)
+    sg0 = 1.0 / (1.0 + np.exp(-w.gates[..., 0:1].astype(np.float64)))
+    np.testing.assert_allclose(o, sg0 * ref, rtol=0, atol=1e-12)
+
+
+def test_split_cross_compressed_orientation():
+    """Only the other-type compressed branch on: a volume token attends the pooled image blocks and
+    an image token the pooled volume blocks (plain means, library attention)."""
+    w, nx = _split_case(seed=25)
+    g = np.full_like(w.gates, -np.inf)
+    g[..., 1] = np.inf
+    g[..., 5] = np.inf
+    o = O.nsa_split_forward(w, nx, g)
+    pooled_k = np.stack([w.k[O.block_slots(w.blk_cnt, w.blk_cap, b)].astype(np.float64).mean(0) for b in range(w.n_blk)])
+    pooled_v = np.stack([w.v[O.block_slots(w.blk_cnt, w.blk_cap, b)].astype(np.float64).mean(0) for b in range(w.n_blk)])
+    for s in w.valid_slots():
+        other = slice(nx, w.n_blk) if s // w.blk_cap < nx else slice(0, nx)
+        ref = sdpa(w.q[s:s + 1], pooled_k[other], pooled_v[other], w.scale)[0]
+        np.testing.assert_allclose(o[s], ref, rtol=0, atol=1e-12)

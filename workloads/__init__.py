@@ -25,7 +25,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "DenseWorkload", "make", "CONFIGS", "bf16_round", "morton2", "morton3",
-    "permute_storage", "custom_block_workload", "resblock_weights", "sdf_lattice",
+    "permute_storage", "custom_block_workload", "resblock_weights", "sdf_lattice", "split_gates",
 ]
 
 
@@ -543,3 +543,16 @@ def resblock_weights(seed: int, n_heads: int, D: int):
     w2 = (rng.standard_normal((n_heads, D, D)) / np.sqrt(D)).astype(np.float32)
     b2 = (0.1 * rng.standard_normal((n_heads, D))).astype(np.float32)
     return w1, b1, w2, b2
+
+
+def split_gates(w, seed: int) -> np.ndarray:
+    """Gate logits for the split self/cross layer: [S, Hq, 7] iid N(0, 1) on valid slots (0 on
+    padding), rounded to the workload's dtype; channel order (self, cross, own-cmp, own-sel,
+    own-loc, other-cmp, other-sel)."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    S = w.n_slots
+    g = np.zeros((S, w.n_qh, 7), dtype=np.float32)
+    vs = w.valid_slots()
+    x = rng.standard_normal((vs.shape[0], w.n_qh, 7), dtype=np.float32)
+    g[vs] = bf16_round(x) if w.dtype == "bf16" else x
+    return g
