@@ -149,6 +149,13 @@ def setup_geometric(w, S, torch, dev):
     rb = [tuple(torch.from_numpy(a).to(dev) for a in W.resblock_weights(s, w.n_kvh, w.head_dim)) for s in (31, 32)]
     fns["pool_kv_resblock"] = lambda: (S.pool_blocks_resblock(L, k, *rb[0], out=ws["k_cmp"]),
                                        S.pool_blocks_resblock(L, v, *rb[1], out=ws["v_cmp"]))
+    # the split self/cross form of the layer (volume blocks first, then image blocks)
+    t = w.blk_type.astype(np.int64)
+    if np.all(np.diff(t) >= 0):
+        n_x_blk = int((t == 0).sum())
+        g7 = torch.from_numpy(W.split_gates(w, 72)).to(dev).to(dt).contiguous()
+        sws = {}
+        fns["split_layer"] = lambda: S.nsa_split_layer(L, q, k, v, pts, n_x_blk, g7, w.top_k, ws=sws)
     # the volume block table from the workload's SDF sampled on a (side + 1)^3 lattice
     if "tau" in w.meta:
         side = int(w.meta["vol_side"])
@@ -301,6 +308,10 @@ def main():
                 # K and V: 4*D^2 FLOP per valid token and KV head (two D x D products)
                 f = 2 * 4 * w.head_dim * w.head_dim * w.n_kvh * int(w.blk_cnt.sum())
                 breakdown[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2)}
+                continue
+            if name == "split_layer":
+                n_tok = int(w.blk_cnt.sum())
+                breakdown[name] = {"ms": round(ms, 4), "tokens_per_s": round(n_tok / (ms * 1e-3), 1)}
                 continue
             if name == "volume_blocks":
                 # 64 trilinear SDF samples per voxel of the side^3 grid

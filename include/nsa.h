@@ -145,6 +145,21 @@ nsa_status nsa_route_geometric(const nsa_layout* layout, const float* pts, int32
                                hipStream_t stream);
 
 /*
+ * Geometric routing over a block range, for the split self/cross form of stage 2 (LSRM pages,
+ * section 方法: stage 2 keeps stage 1's decoupled self and cross attention, eq. o^x, o^y, with
+ * sparse attention in place of dense; volume and image blocks are routed separately).  The metric
+ * and order are those of nsa_route_geometric; only the blocks [kv_blk_lo, kv_blk_hi) are
+ * candidates, and only the rows of the slots of blocks [q_blk_lo, q_blk_hi) are written (other
+ * rows of sel / sel_d2 are left untouched).  Positions beyond the candidate count hold -1.
+ * centroids is rewritten for every block.  0 <= lo <= hi <= n_blk for both ranges
+ * (NSA_ERR_INVALID otherwise); an empty query range launches nothing.
+ */
+nsa_status nsa_route_geometric_range(const nsa_layout* layout, const float* pts, int32_t top_k,
+                                     int32_t q_blk_lo, int32_t q_blk_hi, int32_t kv_blk_lo,
+                                     int32_t kv_blk_hi, int32_t* centroids, int32_t* sel,
+                                     uint32_t* sel_d2, hipStream_t stream);
+
+/*
  * Score routing against the compressed keys ("standard NSA" selection the LSRM pages compare
  * with; Speed3R page, section 2.1, top-K from the compressed score matrix), without storing the
  * score matrix.
@@ -194,6 +209,25 @@ nsa_status nsa_attn_fwd(const nsa_layout* layout, nsa_dtype dtype, uint32_t bran
                         const void* q_cmp, const void* k_cmp, const void* v_cmp,
                         const int32_t* sel, int32_t top_k, int32_t sel_groups,
                         const void* gate_logits, void* o, float* lse, hipStream_t stream);
+
+/*
+ * nsa_attn_fwd over a block range, for the split self/cross form of stage 2 (LSRM pages, section
+ * 方法: eq. o^x, o^y with each attention over one token type's blocks): only the query blocks
+ * [q_blk_lo, q_blk_hi) are computed (their rows of o and lse are written, the others are left
+ * untouched); CMP attends the pooled blocks [kv_blk_lo, kv_blk_hi) only; LOC attends the own block
+ * only when it lies in that range (else it adds 0); SEL attends the routing rows as given (route
+ * them with nsa_route_geometric_range).  Gate channels: the named branches read channels 0, 1, ...
+ * of gate_logits[s][h][*], whose row length is gate_stride (0 means the number of named branches),
+ * so a caller can point gate_logits into a wider gate tensor.  Other arguments and rules are those
+ * of nsa_attn_fwd with NSA_Q_TOKEN; supported for (D, G) = (32, 16) only (NSA_ERR_UNSUPPORTED
+ * otherwise); 0 <= lo <= hi <= n_blk for both ranges and gate_stride <= 64 (NSA_ERR_INVALID).
+ */
+nsa_status nsa_attn_fwd_range(const nsa_layout* layout, nsa_dtype dtype, uint32_t branches,
+                              int32_t q_blk_lo, int32_t q_blk_hi, int32_t kv_blk_lo,
+                              int32_t kv_blk_hi, const void* q, const void* k, const void* v,
+                              const void* k_cmp, const void* v_cmp, const int32_t* sel,
+                              int32_t top_k, int32_t sel_groups, const void* gate_logits,
+                              int32_t gate_stride, void* o, float* lse, hipStream_t stream);
 
 /*
  * Sigmoid-gated sum of branch outputs (LSRM pages, section 方法, Sigmoid gates; Speed3R page,

@@ -21,7 +21,8 @@ NSA_OK, NSA_ERR_INVALID, NSA_ERR_UNSUPPORTED, NSA_ERR_HIP = 0, -1, -2, -3
 NSA_F32, NSA_BF16 = 0, 1
 BR_CMP, BR_SEL, BR_LOC = 1, 2, 4
 Q_TOKEN, Q_BLOCK = 0, 1
-EXPORTS = ("nsa_build_volume_blocks", "nsa_pool_blocks", "nsa_pool_blocks_resblock", "nsa_route_geometric", "nsa_route_scores_topk", "nsa_attn_fwd",
+EXPORTS = ("nsa_build_volume_blocks", "nsa_pool_blocks", "nsa_pool_blocks_resblock", "nsa_route_geometric",
+           "nsa_route_geometric_range", "nsa_attn_fwd_range", "nsa_route_scores_topk", "nsa_attn_fwd",
            "nsa_gate_combine", "dense_gated_xattn_fwd", "nsa_last_error")
 
 
@@ -49,6 +50,8 @@ def _load():
         "nsa_pool_blocks": [LP, I, I, P, P, P],
         "nsa_pool_blocks_resblock": [LP, I, I, P, P, P, P, P, P, P],
         "nsa_route_geometric": [LP, P, I, P, P, P, P],
+        "nsa_route_geometric_range": [LP, P, I, I, I, I, I, P, P, P, P],
+        "nsa_attn_fwd_range": [LP, I, U, I, I, I, I, P, P, P, P, P, P, I, I, P, I, P, P, P],
         "nsa_route_scores_topk": [LP, I, I, P, P, P, I, P, P],
         "nsa_attn_fwd": [LP, I, U, I, P, P, P, P, P, P, P, I, I, P, P, P, P],
         "nsa_gate_combine": [I, I, I, I, I, ctypes.POINTER(ctypes.c_void_p), P, P, P],
@@ -183,8 +186,11 @@ def pool_blocks_resblock(layout: BlockLayout, x, w1, b1, w2, b2, out=None):
     return out
 
 
-def route_geometric(layout: BlockLayout, pts, top_k, sel=None, sel_d2=None, centroids=None, want_d2=True):
-    """Top-k nearest blocks per token on the integer lattice; returns (sel, sel_d2, centroids)."""
+def route_geometric(layout: BlockLayout, pts, top_k, sel=None, sel_d2=None, centroids=None, want_d2=True,
+                    q_blocks=None, kv_blocks=None):
+    """Top-k nearest blocks per token on the integer lattice; returns (sel, sel_d2, centroids).
+    With q_blocks / kv_blocks = (lo, hi): only the slots of those query blocks are routed, among
+    the candidate blocks kv_blocks (nsa_route_geometric_range)."""
     S = layout.n_slots
     assert pts.shape == (S, 3) and pts.dtype == torch.float32
     dev = pts.device
@@ -194,8 +200,15 @@ def route_geometric(layout: BlockLayout, pts, top_k, sel=None, sel_d2=None, cent
         sel_d2 = torch.empty((S, top_k), dtype=torch.int32, device=dev)
     if centroids is None:
         centroids = torch.empty((layout.n_blk, 4), dtype=torch.int32, device=dev)
-    _check(lib.nsa_route_geometric(layout.c, _ptr(pts), int(top_k), _ptr(centroids), _ptr(sel),
-                                   _ptr(sel_d2) if want_d2 else None, _stream()))
+    if q_blocks is None and kv_blocks is None:
+        _check(lib.nsa_route_geometric(layout.c, _ptr(pts), int(top_k), _ptr(centroids), _ptr(sel),
+                                       _ptr(sel_d2) if want_d2 else None, _stream()))
+    else:
+        ql, qh = (0, layout.n_blk) if q_blocks is None else q_blocks
+        kl, kh = (0, layout.n_blk) if kv_blocks is None else kv_blocks
+        _check(lib.nsa_route_geometric_range(layout.c, _ptr(pts), int(top_k), int(ql), int(qh), int(kl), int(kh),
+                                             _ptr(centroids), _ptr(sel), _ptr(sel_d2) if want_d2 else None,
+                                             _stream()))
     return sel, sel_d2, centroids
 
 
@@ -211,13 +224,34 @@ def route_scores_topk(layout: BlockLayout, q, k_cmp, lse, top_k, q_gran=Q_TOKEN,
 
 
 def attn_fwd(layout: BlockLayout, branches, q, k=None, v=None, q_cmp=None, k_cmp=None, v_cmp=None,
-             sel=None, top_k=0, sel_groups=1, gates=None, out=None, lse=None, q_gran=Q_TOKEN):
-    """NSA branches (bitmask of BR_CMP | BR_SEL | BR_LOC), gated and fused when gates is given."""
+             sel=None, top_k=0, sel_groups=1, gates=None, out=None, lse=None, q_gran=Q_TOKEN,
+             q_blocks=None, kv_blocks=None, gate_channel=0):
+    """NSA branches (bitmask of BR_CMP | BR_SEL | BR_LOC), gated and fused when gates is given.
+    With q_blocks / kv_blocks = (lo, hi) (nsa_attn_fwd_range): only those query blocks are
+    computed, against the key blocks kv_blocks; the named branches then read the gate channels
+    gate_channel, gate_channel + 1, ... of gates [S, Hq, C]."""
     if out is None:
         out = torch.empty_like(q)
-    _check(lib.nsa_attn_fwd(layout.c, _dtype(q), int(branches), int(q_gran), _ptr(q), _ptr(k), _ptr(v),
-                            _ptr(q_cmp), _ptr(k_cmp), _ptr(v_cmp), _ptr(sel), int(top_k), int(sel_groups),
-                            _ptr(gates), _ptr(out), _ptr(lse), _stream()))
+    if q_blocks is None and kv_blocks is None and gate_channel == 0:
+        _check(lib.nsa_attn_fwd(layout.c, _dtype(q), int(branches), int(q_gran), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(q_cmp), _ptr(k_cmp), _ptr(v_cmp), _ptr(sel), int(top_k), int(sel_groups),
+                                _ptr(gates), _ptr(out), _ptr(lse), _stream()))
+        return out
+    if q_gran != Q_TOKEN:
+        raise ValueError("block ranges take per-token queries")
+    ql, qh = (0, layout.n_blk) if q_blocks is None else q_blocks
+    kl, kh = (0, layout.n_blk) if kv_blocks is None else kv_blocks
+    gp, gs = None, 0
+    if gates is not None:
+        if not gates.is_contiguous() or gates.dim() != 3:
+            raise ValueError("gates must be a contiguous [S, Hq, C] tensor")
+        gs = int(gates.shape[2])
+        if not 0 <= gate_channel < gs:
+            raise ValueError("gate_channel out of range")
+        gp = ctypes.c_void_p(_ptr(gates) + int(gate_channel) * gates.element_size())
+    _check(lib.nsa_attn_fwd_range(layout.c, _dtype(q), int(branches), int(ql), int(qh), int(kl), int(kh), _ptr(q),
+                                  _ptr(k), _ptr(v), _ptr(k_cmp), _ptr(v_cmp), _ptr(sel), int(top_k), int(sel_groups),
+                                  gp, gs, _ptr(out), _ptr(lse), _stream()))
     return out
 
 
@@ -241,6 +275,46 @@ def dense_gated_xattn(q, k, v, n_x, gates, scale=None, out=None):
     _check(lib.dense_gated_xattn_fwd(_dtype(q), n_tok, int(n_x), n_qh, n_kvh, D, float(scale), _ptr(q),
                                      _ptr(k), _ptr(v), _ptr(gates), _ptr(out), _stream()))
     return out
+
+
+def nsa_split_layer(layout: BlockLayout, q, k, v, pts, n_x_blk, gates, top_k, ws=None):
+    """Stage-2 layer with decoupled self and cross NSA: blocks [0, n_x_blk) hold volume tokens, the
+    rest image tokens; each token gets sigmoid(g0) NSA(own type) + sigmoid(g1) NSA(other type),
+    NSA(own) = CMP + SEL + LOC and NSA(other) = CMP + SEL over that type's blocks, each branch with
+    its own sigmoid gate.  gates [S, Hq, 7] = (self, cross, own-cmp, own-sel, own-loc, other-cmp,
+    other-sel).  A composition of library calls; `ws` may hold preallocated buffers."""
+    ws = {} if ws is None else ws
+    n = layout.n_blk
+    S = layout.n_slots
+    dev = q.device
+    k_cmp = pool_blocks(layout, k, ws.get("k_cmp"))
+    v_cmp = pool_blocks(layout, v, ws.get("v_cmp"))
+    for name in ("sel_self", "sel_cross"):
+        if ws.get(name) is None:
+            ws[name] = torch.empty((S, top_k), dtype=torch.int32, device=dev)
+    if ws.get("centroids") is None:
+        ws["centroids"] = torch.empty((n, 4), dtype=torch.int32, device=dev)
+    for name in ("o_self", "o_cross", "out"):
+        if ws.get(name) is None:
+            ws[name] = torch.empty_like(q)
+    if ws.get("g_outer") is None:
+        ws["g_outer"] = torch.empty((S, q.shape[1], 2), dtype=gates.dtype, device=dev)
+    ws["g_outer"].copy_(gates[:, :, 0:2])
+    x, y = (0, n_x_blk), (n_x_blk, n)
+    for own, other in ((x, y), (y, x)):
+        if own[0] == own[1]:
+            continue
+        route_geometric(layout, pts, top_k, sel=ws["sel_self"], centroids=ws["centroids"], want_d2=False,
+                        q_blocks=own, kv_blocks=own)
+        route_geometric(layout, pts, top_k, sel=ws["sel_cross"], centroids=ws["centroids"], want_d2=False,
+                        q_blocks=own, kv_blocks=other)
+        attn_fwd(layout, BR_CMP | BR_SEL | BR_LOC, q, k, v, k_cmp=k_cmp, v_cmp=v_cmp, sel=ws["sel_self"],
+                 top_k=top_k, gates=gates, gate_channel=2, out=ws["o_self"], q_blocks=own, kv_blocks=own)
+        attn_fwd(layout, BR_CMP | BR_SEL, q, k, v, k_cmp=k_cmp, v_cmp=v_cmp, sel=ws["sel_cross"], top_k=top_k,
+                 gates=gates, gate_channel=5, out=ws["o_cross"], q_blocks=own, kv_blocks=other)
+    gate_combine([ws["o_self"], ws["o_cross"]], ws["g_outer"], out=ws["out"])
+    ws.update(k_cmp=k_cmp, v_cmp=v_cmp)
+    return ws["out"]
 
 
 def nsa_layer(layout: BlockLayout, q, k, v, pts, gates, top_k, ws=None):

@@ -120,15 +120,24 @@ nsa_status nsa_build_volume_blocks(const float* sdf, int32_t G, int32_t N, float
                     "nsa_build_volume_blocks");
 }
 
-nsa_status nsa_route_geometric(const nsa_layout* L, const float* pts, int32_t top_k, int32_t* centroids,
-                               int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
-  nsa_status st = check_layout(L, "nsa_route_geometric");
+static bool range_ok(int32_t lo, int32_t hi, int32_t n) { return lo >= 0 && lo <= hi && hi <= n; }
+
+static nsa_status route_geometric(const char* fn, const nsa_layout* L, const float* pts, int32_t top_k,
+                                  int32_t q_lo, int32_t q_hi, int32_t kv_lo, int32_t kv_hi, int32_t* centroids,
+                                  int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
+  nsa_status st = check_layout(L, fn);
   if (st != NSA_OK) return st;
   if (pts == nullptr || centroids == nullptr || sel == nullptr || L->blk_key == nullptr)
-    return fail(NSA_ERR_INVALID, "nsa_route_geometric: pts, centroids, sel and blk_key must be non-NULL");
-  if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "nsa_route_geometric: top_k must be in 1..64 (got %d)", top_k);
-  NSA_FORCED_FAILURE("nsa_route_geometric");
+    return fail(NSA_ERR_INVALID, "%s: pts, centroids, sel and blk_key must be non-NULL", fn);
+  if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "%s: top_k must be in 1..64 (got %d)", fn, top_k);
+  if (!range_ok(q_lo, q_hi, L->n_blk) || !range_ok(kv_lo, kv_hi, L->n_blk))
+    return fail(NSA_ERR_INVALID, "%s: block ranges must satisfy 0 <= lo <= hi <= n_blk", fn);
+  NSA_FORCED_FAILURE(fn);
   nsa::RouteArgs a;
+  a.q_blk0 = q_lo;
+  a.n_qblk = q_hi - q_lo;
+  a.kv_lo = kv_lo;
+  a.kv_hi = kv_hi;
   a.pts = pts;
   a.blk_cnt = L->blk_cnt;
   a.blk_key = L->blk_key;
@@ -138,7 +147,20 @@ nsa_status nsa_route_geometric(const nsa_layout* L, const float* pts, int32_t to
   a.n_blk = L->n_blk;
   a.cap = L->blk_cap;
   a.top_k = top_k;
-  return hip_status(nsa::launch_route_geometric(a, stream), "nsa_route_geometric");
+  return hip_status(nsa::launch_route_geometric(a, stream), fn);
+}
+
+nsa_status nsa_route_geometric(const nsa_layout* L, const float* pts, int32_t top_k, int32_t* centroids,
+                               int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
+  const int32_t n = L != nullptr ? L->n_blk : 0;
+  return route_geometric("nsa_route_geometric", L, pts, top_k, 0, n, 0, n, centroids, sel, sel_d2, stream);
+}
+
+nsa_status nsa_route_geometric_range(const nsa_layout* L, const float* pts, int32_t top_k, int32_t q_blk_lo,
+                                     int32_t q_blk_hi, int32_t kv_blk_lo, int32_t kv_blk_hi, int32_t* centroids,
+                                     int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
+  return route_geometric("nsa_route_geometric_range", L, pts, top_k, q_blk_lo, q_blk_hi, kv_blk_lo, kv_blk_hi,
+                         centroids, sel, sel_d2, stream);
 }
 
 nsa_status nsa_route_scores_topk(const nsa_layout* L, nsa_dtype dtype, nsa_qgran q_gran, const void* q,
@@ -194,41 +216,51 @@ nsa_status nsa_route_scores_topk(const nsa_layout* L, nsa_dtype dtype, nsa_qgran
   return hip_status(nsa::launch_route_scores(dtype == NSA_BF16, a, stream), "nsa_route_scores_topk");
 }
 
-nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches, nsa_qgran q_gran,
-                        const void* q, const void* k, const void* v, const void* q_cmp, const void* k_cmp,
-                        const void* v_cmp, const int32_t* sel, int32_t top_k, int32_t sel_groups,
-                        const void* gate_logits, void* o, float* lse, hipStream_t stream) {
-  nsa_status st = check_layout(L, "nsa_attn_fwd");
+static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype, uint32_t branches,
+                           nsa_qgran q_gran, int32_t q_lo, int32_t q_hi, int32_t kv_lo, int32_t kv_hi,
+                           const void* q, const void* k, const void* v, const void* q_cmp, const void* k_cmp,
+                           const void* v_cmp, const int32_t* sel, int32_t top_k, int32_t sel_groups,
+                           const void* gate_logits, int32_t gate_stride, void* o, float* lse, hipStream_t stream) {
+  nsa_status st = check_layout(L, fn);
   if (st != NSA_OK) return st;
-  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: unknown dtype");
-  if (branches == 0 || (branches & ~7u) != 0) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: branches must be a non-empty OR of NSA_BR_* bits");
-  if (q_gran != NSA_Q_TOKEN && q_gran != NSA_Q_BLOCK) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: bad q_gran");
+  if (!range_ok(q_lo, q_hi, L->n_blk) || !range_ok(kv_lo, kv_hi, L->n_blk))
+    return fail(NSA_ERR_INVALID, "%s: block ranges must satisfy 0 <= lo <= hi <= n_blk", fn);
+  const bool whole = q_lo == 0 && q_hi == L->n_blk && kv_lo == 0 && kv_hi == L->n_blk;
+  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "%s: unknown dtype", fn);
+  if (branches == 0 || (branches & ~7u) != 0) return fail(NSA_ERR_INVALID, "%s: branches must be a non-empty OR of NSA_BR_* bits", fn);
+  if (q_gran != NSA_Q_TOKEN && q_gran != NSA_Q_BLOCK) return fail(NSA_ERR_INVALID, "%s: bad q_gran", fn);
   const int n_named = __builtin_popcount(branches);
   if (gate_logits == nullptr && n_named != 1)
-    return fail(NSA_ERR_INVALID, "nsa_attn_fwd: several branches need gate_logits to be combined");
-  if (lse != nullptr && n_named != 1) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: lse needs exactly one branch");
-  if (o == nullptr || q == nullptr) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: q and o must be non-NULL");
+    return fail(NSA_ERR_INVALID, "%s: several branches need gate_logits to be combined", fn);
+  if (gate_stride == 0) gate_stride = n_named;
+  if (gate_stride < n_named || gate_stride > 64)
+    return fail(NSA_ERR_INVALID, "%s: gate_stride must be in [number of branches, 64]", fn);
+  if (gate_stride != n_named && L->n_qh == L->n_kvh)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: a gate stride needs the grouped-query kernel (head_dim 32)", fn);
+  if (lse != nullptr && n_named != 1) return fail(NSA_ERR_INVALID, "%s: lse needs exactly one branch", fn);
+  if (o == nullptr || q == nullptr) return fail(NSA_ERR_INVALID, "%s: q and o must be non-NULL", fn);
   if ((branches & (NSA_BR_SEL | NSA_BR_LOC)) && (k == nullptr || v == nullptr))
-    return fail(NSA_ERR_INVALID, "nsa_attn_fwd: SEL and LOC need k and v");
+    return fail(NSA_ERR_INVALID, "%s: SEL and LOC need k and v", fn);
   if ((branches & NSA_BR_CMP) && (k_cmp == nullptr || v_cmp == nullptr))
-    return fail(NSA_ERR_INVALID, "nsa_attn_fwd: CMP needs k_cmp and v_cmp");
+    return fail(NSA_ERR_INVALID, "%s: CMP needs k_cmp and v_cmp", fn);
   if ((branches & NSA_BR_CMP) && q_gran == NSA_Q_BLOCK && q_cmp == nullptr)
-    return fail(NSA_ERR_INVALID, "nsa_attn_fwd: CMP with NSA_Q_BLOCK needs q_cmp");
+    return fail(NSA_ERR_INVALID, "%s: CMP with NSA_Q_BLOCK needs q_cmp", fn);
   if (branches & NSA_BR_SEL) {
-    if (sel == nullptr) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: SEL needs sel");
-    if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "nsa_attn_fwd: top_k must be in 1..64 (got %d)", top_k);
+    if (sel == nullptr) return fail(NSA_ERR_INVALID, "%s: SEL needs sel", fn);
+    if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "%s: top_k must be in 1..64 (got %d)", fn, top_k);
     if (sel_groups != 1 && sel_groups != L->n_kvh)
-      return fail(NSA_ERR_INVALID, "nsa_attn_fwd: sel_groups must be 1 or n_kvh");
-    if (L->n_blk > 65536) return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: SEL supports n_blk <= 65536");
+      return fail(NSA_ERR_INVALID, "%s: sel_groups must be 1 or n_kvh", fn);
+    if (L->n_blk > 65536) return fail(NSA_ERR_UNSUPPORTED, "%s: SEL supports n_blk <= 65536", fn);
   }
   if (L->n_qh == L->n_kvh) {
     // one query head per KV head (score-routed, block-granular layout)
     if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK || dtype != NSA_BF16 || (branches & NSA_BR_LOC) ||
         L->blk_cap > 16 || 64 % L->blk_cap != 0)
       return fail(NSA_ERR_UNSUPPORTED,
-                  "nsa_attn_fwd: with one query head per KV head the compiled kernels take head_dim 64, NSA_Q_BLOCK, "
-                  "bf16, the CMP and SEL branches and blk_cap in {1, 2, 4, 8, 16}");
-    NSA_FORCED_FAILURE("nsa_attn_fwd");
+                  "%s: with one query head per KV head the compiled kernels take head_dim 64, NSA_Q_BLOCK, "
+                  "bf16, the CMP and SEL branches and blk_cap in {1, 2, 4, 8, 16}", fn);
+    if (!whole) return fail(NSA_ERR_UNSUPPORTED, "%s: block ranges need the grouped-query kernel (head_dim 32)", fn);
+    NSA_FORCED_FAILURE(fn);
     nsa::G1Args g{};
     g.q = q;
     g.k = k;
@@ -253,11 +285,11 @@ nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches,
     g.ch_sel = (branches & NSA_BR_CMP) ? 1 : 0;
     g.scale = L->scale;
     g.branches = branches;
-    return hip_status(nsa::launch_attn_g1(g, stream), "nsa_attn_fwd");
+    return hip_status(nsa::launch_attn_g1(g, stream), fn);
   }
   if (L->head_dim != 32 || L->n_qh / L->n_kvh != 16 || q_gran != NSA_Q_TOKEN)
-    return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: compiled for head_dim 32, 16 query heads per KV head, NSA_Q_TOKEN "
-                                     "(or head_dim 64, one query head per KV head, NSA_Q_BLOCK)");
+    return fail(NSA_ERR_UNSUPPORTED, "%s: compiled for head_dim 32, 16 query heads per KV head, NSA_Q_TOKEN "
+                                     "(or head_dim 64, one query head per KV head, NSA_Q_BLOCK)", fn);
   nsa::AttnArgs a;
   a.q = q;
   a.k = k;
@@ -275,7 +307,7 @@ nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches,
   a.n_kvh = L->n_kvh;
   a.top_k = (branches & NSA_BR_SEL) ? top_k : 0;
   a.sel_groups = sel_groups < 1 ? 1 : sel_groups;
-  a.n_gch = n_named;
+  a.n_gch = gate_stride;
   a.scale = L->scale;
   a.branches = branches;
   a.n_words = (L->n_blk + 31) / 32;
@@ -291,10 +323,32 @@ nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches,
     a.ring_spins = stall ? 64 : (1 << 16);
     a.ring_stall = stall ? 1 : 0;
   }
+  a.q_blk0 = q_lo;
+  a.n_qblk = q_hi - q_lo;
+  a.kv_lo = kv_lo;
+  a.kv_hi = kv_hi;
   const size_t lds = nsa::attn_lds_bytes(dtype == NSA_BF16, a);
-  if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "nsa_attn_fwd: LDS need %zu bytes exceeds 160 KiB", lds);
-  NSA_FORCED_FAILURE("nsa_attn_fwd");
-  return hip_status(nsa::launch_attn(dtype == NSA_BF16, a, stream), "nsa_attn_fwd");
+  if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "%s: LDS need %zu bytes exceeds 160 KiB", fn, lds);
+  NSA_FORCED_FAILURE(fn);
+  return hip_status(nsa::launch_attn(dtype == NSA_BF16, a, stream), fn);
+}
+
+nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches, nsa_qgran q_gran,
+                        const void* q, const void* k, const void* v, const void* q_cmp, const void* k_cmp,
+                        const void* v_cmp, const int32_t* sel, int32_t top_k, int32_t sel_groups,
+                        const void* gate_logits, void* o, float* lse, hipStream_t stream) {
+  const int32_t n = L != nullptr ? L->n_blk : 0;
+  return attn_fwd("nsa_attn_fwd", L, dtype, branches, q_gran, 0, n, 0, n, q, k, v, q_cmp, k_cmp, v_cmp, sel, top_k,
+                  sel_groups, gate_logits, 0, o, lse, stream);
+}
+
+nsa_status nsa_attn_fwd_range(const nsa_layout* L, nsa_dtype dtype, uint32_t branches, int32_t q_blk_lo,
+                              int32_t q_blk_hi, int32_t kv_blk_lo, int32_t kv_blk_hi, const void* q, const void* k,
+                              const void* v, const void* k_cmp, const void* v_cmp, const int32_t* sel,
+                              int32_t top_k, int32_t sel_groups, const void* gate_logits, int32_t gate_stride,
+                              void* o, float* lse, hipStream_t stream) {
+  return attn_fwd("nsa_attn_fwd_range", L, dtype, branches, NSA_Q_TOKEN, q_blk_lo, q_blk_hi, kv_blk_lo, kv_blk_hi,
+                  q, k, v, nullptr, k_cmp, v_cmp, sel, top_k, sel_groups, gate_logits, gate_stride, o, lse, stream);
 }
 
 nsa_status nsa_gate_combine(nsa_dtype dtype, int32_t n_rows, int32_t n_qh, int32_t head_dim, int32_t n_branch,

@@ -523,7 +523,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   float* out_lds = reinterpret_cast<float*>(extra);
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = wg / a.n_kvh, j = wg % a.n_kvh;
+  const int b = a.q_blk0 + wg / a.n_kvh, j = wg % a.n_kvh;
   const int cap = a.cap, cnt = a.blk_cnt[b];
   const int w = threadIdx.x >> 6, l = lane_id();
   const int r = l & 15, g = l >> 4;
@@ -675,7 +675,8 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.lo = b * cap;
     src.hi = b * cap + cnt;
     AllPart part{n_valid};
-    run_tiles<T, NT, TPW>(buf, src, 1, part, st, qf);
+    // the own block is a key block only when it lies in the key range (an empty key set adds 0)
+    run_tiles<T, NT, TPW>(buf, src, (b >= a.kv_lo && b < a.kv_hi) ? 1 : 0, part, st, qf);
     finish_all(n_named - 1);
   }
 
@@ -687,10 +688,10 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.base = reinterpret_cast<const T*>(a.k_cmp) + j * HD;
     src.vbase = reinterpret_cast<const T*>(a.v_cmp) + j * HD;
     src.stride = kvs;
-    src.lo = 0;
-    src.hi = a.n_blk;
+    src.lo = a.kv_lo;
+    src.hi = a.kv_hi;
     AllPart part{n_valid};
-    run_tiles<T, NT, TPW>(buf, src, (a.n_blk + TILE - 1) / TILE, part, st, qf);
+    run_tiles<T, NT, TPW>(buf, src, (a.kv_hi - a.kv_lo + TILE - 1) / TILE, part, st, qf);
     finish_all(0);
   }
 
@@ -807,7 +808,8 @@ template <typename T>
 hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
   const size_t lds = attn_lds_t<T>(a);
-  const int nwg = a.n_blk * a.n_kvh;
+  const int nwg = a.n_qblk * a.n_kvh;
+  if (nwg == 0) return hipSuccess;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nsa_attn_kernel<T, WAVES, TPW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

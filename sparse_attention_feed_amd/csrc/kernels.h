@@ -25,6 +25,8 @@ struct AttnArgs {
   int u_cap;           // bound on the number of distinct selected blocks of one query block
   int ring_spins;      // bound on each wait of the selected branch's tile ring
   int ring_stall;      // test hook: extra count the ring waits for (0 in normal use)
+  int q_blk0, n_qblk;  // query blocks [q_blk0, q_blk0 + n_qblk)
+  int kv_lo, kv_hi;    // key blocks of the compressed and local branches: [kv_lo, kv_hi)
 };
 
 struct DenseArgs {
@@ -45,6 +47,8 @@ struct RouteArgs {
   int32_t* sel;
   uint32_t* sel_d2;     // nullable
   int n_blk, cap, top_k;
+  int q_blk0, n_qblk;   // routed query slots: those of blocks [q_blk0, q_blk0 + n_qblk)
+  int kv_lo, kv_hi;     // candidate blocks [kv_lo, kv_hi)
 };
 
 struct ScoreRouteArgs {

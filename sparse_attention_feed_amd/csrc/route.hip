@@ -88,8 +88,8 @@ template <int K>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   __shared__ int2 cs[RCH];        // (x | y << 16, z) of the chunk's centroids
   __shared__ uint32_t ck[RCH];    // their blk_key
-  const int S = a.n_blk * a.cap;
-  const int slot = blockIdx.x * 256 + threadIdx.x;
+  const int S = (a.q_blk0 + a.n_qblk) * a.cap;     // one past the last routed slot
+  const int slot = a.q_blk0 * a.cap + blockIdx.x * 256 + threadIdx.x;
   bool valid = false;
   uint32_t uxy = 0u;
   int uz = 0;
@@ -109,14 +109,16 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     bk[x] = 0xFFFFFFFFu;
     bi[x] = -1;
   }
-  const int nch = (a.n_blk + RCH - 1) / RCH;
-  const int first_blk = min(a.n_blk - 1, (blockIdx.x * 256) / a.cap);
-  const int c0 = first_blk / RCH;       // start near this workgroup's own blocks
+  const int n_cand = a.kv_hi - a.kv_lo;
+  const int nch = (n_cand + RCH - 1) / RCH;
+  const int first_blk = (a.q_blk0 * a.cap + blockIdx.x * 256) / a.cap;
+  // start near this workgroup's own blocks (any chunk order gives the same result)
+  const int c0 = nch > 0 ? min(nch - 1, max(0, first_blk - a.kv_lo) / RCH) : 0;
   const int4* cent = reinterpret_cast<const int4*>(a.cent);
   for (int ci = 0; ci < nch; ++ci) {
     const int c = (c0 + ci) % nch;
-    const int base = c * RCH;
-    const int n = min(RCH, a.n_blk - base);
+    const int base = a.kv_lo + c * RCH;
+    const int n = min(RCH, a.kv_hi - base);
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += 256) {
       const int4 e = cent[base + i];
@@ -293,7 +295,8 @@ __global__ __launch_bounds__(256) void score_route_kernel(ScoreRouteArgs a) {
 
 template <int K>
 hipError_t launch_route_k(const RouteArgs& a, hipStream_t s) {
-  const int S = a.n_blk * a.cap;
+  const int S = a.n_qblk * a.cap;
+  if (S == 0) return hipSuccess;
   hipLaunchKernelGGL(route_kernel<K>, dim3((S + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }

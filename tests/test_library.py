@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 9
+    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 11
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -80,6 +80,44 @@ def test_attn_layout_validation(S, kw, status):
 ])
 def test_attn_argument_validation(S, kw):
     assert attn(S, layout(S), **kw) == -1
+
+
+def attn_range(S, L, **kw):
+    a = dict(dtype=1, branches=7, q_lo=0, q_hi=4, kv_lo=0, kv_hi=4, q=FAKE, k=FAKE, v=FAKE, k_cmp=FAKE, v_cmp=FAKE,
+             sel=FAKE, top_k=4, sel_groups=1, gates=FAKE, gate_stride=0, o=FAKE, lse=None)
+    a.update(kw)
+    return S.lib.nsa_attn_fwd_range(ctypes.byref(L), a["dtype"], a["branches"], a["q_lo"], a["q_hi"], a["kv_lo"],
+                                    a["kv_hi"], a["q"], a["k"], a["v"], a["k_cmp"], a["v_cmp"], a["sel"], a["top_k"],
+                                    a["sel_groups"], a["gates"], a["gate_stride"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q_lo=-1), dict(q_lo=3, q_hi=2), dict(q_hi=5), dict(kv_lo=-1), dict(kv_lo=4, kv_hi=3), dict(kv_hi=5),
+    dict(gate_stride=2), dict(gate_stride=65), dict(gate_stride=-1), dict(branches=0), dict(o=None),
+])
+def test_attn_range_argument_validation(S, kw):
+    assert attn_range(S, layout(S), **kw) == -1
+    assert S.lib.nsa_last_error().decode().startswith("nsa_attn_fwd_range")
+
+
+def test_attn_range_unsupported_and_forced(S, monkeypatch):
+    g1 = layout(S, n_qh=16, n_kvh=16, head_dim=64, blk_cap=16)
+    assert attn_range(S, g1, branches=3) == -2                      # the D = 64 kernels take no ranges
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    assert attn_range(S, layout(S), q_lo=1, q_hi=3, kv_lo=2, kv_hi=4, gate_stride=7) == -3
+    assert attn_range(S, layout(S), q_lo=2, q_hi=2, kv_lo=0, kv_hi=0) == -3   # empty ranges are valid
+
+
+def test_route_range_validation(S, monkeypatch):
+    L = layout(S)
+    r = S.lib.nsa_route_geometric_range
+    assert r(ctypes.byref(L), FAKE, 4, 0, 5, 0, 4, FAKE, FAKE, None, None) == -1
+    assert r(ctypes.byref(L), FAKE, 4, 0, 4, 3, 2, FAKE, FAKE, None, None) == -1
+    assert r(ctypes.byref(L), FAKE, 0, 0, 4, 0, 4, FAKE, FAKE, None, None) == -1
+    assert r(ctypes.byref(L), None, 4, 0, 4, 0, 4, FAKE, FAKE, None, None) == -1
+    assert S.lib.nsa_last_error().decode().startswith("nsa_route_geometric_range")
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    assert r(ctypes.byref(L), FAKE, 4, 1, 3, 0, 0, FAKE, FAKE, None, None) == -3
 
 
 def test_attn_single_branch_needs_no_gate(S, monkeypatch):
