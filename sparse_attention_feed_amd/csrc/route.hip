@@ -51,8 +51,6 @@ __device__ __forceinline__ bool before(uint32_t d, uint32_t k, uint32_t d2, uint
   return d < d2 || (d == d2 && k < k2);
 }
 
-constexpr int RCH = 1024;   // centroids per LDS chunk
-
 // Sorted insertion of (d, key, idx) into the lane's ascending top-K list, if it ranks within it.
 template <int K>
 __device__ __forceinline__ void topk_insert(uint32_t (&bd)[K], uint32_t (&bk)[K], int (&bi)[K], uint32_t d,
@@ -73,7 +71,6 @@ __device__ __forceinline__ void topk_insert(uint32_t (&bd)[K], uint32_t (&bk)[K]
   }
 }
 
-// One thread per query slot; a sorted top-K list (d2, key, index) lives in registers.
 typedef short short2v __attribute__((ext_vector_type(2)));
 
 // Squared lattice distance: x and y as packed 16-bit differences through one dot2, z in 24 bits
@@ -84,23 +81,74 @@ __device__ __forceinline__ uint32_t dist2(uint32_t uxy, int uz, int2 c) {
   return (uint32_t)__builtin_amdgcn_sdot2(d, d, __mul24(dz, dz), false);
 }
 
+// One wave per query block (blk_cap <= 64: lane t is the block's slot t).  Exact candidate pruning
+// with the lattice bounding box [lo, hi] of the block's valid points:
+//   for any point u of the box and centroid c,  dmin(box, c) <= d2(u, c) <= dmax(box, c);
+//   T = the k-th smallest, over the 64 lanes, of each lane's minimum dmax over its share of the
+//       candidates: k distinct centroids lie within T of every point of the box, so every token's
+//       k-th best d2 is <= T;
+//   a centroid with dmin > T is then farther than T from every token and cannot enter any token's
+//       top k (one with d2 == T still can, on blk_key, and is kept).
+// The surviving candidates are gathered in LDS a chunk at a time and each lane ranks them into its
+// register top-K list in the total (d2, blk_key) order, so the result is that of the full scan.
+constexpr int PCH = 1024;   // candidates per LDS chunk
+
+__device__ __forceinline__ uint32_t box_dmax(int x, int y, int z, const int (&lo)[3], const int (&hi)[3]) {
+  const int ax = max(x - lo[0], hi[0] - x), ay = max(y - lo[1], hi[1] - y), az = max(z - lo[2], hi[2] - z);
+  return (uint32_t)(ax * ax + ay * ay + az * az);
+}
+
+__device__ __forceinline__ uint32_t box_dmin(int x, int y, int z, const int (&lo)[3], const int (&hi)[3]) {
+  const int ax = max(lo[0] - x, 0) + max(x - hi[0], 0);
+  const int ay = max(lo[1] - y, 0) + max(y - hi[1], 0);
+  const int az = max(lo[2] - z, 0) + max(z - hi[2], 0);
+  return (uint32_t)(ax * ax + ay * ay + az * az);
+}
+
 template <int K>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-  __shared__ int2 cs[RCH];        // (x | y << 16, z) of the chunk's centroids
-  __shared__ uint32_t ck[RCH];    // their blk_key
-  const int S = (a.q_blk0 + a.n_qblk) * a.cap;     // one past the last routed slot
-  const int slot = a.q_blk0 * a.cap + blockIdx.x * 256 + threadIdx.x;
-  bool valid = false;
-  uint32_t uxy = 0u;
-  int uz = 0;
-  if (slot < S) {
-    valid = (slot % a.cap) < a.blk_cnt[slot / a.cap];
-    if (valid) {
-      const float* p = a.pts + (size_t)slot * 3;
-      uxy = (uint32_t)lattice(p[0]) | ((uint32_t)lattice(p[1]) << 16);
-      uz = lattice(p[2]);
-    }
+__global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
+  __shared__ int2 cs[PCH];        // (x | y << 16, z) of the chunk's surviving centroids
+  __shared__ uint32_t ck[PCH];    // their blk_key
+  __shared__ int ci[PCH];         // their block index
+  const int b = a.q_blk0 + blockIdx.x;
+  const int l = threadIdx.x;
+  const int cnt = a.blk_cnt[b];
+  const bool in_blk = l < a.cap;
+  const bool valid = l < cnt;
+  const int slot = b * a.cap + l;
+  int ux = 0, uy = 0, uz = 0;
+  if (valid) {
+    const float* p = a.pts + (size_t)slot * 3;
+    ux = lattice(p[0]);
+    uy = lattice(p[1]);
+    uz = lattice(p[2]);
   }
+  // the block's bounding box (valid lanes only; lane 0 is always valid)
+  int lo[3] = {valid ? ux : 1 << 30, valid ? uy : 1 << 30, valid ? uz : 1 << 30};
+  int hi[3] = {valid ? ux : -(1 << 30), valid ? uy : -(1 << 30), valid ? uz : -(1 << 30)};
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) {
+      lo[ax] = min(lo[ax], __shfl_xor(lo[ax], o, 64));
+      hi[ax] = max(hi[ax], __shfl_xor(hi[ax], o, 64));
+    }
+  const int4* cent = reinterpret_cast<const int4*>(a.cent);
+  // pass 1: the bound T
+  uint32_t lmin = 0xFFFFFFFFu;
+  for (int c = a.kv_lo + l; c < a.kv_hi; c += 64) {
+    const int4 e = cent[c];
+    lmin = min(lmin, box_dmax(e.x, e.y, e.z, lo, hi));
+  }
+  int rank = 0;
+  for (int i = 0; i < 64; ++i) {
+    const uint32_t v = (uint32_t)__shfl((int)lmin, i, 64);
+    rank += (v < lmin || (v == lmin && i < l)) ? 1 : 0;
+  }
+  const unsigned long long at_k = __builtin_amdgcn_ballot_w64(rank == a.top_k - 1);
+  const uint32_t T = (uint32_t)__shfl((int)lmin, __builtin_ctzll(at_k), 64);   // ranks are a permutation
+  // pass 2: gather the survivors chunk by chunk and rank them
+  const uint32_t uxy = (uint32_t)ux | ((uint32_t)uy << 16);
   uint32_t bd[K], bk[K];
   int bi[K];
 #pragma unroll
@@ -109,27 +157,30 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     bk[x] = 0xFFFFFFFFu;
     bi[x] = -1;
   }
-  const int n_cand = a.kv_hi - a.kv_lo;
-  const int nch = (n_cand + RCH - 1) / RCH;
-  const int first_blk = (a.q_blk0 * a.cap + blockIdx.x * 256) / a.cap;
-  // start near this workgroup's own blocks (any chunk order gives the same result)
-  const int c0 = nch > 0 ? min(nch - 1, max(0, first_blk - a.kv_lo) / RCH) : 0;
-  const int4* cent = reinterpret_cast<const int4*>(a.cent);
-  for (int ci = 0; ci < nch; ++ci) {
-    const int c = (c0 + ci) % nch;
-    const int base = a.kv_lo + c * RCH;
-    const int n = min(RCH, a.kv_hi - base);
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 256) {
-      const int4 e = cent[base + i];
-      cs[i] = make_int2(e.x | (e.y << 16), e.z);
-      ck[i] = (uint32_t)e.w;
+  int c = a.kv_lo;
+  while (c < a.kv_hi) {
+    int n = 0;
+    // fill the chunk: up to PCH survivors (64 centroids per step; stop before a step could overflow)
+    for (; c < a.kv_hi && n + 64 <= PCH; c += 64) {
+      const int cc = c + l;
+      bool keep = false;
+      int4 e = make_int4(0, 0, 0, 0);
+      if (cc < a.kv_hi) {
+        e = cent[cc];
+        keep = box_dmin(e.x, e.y, e.z, lo, hi) <= T;
+      }
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(keep);
+      if (keep) {
+        const int pos = n + __builtin_popcountll(m & ((1ull << l) - 1ull));
+        cs[pos] = make_int2(e.x | (e.y << 16), e.z);
+        ck[pos] = (uint32_t)e.w;
+        ci[pos] = cc;
+      }
+      n += __builtin_popcountll(m);
     }
     __syncthreads();
     if (valid) {
-      // filter on d2 alone (a superset of the candidates: d2 equal to the current K-th may still
-      // win on blk_key), eight centroids at a time; each lane then walks only its own candidates,
-      // so a group costs the wave one insertion per candidate of its busiest lane
+      // filter on d2 alone, eight at a time; each lane then walks only its own candidates
       constexpr int GR = 8;
       int i = 0;
       for (; i + GR <= n; i += GR) {
@@ -146,13 +197,14 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
           uint32_t dd = d[0];
 #pragma unroll
           for (int y = 1; y < GR; ++y) dd = x == y ? d[y] : dd;
-          topk_insert<K>(bd, bk, bi, dd, ck[i + x], base + i + x);
+          topk_insert<K>(bd, bk, bi, dd, ck[i + x], ci[i + x]);
         }
       }
-      for (; i < n; ++i) topk_insert<K>(bd, bk, bi, dist2(uxy, uz, cs[i]), ck[i], base + i);
+      for (; i < n; ++i) topk_insert<K>(bd, bk, bi, dist2(uxy, uz, cs[i]), ck[i], ci[i]);
     }
+    __syncthreads();
   }
-  if (slot < S) {
+  if (in_blk) {
     int32_t* so = a.sel + (size_t)slot * a.top_k;
     uint32_t* dout = a.sel_d2 ? a.sel_d2 + (size_t)slot * a.top_k : nullptr;
 #pragma unroll
@@ -295,9 +347,8 @@ __global__ __launch_bounds__(256) void score_route_kernel(ScoreRouteArgs a) {
 
 template <int K>
 hipError_t launch_route_k(const RouteArgs& a, hipStream_t s) {
-  const int S = a.n_qblk * a.cap;
-  if (S == 0) return hipSuccess;
-  hipLaunchKernelGGL(route_kernel<K>, dim3((S + 255) / 256), dim3(256), 0, s, a);
+  if (a.n_qblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(route_kernel<K>, dim3(a.n_qblk), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
