@@ -89,9 +89,11 @@ __device__ __forceinline__ uint32_t dist2(uint32_t uxy, int uz, int2 c) {
 //       k-th best d2 is <= T;
 //   a centroid with dmin > T is then farther than T from every token and cannot enter any token's
 //       top k (one with d2 == T still can, on blk_key, and is kept).
-// The surviving candidates are gathered in LDS a chunk at a time and each lane ranks them into its
-// register top-K list in the total (d2, blk_key) order, so the result is that of the full scan.
-constexpr int PCH = 1024;   // candidates per LDS chunk
+// The surviving candidates are gathered in LDS a chunk at a time, sorted nearest box first, and each
+// lane ranks them into its register top-K list in the total (d2, blk_key) order, so the result is
+// that of the full scan; with the nearest candidates seen first, the list's threshold settles early
+// and few later candidates still enter it.
+constexpr int PCH = 512;    // candidates per LDS chunk
 
 __device__ __forceinline__ uint32_t box_dmax(int x, int y, int z, const int (&lo)[3], const int (&hi)[3]) {
   const int ax = max(x - lo[0], hi[0] - x), ay = max(y - lo[1], hi[1] - y), az = max(z - lo[2], hi[2] - z);
@@ -110,6 +112,7 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
   __shared__ int2 cs[PCH];        // (x | y << 16, z) of the chunk's surviving centroids
   __shared__ uint32_t ck[PCH];    // their blk_key
   __shared__ int ci[PCH];         // their block index
+  __shared__ unsigned long long so[PCH];   // (dmin << 32 | position), sorted
   const int b = a.q_blk0 + blockIdx.x;
   const int l = threadIdx.x;
   const int cnt = a.blk_cnt[b];
@@ -164,10 +167,12 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
     for (; c < a.kv_hi && n + 64 <= PCH; c += 64) {
       const int cc = c + l;
       bool keep = false;
+      uint32_t dm = 0u;
       int4 e = make_int4(0, 0, 0, 0);
       if (cc < a.kv_hi) {
         e = cent[cc];
-        keep = box_dmin(e.x, e.y, e.z, lo, hi) <= T;
+        dm = box_dmin(e.x, e.y, e.z, lo, hi);
+        keep = dm <= T;
       }
       const unsigned long long m = __builtin_amdgcn_ballot_w64(keep);
       if (keep) {
@@ -175,18 +180,41 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
         cs[pos] = make_int2(e.x | (e.y << 16), e.z);
         ck[pos] = (uint32_t)e.w;
         ci[pos] = cc;
+        so[pos] = ((unsigned long long)dm << 32) | (unsigned)pos;
       }
       n += __builtin_popcountll(m);
     }
+    // sort the survivors nearest box first (bitonic, padded to a power of two)
+    int N = 64;
+    while (N < n) N <<= 1;
+    for (int i = n + l; i < N; i += 64) so[i] = ~0ull;
     __syncthreads();
+    for (int size = 2; size <= N; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = l; i < N; i += 64) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const unsigned long long x0 = so[i], x1 = so[j];
+            if ((x0 > x1) == ((i & size) == 0)) {
+              so[i] = x1;
+              so[j] = x0;
+            }
+          }
+        }
+        __syncthreads();
+      }
     if (valid) {
+      int i = 0;
       // filter on d2 alone, eight at a time; each lane then walks only its own candidates
       constexpr int GR = 8;
-      int i = 0;
       for (; i + GR <= n; i += GR) {
         uint32_t d[GR];
+        int q[GR];
 #pragma unroll
-        for (int x = 0; x < GR; ++x) d[x] = dist2(uxy, uz, cs[i + x]);
+        for (int x = 0; x < GR; ++x) {
+          q[x] = (int)(unsigned)so[i + x];
+          d[x] = dist2(uxy, uz, cs[q[x]]);
+        }
         const uint32_t thr = bd[K - 1];
         uint32_t m = 0u;
 #pragma unroll
@@ -195,12 +223,19 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
           const int x = __builtin_ctz(m);
           m &= m - 1u;
           uint32_t dd = d[0];
+          int p = q[0];
 #pragma unroll
-          for (int y = 1; y < GR; ++y) dd = x == y ? d[y] : dd;
-          topk_insert<K>(bd, bk, bi, dd, ck[i + x], ci[i + x]);
+          for (int y = 1; y < GR; ++y) {
+            dd = x == y ? d[y] : dd;
+            p = x == y ? q[y] : p;
+          }
+          topk_insert<K>(bd, bk, bi, dd, ck[p], ci[p]);
         }
       }
-      for (; i < n; ++i) topk_insert<K>(bd, bk, bi, dist2(uxy, uz, cs[i]), ck[i], ci[i]);
+      for (; i < n; ++i) {
+        const int p = (int)(unsigned)so[i];
+        topk_insert<K>(bd, bk, bi, dist2(uxy, uz, cs[p]), ck[p], ci[p]);
+      }
     }
     __syncthreads();
   }
