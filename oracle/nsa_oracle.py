@@ -479,6 +479,69 @@ def nsa_forward(w, rows=None, return_parts=False):
 
 
 # ----------------------------------------------------------------------------------------------
+# routing with image blocks found through the views
+# ----------------------------------------------------------------------------------------------
+
+def project_cell(p, proj_row, cell):
+    """Cell coordinate of point p along one image axis: the patch coordinate
+    ((A0 p0 + A1 p1) + A2 p2) + A3, each operation rounded to float32 in that order, divided by
+    the cell size (a power of two, so exact) and floored."""
+    f32 = np.float32
+    x = f32(f32(f32(proj_row[0]) * f32(p[0])) + f32(f32(proj_row[1]) * f32(p[1])))
+    x = f32(x + f32(f32(proj_row[2]) * f32(p[2])))
+    x = f32(x + f32(proj_row[3]))
+    return int(math.floor(float(x) / cell))
+
+
+def route_geometric_views(pts, blk_cnt, blk_key, cap, top_k, n_vol_blk, view_proj, cell_blk, cell, radius,
+                          rows=None):
+    """3D-aware routing with the image-block rule of [LSRM-cn] (routing paragraph): the query point is
+    projected into every view, the image blocks of the cells within `radius` cells of the projection
+    are that view's candidates, and an image candidate's metric is the smallest squared distance
+    between the query and any of its tokens' points.  Volume blocks [0, n_vol_blk) keep the
+    block-centre metric (d2 to the centroid).  Both on the 2^-12 lattice, exact integers; one
+    ranking over all candidates in ascending (d2, blk_key) order, top_k, best first.
+    view_proj [V, 2, 4] float32 maps a point to continuous patch coordinates (project_cell);
+    cell_blk [V, n_cell, n_cell] int32 is the block of each (view, cell row, cell column) or -1.
+    Returns sel int32 [len(rows), top_k] and d2 uint32 (padding rows and missing ranks: -1 /
+    0xFFFFFFFF)."""
+    blk_cnt = np.asarray(blk_cnt)
+    blk_key = np.asarray(blk_key, dtype=np.int64)
+    S = blk_cnt.shape[0] * cap
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    valid = valid_mask(blk_cnt, cap)
+    cen = block_centroids(pts, blk_cnt, cap)
+    u = lattice_coords(pts)
+    V, nc = cell_blk.shape[0], cell_blk.shape[1]
+    sel = np.full((rows.shape[0], top_k), -1, dtype=np.int32)
+    dd = np.full((rows.shape[0], top_k), 0xFFFFFFFF, dtype=np.uint32)
+    vol = np.arange(n_vol_blk)
+    for i, r in enumerate(rows):
+        if not valid[r]:
+            continue
+        cand = list(vol)
+        metric = list(((u[r][None, :] - cen[vol]) ** 2).sum(axis=1)) if n_vol_blk else []
+        for v in range(V):
+            cx = project_cell(pts[r], view_proj[v, 0], cell)
+            cy = project_cell(pts[r], view_proj[v, 1], cell)
+            for y in range(max(cy - radius, 0), min(cy + radius, nc - 1) + 1):
+                for x in range(max(cx - radius, 0), min(cx + radius, nc - 1) + 1):
+                    b = int(cell_blk[v, y, x])
+                    if b < 0:
+                        continue
+                    members = u[block_slots(blk_cnt, cap, b)]
+                    cand.append(b)
+                    metric.append(int(((members - u[r][None, :]) ** 2).sum(axis=1).min()))
+        cand = np.asarray(cand, dtype=np.int64)
+        metric = np.asarray(metric, dtype=np.int64)
+        kk = min(top_k, cand.shape[0])
+        order = np.lexsort((blk_key[cand], metric))[:kk]
+        sel[i, :kk] = cand[order]
+        dd[i, :kk] = metric[order]
+    return sel, dd
+
+
+# ----------------------------------------------------------------------------------------------
 # split self/cross NSA: stage 2 keeping stage 1's decoupled branches
 # ----------------------------------------------------------------------------------------------
 

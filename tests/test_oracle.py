@@ -583,3 +583,91 @@ def test_split_cross_compressed_orientation():
         other = slice(nx, w.n_blk) if s // w.blk_cap < nx else slice(0, nx)
         ref = sdpa(w.q[s:s + 1], pooled_k[other], pooled_v[other], w.scale)[0]
         np.testing.assert_allclose(o[s], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# routing with image blocks found through the views
+# ---------------------------------------------------------------------------------------------
+
+def test_views_projection_recovers_own_cell():
+    w = W.make("stage2_small")
+    proj, cell_blk = W.view_cameras(w)
+    for b in np.nonzero(w.blk_type == 1)[0]:
+        v = int((int(w.blk_key[b]) >> 20) & 0x7FF)
+        cy, cx = [int(x[0]) for x in np.nonzero(cell_blk[v] == b)]
+        for s in O.block_slots(w.blk_cnt, w.blk_cap, b):
+            assert O.project_cell(w.pts[s], proj[v, 0], 8) == cx
+            assert O.project_cell(w.pts[s], proj[v, 1], 8) == cy
+
+
+def test_views_whole_grid_window_is_all_blocks():
+    """A window covering every cell makes every image block a candidate: the ranking is then the
+    plain one over all blocks with each image block's nearest-member metric (vectorised here)."""
+    w = W.make("stage2_small")
+    proj, cell_blk = W.view_cameras(w)
+    nv = int((w.blk_type == 0).sum())
+    rows = np.array([0, 5, 63, nv * 64 + 3, nv * 64 + 200, (w.n_blk - 1) * 64])
+    rows = rows[w.valid_mask()[rows]]
+    sel, d2 = O.route_geometric_views(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k, nv, proj, cell_blk, 8,
+                                      cell_blk.shape[1], rows=rows)
+    u = O.lattice_coords(w.pts).astype(np.int64)
+    cen = O.block_centroids(w.pts, w.blk_cnt, w.blk_cap).astype(np.int64)
+    for i, r in enumerate(rows):
+        m = ((cen - u[r]) ** 2).sum(axis=1)
+        for b in range(nv, w.n_blk):
+            m[b] = ((u[O.block_slots(w.blk_cnt, w.blk_cap, b)] - u[r]) ** 2).sum(axis=1).min()
+        order = np.lexsort((w.blk_key.astype(np.int64), m))[:w.top_k]
+        assert sel[i].tolist() == order.tolist()
+        assert d2[i].astype(np.int64).tolist() == m[order].tolist()
+
+
+def test_views_brute_force_python():
+    """Two axis-aligned views on a 2x2 cell grid, hand-made: pure-Python candidate windows and
+    nearest-member metrics, sorted as tuples."""
+    w = W.custom_block_workload(41, [3, 5, 2, 4, 6, 1, 3, 2], 8, 4, 2, 8, "f32", 4)
+    nv = 3                                                   # blocks 0..2 volume, 3..7 image
+    # view 0 sees (x, y), view 1 sees (y, z): patch coordinate 8 (c + 1) on a 16-patch side
+    proj = np.zeros((2, 2, 4), dtype=np.float32)
+    proj[0, 0, 0] = proj[0, 1, 1] = proj[1, 0, 1] = proj[1, 1, 2] = 8.0
+    proj[:, :, 3] = 8.0
+    cell_blk = np.full((2, 2, 2), -1, dtype=np.int32)
+    cell_blk[0, 0, 0], cell_blk[0, 1, 1], cell_blk[1, 0, 1], cell_blk[1, 1, 0], cell_blk[1, 1, 1] = 3, 4, 5, 6, 7
+    for radius in (0, 1):
+        sel, d2 = O.route_geometric_views(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k, nv, proj, cell_blk, 8, radius)
+        lat = lambda x: int(round(4096 * float(x))) + 4096  # noqa: E731
+        P = w.pts.tolist()
+        U = [[lat(c) for c in p] for p in P]
+        members = {b: [b * 8 + i for i in range(int(w.blk_cnt[b]))] for b in range(8)}
+        cents = {b: [(2 * sum(U[t][a] for t in members[b]) + len(members[b])) // (2 * len(members[b]))
+                     for a in range(3)] for b in range(8)}
+        where = {int(cell_blk[v, y, x]): (v, y, x) for v in range(2) for y in range(2) for x in range(2)
+                 if cell_blk[v, y, x] >= 0}
+        for s in range(w.n_slots):
+            if s % 8 >= w.blk_cnt[s // 8]:
+                assert (sel[s] == -1).all()
+                continue
+            d = lambda a, b: sum((a[i] - b[i]) ** 2 for i in range(3))  # noqa: E731
+            cand = [(d(U[s], cents[b]), int(w.blk_key[b]), b) for b in range(nv)]
+            for b, (v, y, x) in where.items():
+                cx = O.project_cell(P[s], proj[v, 0], 8)
+                cy = O.project_cell(P[s], proj[v, 1], 8)
+                if abs(x - cx) <= radius and abs(y - cy) <= radius:
+                    cand.append((min(d(U[s], U[t]) for t in members[b]), int(w.blk_key[b]), b))
+            cand.sort()
+            want = [b for _, _, b in cand[:w.top_k]]
+            assert sel[s, :len(want)].tolist() == want
+            assert (sel[s, len(want):] == -1).all()
+
+
+def test_views_image_query_finds_its_own_block():
+    """An image token lies in its own view's projection cell and is its own block's member at
+    distance 0, so with any window its own block ranks first (or ties at d2 = 0)."""
+    w = W.make("stage2_small")
+    proj, cell_blk = W.view_cameras(w)
+    nv = int((w.blk_type == 0).sum())
+    rows = np.arange(nv * 64, w.n_slots, 37)
+    rows = rows[w.valid_mask()[rows]]
+    sel, d2 = O.route_geometric_views(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k, nv, proj, cell_blk, 8, 0,
+                                      rows=rows)
+    assert np.all(d2[:, 0] == 0)
+    assert np.mean(sel[:, 0] == rows // 64) > 0.9

@@ -26,6 +26,7 @@ import numpy as np
 __all__ = [
     "Workload", "DenseWorkload", "make", "CONFIGS", "bf16_round", "morton2", "morton3",
     "permute_storage", "custom_block_workload", "resblock_weights", "sdf_lattice", "split_gates",
+    "view_cameras",
 ]
 
 
@@ -392,6 +393,8 @@ def _lsrm_geometric(name, seed, dtype, vol_side, vol_shape, vol_target, n_views,
     else:
         patches = _foreground_patches(img_side, fg)
         dirs = _fibonacci_dirs(n_views)
+        meta.update(cam_dirs=dirs.tolist(), cam_centre=np.asarray(sph_c, dtype=np.float64).tolist(),
+                    cam_half=float(sph_r * math.sqrt(math.pi / 2.0)), img_side=img_side, n_views=n_views)
         for vi in range(n_views):
             p = _image_points(dirs[vi:vi + 1], patches, img_side, sph_c, sph_r)
             cell = morton2(patches[:, 0] // 8, patches[:, 1] // 8)
@@ -556,3 +559,35 @@ def split_gates(w, seed: int) -> np.ndarray:
     x = rng.standard_normal((vs.shape[0], w.n_qh, 7), dtype=np.float32)
     g[vs] = bf16_round(x) if w.dtype == "bf16" else x
     return g
+
+
+def view_cameras(w, cell: int = 8):
+    """The orthographic cameras of a geometric workload's image views, as the routing takes them:
+    view_proj float32 [V, 2, 4], an affine map from a 3D point to continuous patch coordinates
+    (a, b) of the view (patch (a, b) covers [a, a + 1) x [b, b + 1)), and cell_blk int32
+    [V, side / cell, side / cell], the storage block of each (view, cell) or -1.  Returns
+    (view_proj, cell_blk)."""
+    m = w.meta
+    side = int(m["img_side"])
+    half = float(m["cam_half"])
+    c = np.asarray(m["cam_centre"], dtype=np.float64)
+    dirs = np.asarray(m["cam_dirs"], dtype=np.float64)
+    k = side / (2.0 * half)
+    proj = np.zeros((dirs.shape[0], 2, 4))
+    for v, d in enumerate(dirs):
+        r, u = _view_basis(d)
+        for row, e in enumerate((r, u)):
+            proj[v, row, :3] = e * k
+            proj[v, row, 3] = side / 2.0 - float(c @ e) * k
+    nc = side // cell
+    cell_blk = np.full((dirs.shape[0], nc, nc), -1, dtype=np.int32)
+    keys = w.blk_key.astype(np.int64)
+    for b in np.nonzero(w.blk_type == 1)[0]:
+        view = int((keys[b] >> 20) & 0x7FF)
+        code = int(keys[b] & 0xFFFFF)
+        cx = cy = 0
+        for bit in range(10):
+            cx |= ((code >> (2 * bit)) & 1) << bit
+            cy |= ((code >> (2 * bit + 1)) & 1) << bit
+        cell_blk[view, cy, cx] = b
+    return proj.astype(np.float32), cell_blk
