@@ -156,6 +156,17 @@ def setup_geometric(w, S, torch, dev):
         g7 = torch.from_numpy(W.split_gates(w, 72)).to(dev).to(dt).contiguous()
         sws = {}
         fns["split_layer"] = lambda: S.nsa_split_layer(L, q, k, v, pts, n_x_blk, g7, w.top_k, ws=sws)
+    # routing with the image blocks found through the views (radius 1: the 3 x 3 cells around the
+    # projection in every view)
+    if "cam_dirs" in w.meta:
+        vp, cb = W.view_cameras(w)
+        vp_d, cb_d = torch.from_numpy(vp).to(dev), torch.from_numpy(cb).to(dev)
+        n_vol = int((w.blk_type == 0).sum())
+        vsel = torch.empty((w.n_slots, w.top_k), dtype=torch.int32, device=dev)
+        vcent = torch.empty((w.n_blk, 4), dtype=torch.int32, device=dev)
+        vbox = torch.empty((w.n_blk, 8), dtype=torch.int32, device=dev)
+        fns["route_views"] = lambda: S.route_geometric_views(L, pts, w.top_k, n_vol, vp_d, cb_d, cell_size=8, radius=1,
+                                                             sel=vsel, centroids=vcent, boxes=vbox, want_d2=False)
     # the volume block table from the workload's SDF sampled on a (side + 1)^3 lattice
     if "tau" in w.meta:
         side = int(w.meta["vol_side"])
@@ -308,6 +319,9 @@ def main():
                 # K and V: 4*D^2 FLOP per valid token and KV head (two D x D products)
                 f = 2 * 4 * w.head_dim * w.head_dim * w.n_kvh * int(w.blk_cnt.sum())
                 breakdown[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2)}
+                continue
+            if name == "route_views":
+                breakdown[name] = {"ms": round(ms, 4)}
                 continue
             if name == "split_layer":
                 n_tok = int(w.blk_cnt.sum())

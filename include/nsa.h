@@ -145,6 +145,32 @@ nsa_status nsa_route_geometric(const nsa_layout* layout, const float* pts, int32
                                hipStream_t stream);
 
 /*
+ * Geometric routing with the image blocks found through the views (LSRM pages, section 方法,
+ * routing paragraph: for image blocks the query point is projected into every input view, nearby
+ * image blocks are gathered per view and ranked by their smallest 3D distance to the query; volume
+ * blocks are ranked by the distance to their centres).  On the lattice of nsa_route_geometric:
+ *   volume candidates: blocks [0, n_vol_blk), metric d2(u_t, c_b) to the block centroid;
+ *   image candidates: for each view v, the cell (cx, cy) = floor(proj_v(p_t) / cell_size) with
+ *     proj_v(p) = ((A0 p.x + A1 p.y) + A2 p.z) + A3 per image axis (A = view_proj[v][axis][0..3],
+ *     every operation rounded to float32 in that order), then the blocks cell_blk[v][y][x] >= 0 of
+ *     the cells |x - cx| <= radius, |y - cy| <= radius inside the n_cell x n_cell grid; metric =
+ *     min over the block's valid tokens s of d2(u_t, u_s).
+ * One ranking of all candidates by ascending (d2, blk_key), top_k best first, as in
+ * nsa_route_geometric; every valid slot's row is written (-1 / 0xFFFFFFFF past the candidates).
+ *   view_proj [n_views][2][4] float32, cell_blk [n_views][n_cell][n_cell] int32 (device); every
+ *   entry >= 0 names a block outside [0, n_vol_blk), and a block appears at most once;
+ *   centroids [n_blk][4] and boxes [n_blk][8] int32 are workspaces (boxes: each block's lattice
+ *   bounding box, used to skip candidates that cannot reach a token's current top k).
+ * 0 <= n_vol_blk <= n_blk, n_views >= 0 (0: volume blocks only), 1 <= n_cell <= 4096, cell_size
+ * a power of two <= 1024, 0 <= radius <= 16, 1 <= top_k <= 64 (NSA_ERR_INVALID otherwise).
+ */
+nsa_status nsa_route_geometric_views(const nsa_layout* layout, const float* pts, int32_t top_k,
+                                     int32_t n_vol_blk, int32_t n_views, const float* view_proj,
+                                     const int32_t* cell_blk, int32_t n_cell, int32_t cell_size,
+                                     int32_t radius, int32_t* centroids, int32_t* boxes,
+                                     int32_t* sel, uint32_t* sel_d2, hipStream_t stream);
+
+/*
  * Geometric routing over a block range, for the split self/cross form of stage 2 (LSRM pages,
  * section 方法: stage 2 keeps stage 1's decoupled self and cross attention, eq. o^x, o^y, with
  * sparse attention in place of dense; volume and image blocks are routed separately).  The metric

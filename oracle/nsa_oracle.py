@@ -490,7 +490,7 @@ def project_cell(p, proj_row, cell):
     x = f32(f32(f32(proj_row[0]) * f32(p[0])) + f32(f32(proj_row[1]) * f32(p[1])))
     x = f32(x + f32(f32(proj_row[2]) * f32(p[2])))
     x = f32(x + f32(proj_row[3]))
-    return int(math.floor(float(x) / cell))
+    return int(math.floor(float(x) / cell))     # cells far outside the grid all give empty windows
 
 
 def route_geometric_views(pts, blk_cnt, blk_key, cap, top_k, n_vol_blk, view_proj, cell_blk, cell, radius,

@@ -22,7 +22,7 @@ NSA_F32, NSA_BF16 = 0, 1
 BR_CMP, BR_SEL, BR_LOC = 1, 2, 4
 Q_TOKEN, Q_BLOCK = 0, 1
 EXPORTS = ("nsa_build_volume_blocks", "nsa_pool_blocks", "nsa_pool_blocks_resblock", "nsa_route_geometric",
-           "nsa_route_geometric_range", "nsa_attn_fwd_range", "nsa_route_scores_topk", "nsa_attn_fwd",
+           "nsa_route_geometric_range", "nsa_route_geometric_views", "nsa_attn_fwd_range", "nsa_route_scores_topk", "nsa_attn_fwd",
            "nsa_gate_combine", "dense_gated_xattn_fwd", "nsa_last_error")
 
 
@@ -51,6 +51,7 @@ def _load():
         "nsa_pool_blocks_resblock": [LP, I, I, P, P, P, P, P, P, P],
         "nsa_route_geometric": [LP, P, I, P, P, P, P],
         "nsa_route_geometric_range": [LP, P, I, I, I, I, I, P, P, P, P],
+        "nsa_route_geometric_views": [LP, P, I, I, I, P, P, I, I, I, P, P, P, P, P],
         "nsa_attn_fwd_range": [LP, I, U, I, I, I, I, P, P, P, P, P, P, I, I, P, I, P, P, P],
         "nsa_route_scores_topk": [LP, I, I, P, P, P, I, P, P],
         "nsa_attn_fwd": [LP, I, U, I, P, P, P, P, P, P, P, I, I, P, P, P, P],
@@ -209,6 +210,32 @@ def route_geometric(layout: BlockLayout, pts, top_k, sel=None, sel_d2=None, cent
         _check(lib.nsa_route_geometric_range(layout.c, _ptr(pts), int(top_k), int(ql), int(qh), int(kl), int(kh),
                                              _ptr(centroids), _ptr(sel), _ptr(sel_d2) if want_d2 else None,
                                              _stream()))
+    return sel, sel_d2, centroids
+
+
+def route_geometric_views(layout: BlockLayout, pts, top_k, n_vol_blk, view_proj, cell_blk, cell_size=8,
+                          radius=1, sel=None, sel_d2=None, centroids=None, boxes=None, want_d2=True):
+    """Top-k blocks per token: volume blocks [0, n_vol_blk) by centroid distance, image blocks found
+    by projecting the token into every view (view_proj [V, 2, 4], cell_blk [V, n_cell, n_cell]) and
+    ranked by their nearest member; returns (sel, sel_d2, centroids)."""
+    S = layout.n_slots
+    dev = pts.device
+    if sel is None:
+        sel = torch.empty((S, top_k), dtype=torch.int32, device=dev)
+    if want_d2 and sel_d2 is None:
+        sel_d2 = torch.empty((S, top_k), dtype=torch.int32, device=dev)
+    if centroids is None:
+        centroids = torch.empty((layout.n_blk, 4), dtype=torch.int32, device=dev)
+    if boxes is None:
+        boxes = torch.empty((layout.n_blk, 8), dtype=torch.int32, device=dev)
+    n_views = int(view_proj.shape[0])
+    n_cell = int(cell_blk.shape[1])
+    if n_views and (tuple(view_proj.shape) != (n_views, 2, 4) or tuple(cell_blk.shape) != (n_views, n_cell, n_cell)):
+        raise ValueError("view_proj must be [V, 2, 4] and cell_blk [V, n_cell, n_cell]")
+    _check(lib.nsa_route_geometric_views(layout.c, _ptr(pts), int(top_k), int(n_vol_blk), n_views,
+                                         _ptr(view_proj), _ptr(cell_blk), n_cell, int(cell_size), int(radius),
+                                         _ptr(centroids), _ptr(boxes), _ptr(sel),
+                                         _ptr(sel_d2) if want_d2 else None, _stream()))
     return sel, sel_d2, centroids
 
 

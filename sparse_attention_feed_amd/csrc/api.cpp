@@ -133,7 +133,7 @@ static nsa_status route_geometric(const char* fn, const nsa_layout* L, const flo
   if (!range_ok(q_lo, q_hi, L->n_blk) || !range_ok(kv_lo, kv_hi, L->n_blk))
     return fail(NSA_ERR_INVALID, "%s: block ranges must satisfy 0 <= lo <= hi <= n_blk", fn);
   NSA_FORCED_FAILURE(fn);
-  nsa::RouteArgs a;
+  nsa::RouteArgs a{};
   a.q_blk0 = q_lo;
   a.n_qblk = q_hi - q_lo;
   a.kv_lo = kv_lo;
@@ -154,6 +154,51 @@ nsa_status nsa_route_geometric(const nsa_layout* L, const float* pts, int32_t to
                                int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
   const int32_t n = L != nullptr ? L->n_blk : 0;
   return route_geometric("nsa_route_geometric", L, pts, top_k, 0, n, 0, n, centroids, sel, sel_d2, stream);
+}
+
+nsa_status nsa_route_geometric_views(const nsa_layout* L, const float* pts, int32_t top_k, int32_t n_vol_blk,
+                                     int32_t n_views, const float* view_proj, const int32_t* cell_blk,
+                                     int32_t n_cell, int32_t cell_size, int32_t radius, int32_t* centroids,
+                                     int32_t* boxes, int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
+  const char* fn = "nsa_route_geometric_views";
+  nsa_status st = check_layout(L, fn);
+  if (st != NSA_OK) return st;
+  if (pts == nullptr || centroids == nullptr || sel == nullptr || L->blk_key == nullptr)
+    return fail(NSA_ERR_INVALID, "%s: pts, centroids, sel and blk_key must be non-NULL", fn);
+  if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "%s: top_k must be in 1..64 (got %d)", fn, top_k);
+  if (n_vol_blk < 0 || n_vol_blk > L->n_blk) return fail(NSA_ERR_INVALID, "%s: n_vol_blk must be in [0, n_blk]", fn);
+  if (n_views < 0) return fail(NSA_ERR_INVALID, "%s: n_views must be >= 0", fn);
+  if (n_views > 0) {
+    if (view_proj == nullptr || cell_blk == nullptr || boxes == nullptr)
+      return fail(NSA_ERR_INVALID, "%s: view_proj, cell_blk and boxes must be non-NULL with views", fn);
+    if (n_cell < 1 || n_cell > 4096) return fail(NSA_ERR_INVALID, "%s: n_cell must be in 1..4096", fn);
+    if (cell_size < 1 || cell_size > 1024 || (cell_size & (cell_size - 1)) != 0)
+      return fail(NSA_ERR_INVALID, "%s: cell_size must be a power of two in 1..1024", fn);
+    if (radius < 0 || radius > 16) return fail(NSA_ERR_INVALID, "%s: radius must be in 0..16", fn);
+  }
+  NSA_FORCED_FAILURE(fn);
+  nsa::RouteArgs a{};
+  a.q_blk0 = 0;
+  a.n_qblk = L->n_blk;
+  a.kv_lo = 0;
+  a.kv_hi = n_vol_blk;
+  a.pts = pts;
+  a.blk_cnt = L->blk_cnt;
+  a.blk_key = L->blk_key;
+  a.cent = centroids;
+  a.sel = sel;
+  a.sel_d2 = sel_d2;
+  a.n_blk = L->n_blk;
+  a.cap = L->blk_cap;
+  a.top_k = top_k;
+  a.view_proj = view_proj;
+  a.cell_blk = cell_blk;
+  a.boxes = boxes;
+  a.n_views = n_views;
+  a.n_cell = n_cell;
+  a.cell_shift = __builtin_ctz((unsigned)cell_size);
+  a.radius = radius;
+  return hip_status(nsa::launch_route_geometric(a, stream), fn);
 }
 
 nsa_status nsa_route_geometric_range(const nsa_layout* L, const float* pts, int32_t top_k, int32_t q_blk_lo,

@@ -48,7 +48,12 @@ struct RouteArgs {
   uint32_t* sel_d2;     // nullable
   int n_blk, cap, top_k;
   int q_blk0, n_qblk;   // routed query slots: those of blocks [q_blk0, q_blk0 + n_qblk)
-  int kv_lo, kv_hi;     // candidate blocks [kv_lo, kv_hi)
+  int kv_lo, kv_hi;     // candidate blocks [kv_lo, kv_hi) (with views: the volume blocks)
+  // image blocks found through the views (n_views == 0: none)
+  const float* view_proj;   // [n_views][2][4]
+  const int32_t* cell_blk;  // [n_views][n_cell][n_cell]
+  int32_t* boxes;           // [n_blk][8] workspace: lattice box (lo xyz, -, hi xyz, -) of each block
+  int n_views, n_cell, cell_shift, radius;
 };
 
 struct ScoreRouteArgs {

@@ -19,23 +19,37 @@ namespace {
 __device__ __forceinline__ int lattice(float p) { return (int)rintf(4096.0f * p) + 4096; }
 
 // One wave per block: integer centroid of the block's valid points plus its key.
+// With `boxes`, also the lattice bounding box of the block's points.
 __global__ __launch_bounds__(64) void centroid_kernel(const float* __restrict__ pts, const int32_t* __restrict__ blk_cnt,
                                                       const uint32_t* __restrict__ blk_key, int32_t* __restrict__ cent,
-                                                      int cap) {
+                                                      int32_t* __restrict__ boxes, int cap) {
   const int b = blockIdx.x, l = threadIdx.x;
   const int cnt = blk_cnt[b];
   int sx = 0, sy = 0, sz = 0;
+  int lo[3] = {1 << 30, 1 << 30, 1 << 30}, hi[3] = {-(1 << 30), -(1 << 30), -(1 << 30)};
   for (int t = l; t < cnt; t += 64) {
     const float* p = pts + (size_t)(b * cap + t) * 3;
-    sx += lattice(p[0]);
-    sy += lattice(p[1]);
-    sz += lattice(p[2]);
+    const int x = lattice(p[0]), y = lattice(p[1]), z = lattice(p[2]);
+    sx += x;
+    sy += y;
+    sz += z;
+    lo[0] = min(lo[0], x), lo[1] = min(lo[1], y), lo[2] = min(lo[2], z);
+    hi[0] = max(hi[0], x), hi[1] = max(hi[1], y), hi[2] = max(hi[2], z);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     sx += __shfl_xor(sx, o, 64);
     sy += __shfl_xor(sy, o, 64);
     sz += __shfl_xor(sz, o, 64);
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) {
+      lo[ax] = min(lo[ax], __shfl_xor(lo[ax], o, 64));
+      hi[ax] = max(hi[ax], __shfl_xor(hi[ax], o, 64));
+    }
+  }
+  if (l == 0 && boxes != nullptr) {
+    reinterpret_cast<int4*>(boxes)[2 * b] = make_int4(lo[0], lo[1], lo[2], 0);
+    reinterpret_cast<int4*>(boxes)[2 * b + 1] = make_int4(hi[0], hi[1], hi[2], 0);
   }
   if (l == 0) {
     int4 c;
@@ -94,6 +108,21 @@ __device__ __forceinline__ uint32_t dist2(uint32_t uxy, int uz, int2 c) {
 // that of the full scan; with the nearest candidates seen first, the list's threshold settles early
 // and few later candidates still enter it.
 constexpr int PCH = 512;    // candidates per LDS chunk
+
+// Continuous patch coordinate of a point along one image axis: ((A0 x + A1 y) + A2 z) + A3, every
+// operation rounded to float32 in this order (no fused multiply-add), so the cell decision is
+// reproducible bit for bit.
+__device__ __forceinline__ float project_axis(const float* A, float x, float y, float z) {
+#pragma clang fp contract(off)
+  return ((A[0] * x + A[1] * y) + A[2] * z) + A[3];
+}
+
+// floor(x / 2^shift) through an exact integer floor; far-off values are clamped to +-2^30, which
+// leaves their window outside every cell grid.
+__device__ __forceinline__ int cell_of(float x, int shift) {
+  const float f = fminf(fmaxf(floorf(x), -1073741824.0f), 1073741824.0f);
+  return (int)f >> shift;
+}
 
 __device__ __forceinline__ uint32_t box_dmax(int x, int y, int z, const int (&lo)[3], const int (&hi)[3]) {
   const int ax = max(x - lo[0], hi[0] - x), ay = max(y - lo[1], hi[1] - y), az = max(z - lo[2], hi[2] - z);
@@ -238,6 +267,37 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
       }
     }
     __syncthreads();
+  }
+  // image blocks through the views: every view's projection cell and its window; a candidate's
+  // metric is its nearest member's d2, computed only when the block's box could still beat the
+  // lane's current k-th (d2 == k-th may still win on blk_key)
+  if (a.n_views > 0 && valid) {
+    const float* pp = a.pts + (size_t)slot * 3;
+    const float px = pp[0], py = pp[1], pz = pp[2];
+    const int4* box = reinterpret_cast<const int4*>(a.boxes);
+    for (int v = 0; v < a.n_views; ++v) {
+      const float* A = a.view_proj + 8 * v;
+      const int cx = cell_of(project_axis(A, px, py, pz), a.cell_shift);
+      const int cy = cell_of(project_axis(A + 4, px, py, pz), a.cell_shift);
+      const int y0 = max(cy - a.radius, 0), y1 = min(cy + a.radius, a.n_cell - 1);
+      const int x0 = max(cx - a.radius, 0), x1 = min(cx + a.radius, a.n_cell - 1);
+      for (int y = y0; y <= y1; ++y)
+        for (int x = x0; x <= x1; ++x) {
+          const int bb = a.cell_blk[((size_t)v * a.n_cell + y) * a.n_cell + x];
+          if (bb < 0 || bb >= a.n_blk) continue;
+          const int4 blo = box[2 * bb], bhi = box[2 * bb + 1];
+          const int lo3[3] = {blo.x, blo.y, blo.z}, hi3[3] = {bhi.x, bhi.y, bhi.z};
+          if (box_dmin(ux, uy, uz, lo3, hi3) > bd[K - 1]) continue;
+          uint32_t best = 0xFFFFFFFFu;
+          const int mc = a.blk_cnt[bb];
+          const float* mp = a.pts + (size_t)bb * a.cap * 3;
+          for (int t = 0; t < mc; ++t) {
+            const int dx = lattice(mp[3 * t]) - ux, dy = lattice(mp[3 * t + 1]) - uy, dz = lattice(mp[3 * t + 2]) - uz;
+            best = min(best, (uint32_t)(dx * dx + dy * dy + dz * dz));
+          }
+          topk_insert<K>(bd, bk, bi, best, a.blk_key[bb], bb);
+        }
+    }
   }
   if (in_blk) {
     int32_t* so = a.sel + (size_t)slot * a.top_k;
@@ -405,7 +465,8 @@ hipError_t launch_score_t(const ScoreRouteArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_route_geometric(const RouteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(centroid_kernel, dim3(a.n_blk), dim3(64), 0, s, a.pts, a.blk_cnt, a.blk_key, a.cent, a.cap);
+  hipLaunchKernelGGL(centroid_kernel, dim3(a.n_blk), dim3(64), 0, s, a.pts, a.blk_cnt, a.blk_key, a.cent,
+                     a.n_views > 0 ? a.boxes : nullptr, a.cap);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.top_k <= 4) return launch_route_k<4>(a, s);
