@@ -35,10 +35,16 @@ def edge(kind):
         return W.custom_block_workload(8, [1] * 150, 1, 32, 2, 32, "f32", 12, pts_mode="lattice")
     if kind == "cnt_one_blocks":
         return W.custom_block_workload(9, [1, 64, 1, 1, 64, 2] * 20, 64, 32, 2, 32, "f32", 5)
+    if kind == "k48_cap16":       # the 64-entry routing list and selections of up to 48 blocks
+        cnt = np.random.default_rng(10).integers(1, 17, size=100).tolist()
+        return W.custom_block_workload(10, cnt, 16, 32, 2, 32, "bf16", 48)
+    if kind == "k64_cap8":
+        cnt = np.random.default_rng(11).integers(1, 9, size=90).tolist()
+        return W.custom_block_workload(11, cnt, 8, 32, 2, 32, "f32", 64)
     raise KeyError(kind)
 
 
-EDGES = ["ragged_cap16", "single_block", "k_beyond_blocks", "lattice_ties", "cnt_one_blocks"]
+EDGES = ["ragged_cap16", "single_block", "k_beyond_blocks", "lattice_ties", "cnt_one_blocks", "k48_cap16", "k64_cap8"]
 
 
 def get(name):
@@ -93,7 +99,7 @@ def test_pool_blocks_resblock(name):
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", SMALL + ["ragged_cap16", "single_block", "k_beyond_blocks", "lattice_ties",
-                                          "cnt_one_blocks"])
+                                          "cnt_one_blocks", "k48_cap16", "k64_cap8"])
 def test_route_geometric_bit_exact(name):
     import sparse_attention_feed_amd as S
     w = get(name)
@@ -164,7 +170,8 @@ def test_single_branch(name, branch):
 # fused gated layer (pool + route + three branches + gate) against the whole oracle layer
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", SMALL + ["ragged_cap16", "k_beyond_blocks", "cnt_one_blocks"])
+@pytest.mark.parametrize("name", SMALL + ["ragged_cap16", "k_beyond_blocks", "cnt_one_blocks", "k48_cap16",
+                                          "k64_cap8"])
 def test_fused_layer(name):
     import sparse_attention_feed_amd as S
     w = get(name)
