@@ -353,10 +353,12 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
 // Barrier-free tile ring for the selected branch.  R LDS buffers; tile t lives in buffer t % R.
 // Every wave stages its own share of each tile (the chunks its threads own) and then adds 1 to
 // ready[t % R]; it computes tile t once ready shows all WAVES shares of that use of the buffer, and
-// adds 1 to done[t % R] after its last read.  A wave stages tile t + R - 1 into the buffer of tile
-// t - 1 only after done shows that every wave has finished tile t - 1.  Each wait names a strictly
-// earlier event of other waves, so the ring cannot deadlock; it lets a wave run up to R - 2 tiles
-// ahead of the slowest, instead of meeting at a barrier after every tile (the work per wave and
+// adds 1 to done[t % R] after its last read.  A wave stages tile t + R - 2 into the buffer of tile
+// t - 2 only after done shows that every wave has finished tile t - 2.  Both counts are read early
+// (the next tile's ready count and tile t - 2's done count before tile t's compute), so a wait that
+// is already satisfied costs no LDS round trip of its own; only a short count is read again.  Each
+// wait names a strictly earlier event of other waves, so the ring cannot deadlock; it lets a wave
+// run ahead of the slowest instead of meeting at a barrier after every tile (the work per wave and
 // tile varies with how many of its tokens selected the tile's block).  Waits are bounded: if a
 // count ever failed to arrive, the wave marks the workgroup broken and stops waiting; the kernel
 // still ends and the branch's output is NaN.
@@ -381,7 +383,7 @@ __device__ __forceinline__ void ring_signal(int* ctr) {
 }
 
 // Buffers 0 and 1 of the ring are the workgroup's two staging tiles at the start of LDS; buffers 2
-// and 3 sit at byte offset hi_off.  The address is formed from the LDS base by integer offsets so
+// and up sit one after another from byte offset hi_off.  The address is formed from the LDS base by integer offsets so
 // that every access stays an LDS (ds_*) access.
 template <typename T> struct RingBufs {
   unsigned char* lds;
@@ -396,20 +398,28 @@ template <typename T, int NT, int TPW, int R, class Src, class Part>
 __device__ __forceinline__ void run_tiles_ring(const RingBufs<T>& rb, int* ready, int* done, int* broken,
                                                int spin_limit, int stall, const Src& src, int ntiles,
                                                const Part& part, TokState (&st)[TPW], const QF<T> (&qf)[TPW]) {
-  static_assert(R == 4, "the ring has four buffers");
+  static_assert(R >= 4, "the ring needs four buffers or more");
   constexpr int WAVES = NT / 64;
   Stager<T, NT> sg;
   __builtin_amdgcn_s_waitcnt(0);   // as in run_tiles: no earlier load stays in flight into the loop
-  for (int t = 0; t < R - 1 && t < ntiles; ++t) {
+  for (int t = 0; t < R - 2 && t < ntiles; ++t) {
     sg.load(src.kptr(t), src.vptr(t), src.stride, src.nk(t));
     sg.store(rb[t]);
     ring_signal(&ready[t]);
   }
+  int rdy = -1;                                   // ready count of tile u's buffer read early
   for (int u = 0; u < ntiles; ++u) {
-    const int ahead = u + R - 1;                  // the tile this iteration stages
-    if (ahead < ntiles) sg.load(src.kptr(ahead), src.vptr(ahead), src.stride, src.nk(ahead));
+    const int x = u + R - 2;                      // the tile this iteration stages
+    if (x < ntiles) sg.load(src.kptr(x), src.vptr(x), src.stride, src.nk(x));
     const int bu = u % R;
-    ring_wait(&ready[bu], WAVES * (u / R + 1) + stall, broken, spin_limit);
+    const int need = WAVES * (u / R + 1) + stall;
+    if (rdy < need) ring_wait(&ready[bu], need, broken, spin_limit);
+    else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const int rdy_next =
+        u + 1 < ntiles ? __hip_atomic_load(&ready[(u + 1) % R], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0;
+    const int dn = (x < ntiles && u >= 2)
+                       ? __hip_atomic_load(&done[(u - 2) % R], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                       : 0;
     const TileBuf<T>& b = rb[bu];
     const int nk = src.nk(u);
     const uint32_t pm = part.wave_mask(u);
@@ -421,12 +431,17 @@ __device__ __forceinline__ void run_tiles_ring(const RingBufs<T>& rb, int* ready
       tile_masked<T, TPW>(st, qf, pm, kf, vf, cm, nk == TILE);
     }
     ring_signal(&done[bu]);
-    if (ahead < ntiles) {
-      const int bp = (u + R - 1) % R;              // == (u - 1) % R, the buffer of tile u - 1
-      if (u >= 1) ring_wait(&done[bp], WAVES * ((u - 1) / R + 1), broken, spin_limit);
+    if (x < ntiles) {
+      const int bp = x % R;                        // == (u - 2) % R, the buffer of tile u - 2
+      if (u >= 2) {
+        const int fin = WAVES * ((u - 2) / R + 1);
+        if (__builtin_amdgcn_readfirstlane(dn) < fin) ring_wait(&done[bp], fin, broken, spin_limit);
+        else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      }
       sg.store(rb[bp]);
       ring_signal(&ready[bp]);
     }
+    rdy = __builtin_amdgcn_readfirstlane(rdy_next);
   }
   __syncthreads();
   if (*broken) {
@@ -510,6 +525,10 @@ __device__ int block_exclusive_scan(int x, int* scratch /* NT/64 + 1 ints */) {
 // bf16 kernel within 256 VGPRs per lane.
 template <typename T> struct OutInLds { static constexpr bool value = sizeof(T) == 2; };
 
+// Tile buffers of the selected branch's ring.  The bf16 ring's extra buffers fit beside the union
+// tables inside the region the running gated sum takes later, so they cost no LDS.
+template <typename T> struct RingSize { static constexpr int value = sizeof(T) == 2 ? 8 : 4; };
+
 template <typename T, int WAVES, int TPW>
 __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   constexpr int NT = WAVES * 64;
@@ -591,14 +610,15 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   // ---- selected branch: union of the block's routing rows, streamed once ----
   if (a.branches & 2) {
     // byte offsets from `extra` (kept as offsets so the pointers stay LDS pointers): bitmap,
-    // per-word prefix, union list, scan scratch, per-wave token masks, ring buffers 2 and 3, and
-    // the ring counters ready[4], done[4], broken
+    // per-word prefix, union list, scan scratch, per-wave token masks, ring buffers 2 .. R-1, and
+    // the ring counters ready[R], done[R], broken
+    constexpr int R = RingSize<T>::value;
     const int off_wpre = a.n_words * 4;
     const int off_ulist = off_wpre + a.n_words * 4;
     const int off_scratch = off_ulist + a.u_cap * 4;
     const int off_umask = (off_scratch + (NT / 64 + 1) * 4 + 7) & ~7;
     const int off_ring = (off_umask + a.u_cap * 8 + 15) & ~15;
-    const int off_ctr = off_ring + 2 * (int)sizeof(TileBuf<T>);
+    const int off_ctr = off_ring + (R - 2) * (int)sizeof(TileBuf<T>);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(extra);
     int* wpre = reinterpret_cast<int*>(extra + off_wpre);
     int* ulist = reinterpret_cast<int*>(extra + off_ulist);
@@ -608,7 +628,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     const int grp = a.sel_groups == 1 ? 0 : j;
     const int kk = a.top_k;
     for (int i = threadIdx.x; i < a.n_words; i += NT) bitmap[i] = 0u;
-    if (threadIdx.x < 9) ring_ctr[threadIdx.x] = 0;
+    if (threadIdx.x < 2 * R + 1) ring_ctr[threadIdx.x] = 0;
     __syncthreads();
     for (int e = threadIdx.x; e < cnt * kk; e += NT) {
       const int t = e / kk, s = e % kk;
@@ -659,7 +679,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     src.ulist = ulist;
     UnionPart<WAVES, TPW> part{umask, w};
     const RingBufs<T> rb{smem, 2 * (int)sizeof(TileBuf<T>) + off_ring};
-    run_tiles_ring<T, NT, TPW, 4>(rb, ring_ctr, ring_ctr + 4, ring_ctr + 8, a.ring_spins, a.ring_stall, src, n_union,
+    run_tiles_ring<T, NT, TPW, R>(rb, ring_ctr, ring_ctr + R, ring_ctr + 2 * R, a.ring_spins, a.ring_stall, src, n_union,
                                   part, st, qf);   // ends with a barrier
     finish_all((a.branches & 1) ? 1 : 0);
   }
@@ -794,9 +814,10 @@ template <typename T>
 size_t attn_lds_t(const AttnArgs& a) {
   constexpr int NT = Shape<T>::WAVES * 64;
   size_t extra = 0;
-  if (a.branches & 2)   // union tables, two more ring buffers, ring counters (with alignment slack)
+  constexpr int R = RingSize<T>::value;
+  if (a.branches & 2)   // union tables, R - 2 more ring buffers, ring counters (with alignment slack)
     extra = (size_t)a.n_words * 8 + (size_t)a.u_cap * 4 + (NT / 64 + 1) * 4 + 8 + (size_t)a.u_cap * 8 + 16 +
-            2 * sizeof(TileBuf<T>) + 9 * sizeof(int);
+            (R - 2) * sizeof(TileBuf<T>) + (2 * R + 1) * sizeof(int);
   if (OutInLds<T>::value && __builtin_popcount(a.branches) > 1) {
     const size_t out_bytes = (size_t)64 * GRP * HD * sizeof(float);
     if (out_bytes > extra) extra = out_bytes;
