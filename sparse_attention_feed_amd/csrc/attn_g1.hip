@@ -320,9 +320,11 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
 // Each wave scores CG column groups (16 query rows each) against a staged 64-key tile with MFMA.
 // Lane (r, g) sees a quarter of every row's keys and keeps a sorted list of its best K.  Candidates
 // are filtered first against a row-level bound of the row's current k-th best (the lists of the
-// four lanes of a row give one): after the first tiles almost no score passes, so the sorted
-// insertions run for few lanes and few steps.  The tile's scores go to wave-private LDS so that
-// each lane can walk only its own candidates.  Ranking key: (score, then smaller blk_key) packed
+// four lanes of a row give one): after the first tiles few scores pass.  The tile's scores go to
+// wave-private LDS so that each lane can walk only its own candidates into a short queue; the
+// sorted insertions run for the whole wave at once whenever some lane's queue is full (a pass in
+// one lane alone would otherwise cost the wave a whole insertion), and the row bound is refreshed
+// after each such step.  Ranking key: (score, then smaller blk_key) packed
 // into 64 bits so that one unsigned compare orders both.
 
 constexpr int RW = 8;       // waves per workgroup
@@ -408,13 +410,33 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
   TopList<K> lst[CG];
   float thr[CG];
   int row_of[CG];
+  // candidates that passed the row bound but are not yet ranked: QN per lane and column group
+  // (one for the 64-long lists, whose registers leave no room for a queue)
+  constexpr int QN = K <= 32 ? 4 : 1;
+  uint64_t qk[CG][QN];
+  int qi[CG][QN];
+  int qn[CG];
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
     row_of[c] = rg * rows_per_wg + (w * CG + c) * 16 + r;
     q[c] = load_q_row(qc + ((size_t)row_of[c] * a.n_qh + h) * DG, row_of[c] < a.n_blk);
     toplist_init(lst[c]);
     thr[c] = -INFINITY;
+    qn[c] = 0;
+#pragma unroll
+    for (int x = 0; x < QN; ++x) {
+      qk[c][x] = 0ull;
+      qi[c][x] = -1;
+    }
   }
+  // rank the queued candidates of column group c (every lane, so the row bound can be shared)
+  auto flush = [&](int c) {
+#pragma unroll
+    for (int x = 0; x < QN; ++x)
+      if (x < qn[c]) toplist_insert(lst[c], qk[c][x], qi[c][x]);
+    qn[c] = 0;
+    thr[c] = row_threshold(lst[c]);
+  };
   const int ntiles = (a.n_blk + KT - 1) / KT;
   // staging: thread t copies 16 bytes (key t / 8, piece t % 8) of the K tile; threads < 64 the keys
   const int s_key = tid >> 3, s_part = tid & 7;
@@ -462,19 +484,32 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
       if (__builtin_amdgcn_ballot_w64(m != 0u) == 0ull) continue;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) sc_lds[w][kt][l] = s[kt];
-      while (m != 0u) {
-        const int j = __builtin_ctz(m);
-        m &= m - 1u;
-        const float v = reinterpret_cast<const float*>(&sc_lds[w][j >> 2][l])[j & 3];
-        const int key = 16 * (j >> 2) + 4 * g + (j & 3);
-        toplist_insert(lst[c], rank_key(v, keys_lds[cur][key]), u * KT + key);
+      // one candidate per lane per round into its queue; whenever some lane's queue is full, the
+      // whole wave ranks its queues (so the sorted insertions run in few, shared steps)
+      while (__builtin_amdgcn_ballot_w64(m != 0u) != 0ull) {
+        if (m != 0u) {
+          const int j = __builtin_ctz(m);
+          m &= m - 1u;
+          const float v = reinterpret_cast<const float*>(&sc_lds[w][j >> 2][l])[j & 3];
+          const int key = 16 * (j >> 2) + 4 * g + (j & 3);
+          const uint64_t ck = rank_key(v, keys_lds[cur][key]);
+          const int ci = u * KT + key;
+#pragma unroll
+          for (int x = 0; x < QN; ++x) {
+            qk[c][x] = qn[c] == x ? ck : qk[c][x];
+            qi[c][x] = qn[c] == x ? ci : qi[c][x];
+          }
+          ++qn[c];
+        }
+        if (__builtin_amdgcn_ballot_w64(qn[c] == QN) != 0ull) flush(c);
       }
-      thr[c] = row_threshold(lst[c]);
     }
     // every wave finished tile u - 1 (the previous barrier), so buffer cur ^ 1 is free
     if (u + 1 < ntiles) store(cur ^ 1, kv, bkey);
     __syncthreads();
   }
+#pragma unroll
+  for (int c = 0; c < CG; ++c) flush(c);
   // merge the four lane lists of each row: top_k rounds of arg-best over the list heads
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
