@@ -50,19 +50,37 @@ __global__ __launch_bounds__(64) void activity_kernel(const float* __restrict__ 
   }
   const size_t sy = (size_t)G, sz = (size_t)G * G;
   float mn = INFINITY, mx = -INFINITY, mabs = INFINITY;
-  for (int c = 0; c < 4; ++c)
-    for (int b = 0; b < 4; ++b)
+  if (gx[0] == gx[3] && gy[0] == gy[3] && gz[0] == gz[3]) {
+    // all 64 sub-samples in one lattice cell (the usual case when the lattice is no finer than the
+    // voxels): its eight corners once, the same operations on the same values as below
+    const float* p = sdf + gz[0] * sz + gy[0] * sy + gx[0];
+    const float c000 = p[0], c001 = p[1], c010 = p[sy], c011 = p[sy + 1];
+    const float c100 = p[sz], c101 = p[sz + 1], c110 = p[sz + sy], c111 = p[sz + sy + 1];
+    for (int c = 0; c < 4; ++c)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float* p = sdf + gz[c] * sz + gy[b] * sy + gx[a];
-        const float s = lerp_rn(lerp_rn(lerp_rn(p[0], p[1], fx[a]), lerp_rn(p[sy], p[sy + 1], fx[a]), fy[b]),
-                                lerp_rn(lerp_rn(p[sz], p[sz + 1], fx[a]), lerp_rn(p[sz + sy], p[sz + sy + 1], fx[a]),
-                                        fy[b]),
-                                fz[c]);
-        mn = fminf(mn, s);
-        mx = fmaxf(mx, s);
-        mabs = fminf(mabs, fabsf(s));
-      }
+        for (int a = 0; a < 4; ++a) {
+          const float s = lerp_rn(lerp_rn(lerp_rn(c000, c001, fx[a]), lerp_rn(c010, c011, fx[a]), fy[b]),
+                                  lerp_rn(lerp_rn(c100, c101, fx[a]), lerp_rn(c110, c111, fx[a]), fy[b]), fz[c]);
+          mn = fminf(mn, s);
+          mx = fmaxf(mx, s);
+          mabs = fminf(mabs, fabsf(s));
+        }
+  } else {
+    for (int c = 0; c < 4; ++c)
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float* p = sdf + gz[c] * sz + gy[b] * sy + gx[a];
+          const float s = lerp_rn(lerp_rn(lerp_rn(p[0], p[1], fx[a]), lerp_rn(p[sy], p[sy + 1], fx[a]), fy[b]),
+                                  lerp_rn(lerp_rn(p[sz], p[sz + 1], fx[a]), lerp_rn(p[sz + sy], p[sz + sy + 1], fx[a]),
+                                          fy[b]),
+                                  fz[c]);
+          mn = fminf(mn, s);
+          mx = fmaxf(mx, s);
+          mabs = fminf(mabs, fabsf(s));
+        }
+  }
   const bool active = mabs <= tau || mn * mx <= 0.f;
   const unsigned long long bits = __builtin_amdgcn_ballot_w64(active);
   if (l == 0) cell_mask[mc] = bits;
