@@ -164,9 +164,9 @@ def setup_geometric(w, S, torch, dev):
         n_vol = int((w.blk_type == 0).sum())
         vsel = torch.empty((w.n_slots, w.top_k), dtype=torch.int32, device=dev)
         vcent = torch.empty((w.n_blk, 4), dtype=torch.int32, device=dev)
-        vbox = torch.empty((w.n_blk, 8), dtype=torch.int32, device=dev)
+        vgeom = torch.empty(w.n_blk * 8 + w.n_slots * 2, dtype=torch.int32, device=dev)
         fns["route_views"] = lambda: S.route_geometric_views(L, pts, w.top_k, n_vol, vp_d, cb_d, cell_size=8, radius=1,
-                                                             sel=vsel, centroids=vcent, boxes=vbox, want_d2=False)
+                                                             sel=vsel, centroids=vcent, geom=vgeom, want_d2=False)
     # the volume block table from the workload's SDF sampled on a (side + 1)^3 lattice
     if "tau" in w.meta:
         side = int(w.meta["vol_side"])

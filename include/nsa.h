@@ -159,15 +159,16 @@ nsa_status nsa_route_geometric(const nsa_layout* layout, const float* pts, int32
  * nsa_route_geometric; every valid slot's row is written (-1 / 0xFFFFFFFF past the candidates).
  *   view_proj [n_views][2][4] float32, cell_blk [n_views][n_cell][n_cell] int32 (device); every
  *   entry >= 0 names a block outside [0, n_vol_blk), and a block appears at most once;
- *   centroids [n_blk][4] and boxes [n_blk][8] int32 are workspaces (boxes: each block's lattice
- *   bounding box, used to skip candidates that cannot reach a token's current top k).
+ *   centroids [n_blk][4] and geom [n_blk * 8 + S * 2] int32 are workspaces (geom: each block's
+ *   lattice bounding box, used to skip candidates that cannot reach a token's current top k, then
+ *   every slot's lattice point).
  * 0 <= n_vol_blk <= n_blk, n_views >= 0 (0: volume blocks only), 1 <= n_cell <= 4096, cell_size
  * a power of two <= 1024, 0 <= radius <= 16, 1 <= top_k <= 64 (NSA_ERR_INVALID otherwise).
  */
 nsa_status nsa_route_geometric_views(const nsa_layout* layout, const float* pts, int32_t top_k,
                                      int32_t n_vol_blk, int32_t n_views, const float* view_proj,
                                      const int32_t* cell_blk, int32_t n_cell, int32_t cell_size,
-                                     int32_t radius, int32_t* centroids, int32_t* boxes,
+                                     int32_t radius, int32_t* centroids, int32_t* geom,
                                      int32_t* sel, uint32_t* sel_d2, hipStream_t stream);
 
 /*

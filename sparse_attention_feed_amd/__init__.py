@@ -214,7 +214,7 @@ def route_geometric(layout: BlockLayout, pts, top_k, sel=None, sel_d2=None, cent
 
 
 def route_geometric_views(layout: BlockLayout, pts, top_k, n_vol_blk, view_proj, cell_blk, cell_size=8,
-                          radius=1, sel=None, sel_d2=None, centroids=None, boxes=None, want_d2=True):
+                          radius=1, sel=None, sel_d2=None, centroids=None, geom=None, want_d2=True):
     """Top-k blocks per token: volume blocks [0, n_vol_blk) by centroid distance, image blocks found
     by projecting the token into every view (view_proj [V, 2, 4], cell_blk [V, n_cell, n_cell]) and
     ranked by their nearest member; returns (sel, sel_d2, centroids)."""
@@ -226,15 +226,15 @@ def route_geometric_views(layout: BlockLayout, pts, top_k, n_vol_blk, view_proj,
         sel_d2 = torch.empty((S, top_k), dtype=torch.int32, device=dev)
     if centroids is None:
         centroids = torch.empty((layout.n_blk, 4), dtype=torch.int32, device=dev)
-    if boxes is None:
-        boxes = torch.empty((layout.n_blk, 8), dtype=torch.int32, device=dev)
+    if geom is None:
+        geom = torch.empty(layout.n_blk * 8 + S * 2, dtype=torch.int32, device=dev)
     n_views = int(view_proj.shape[0])
     n_cell = int(cell_blk.shape[1])
     if n_views and (tuple(view_proj.shape) != (n_views, 2, 4) or tuple(cell_blk.shape) != (n_views, n_cell, n_cell)):
         raise ValueError("view_proj must be [V, 2, 4] and cell_blk [V, n_cell, n_cell]")
     _check(lib.nsa_route_geometric_views(layout.c, _ptr(pts), int(top_k), int(n_vol_blk), n_views,
                                          _ptr(view_proj), _ptr(cell_blk), n_cell, int(cell_size), int(radius),
-                                         _ptr(centroids), _ptr(boxes), _ptr(sel),
+                                         _ptr(centroids), _ptr(geom), _ptr(sel),
                                          _ptr(sel_d2) if want_d2 else None, _stream()))
     return sel, sel_d2, centroids
 

@@ -159,7 +159,7 @@ nsa_status nsa_route_geometric(const nsa_layout* L, const float* pts, int32_t to
 nsa_status nsa_route_geometric_views(const nsa_layout* L, const float* pts, int32_t top_k, int32_t n_vol_blk,
                                      int32_t n_views, const float* view_proj, const int32_t* cell_blk,
                                      int32_t n_cell, int32_t cell_size, int32_t radius, int32_t* centroids,
-                                     int32_t* boxes, int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
+                                     int32_t* geom, int32_t* sel, uint32_t* sel_d2, hipStream_t stream) {
   const char* fn = "nsa_route_geometric_views";
   nsa_status st = check_layout(L, fn);
   if (st != NSA_OK) return st;
@@ -169,8 +169,8 @@ nsa_status nsa_route_geometric_views(const nsa_layout* L, const float* pts, int3
   if (n_vol_blk < 0 || n_vol_blk > L->n_blk) return fail(NSA_ERR_INVALID, "%s: n_vol_blk must be in [0, n_blk]", fn);
   if (n_views < 0) return fail(NSA_ERR_INVALID, "%s: n_views must be >= 0", fn);
   if (n_views > 0) {
-    if (view_proj == nullptr || cell_blk == nullptr || boxes == nullptr)
-      return fail(NSA_ERR_INVALID, "%s: view_proj, cell_blk and boxes must be non-NULL with views", fn);
+    if (view_proj == nullptr || cell_blk == nullptr || geom == nullptr)
+      return fail(NSA_ERR_INVALID, "%s: view_proj, cell_blk and geom must be non-NULL with views", fn);
     if (n_cell < 1 || n_cell > 4096) return fail(NSA_ERR_INVALID, "%s: n_cell must be in 1..4096", fn);
     if (cell_size < 1 || cell_size > 1024 || (cell_size & (cell_size - 1)) != 0)
       return fail(NSA_ERR_INVALID, "%s: cell_size must be a power of two in 1..1024", fn);
@@ -193,7 +193,8 @@ nsa_status nsa_route_geometric_views(const nsa_layout* L, const float* pts, int3
   a.top_k = top_k;
   a.view_proj = view_proj;
   a.cell_blk = cell_blk;
-  a.boxes = boxes;
+  a.boxes = geom;
+  a.lat = geom != nullptr ? geom + (size_t)8 * L->n_blk : nullptr;
   a.n_views = n_views;
   a.n_cell = n_cell;
   a.cell_shift = __builtin_ctz((unsigned)cell_size);

@@ -53,6 +53,7 @@ struct RouteArgs {
   const float* view_proj;   // [n_views][2][4]
   const int32_t* cell_blk;  // [n_views][n_cell][n_cell]
   int32_t* boxes;           // [n_blk][8] workspace: lattice box (lo xyz, -, hi xyz, -) of each block
+  int32_t* lat;             // [S][2] workspace: lattice point (x | y << 16, z) of every valid slot
   int n_views, n_cell, cell_shift, radius;
 };
 

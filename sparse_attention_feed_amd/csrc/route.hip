@@ -19,10 +19,11 @@ namespace {
 __device__ __forceinline__ int lattice(float p) { return (int)rintf(4096.0f * p) + 4096; }
 
 // One wave per block: integer centroid of the block's valid points plus its key.
-// With `boxes`, also the lattice bounding box of the block's points.
+// With `boxes`, also the lattice bounding box of the block's points and (`lat`) each point's packed
+// lattice coordinates.
 __global__ __launch_bounds__(64) void centroid_kernel(const float* __restrict__ pts, const int32_t* __restrict__ blk_cnt,
                                                       const uint32_t* __restrict__ blk_key, int32_t* __restrict__ cent,
-                                                      int32_t* __restrict__ boxes, int cap) {
+                                                      int32_t* __restrict__ boxes, int32_t* __restrict__ lat, int cap) {
   const int b = blockIdx.x, l = threadIdx.x;
   const int cnt = blk_cnt[b];
   int sx = 0, sy = 0, sz = 0;
@@ -30,6 +31,7 @@ __global__ __launch_bounds__(64) void centroid_kernel(const float* __restrict__ 
   for (int t = l; t < cnt; t += 64) {
     const float* p = pts + (size_t)(b * cap + t) * 3;
     const int x = lattice(p[0]), y = lattice(p[1]), z = lattice(p[2]);
+    if (lat != nullptr) reinterpret_cast<int2*>(lat)[b * cap + t] = make_int2(x | (y << 16), z);
     sx += x;
     sy += y;
     sz += z;
@@ -290,11 +292,8 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
           if (box_dmin(ux, uy, uz, lo3, hi3) > bd[K - 1]) continue;
           uint32_t best = 0xFFFFFFFFu;
           const int mc = a.blk_cnt[bb];
-          const float* mp = a.pts + (size_t)bb * a.cap * 3;
-          for (int t = 0; t < mc; ++t) {
-            const int dx = lattice(mp[3 * t]) - ux, dy = lattice(mp[3 * t + 1]) - uy, dz = lattice(mp[3 * t + 2]) - uz;
-            best = min(best, (uint32_t)(dx * dx + dy * dy + dz * dz));
-          }
+          const int2* mp = reinterpret_cast<const int2*>(a.lat) + (size_t)bb * a.cap;
+          for (int t = 0; t < mc; ++t) best = min(best, dist2(uxy, uz, mp[t]));
           topk_insert<K>(bd, bk, bi, best, a.blk_key[bb], bb);
         }
     }
@@ -466,7 +465,7 @@ hipError_t launch_score_t(const ScoreRouteArgs& a, hipStream_t s) {
 
 hipError_t launch_route_geometric(const RouteArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(centroid_kernel, dim3(a.n_blk), dim3(64), 0, s, a.pts, a.blk_cnt, a.blk_key, a.cent,
-                     a.n_views > 0 ? a.boxes : nullptr, a.cap);
+                     a.n_views > 0 ? a.boxes : nullptr, a.n_views > 0 ? a.lat : nullptr, a.cap);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.top_k <= 4) return launch_route_k<4>(a, s);

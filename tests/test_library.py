@@ -123,21 +123,21 @@ def test_route_range_validation(S, monkeypatch):
 def test_route_views_validation(S, monkeypatch):
     L = layout(S)
     r = S.lib.nsa_route_geometric_views
-    ok = dict(pts=FAKE, k=4, nv=2, views=3, proj=FAKE, cells=FAKE, n_cell=4, cell=8, radius=1, cent=FAKE, boxes=FAKE,
+    ok = dict(pts=FAKE, k=4, nv=2, views=3, proj=FAKE, cells=FAKE, n_cell=4, cell=8, radius=1, cent=FAKE, geom=FAKE,
               sel=FAKE)
 
     def call(**kw):
         a = dict(ok)
         a.update(kw)
         return r(ctypes.byref(L), a["pts"], a["k"], a["nv"], a["views"], a["proj"], a["cells"], a["n_cell"], a["cell"],
-                 a["radius"], a["cent"], a["boxes"], a["sel"], None, None)
-    for kw in (dict(nv=5), dict(nv=-1), dict(views=-1), dict(proj=None), dict(cells=None), dict(boxes=None),
+                 a["radius"], a["cent"], a["geom"], a["sel"], None, None)
+    for kw in (dict(nv=5), dict(nv=-1), dict(views=-1), dict(proj=None), dict(cells=None), dict(geom=None),
                dict(n_cell=0), dict(cell=6), dict(cell=2048), dict(radius=17), dict(k=0), dict(sel=None)):
         assert call(**kw) == -1, kw
     assert S.lib.nsa_last_error().decode().startswith("nsa_route_geometric_views")
     monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
     assert call() == -3
-    assert call(views=0, proj=None, cells=None, boxes=None) == -3      # no views: volume blocks only
+    assert call(views=0, proj=None, cells=None, geom=None) == -3       # no views: volume blocks only
 
 
 def test_attn_single_branch_needs_no_gate(S, monkeypatch):
