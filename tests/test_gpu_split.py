@@ -138,3 +138,18 @@ def test_split_layer_single_type(nx):
     torch.cuda.synchronize()
     ref = O.nsa_split_forward(w, n, g7)
     assert max_err(host(out), ref) <= tol(w)
+
+
+def test_attn_range_local_outside_key_range_is_zero():
+    """The local branch over a key range that excludes the query's own block has no keys: 0."""
+    import sparse_attention_feed_amd as S
+    w = wl("large_small")
+    d = to_dev(w)
+    nx, _ = ranges(w)
+    say("attn range, local branch outside the key range")
+    out = torch.full_like(d["q"], 7.0)
+    S.attn_fwd(d["layout"], S.BR_LOC, d["q"], d["k"], d["v"], out=out, q_blocks=(0, nx), kv_blocks=(nx, w.n_blk))
+    torch.cuda.synchronize()
+    o = host(out)
+    assert np.all(o[:nx * w.blk_cap] == 0.0)
+    assert np.all(o[nx * w.blk_cap:] == 7.0)
