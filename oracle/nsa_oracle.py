@@ -329,7 +329,7 @@ def route_scores(q_rows, k_cmp, blk_key, scale, top_k, lse=None, row_valid=None)
 # A4-A6: the three attention branches
 # ----------------------------------------------------------------------------------------------
 
-def attn_branch(branch, q, k, v, blk_cnt, cap, scale, sel=None, q_gran="token", rows=None):
+def attn_branch(branch, q, k, v, blk_cnt, cap, scale, sel=None, q_gran="token", rows=None, forced=None):
     """One NSA branch for the query rows `rows` (storage slots; default all).
 
     branch CMP ([LSRM-cn] compressed branch; [Speed3R] compression branch): keys/values are the
@@ -338,7 +338,9 @@ def attn_branch(branch, q, k, v, blk_cnt, cap, scale, sel=None, q_gran="token", 
       and its output is given to each valid token of block b.
     branch LOC ([LSRM-cn] window attention): the valid tokens of the query's own block.
     branch SEL ([LSRM-cn] selected blocks; [Speed3R] selection branch): the valid tokens of the
-      blocks listed in sel (a set; -1 entries skipped).  sel is [S, top_k] (one list per token,
+      blocks listed in sel (a set; -1 entries skipped), together with the blocks of the range
+      forced = (lo, hi) when given ([Speed3R] 2.2, VGGT variant: the reference frame is always
+      attended).  sel is [S, top_k] (one list per token,
       shared by all heads), [S, Hkv, top_k] (one list per token and KV group), or with q_gran
       'block' [n_blk, top_k] / [n_blk, Hkv, top_k] (one list per query block).
     Returns o [len(rows), Hq, D] and lse [len(rows), Hq] (padding rows: 0 and -inf).
@@ -371,13 +373,14 @@ def attn_branch(branch, q, k, v, blk_cnt, cap, scale, sel=None, q_gran="token", 
         elif branch == SEL:
             lst = sel[b] if q_gran == "block" else sel[r]
             lst = np.asarray(lst)
+            always = set(range(forced[0], forced[1])) if forced is not None else set()
             if lst.ndim == 1:
-                blocks = sorted(set(int(x) for x in lst if x >= 0))
+                blocks = sorted(set(int(x) for x in lst if x >= 0) | always)
                 ks = np.concatenate([block_slots(blk_cnt, cap, x) for x in blocks]) if blocks else np.zeros(0, int)
                 o[i], lse[i] = attend(q[r], k[ks], v[ks], scale)
             else:
                 for j in range(Hkv):
-                    blocks = sorted(set(int(x) for x in lst[j] if x >= 0))
+                    blocks = sorted(set(int(x) for x in lst[j] if x >= 0) | always)
                     ks = np.concatenate([block_slots(blk_cnt, cap, x) for x in blocks]) if blocks else np.zeros(0, int)
                     hs = slice(j * G, (j + 1) * G)
                     oj, lj = attend(q[r, hs], k[ks][:, j:j + 1], v[ks][:, j:j + 1], scale)
@@ -427,7 +430,7 @@ def dense_gated_xattn(q, k, v, n_x, gate_logits, scale, rows=None):
 # whole layer
 # ----------------------------------------------------------------------------------------------
 
-def nsa_forward(w, rows=None, return_parts=False):
+def nsa_forward(w, rows=None, return_parts=False, forced=None):
     """One NSA layer on a block-major workload `w` (see workloads.Workload):
     compress K and V (and Q for block-granular queries), route, run the branches listed in
     w.branches and combine them with the sigmoid gates (channel c = c-th listed branch).
@@ -467,7 +470,7 @@ def nsa_forward(w, rows=None, return_parts=False):
                 oc, lc = attn_branch(CMP, w.q, k_cmp, v_cmp, w.blk_cnt, cap, w.scale, rows=rows)
         elif br == SEL:
             oc, lc = attn_branch(SEL, w.q, w.k, w.v, w.blk_cnt, cap, w.scale, sel=sel,
-                                 q_gran=q_gran_sel, rows=rows)
+                                 q_gran=q_gran_sel, rows=rows, forced=forced)
         else:
             oc, lc = attn_branch(LOC, w.q, w.k, w.v, w.blk_cnt, cap, w.scale, rows=rows)
         parts["o_" + name] = oc

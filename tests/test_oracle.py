@@ -671,3 +671,45 @@ def test_views_image_query_finds_its_own_block():
                                       rows=rows)
     assert np.all(d2[:, 0] == 0)
     assert np.mean(sel[:, 0] == rows // 64) > 0.9
+
+
+# ---------------------------------------------------------------------------------------------
+# forced-include blocks in the selected branch (Speed3R, VGGT variant)
+# ---------------------------------------------------------------------------------------------
+
+def _s3_case():
+    w = W.custom_block_workload(61, [16, 4, 16, 1, 16, 4, 9, 16], 16, 4, 4, 8, "f32", 2, routing="scores",
+                                q_gran="block", branches=("cmp", "sel"))
+    rng = np.random.default_rng(62)
+    sel = rng.integers(-1, w.n_blk, size=(w.n_blk, w.n_kvh, w.top_k)).astype(np.int32)
+    return w, sel
+
+
+def test_forced_all_blocks_is_dense_attention():
+    """Forcing every block makes each query attend every valid token, whatever its routing row."""
+    w, sel = _s3_case()
+    o, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel, q_gran="block",
+                         forced=(0, w.n_blk))
+    vs = w.valid_slots()
+    np.testing.assert_allclose(o[vs], sdpa(w.q[vs], w.k[vs], w.v[vs], w.scale), rtol=0, atol=1e-12)
+
+
+def test_forced_range_adds_its_blocks_once():
+    """An empty forced range changes nothing; forcing blocks every routing row already lists changes
+    nothing either (a block counts once); forcing other blocks equals listing them explicitly."""
+    w, sel = _s3_case()
+    base, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel, q_gran="block")
+    empty, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel, q_gran="block",
+                             forced=(3, 3))
+    np.testing.assert_array_equal(empty, base)
+    sel2 = sel.copy()
+    sel2[:, :, 0] = 5
+    a, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel2, q_gran="block")
+    b, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel2, q_gran="block",
+                         forced=(5, 6))
+    np.testing.assert_array_equal(a, b)
+    wide = np.concatenate([sel, np.broadcast_to(np.array([1, 2], np.int32), sel.shape[:2] + (2,))], axis=2)
+    c, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=wide, q_gran="block")
+    f, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel, q_gran="block",
+                         forced=(1, 3))
+    np.testing.assert_allclose(f, c, rtol=0, atol=1e-13)

@@ -26,7 +26,7 @@ import numpy as np
 __all__ = [
     "Workload", "DenseWorkload", "make", "CONFIGS", "bf16_round", "morton2", "morton3",
     "permute_storage", "custom_block_workload", "resblock_weights", "sdf_lattice", "split_gates",
-    "view_cameras",
+    "view_cameras", "reference_view_blocks",
 ]
 
 
@@ -591,3 +591,14 @@ def view_cameras(w, cell: int = 8):
             cy |= ((code >> (2 * bit + 1)) & 1) << bit
         cell_blk[view, cy, cx] = b
     return proj.astype(np.float32), cell_blk
+
+
+def reference_view_blocks(w, view: int = 0):
+    """The storage block range (lo, hi) of one image view (by default the first, the reference
+    frame of a multi-view sequence); its blocks are contiguous in storage."""
+    keys = w.blk_key.astype(np.int64)
+    b = np.nonzero((w.blk_type == 1) & (((keys >> 20) & 0x7FF) == view))[0]
+    if b.shape[0] == 0:
+        return (0, 0)
+    assert np.all(np.diff(b) == 1), "a view's blocks are contiguous"
+    return (int(b[0]), int(b[-1]) + 1)
