@@ -178,11 +178,13 @@ def setup_geometric(w, S, torch, dev):
 
 
 def setup_speed3r(w, S, torch, dev):
+    import workloads as W
     dt = torch.bfloat16
     q, k, v, g = (torch.from_numpy(getattr(w, n)).to(dev).to(dt).contiguous() for n in ("q", "k", "v", "gates"))
     L = S.BlockLayout(torch.from_numpy(w.blk_cnt).to(dev), torch.from_numpy(w.blk_key.view(np.int32)).to(dev),
                       w.blk_cap, w.n_qh, w.n_kvh, w.head_dim)
     shp = (w.n_blk, w.n_kvh, w.head_dim)
+    fr = W.reference_view_blocks(w)
     ws = {n: torch.empty(shp, dtype=dt, device=dev) for n in ("q_cmp", "k_cmp", "v_cmp")}
     ws["sel"] = torch.empty((w.n_blk, w.n_kvh, w.top_k), dtype=torch.int32, device=dev)
     ws["out"] = torch.empty_like(q)
@@ -203,9 +205,15 @@ def setup_speed3r(w, S, torch, dev):
         per = 4 * w.head_dim
         sel = ws["sel"].cpu().numpy()                       # [n_blk, H, k]
         sel_cnt = np.where(sel >= 0, cnt[np.clip(sel, 0, None)], 0).sum(axis=2)   # [n_blk, H]
-        return {"cmp": per * w.n_blk * w.n_blk * w.n_qh,
-                "sel": per * int((sel_cnt * cnt[:, None]).sum()),
-                "route": per // 2 * w.n_blk * w.n_blk * w.n_qh}
+        out = {"cmp": per * w.n_blk * w.n_blk * w.n_qh,
+               "sel": per * int((sel_cnt * cnt[:, None]).sum()),
+               "route": per // 2 * w.n_blk * w.n_blk * w.n_qh}
+        if fr[1] > fr[0]:
+            # routed blocks outside the forced range (a routing row lists distinct blocks), plus the range
+            inside = (sel >= fr[0]) & (sel < fr[1])
+            keys = np.where((sel >= 0) & ~inside, cnt[np.clip(sel, 0, None)], 0).sum(axis=2) + cnt[fr[0]:fr[1]].sum()
+            out["sel_forced_ref_frame"] = per * int((keys * cnt[:, None]).sum())
+        return out
 
     def branch(bits):
         nb = bin(bits).count("1")
@@ -214,7 +222,13 @@ def setup_speed3r(w, S, torch, dev):
                                   sel=ws["sel"], top_k=w.top_k, sel_groups=w.n_kvh, gates=gg, out=ws["out"],
                                   q_gran=S.Q_BLOCK)
 
-    return stages, flops, {"cmp": branch(S.BR_CMP), "sel": branch(S.BR_SEL)}, "attn_fused"
+    fns = {"cmp": branch(S.BR_CMP), "sel": branch(S.BR_SEL)}
+    if fr[1] > fr[0]:
+        # the variant with a reference frame: its blocks are attended by every query
+        fns["sel_forced_ref_frame"] = lambda: S.attn_fwd(
+            L, S.BR_SEL, q, k, v, sel=ws["sel"], top_k=w.top_k, sel_groups=w.n_kvh, out=ws["out"],
+            q_gran=S.Q_BLOCK, forced=fr)
+    return stages, flops, fns, "attn_fused"
 
 
 def setup_dense(w, S, torch, dev):

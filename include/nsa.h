@@ -238,6 +238,23 @@ nsa_status nsa_attn_fwd(const nsa_layout* layout, nsa_dtype dtype, uint32_t bran
                         const void* gate_logits, void* o, float* lse, hipStream_t stream);
 
 /*
+ * nsa_attn_fwd with a forced block range in the selected branch (Speed3R page, section 2.2: in the
+ * variant for a model with a reference frame, that frame's tokens are always attended, whatever the
+ * routing picks).  SEL's key set for every row becomes the valid tokens of the union of the routed
+ * blocks and the blocks [forced_lo, forced_hi); a block both routed and forced counts once.  All
+ * other arguments, branches and gates are those of nsa_attn_fwd.  forced_lo == forced_hi is
+ * nsa_attn_fwd itself.  Supported for (D, G) = (64, 1) with NSA_Q_BLOCK (the score-routed path)
+ * and at most 192 forced blocks (NSA_ERR_UNSUPPORTED otherwise); 0 <= forced_lo <= forced_hi <=
+ * n_blk, and SEL among the branches when the range is non-empty (NSA_ERR_INVALID).
+ */
+nsa_status nsa_attn_fwd_forced(const nsa_layout* layout, nsa_dtype dtype, uint32_t branches,
+                               nsa_qgran q_gran, const void* q, const void* k, const void* v,
+                               const void* q_cmp, const void* k_cmp, const void* v_cmp,
+                               const int32_t* sel, int32_t top_k, int32_t sel_groups,
+                               int32_t forced_lo, int32_t forced_hi, const void* gate_logits,
+                               void* o, float* lse, hipStream_t stream);
+
+/*
  * nsa_attn_fwd over a block range, for the split self/cross form of stage 2 (LSRM pages, section
  * 方法: eq. o^x, o^y with each attention over one token type's blocks): only the query blocks
  * [q_blk_lo, q_blk_hi) are computed (their rows of o and lse are written, the others are left

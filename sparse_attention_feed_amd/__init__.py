@@ -23,6 +23,7 @@ BR_CMP, BR_SEL, BR_LOC = 1, 2, 4
 Q_TOKEN, Q_BLOCK = 0, 1
 EXPORTS = ("nsa_build_volume_blocks", "nsa_pool_blocks", "nsa_pool_blocks_resblock", "nsa_route_geometric",
            "nsa_route_geometric_range", "nsa_route_geometric_views", "nsa_attn_fwd_range", "nsa_route_scores_topk", "nsa_attn_fwd",
+           "nsa_attn_fwd_forced",
            "nsa_gate_combine", "dense_gated_xattn_fwd", "nsa_last_error")
 
 
@@ -55,6 +56,7 @@ def _load():
         "nsa_attn_fwd_range": [LP, I, U, I, I, I, I, P, P, P, P, P, P, I, I, P, I, P, P, P],
         "nsa_route_scores_topk": [LP, I, I, P, P, P, I, P, P],
         "nsa_attn_fwd": [LP, I, U, I, P, P, P, P, P, P, P, I, I, P, P, P, P],
+        "nsa_attn_fwd_forced": [LP, I, U, I, P, P, P, P, P, P, P, I, I, I, I, P, P, P, P],
         "nsa_gate_combine": [I, I, I, I, I, ctypes.POINTER(ctypes.c_void_p), P, P, P],
         "dense_gated_xattn_fwd": [I, I, I, I, I, I, F, P, P, P, P, P, P],
     }
@@ -252,13 +254,22 @@ def route_scores_topk(layout: BlockLayout, q, k_cmp, lse, top_k, q_gran=Q_TOKEN,
 
 def attn_fwd(layout: BlockLayout, branches, q, k=None, v=None, q_cmp=None, k_cmp=None, v_cmp=None,
              sel=None, top_k=0, sel_groups=1, gates=None, out=None, lse=None, q_gran=Q_TOKEN,
-             q_blocks=None, kv_blocks=None, gate_channel=0):
+             q_blocks=None, kv_blocks=None, gate_channel=0, forced=None):
     """NSA branches (bitmask of BR_CMP | BR_SEL | BR_LOC), gated and fused when gates is given.
     With q_blocks / kv_blocks = (lo, hi) (nsa_attn_fwd_range): only those query blocks are
     computed, against the key blocks kv_blocks; the named branches then read the gate channels
-    gate_channel, gate_channel + 1, ... of gates [S, Hq, C]."""
+    gate_channel, gate_channel + 1, ... of gates [S, Hq, C].  With forced = (lo, hi)
+    (nsa_attn_fwd_forced) the selected branch also attends every block of [lo, hi)."""
     if out is None:
         out = torch.empty_like(q)
+    if forced is not None:
+        if q_blocks is not None or kv_blocks is not None or gate_channel != 0:
+            raise ValueError("a forced block range does not combine with block ranges")
+        _check(lib.nsa_attn_fwd_forced(layout.c, _dtype(q), int(branches), int(q_gran), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(q_cmp), _ptr(k_cmp), _ptr(v_cmp), _ptr(sel), int(top_k),
+                                       int(sel_groups), int(forced[0]), int(forced[1]), _ptr(gates), _ptr(out),
+                                       _ptr(lse), _stream()))
+        return out
     if q_blocks is None and kv_blocks is None and gate_channel == 0:
         _check(lib.nsa_attn_fwd(layout.c, _dtype(q), int(branches), int(q_gran), _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(q_cmp), _ptr(k_cmp), _ptr(v_cmp), _ptr(sel), int(top_k), int(sel_groups),

@@ -266,11 +266,14 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
                            nsa_qgran q_gran, int32_t q_lo, int32_t q_hi, int32_t kv_lo, int32_t kv_hi,
                            const void* q, const void* k, const void* v, const void* q_cmp, const void* k_cmp,
                            const void* v_cmp, const int32_t* sel, int32_t top_k, int32_t sel_groups,
-                           const void* gate_logits, int32_t gate_stride, void* o, float* lse, hipStream_t stream) {
+                           const void* gate_logits, int32_t gate_stride, void* o, float* lse, int32_t f_lo,
+                           int32_t f_hi, hipStream_t stream) {
   nsa_status st = check_layout(L, fn);
   if (st != NSA_OK) return st;
-  if (!range_ok(q_lo, q_hi, L->n_blk) || !range_ok(kv_lo, kv_hi, L->n_blk))
+  if (!range_ok(q_lo, q_hi, L->n_blk) || !range_ok(kv_lo, kv_hi, L->n_blk) || !range_ok(f_lo, f_hi, L->n_blk))
     return fail(NSA_ERR_INVALID, "%s: block ranges must satisfy 0 <= lo <= hi <= n_blk", fn);
+  const bool forced = f_hi > f_lo;
+  if (forced && !(branches & NSA_BR_SEL)) return fail(NSA_ERR_INVALID, "%s: a forced block range needs SEL", fn);
   const bool whole = q_lo == 0 && q_hi == L->n_blk && kv_lo == 0 && kv_hi == L->n_blk;
   if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "%s: unknown dtype", fn);
   if (branches == 0 || (branches & ~7u) != 0) return fail(NSA_ERR_INVALID, "%s: branches must be a non-empty OR of NSA_BR_* bits", fn);
@@ -306,6 +309,8 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
                   "%s: with one query head per KV head the compiled kernels take head_dim 64, NSA_Q_BLOCK, "
                   "bf16, the CMP and SEL branches and blk_cap in {1, 2, 4, 8, 16}", fn);
     if (!whole) return fail(NSA_ERR_UNSUPPORTED, "%s: block ranges need the grouped-query kernel (head_dim 32)", fn);
+    if (f_hi - f_lo > nsa::kMaxForcedBlocks)
+      return fail(NSA_ERR_UNSUPPORTED, "%s: at most %d forced blocks", fn, nsa::kMaxForcedBlocks);
     NSA_FORCED_FAILURE(fn);
     nsa::G1Args g{};
     g.q = q;
@@ -331,8 +336,12 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
     g.ch_sel = (branches & NSA_BR_CMP) ? 1 : 0;
     g.scale = L->scale;
     g.branches = branches;
+    g.f_lo = f_lo;
+    g.f_hi = f_hi;
     return hip_status(nsa::launch_attn_g1(g, stream), fn);
   }
+  if (forced)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: a forced block range needs the one-head-per-KV-head kernels (head_dim 64)", fn);
   if (L->head_dim != 32 || L->n_qh / L->n_kvh != 16 || q_gran != NSA_Q_TOKEN)
     return fail(NSA_ERR_UNSUPPORTED, "%s: compiled for head_dim 32, 16 query heads per KV head, NSA_Q_TOKEN "
                                      "(or head_dim 64, one query head per KV head, NSA_Q_BLOCK)", fn);
@@ -385,7 +394,17 @@ nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches,
                         const void* gate_logits, void* o, float* lse, hipStream_t stream) {
   const int32_t n = L != nullptr ? L->n_blk : 0;
   return attn_fwd("nsa_attn_fwd", L, dtype, branches, q_gran, 0, n, 0, n, q, k, v, q_cmp, k_cmp, v_cmp, sel, top_k,
-                  sel_groups, gate_logits, 0, o, lse, stream);
+                  sel_groups, gate_logits, 0, o, lse, 0, 0, stream);
+}
+
+nsa_status nsa_attn_fwd_forced(const nsa_layout* L, nsa_dtype dtype, uint32_t branches, nsa_qgran q_gran,
+                               const void* q, const void* k, const void* v, const void* q_cmp, const void* k_cmp,
+                               const void* v_cmp, const int32_t* sel, int32_t top_k, int32_t sel_groups,
+                               int32_t forced_lo, int32_t forced_hi, const void* gate_logits, void* o, float* lse,
+                               hipStream_t stream) {
+  const int32_t n = L != nullptr ? L->n_blk : 0;
+  return attn_fwd("nsa_attn_fwd_forced", L, dtype, branches, q_gran, 0, n, 0, n, q, k, v, q_cmp, k_cmp, v_cmp, sel,
+                  top_k, sel_groups, gate_logits, 0, o, lse, forced_lo, forced_hi, stream);
 }
 
 nsa_status nsa_attn_fwd_range(const nsa_layout* L, nsa_dtype dtype, uint32_t branches, int32_t q_blk_lo,
@@ -394,7 +413,8 @@ nsa_status nsa_attn_fwd_range(const nsa_layout* L, nsa_dtype dtype, uint32_t bra
                               int32_t top_k, int32_t sel_groups, const void* gate_logits, int32_t gate_stride,
                               void* o, float* lse, hipStream_t stream) {
   return attn_fwd("nsa_attn_fwd_range", L, dtype, branches, NSA_Q_TOKEN, q_blk_lo, q_blk_hi, kv_blk_lo, kv_blk_hi,
-                  q, k, v, nullptr, k_cmp, v_cmp, sel, top_k, sel_groups, gate_logits, gate_stride, o, lse, stream);
+                  q, k, v, nullptr, k_cmp, v_cmp, sel, top_k, sel_groups, gate_logits, gate_stride, o, lse, 0, 0,
+                  stream);
 }
 
 nsa_status nsa_gate_combine(nsa_dtype dtype, int32_t n_rows, int32_t n_qh, int32_t head_dim, int32_t n_branch,

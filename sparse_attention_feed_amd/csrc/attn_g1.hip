@@ -546,9 +546,11 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
 // selected branch with block routing rows: one wave per (query block, head)
 // ---------------------------------------------------------------------------------------------
 
+// NF: capacity for forced blocks (0: the forced range is ignored, and the key list stays small)
+template <int NF>
 __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
   __shared__ TileG1 tb;
-  __shared__ int keys_lds[64 * 16 + KT];   // source rows of the selected valid tokens, packed
+  __shared__ int keys_lds[(64 + NF) * 16 + KT];   // source rows of the selected valid tokens, packed
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int b = wg / a.n_kvh, h = wg % a.n_kvh;
   const int l = lane_id(), r = l & 15, g = l >> 4;
@@ -563,20 +565,28 @@ __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
   const int grp = a.sel_groups == 1 ? 0 : h;
   const int32_t* srow = a.sel + ((size_t)b * a.sel_groups + grp) * a.top_k;
   const int sb = l < a.top_k ? srow[l] : -1;
-  bool keep = sb >= 0 && sb < a.n_blk;
+  const int nf = NF > 0 ? a.f_hi - a.f_lo : 0;
+  bool keep = sb >= 0 && sb < a.n_blk && !(sb >= a.f_lo && sb - a.f_lo < nf);   // forced blocks come below
   for (int y = 0; y < a.top_k; ++y) {
     const int sy = __builtin_amdgcn_readlane(sb, y);
     keep = keep && !(y < l && sy == sb);
   }
-  const int c = keep ? a.blk_cnt[sb] : 0;
-  int inc = c;
+  int total = 0;
+  // the routed blocks, then the forced range 64 blocks at a time, packed one after another
+  for (int f0 = -64; f0 < nf; f0 += 64) {
+    const int fb = a.f_lo + f0 + l;                          // forced block of this lane (f0 >= 0)
+    const int blk = f0 < 0 ? sb : fb;
+    const bool on = f0 < 0 ? keep : (f0 + l < nf);
+    const int c = on ? a.blk_cnt[blk] : 0;
+    int inc = c;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o, 64);
-    if (l >= o) inc += y;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (l >= o) inc += y;
+    }
+    for (int t = 0; t < c; ++t) keys_lds[total + inc - c + t] = blk * cap + t;
+    total += __builtin_amdgcn_readlane(inc, 63);
   }
-  const int total = __builtin_amdgcn_readlane(inc, 63);
-  for (int t = 0; t < c; ++t) keys_lds[inc - c + t] = sb * cap + t;
   const int ntiles = (total + KT - 1) / KT;
   for (int i = total + l; i < ntiles * KT; i += 64) keys_lds[i] = -1;
   __syncthreads();
@@ -645,7 +655,10 @@ hipError_t launch_attn_g1(const G1Args& a0, hipStream_t s) {
   }
   if (a.branches & 2) {
     a.accumulate = (a.branches & 1) ? 1 : 0;
-    hipLaunchKernelGGL(sel_g1_kernel, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+    if (a.f_hi > a.f_lo)
+      hipLaunchKernelGGL(sel_g1_kernel<kMaxForcedBlocks>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL(sel_g1_kernel<0>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;

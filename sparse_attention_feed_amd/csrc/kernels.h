@@ -86,7 +86,10 @@ struct G1Args {
   float scale;
   uint32_t branches;
   int accumulate;       // selected branch adds to o (the compressed branch wrote it first)
+  int f_lo, f_hi;       // blocks [f_lo, f_hi) are always in the selected branch's key set
 };
+
+constexpr int kMaxForcedBlocks = 192;   // longest forced range of the selected branch (blk_cap <= 16)
 hipError_t launch_route_g1(const G1Args& a, hipStream_t s);
 hipError_t launch_attn_g1(const G1Args& a, hipStream_t s);
 

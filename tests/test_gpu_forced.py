@@ -1,0 +1,127 @@
+"""GPU parity of the selected branch with a forced block range (Speed3R page, section 2.2: in the
+variant with a reference frame, that frame's tokens are attended by every query whatever the
+routing picks): the key set is the routed blocks together with the forced range, each block once,
+against the fp64 oracle (max-abs 2e-2 in bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import host, max_err, rounded, say, to_dev
+from test_gpu_speed3r import lse_bound
+
+pytestmark = pytest.mark.gpu
+_cache = {}
+
+
+def wl(name):
+    if name not in _cache:
+        _cache[name] = W.make(name)
+    return _cache[name]
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
+
+
+def pooled(w):
+    return [rounded(O.pool_blocks(x, w.blk_cnt, w.blk_cap), "bf16") for x in (w.q, w.k, w.v)]
+
+
+def test_reference_frame_selected_branch():
+    """speed3r_small: the oracle's routing rows plus the reference frame's 100 blocks, with lse."""
+    import sparse_attention_feed_amd as S
+    w = wl("speed3r_small")
+    d = to_dev(w)
+    qc, kc, _ = pooled(w)
+    sel, _ = O.route_scores(qc, kc, w.blk_key, w.scale, w.top_k)
+    fr = W.reference_view_blocks(w)
+    assert fr[1] - fr[0] >= 65                         # the forced range spans two 64-block chunks
+    lse = torch.empty((w.n_slots, w.n_qh), dtype=torch.float32, device="cuda")
+    say("sel_g1 forced", fr)
+    o = S.attn_fwd(d["layout"], S.BR_SEL, d["q"], d["k"], d["v"], sel=torch.from_numpy(sel).cuda(),
+                   top_k=w.top_k, sel_groups=w.n_kvh, lse=lse, q_gran=S.Q_BLOCK, forced=fr)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel, q_gran="block",
+                                 forced=fr)
+    vm = w.valid_mask()
+    assert max_err(host(o), ref) <= 2e-2
+    assert np.all(host(o)[~vm] == 0)
+    gl = host(lse)
+    assert np.all(np.isneginf(gl[~vm]))
+    assert max_err(gl[vm], ref_lse[vm]) <= lse_bound(w, w.q, w.k)
+
+
+@pytest.mark.parametrize("lo,hi,k", [(0, 90, 16), (13, 147, 40), (60, 61, 8), (0, 0, 16)])
+def test_forced_range_with_repeats_and_gaps(lo, hi, k):
+    """Ragged block counts; routing rows with repeats, -1 and entries inside the forced range; forced
+    ranges that start at 0, start mid-sequence, hold a single block, or are empty."""
+    import sparse_attention_feed_amd as S
+    rng = np.random.default_rng(lo + 3 * hi + k)
+    n_blk = 150
+    cnt = rng.integers(1, 17, size=n_blk)
+    w = W.custom_block_workload(90 + k, cnt, 16, 16, 16, 64, "bf16", k, routing="scores", q_gran="block",
+                                branches=("cmp", "sel"))
+    d = to_dev(w)
+    sel = rng.integers(-1, n_blk, size=(n_blk, 16, k)).astype(np.int32)
+    sel[:, :, 1] = sel[:, :, 0]
+    sel[::5, :, 2] = lo                               # an entry inside the forced range
+    sel[::7, :, :] = -1                               # rows that route to nothing
+    say("sel_g1 forced edges", lo, hi, k)
+    o = S.attn_fwd(d["layout"], S.BR_SEL, d["q"], d["k"], d["v"], sel=torch.from_numpy(sel).cuda(), top_k=k,
+                   sel_groups=16, q_gran=S.Q_BLOCK, forced=(lo, hi))
+    torch.cuda.synchronize()
+    ref, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel, q_gran="block",
+                           forced=(lo, hi) if hi > lo else None)
+    assert max_err(host(o), ref) <= 2e-2
+
+
+def test_forced_all_blocks_is_dense_attention():
+    """Forcing every block makes the selected branch dense attention over all valid tokens, whatever
+    the routing rows hold (here every row is -1)."""
+    import sparse_attention_feed_amd as S
+    rng = np.random.default_rng(3)
+    n_blk = 192
+    cnt = rng.integers(1, 17, size=n_blk)
+    w = W.custom_block_workload(55, cnt, 16, 16, 16, 64, "bf16", 8, routing="scores", q_gran="block",
+                                branches=("cmp", "sel"))
+    d = to_dev(w)
+    sel = np.full((n_blk, 16, 8), -1, dtype=np.int32)
+    say("sel_g1 forced all", n_blk)
+    o = S.attn_fwd(d["layout"], S.BR_SEL, d["q"], d["k"], d["v"], sel=torch.from_numpy(sel).cuda(), top_k=8,
+                   sel_groups=16, q_gran=S.Q_BLOCK, forced=(0, n_blk))
+    torch.cuda.synchronize()
+    got = host(o)
+    vs = w.valid_slots()
+    rows = np.sort(rng.choice(vs, 64, replace=False))
+    for r in rows:
+        ref, _ = O.attend(w.q[r], w.k[vs], w.v[vs], w.scale)
+        assert max_err(got[r], ref) <= 2e-2, r
+
+
+def test_forced_layer_full_size_sampled():
+    """The whole score-routed layer at full size with the reference frame forced: pooled Q/K/V, score
+    routing, gated compressed + selected branches, sampled tokens against the oracle's branches on
+    the GPU's routing rows and pooled values (inputs of the attention call)."""
+    import sparse_attention_feed_amd as S
+    w = wl("speed3r")
+    d = to_dev(w)
+    L = d["layout"]
+    fr = W.reference_view_blocks(w)
+    say("speed3r layer full, forced", fr)
+    qc = S.pool_blocks(L, d["q"])
+    kc = S.pool_blocks(L, d["k"])
+    vc = S.pool_blocks(L, d["v"])
+    sel = S.route_scores_topk(L, qc, kc, None, w.top_k, q_gran=S.Q_BLOCK)
+    o = S.attn_fwd(L, S.BR_CMP | S.BR_SEL, d["q"], d["k"], d["v"], q_cmp=qc, k_cmp=kc, v_cmp=vc, sel=sel,
+                   top_k=w.top_k, sel_groups=w.n_kvh, gates=d["gates"], q_gran=S.Q_BLOCK, forced=fr)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    toks = np.sort(rng.choice(w.valid_slots(), 48, replace=False))
+    qch, kch, vch, selh = host(qc), host(kc), host(vc), host(sel)
+    o_cmp, _ = O.attn_branch(O.CMP, qch, kch, vch, w.blk_cnt, w.blk_cap, w.scale, q_gran="block", rows=toks)
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=selh, q_gran="block",
+                             rows=toks, forced=fr)
+    ref = O.gate_combine([o_cmp, o_sel], w.gates[toks])
+    assert max_err(host(o)[toks], ref) <= 2e-2

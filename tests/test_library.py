@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 12
+    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 13
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -106,6 +106,29 @@ def test_attn_range_unsupported_and_forced(S, monkeypatch):
     monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
     assert attn_range(S, layout(S), q_lo=1, q_hi=3, kv_lo=2, kv_hi=4, gate_stride=7) == -3
     assert attn_range(S, layout(S), q_lo=2, q_hi=2, kv_lo=0, kv_hi=0) == -3   # empty ranges are valid
+
+
+def attn_forced(S, L, lo, hi, **kw):
+    a = dict(dtype=1, branches=3, q_gran=1, q=FAKE, k=FAKE, v=FAKE, q_cmp=FAKE, k_cmp=FAKE, v_cmp=FAKE,
+             sel=FAKE, top_k=4, sel_groups=1, gates=FAKE, o=FAKE, lse=None)
+    a.update(kw)
+    return S.lib.nsa_attn_fwd_forced(ctypes.byref(L), a["dtype"], a["branches"], a["q_gran"], a["q"], a["k"],
+                                     a["v"], a["q_cmp"], a["k_cmp"], a["v_cmp"], a["sel"], a["top_k"],
+                                     a["sel_groups"], lo, hi, a["gates"], a["o"], a["lse"], None)
+
+
+def test_attn_forced_validation(S, monkeypatch):
+    g1 = layout(S, n_blk=400, n_qh=16, n_kvh=16, head_dim=64, blk_cap=16)
+    for lo, hi in ((-1, 2), (3, 2), (0, 401)):
+        assert attn_forced(S, g1, lo, hi) == -1, (lo, hi)
+    assert attn_forced(S, g1, 0, 4, branches=1, sel=None) == -1            # forcing needs SEL
+    assert S.lib.nsa_last_error().decode().startswith("nsa_attn_fwd_forced")
+    assert attn_forced(S, g1, 0, 193) == -2                                 # more than 192 forced blocks
+    assert attn_forced(S, layout(S), 0, 2, branches=7, q_gran=0) == -2     # grouped-query kernels: no forcing
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    assert attn_forced(S, g1, 0, 192) == -3
+    assert attn_forced(S, g1, 5, 5, branches=1, sel=None) == -3             # empty range: plain nsa_attn_fwd
+    assert attn_forced(S, layout(S), 1, 1, branches=7, q_gran=0) == -3
 
 
 def test_route_range_validation(S, monkeypatch):
