@@ -213,6 +213,37 @@ def test_fused_equals_unfused_combine():
     assert max_err(host(two), ref2) <= tol(w)
 
 
+@pytest.mark.parametrize("kind", ["peaked", "flat", "far_below", "far_above"])
+def test_logit_range_extremes(kind):
+    """Logits far from the running reference max's start at 0 exercise the online softmax's exact
+    path: peaked (q x 64: the max moves up often), flat (q / 64), every logit about -230 or +230
+    (base 2; the first tile has no representable mass, or overflows, until the max moves).  The
+    fused layer against the whole oracle layer on fp32 inputs."""
+    import copy
+    import sparse_attention_feed_amd as S
+    w = copy.copy(wl("tiny"))
+    rng = np.random.default_rng(12)
+    if kind in ("peaked", "flat"):
+        w.q = (w.q * (64.0 if kind == "peaked" else 1.0 / 64)).astype(np.float32)
+    else:
+        u = rng.standard_normal((1, w.n_kvh, w.head_dim))
+        u /= np.linalg.norm(u, axis=2, keepdims=True)
+        sign = -1.0 if kind == "far_below" else 1.0
+        w.k = (3.0 * u + 0.05 * rng.standard_normal(w.k.shape)).astype(np.float32)
+        qu = np.repeat(u, w.n_qh // w.n_kvh, axis=1)
+        w.q = (sign * 300.0 * qu + 0.5 * rng.standard_normal(w.q.shape)).astype(np.float32)
+        w.q[~w.valid_mask()] = 0
+        w.k[~w.valid_mask()] = 0
+    d = to_dev(w)
+    say("layer logit range", kind)
+    o = S.nsa_layer(d["layout"], d["q"], d["k"], d["v"], d["pts"], d["gates"], w.top_k)
+    torch.cuda.synchronize()
+    ref = O.nsa_forward(w)
+    got = host(o)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, ref) <= tol(w)
+
+
 def test_per_group_selection_lists():
     import sparse_attention_feed_amd as S
     w = wl("stage2_small")
