@@ -66,6 +66,21 @@ template <typename T, int NT> struct Stager {
       }
     }
   }
+  // Every lane loads: rows at or beyond nk repeat row nk - 1 (row 0 if nk < 1), which the -inf
+  // seed of the padding keys masks out of every result.  With no branch around the load, the
+  // wait before the store of this set need not cover a load issued later into another set.
+  __device__ __forceinline__ void load_all(const T* kb, const T* vb, int stride, int nk) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int c = threadIdx.x + i * NT;
+      if (PER * NT == 2 * CH || c < 2 * CH) {     // no branch when the threads cover the tile exactly
+        bool isv = c >= CH;
+        int cc = isv ? c - CH : c;
+        int key = min(cc / CPR, max(nk - 1, 0)), part = cc % CPR;
+        r[i] = *reinterpret_cast<const uint4*>((isv ? vb : kb) + (size_t)key * stride + part * E);
+      }
+    }
+  }
   __device__ __forceinline__ void store(TileBuf<T>& b) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -400,17 +415,23 @@ __device__ __forceinline__ void run_tiles_ring(const RingBufs<T>& rb, int* ready
                                                const Part& part, TokState (&st)[TPW], const QF<T> (&qf)[TPW]) {
   static_assert(R >= 4, "the ring needs four buffers or more");
   constexpr int WAVES = NT / 64;
-  Stager<T, NT> sg;
+  // global loads run one step ahead of the store that needs them (two register sets)
+  Stager<T, NT> sg, nx;
   __builtin_amdgcn_s_waitcnt(0);   // as in run_tiles: no earlier load stays in flight into the loop
   for (int t = 0; t < R - 2 && t < ntiles; ++t) {
     sg.load(src.kptr(t), src.vptr(t), src.stride, src.nk(t));
     sg.store(rb[t]);
     ring_signal(&ready[t]);
   }
+  if (R - 2 < ntiles) sg.load_all(src.kptr(R - 2), src.vptr(R - 2), src.stride, src.nk(R - 2));
   int rdy = -1;                                   // ready count of tile u's buffer read early
-  for (int u = 0; u < ntiles; ++u) {
-    const int x = u + R - 2;                      // the tile this iteration stages
-    if (x < ntiles) sg.load(src.kptr(x), src.vptr(x), src.stride, src.nk(x));
+  // one step: compute tile u, stage tile u + R - 2 from cur (loaded one step earlier), and start
+  // the load of the tile after it into nxt; the loop is unrolled by two so the sets swap roles
+  // without a register copy (a copy would wait for the load it is meant to leave in flight)
+  auto step = [&](int u, Stager<T, NT>& cur, Stager<T, NT>& nxt) {
+    const int x = u + R - 2;
+    const int xl = min(x + 1, ntiles - 1);        // past the end: a harmless load of the last tile
+    nxt.load_all(src.kptr(xl), src.vptr(xl), src.stride, src.nk(xl));
     const int bu = u % R;
     const int need = WAVES * (u / R + 1) + stall;
     if (rdy < need) ring_wait(&ready[bu], need, broken, spin_limit);
@@ -438,10 +459,14 @@ __device__ __forceinline__ void run_tiles_ring(const RingBufs<T>& rb, int* ready
         if (__builtin_amdgcn_readfirstlane(dn) < fin) ring_wait(&done[bp], fin, broken, spin_limit);
         else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       }
-      sg.store(rb[bp]);
+      cur.store(rb[bp]);
       ring_signal(&ready[bp]);
     }
     rdy = __builtin_amdgcn_readfirstlane(rdy_next);
+  };
+  for (int u = 0; u < ntiles; u += 2) {
+    step(u, sg, nx);
+    if (u + 1 < ntiles) step(u + 1, nx, sg);
   }
   __syncthreads();
   if (*broken) {
