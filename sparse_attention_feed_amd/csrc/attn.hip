@@ -368,9 +368,10 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
 // Barrier-free tile ring for the selected branch.  R LDS buffers; tile t lives in buffer t % R.
 // Every wave stages its own share of each tile (the chunks its threads own) and then adds 1 to
 // ready[t % R]; it computes tile t once ready shows all WAVES shares of that use of the buffer, and
-// adds 1 to done[t % R] after its last read.  A wave stages tile t + R - 2 into the buffer of tile
-// t - 2 only after done shows that every wave has finished tile t - 2.  Both counts are read early
-// (the next tile's ready count and tile t - 2's done count before tile t's compute), so a wait that
+// adds 1 to done[t % R] after its last read.  A wave stages tile t + R - L into the buffer of tile
+// t - L only after done shows that every wave has finished tile t - L (the lag L is 3 with 8
+// buffers, 2 with fewer).  Both counts are read early (the next tile's ready count and tile t - L's
+// done count before tile t's compute), so a wait that
 // is already satisfied costs no LDS round trip of its own; only a short count is read again.  Each
 // wait names a strictly earlier event of other waves, so the ring cannot deadlock; it lets a wave
 // run ahead of the slowest instead of meeting at a barrier after every tile (the work per wave and
@@ -415,21 +416,22 @@ __device__ __forceinline__ void run_tiles_ring(const RingBufs<T>& rb, int* ready
                                                const Part& part, TokState (&st)[TPW], const QF<T> (&qf)[TPW]) {
   static_assert(R >= 4, "the ring needs four buffers or more");
   constexpr int WAVES = NT / 64;
+  constexpr int L = R >= 8 ? 3 : 2;                // lag between a tile's compute and its buffer's reuse
   // global loads run one step ahead of the store that needs them (two register sets)
   Stager<T, NT> sg, nx;
   __builtin_amdgcn_s_waitcnt(0);   // as in run_tiles: no earlier load stays in flight into the loop
-  for (int t = 0; t < R - 2 && t < ntiles; ++t) {
+  for (int t = 0; t < R - L && t < ntiles; ++t) {
     sg.load(src.kptr(t), src.vptr(t), src.stride, src.nk(t));
     sg.store(rb[t]);
     ring_signal(&ready[t]);
   }
-  if (R - 2 < ntiles) sg.load_all(src.kptr(R - 2), src.vptr(R - 2), src.stride, src.nk(R - 2));
+  if (R - L < ntiles) sg.load_all(src.kptr(R - L), src.vptr(R - L), src.stride, src.nk(R - L));
   int rdy = -1;                                   // ready count of tile u's buffer read early
-  // one step: compute tile u, stage tile u + R - 2 from cur (loaded one step earlier), and start
+  // one step: compute tile u, stage tile u + R - L from cur (loaded one step earlier), and start
   // the load of the tile after it into nxt; the loop is unrolled by two so the sets swap roles
   // without a register copy (a copy would wait for the load it is meant to leave in flight)
   auto step = [&](int u, Stager<T, NT>& cur, Stager<T, NT>& nxt) {
-    const int x = u + R - 2;
+    const int x = u + R - L;
     const int xl = min(x + 1, ntiles - 1);        // past the end: a harmless load of the last tile
     nxt.load_all(src.kptr(xl), src.vptr(xl), src.stride, src.nk(xl));
     const int bu = u % R;
@@ -438,8 +440,8 @@ __device__ __forceinline__ void run_tiles_ring(const RingBufs<T>& rb, int* ready
     else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const int rdy_next =
         u + 1 < ntiles ? __hip_atomic_load(&ready[(u + 1) % R], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0;
-    const int dn = (x < ntiles && u >= 2)
-                       ? __hip_atomic_load(&done[(u - 2) % R], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+    const int dn = (x < ntiles && u >= L)
+                       ? __hip_atomic_load(&done[(u - L) % R], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
                        : 0;
     const TileBuf<T>& b = rb[bu];
     const int nk = src.nk(u);
@@ -453,9 +455,9 @@ __device__ __forceinline__ void run_tiles_ring(const RingBufs<T>& rb, int* ready
     }
     ring_signal(&done[bu]);
     if (x < ntiles) {
-      const int bp = x % R;                        // == (u - 2) % R, the buffer of tile u - 2
-      if (u >= 2) {
-        const int fin = WAVES * ((u - 2) / R + 1);
+      const int bp = x % R;                        // == (u - L) % R, the buffer of tile u - L
+      if (u >= L) {
+        const int fin = WAVES * ((u - L) / R + 1);
         if (__builtin_amdgcn_readfirstlane(dn) < fin) ring_wait(&done[bp], fin, broken, spin_limit);
         else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       }
