@@ -336,18 +336,21 @@ __device__ __forceinline__ void tok_finish(const TokState& st, f32x4 (&res)[2], 
 template <typename T, int NT, int TPW, class Src, class Part>
 __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int ntiles, const Part& part,
                                           TokState (&st)[TPW], const QF<T> (&qf)[TPW]) {
-  // Global loads run two tiles ahead of the compute (two register sets), LDS holds two tiles.
-  Stager<T, NT> next, after;
+  // Global loads run two tiles ahead of the compute (two register sets), LDS holds two tiles.  The
+  // loop is unrolled by two so the register sets swap roles without a copy.
+  Stager<T, NT> sa, sb;
   if (ntiles <= 0) return;
   // Settle every outstanding load of earlier phases here: the compiler's wait insertion would
   // otherwise merge them with the prefetch in flight and wait for that prefetch inside the loop.
   __builtin_amdgcn_s_waitcnt(0);
-  next.load(src.kptr(0), src.vptr(0), src.stride, src.nk(0));
-  next.store(buf[0]);
-  if (ntiles > 1) next.load(src.kptr(1), src.vptr(1), src.stride, src.nk(1));
+  sa.load_all(src.kptr(0), src.vptr(0), src.stride, src.nk(0));
+  sa.store(buf[0]);
+  sa.load_all(src.kptr(min(1, ntiles - 1)), src.vptr(min(1, ntiles - 1)), src.stride, src.nk(min(1, ntiles - 1)));
   __syncthreads();
-  for (int u = 0; u < ntiles; ++u) {
-    if (u + 2 < ntiles) after.load(src.kptr(u + 2), src.vptr(u + 2), src.stride, src.nk(u + 2));
+  // one step: tile u+1's rows are in cur, start tile u+2's load into nxt, compute tile u, store cur
+  auto step = [&](int u, Stager<T, NT>& cur, Stager<T, NT>& nxt) {
+    const int xl = min(u + 2, ntiles - 1);       // past the end: a harmless load of the last tile
+    nxt.load_all(src.kptr(xl), src.vptr(xl), src.stride, src.nk(xl));
     const TileBuf<T>& b = buf[u & 1];
     const int nk = src.nk(u);
     const uint32_t pm = Part::kAll ? 0u : part.wave_mask(u);
@@ -359,9 +362,12 @@ __device__ __forceinline__ void run_tiles(TileBuf<T>* buf, const Src& src, int n
       if constexpr (Part::kAll) tile_prefix<T, TPW>(st, qf, part.n, kf, vf, cm, nk == TILE);
       else tile_masked<T, TPW>(st, qf, pm, kf, vf, cm, nk == TILE);
     }
-    if (u + 1 < ntiles) next.store(buf[(u + 1) & 1]);
-    next = after;
+    if (u + 1 < ntiles) cur.store(buf[(u + 1) & 1]);
     __syncthreads();
+  };
+  for (int u = 0; u < ntiles; u += 2) {
+    step(u, sa, sb);
+    if (u + 1 < ntiles) step(u + 1, sb, sa);
   }
 }
 
