@@ -566,7 +566,8 @@ template <typename T, int WAVES, int TPW>
 __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr bool kOutLds = OutInLds<T>::value;
-  static_assert(WAVES * TPW == 64, "a workgroup covers 64 query slots");
+  constexpr int SLOTS = WAVES * TPW;             // query slots of one workgroup: a block or half a block
+  static_assert(SLOTS == 64 || SLOTS == 32, "a workgroup covers 64 or 32 query slots");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   TileBuf<T>* buf = reinterpret_cast<TileBuf<T>*>(smem);
   // region after the tiles: the selection-union tables during the SEL phase, then (bf16, several
@@ -575,8 +576,12 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   float* out_lds = reinterpret_cast<float*>(extra);
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = a.q_blk0 + wg / a.n_kvh, j = wg % a.n_kvh;
-  const int cap = a.cap, cnt = a.blk_cnt[b];
+  const int cap = a.cap, n_part = (cap + SLOTS - 1) / SLOTS;
+  const int j = wg % a.n_kvh, bp = wg / a.n_kvh;
+  const int b = a.q_blk0 + bp / n_part;
+  const int s0 = (bp % n_part) * SLOTS;          // first block slot of this workgroup
+  const int cnt = a.blk_cnt[b];
+  const int cnt_p = min(max(cnt - s0, 0), SLOTS);  // valid slots of this workgroup: [s0, s0 + cnt_p)
   const int w = threadIdx.x >> 6, l = lane_id();
   const int r = l & 15, g = l >> 4;
   const int hh = j * GRP + r;                  // query head of this lane
@@ -585,14 +590,14 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   const T* q = reinterpret_cast<const T*>(a.q);
   const int n_named = __builtin_popcount(a.branches);
 
-  // queries of this wave's tokens: token t of wave w is block slot t * WAVES + w, so the valid
-  // slots [0, cnt) spread evenly over the waves and each wave's valid tokens are a prefix
+  // queries of this wave's tokens: token t of wave w is block slot s0 + t * WAVES + w, so the
+  // valid slots spread evenly over the waves and each wave's valid tokens are a prefix
   QF<T> qf[TPW];
-  const int n_valid = cnt > w ? min(TPW, (cnt - w + WAVES - 1) / WAVES) : 0;
+  const int n_valid = cnt_p > w ? min(TPW, (cnt_p - w + WAVES - 1) / WAVES) : 0;
   const uint32_t valid = (1u << n_valid) - 1u;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int slot = t * WAVES + w;
+    const int slot = s0 + t * WAVES + w;
     if (t < n_valid) qf[t] = make_qf(q + ((size_t)(b * cap + slot) * a.n_qh + hh) * HD + 8 * g, c2);
     else qf[t] = zero_qf<T>();
   }
@@ -607,7 +612,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     const bool first = done == 0, last = done == n_named - 1;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const int slot = t * WAVES + w;
+      const int slot = s0 + t * WAVES + w;
       if (!(valid & (1u << t))) continue;
       const size_t row = (size_t)(b * cap + slot);
       float wgt = 1.f;
@@ -618,7 +623,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
       float* lp = a.lse ? a.lse + row * a.n_qh + hh : nullptr;
       f32x4 res[2];
       tok_finish(st[t], res, wgt, lp);
-      float* ol = out_lds + ((size_t)slot * GRP + r) * HD + 4 * g;
+      float* ol = out_lds + ((size_t)(slot - s0) * GRP + r) * HD + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         f32x4 acc = res[dt];
@@ -663,8 +668,8 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     for (int i = threadIdx.x; i < a.n_words; i += NT) bitmap[i] = 0u;
     if (threadIdx.x < 2 * R + 1) ring_ctr[threadIdx.x] = 0;
     __syncthreads();
-    for (int e = threadIdx.x; e < cnt * kk; e += NT) {
-      const int t = e / kk, s = e % kk;
+    for (int e = threadIdx.x; e < cnt_p * kk; e += NT) {
+      const int t = s0 + e / kk, s = e % kk;
       const int blk = a.sel[((size_t)(b * cap + t) * a.sel_groups + grp) * kk + s];
       if (blk >= 0 && blk < a.n_blk) atomicOr(&bitmap[blk >> 5], 1u << (blk & 31));
     }
@@ -692,9 +697,9 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     }
     for (int i = threadIdx.x; i < n_union; i += NT) umask[i] = 0ull;
     __syncthreads();
-    for (int e = threadIdx.x; e < cnt * kk; e += NT) {
-      const int t = e / kk, s = e % kk;
-      const int blk = a.sel[((size_t)(b * cap + t) * a.sel_groups + grp) * kk + s];
+    for (int e = threadIdx.x; e < cnt_p * kk; e += NT) {
+      const int t = e / kk, s = e % kk;          // t: slot s0 + t
+      const int blk = a.sel[((size_t)(b * cap + s0 + t) * a.sel_groups + grp) * kk + s];
       if (blk >= 0 && blk < a.n_blk) {
         const int wi = blk >> 5;
         const int u = wpre[wi] + __builtin_popcount(bitmap[wi] & ((1u << (blk & 31)) - 1u));
@@ -751,7 +756,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   // ---- padding slots of the block: zero output (and -inf lse) ----
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int slot = t * WAVES + w;
+    const int slot = s0 + t * WAVES + w;
     if (slot >= cap || slot < cnt) continue;
     const size_t row = (size_t)(b * cap + slot);
 #pragma unroll
@@ -785,13 +790,14 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
   const T* q = reinterpret_cast<const T*>(a.q);
   const T* gp = reinterpret_cast<const T*>(a.gates);
 
+  constexpr int SLOTS = WAVES * TPW;             // tokens of one workgroup
   QF<T> qf[TPW];
-  const int rem = a.n_tok - qb * 64;            // tokens of this workgroup: slots [0, rem)
+  const int rem = a.n_tok - qb * SLOTS;         // tokens of this workgroup: slots [0, rem)
   const int n_valid = rem > w ? min(TPW, (rem - w + WAVES - 1) / WAVES) : 0;
   const uint32_t valid = (1u << n_valid) - 1u;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int tok = qb * 64 + t * WAVES + w;
+    const int tok = qb * SLOTS + t * WAVES + w;
     if (t < n_valid) qf[t] = make_qf(q + ((size_t)tok * a.n_qh + hh) * HD + 8 * g, c2);
     else qf[t] = zero_qf<T>();
   }
@@ -813,7 +819,7 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int slot = t * WAVES + w;
-      const int tok = qb * 64 + slot;
+      const int tok = qb * SLOTS + slot;
       if (!(valid & (1u << t))) continue;
       // phase 0 holds x keys: self for x tokens, cross for y tokens
       const int ch = ((tok < a.n_x) == (ph == 0)) ? 0 : 1;
@@ -841,7 +847,7 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
 
 template <typename T> struct Shape;
 template <> struct Shape<bf16> { static constexpr int WAVES = 8, TPW = 8; };
-template <> struct Shape<float> { static constexpr int WAVES = 16, TPW = 4; };
+template <> struct Shape<float> { static constexpr int WAVES = 8, TPW = 4; };   // half a block per workgroup
 
 template <typename T>
 size_t attn_lds_t(const AttnArgs& a) {
@@ -852,7 +858,7 @@ size_t attn_lds_t(const AttnArgs& a) {
     extra = (size_t)a.n_words * 8 + (size_t)a.u_cap * 4 + (NT / 64 + 1) * 4 + 8 + (size_t)a.u_cap * 8 + 16 +
             (R - 2) * sizeof(TileBuf<T>) + (2 * R + 1) * sizeof(int);
   if (OutInLds<T>::value && __builtin_popcount(a.branches) > 1) {
-    const size_t out_bytes = (size_t)64 * GRP * HD * sizeof(float);
+    const size_t out_bytes = (size_t)Shape<T>::WAVES * Shape<T>::TPW * GRP * HD * sizeof(float);
     if (out_bytes > extra) extra = out_bytes;
   }
   return 2 * sizeof(TileBuf<T>) + extra;
@@ -862,7 +868,8 @@ template <typename T>
 hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
   const size_t lds = attn_lds_t<T>(a);
-  const int nwg = a.n_qblk * a.n_kvh;
+  const int n_part = (a.cap + WAVES * TPW - 1) / (WAVES * TPW);   // workgroups per block and KV head
+  const int nwg = a.n_qblk * n_part * a.n_kvh;
   if (nwg == 0) return hipSuccess;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nsa_attn_kernel<T, WAVES, TPW>),
@@ -876,8 +883,9 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
 template <typename T>
 hipError_t launch_dense_t(const DenseArgs& a, hipStream_t s) {
   constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
-  const size_t lds = 2 * sizeof(TileBuf<T>) + (OutInLds<T>::value ? (size_t)64 * GRP * HD * sizeof(float) : 0);
-  const int nwg = ((a.n_tok + 63) / 64) * a.n_kvh;
+  constexpr int SLOTS = WAVES * TPW;
+  const size_t lds = 2 * sizeof(TileBuf<T>) + (OutInLds<T>::value ? (size_t)SLOTS * GRP * HD * sizeof(float) : 0);
+  const int nwg = ((a.n_tok + SLOTS - 1) / SLOTS) * a.n_kvh;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dense_xattn_kernel<T, WAVES, TPW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
