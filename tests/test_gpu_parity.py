@@ -367,6 +367,29 @@ def test_full_size_layer_sampled(name):
     assert np.all(host(o)[~vm] == 0)
 
 
+def test_layer_at_the_block_limit_sampled():
+    """The largest layout the selected branch takes: 65536 blocks (2048 bitmap words in the union
+    tables), ragged counts of 1 or 2 tokens, top_k = 64 (the longest routing row): the fused layer
+    on sampled tokens and routing bit-exact on a larger sample."""
+    import sparse_attention_feed_amd as S
+    cnt = np.random.default_rng(14).integers(1, 3, size=65536).tolist()
+    w = W.custom_block_workload(14, cnt, 2, 32, 2, 32, "bf16", 64)
+    d = to_dev(w)
+    ws = {}
+    say("layer at the block limit", w.n_blk, "blocks,", w.n_valid, "tokens, k", w.top_k)
+    o = S.nsa_layer(d["layout"], d["q"], d["k"], d["v"], d["pts"], d["gates"], w.top_k, ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(15)
+    vs = w.valid_slots()
+    rows = np.sort(rng.choice(vs, 32, replace=False))
+    ref = O.nsa_forward(w, rows=rows)
+    assert max_err(host(o)[rows], ref) <= tol(w)
+    rows_r = np.sort(rng.choice(vs, 256, replace=False))
+    ref_sel, _ = O.route_geometric(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k, rows=rows_r)
+    np.testing.assert_array_equal(host(ws["sel"])[rows_r], ref_sel)
+    assert np.all(host(o)[~w.valid_mask()] == 0)
+
+
 def test_full_size_dense_sampled():
     import sparse_attention_feed_amd as S
     w = W.make("dense")
