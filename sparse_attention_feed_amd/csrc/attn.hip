@@ -667,14 +667,25 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     const int kk = a.top_k;
     for (int i = threadIdx.x; i < a.n_words; i += NT) bitmap[i] = 0u;
     if (threadIdx.x < 2 * R + 1) ring_ctr[threadIdx.x] = 0;
-    __syncthreads();
-    for (int e = threadIdx.x; e < cnt_p * kk; e += NT) {
-      const int t = s0 + e / kk, s = e % kk;
-      const int blk = a.sel[((size_t)(b * cap + t) * a.sel_groups + grp) * kk + s];
-      if (blk >= 0 && blk < a.n_blk) atomicOr(&bitmap[blk >> 5], 1u << (blk & 31));
+    // this thread's routing entries e = tid + i NT (row e / kk, entry e % kk of the workgroup's
+    // rows) and their blocks' token counts, all loads issued at once: a loop of dependent loads
+    // would pay one memory round trip per entry, exposed with one workgroup per CU
+    constexpr int MAXE = (64 * 64 + NT - 1) / NT;   // rows <= 64, entries per row <= 64
+    int eblk[MAXE], ecnt[MAXE];
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i) {
+      const int e = threadIdx.x + i * NT;
+      eblk[i] = e < cnt_p * kk ? a.sel[((size_t)(b * cap + s0 + e / kk) * a.sel_groups + grp) * kk + e % kk] : -1;
     }
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i) ecnt[i] = (eblk[i] >= 0 && eblk[i] < a.n_blk) ? a.blk_cnt[eblk[i]] : 0;
     __syncthreads();
-    // exclusive prefix of popcounts over the bitmap words (contiguous ranges per thread)
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i)
+      if (eblk[i] >= 0 && eblk[i] < a.n_blk) atomicOr(&bitmap[eblk[i] >> 5], 1u << (eblk[i] & 31));
+    __syncthreads();
+    // union position of a block = exclusive prefix of popcounts over the bitmap words (contiguous
+    // word ranges per thread) plus its rank inside its word
     const int per = (a.n_words + NT - 1) / NT;
     const int w0 = threadIdx.x * per;
     int mine = 0;
@@ -686,23 +697,21 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
       const int wi = w0 + i;
       if (wi < a.n_words) {
         wpre[wi] = base;
-        uint32_t bits = bitmap[wi];
-        while (bits) {
-          const int bit = __builtin_ctz(bits);
-          bits &= bits - 1;
-          const int blk = 32 * wi + bit;
-          ulist[base++] = blk | (a.blk_cnt[blk] << 16);
-        }
+        base += __builtin_popcount(bitmap[wi]);
       }
     }
     for (int i = threadIdx.x; i < n_union; i += NT) umask[i] = 0ull;
     __syncthreads();
-    for (int e = threadIdx.x; e < cnt_p * kk; e += NT) {
-      const int t = e / kk, s = e % kk;          // t: slot s0 + t
-      const int blk = a.sel[((size_t)(b * cap + s0 + t) * a.sel_groups + grp) * kk + s];
+    // every union block is named by some entry: each entry writes its block's list word (the
+    // same value from every entry of that block) and its token's bit of the block's mask
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i) {
+      const int blk = eblk[i];
       if (blk >= 0 && blk < a.n_blk) {
+        const int t = (threadIdx.x + i * NT) / kk;   // row: slot s0 + t
         const int wi = blk >> 5;
         const int u = wpre[wi] + __builtin_popcount(bitmap[wi] & ((1u << (blk & 31)) - 1u));
+        ulist[u] = blk | (ecnt[i] << 16);
         atomicOr(&umask[u], 1ull << (TPW * (t % WAVES) + t / WAVES));   // wave t % WAVES, its token t / WAVES
       }
     }
