@@ -149,27 +149,25 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // Pre-scaled query fragment of one token: the MFMA B operand of S^T = K Q^T.
 template <typename T> struct QF { Frag8<T> hi; };
 
-__device__ __forceinline__ QF<bf16> make_qf(const bf16* p, float c2) {
-  const bf16x8 raw = *reinterpret_cast<const bf16x8*>(p);
-  QF<bf16> q;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) q.hi.v[e] = (bf16)((float)raw[e] * c2);
-  return q;
+// The lane's eight query elements as stored, and the fragment made from them (valid tokens) or
+// zero: the loads of all of a wave's tokens are issued before any conversion, so they share one
+// memory round trip.
+__device__ __forceinline__ Frag8<bf16> load_q8(const bf16* p) {
+  Frag8<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
 }
-__device__ __forceinline__ QF<float> make_qf(const float* p, float c2) {
-  QF<float> q;
+__device__ __forceinline__ Frag8<float> load_q8(const float* p) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(p);
   const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    q.hi.v[e] = a[e] * c2;
-    q.hi.v[e + 4] = b[e] * c2;
-  }
-  return q;
+  Frag8<float> f;
+  f.v = (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
 }
-template <typename T> __device__ __forceinline__ QF<T> zero_qf() {
+template <typename T> __device__ __forceinline__ QF<T> make_qf(const Frag8<T>& raw, float c2, bool valid) {
   QF<T> q;
-  q.hi.v = decltype(q.hi.v){};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q.hi.v[e] = valid ? (T)((float)raw.v[e] * c2) : (T)0.f;
   return q;
 }
 
@@ -595,11 +593,13 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   QF<T> qf[TPW];
   const int n_valid = cnt_p > w ? min(TPW, (cnt_p - w + WAVES - 1) / WAVES) : 0;
   const uint32_t valid = (1u << n_valid) - 1u;
+  {
+    Frag8<T> raw[TPW];   // every slot of the block has a query row (padding rows are never used)
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int slot = s0 + t * WAVES + w;
-    if (t < n_valid) qf[t] = make_qf(q + ((size_t)(b * cap + slot) * a.n_qh + hh) * HD + 8 * g, c2);
-    else qf[t] = zero_qf<T>();
+    for (int t = 0; t < TPW; ++t)
+      raw[t] = load_q8(q + ((size_t)(b * cap + min(s0 + t * WAVES + w, cap - 1)) * a.n_qh + hh) * HD + 8 * g);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) qf[t] = make_qf<T>(raw[t], c2, t < n_valid);
   }
 
   f32x4 out_reg[kOutLds ? 1 : TPW][2];
@@ -610,16 +610,23 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   // Close a branch: normalise, gate, and either store (last branch) or fold into the running sum.
   auto finish_all = [&](int ch) {
     const bool first = done == 0, last = done == n_named - 1;
+    // gate logits of the wave's tokens, loaded together: loaded inside the token loop, each would
+    // wait a memory round trip behind the previous token's output stores
+    // (every slot of the block has a gate row, so the loads need no per-token branch)
+    T gl[TPW];
+    if (a.gates) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const size_t row = (size_t)(b * cap + min(s0 + t * WAVES + w, cap - 1));
+        gl[t] = reinterpret_cast<const T*>(a.gates)[(row * a.n_qh + hh) * a.n_gch + ch];
+      }
+    }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int slot = s0 + t * WAVES + w;
       if (!(valid & (1u << t))) continue;
       const size_t row = (size_t)(b * cap + slot);
-      float wgt = 1.f;
-      if (a.gates) {
-        const T* gp = reinterpret_cast<const T*>(a.gates);
-        wgt = sigmoidf_(to_f32(gp[(row * a.n_qh + hh) * a.n_gch + ch]));
-      }
+      const float wgt = a.gates ? sigmoidf_(to_f32(gl[t])) : 1.f;
       float* lp = a.lse ? a.lse + row * a.n_qh + hh : nullptr;
       f32x4 res[2];
       tok_finish(st[t], res, wgt, lp);
@@ -804,11 +811,13 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
   const int rem = a.n_tok - qb * SLOTS;         // tokens of this workgroup: slots [0, rem)
   const int n_valid = rem > w ? min(TPW, (rem - w + WAVES - 1) / WAVES) : 0;
   const uint32_t valid = (1u << n_valid) - 1u;
+  {
+    Frag8<T> raw[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tok = qb * SLOTS + t * WAVES + w;
-    if (t < n_valid) qf[t] = make_qf(q + ((size_t)tok * a.n_qh + hh) * HD + 8 * g, c2);
-    else qf[t] = zero_qf<T>();
+    for (int t = 0; t < TPW; ++t)
+      raw[t] = load_q8(q + ((size_t)min(qb * SLOTS + t * WAVES + w, a.n_tok - 1) * a.n_qh + hh) * HD + 8 * g);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) qf[t] = make_qf<T>(raw[t], c2, t < n_valid);
   }
   f32x4 out_reg[kOutLds ? 1 : TPW][2];
   TokState st[TPW];
@@ -825,14 +834,21 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
     src.hi = hi;
     AllPart part{n_valid};
     run_tiles<T, NT, TPW>(buf, src, (hi - lo + TILE - 1) / TILE, part, st, qf);
+    // gate logits of the wave's tokens, loaded together (phase 0 holds x keys: self for x tokens,
+    // cross for y tokens)
+    T gl[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tok = min(qb * SLOTS + t * WAVES + w, a.n_tok - 1);
+      const int ch = ((tok < a.n_x) == (ph == 0)) ? 0 : 1;
+      gl[t] = gp[((size_t)tok * a.n_qh + hh) * 2 + ch];
+    }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int slot = t * WAVES + w;
       const int tok = qb * SLOTS + slot;
       if (!(valid & (1u << t))) continue;
-      // phase 0 holds x keys: self for x tokens, cross for y tokens
-      const int ch = ((tok < a.n_x) == (ph == 0)) ? 0 : 1;
-      const float wgt = sigmoidf_(to_f32(gp[((size_t)tok * a.n_qh + hh) * 2 + ch]));
+      const float wgt = sigmoidf_(to_f32(gl[t]));
       f32x4 res[2];
       tok_finish(st[t], res, wgt, nullptr);
       float* ol = out_lds + ((size_t)slot * GRP + r) * HD + 4 * g;
