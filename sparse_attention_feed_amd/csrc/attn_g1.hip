@@ -88,21 +88,32 @@ __device__ __forceinline__ void scores_g1(const TileFragsG1& f, const QG1& q, co
   for (int kt = 0; kt < 4; ++kt) s[kt] = mma16(f.k[kt][1], q.h[1], mma16(f.k[kt][0], q.h[0], seed[kt]));
 }
 
-// Stage 64 keys into LDS: rows given by a per-key source row (or -1 for padding: zero).  Every thread
-// of the group (nt threads) copies 16-byte pieces; V goes to the permuted transposed layout.
-__device__ __forceinline__ void stage_rows_g1(TileG1& t, const bf16* kb, const bf16* vb, int stride,
-                                              const int* rows /* LDS [64] */, int tid, int nt) {
-  for (int c = tid; c < 2 * KT * 8; c += nt) {       // 8 pieces of 8 elements per 64-element row
-    const bool isv = c >= KT * 8;
-    const int cc = isv ? c - KT * 8 : c;
+// One wave's share of a gathered 64-key tile: chunk tid + 64 i (i < 8: K rows, else V rows) of
+// the 1024 16-byte chunks.  All sixteen loads are issued before any is used, so a tile costs one
+// memory round trip, and the next tile's gather runs during the current tile's compute.  Padding
+// keys (row -1) read row 0: their scores are masked to -inf, so they weigh nothing.
+struct RowsG1 { uint4 v[16]; };
+
+__device__ __forceinline__ void gather_rows_g1(RowsG1& g, const bf16* kb, const bf16* vb, int stride,
+                                               const int* rows /* LDS [64] */, int tid) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int cc = tid + (i & 7) * 64;
     const int key = cc >> 3, part = cc & 7;
-    const int src = rows[key];
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (src >= 0) val = *reinterpret_cast<const uint4*>((isv ? vb : kb) + (size_t)src * stride + part * 8);
-    if (!isv) {
-      *reinterpret_cast<uint4*>(&t.k[key][part * 8]) = val;
+    const int src = max(rows[key], 0);
+    g.v[i] = *reinterpret_cast<const uint4*>((i >= 8 ? vb : kb) + (size_t)src * stride + part * 8);
+  }
+}
+
+__device__ __forceinline__ void store_rows_g1(TileG1& t, const RowsG1& g, int tid) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int cc = tid + (i & 7) * 64;
+    const int key = cc >> 3, part = cc & 7;
+    if (i < 8) {
+      *reinterpret_cast<uint4*>(&t.k[key][part * 8]) = g.v[i];
     } else {
-      const bf16* e = reinterpret_cast<const bf16*>(&val);
+      const bf16* e = reinterpret_cast<const bf16*>(&g.v[i]);
       const int pos = vt_pos_g1(key);
 #pragma unroll
       for (int x = 0; x < 8; ++x) t.vt[part * 8 + x][pos] = e[x];
@@ -593,9 +604,12 @@ __global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
   StateG1 st;
   state_init(st);
   const QG1 qq = load_q_row(q + ((size_t)(b * cap + r) * a.n_qh + h) * DG, r < cnt, c2);
+  RowsG1 pre;
+  if (ntiles > 0) gather_rows_g1(pre, kb, vb, stride, keys_lds, l);
   for (int u = 0; u < ntiles; ++u) {
-    stage_rows_g1(tb, kb, vb, stride, keys_lds + u * KT, l, 64);
+    store_rows_g1(tb, pre, l);
     __syncthreads();
+    if (u + 1 < ntiles) gather_rows_g1(pre, kb, vb, stride, keys_lds + (u + 1) * KT, l);
     TileFragsG1 f;
     load_frags_g1(tb, f);
     const int nk = min(KT, total - u * KT);
