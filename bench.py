@@ -309,7 +309,9 @@ def main():
     value = n_tok / (ms_step * 1e-3)
 
     fl = flops_fn()
-    dom_flops = sum(v for kk, v in fl.items() if kk != "route")
+    # the dominant kernel's branches: routing runs in its own kernel, and the forced-range variant
+    # is a separate breakdown item, not part of the timed step
+    dom_flops = sum(v for kk, v in fl.items() if kk not in ("route", "sel_forced_ref_frame"))
     achieved = dom_flops / (kern_ms[dominant] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     log("step %.3f ms; %s; %s %.1f TFLOP/s" % (ms_step, ", ".join("%s %.3f" % kv for kv in kern_ms.items()),
