@@ -88,36 +88,45 @@ __device__ __forceinline__ void scores_g1(const TileFragsG1& f, const QG1& q, co
   for (int kt = 0; kt < 4; ++kt) s[kt] = mma16(f.k[kt][1], q.h[1], mma16(f.k[kt][0], q.h[0], seed[kt]));
 }
 
-// One wave's share of a gathered 64-key tile: chunk tid + 64 i (i < 8: K rows, else V rows) of
-// the 1024 16-byte chunks.  All sixteen loads are issued before any is used, so a tile costs one
+// One wave's share of a gathered 64-key tile: chunk tid + 64 i (i < 8) of the 512 16-byte chunks
+// of K and the same chunk of V.  All sixteen loads are issued before any is used, so a tile costs one
 // memory round trip, and the next tile's gather runs during the current tile's compute.  Padding
 // keys (row -1) read row 0: their scores are masked to -inf, so they weigh nothing.
-struct RowsG1 { uint4 v[16]; };
+// (vector types, not arrays: an array carried across the tile loop was placed in scratch memory)
+typedef uint32_t u32x32 __attribute__((ext_vector_type(32)));
+struct RowsG1 { u32x32 k, v; };
+
+__device__ __forceinline__ void put4(u32x32& d, int i, uint4 x) {
+  d[4 * i] = x.x;
+  d[4 * i + 1] = x.y;
+  d[4 * i + 2] = x.z;
+  d[4 * i + 3] = x.w;
+}
 
 __device__ __forceinline__ void gather_rows_g1(RowsG1& g, const bf16* kb, const bf16* vb, int stride,
                                                const int* rows /* LDS [64] */, int tid) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int cc = tid + (i & 7) * 64;
+  for (int i = 0; i < 8; ++i) {
+    const int cc = tid + i * 64;
     const int key = cc >> 3, part = cc & 7;
-    const int src = max(rows[key], 0);
-    g.v[i] = *reinterpret_cast<const uint4*>((i >= 8 ? vb : kb) + (size_t)src * stride + part * 8);
+    const size_t off = (size_t)max(rows[key], 0) * stride + part * 8;
+    put4(g.k, i, *reinterpret_cast<const uint4*>(kb + off));
+    put4(g.v, i, *reinterpret_cast<const uint4*>(vb + off));
   }
 }
 
 __device__ __forceinline__ void store_rows_g1(TileG1& t, const RowsG1& g, int tid) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int cc = tid + (i & 7) * 64;
+  for (int i = 0; i < 8; ++i) {
+    const int cc = tid + i * 64;
     const int key = cc >> 3, part = cc & 7;
-    if (i < 8) {
-      *reinterpret_cast<uint4*>(&t.k[key][part * 8]) = g.v[i];
-    } else {
-      const bf16* e = reinterpret_cast<const bf16*>(&g.v[i]);
-      const int pos = vt_pos_g1(key);
+    *reinterpret_cast<uint4*>(&t.k[key][part * 8]) = make_uint4(g.k[4 * i], g.k[4 * i + 1], g.k[4 * i + 2], g.k[4 * i + 3]);
+    // the eight bf16 values by shifts
+    const uint32_t wd[4] = {g.v[4 * i], g.v[4 * i + 1], g.v[4 * i + 2], g.v[4 * i + 3]};
+    const int pos = vt_pos_g1(key);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) t.vt[part * 8 + x][pos] = e[x];
-    }
+    for (int x = 0; x < 8; ++x)
+      t.vt[part * 8 + x][pos] = __builtin_bit_cast(bf16, (uint16_t)(wd[x >> 1] >> (16 * (x & 1))));
   }
 }
 
@@ -558,8 +567,10 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
 // ---------------------------------------------------------------------------------------------
 
 // NF: capacity for forced blocks (0: the forced range is ignored, and the key list stays small)
+// Two waves per SIMD (at most 256 registers each) where LDS allows eight workgroups per CU; the
+// forced variant's key list allows four.
 template <int NF>
-__global__ __launch_bounds__(64) void sel_g1_kernel(G1Args a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 ? 1 : 2))) void sel_g1_kernel(G1Args a) {
   __shared__ TileG1 tb;
   __shared__ int keys_lds[(64 + NF) * 16 + KT];   // source rows of the selected valid tokens, packed
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
