@@ -269,21 +269,20 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
   // staging: thread t copies the 16-byte piece (key t / 8, part t % 8) of both K and V; the next
   // tile's loads are issued before the current tile's compute
   const int s_key = threadIdx.x >> 3, s_part = threadIdx.x & 7;
+  // (no branch around the loads and no unpacking before the store: either would make the next
+  // tile's load wait at once; keys past the end repeat the last row, masked out of the scores)
   auto fetch = [&](int u, uint4& kv, uint4& vv) {
-    const int key = u * KT + s_key;
-    kv = make_uint4(0u, 0u, 0u, 0u);
-    vv = kv;
-    if (key < a.n_blk) {
-      kv = *reinterpret_cast<const uint4*>(kb + (size_t)key * stride + s_part * 8);
-      vv = *reinterpret_cast<const uint4*>(vb + (size_t)key * stride + s_part * 8);
-    }
+    const size_t off = (size_t)min(u * KT + s_key, a.n_blk - 1) * stride + s_part * 8;
+    kv = *reinterpret_cast<const uint4*>(kb + off);
+    vv = *reinterpret_cast<const uint4*>(vb + off);
   };
   auto store = [&](TileG1& t, const uint4& kv, const uint4& vv) {
     *reinterpret_cast<uint4*>(&t.k[s_key][s_part * 8]) = kv;
-    const bf16* e = reinterpret_cast<const bf16*>(&vv);
+    const uint32_t wd[4] = {vv.x, vv.y, vv.z, vv.w};
     const int pos = vt_pos_g1(s_key);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) t.vt[s_part * 8 + x][pos] = e[x];
+    for (int x = 0; x < 8; ++x)
+      t.vt[s_part * 8 + x][pos] = __builtin_bit_cast(bf16, (uint16_t)(wd[x >> 1] >> (16 * (x & 1))));
   };
   uint4 kv, vv;
   fetch(0, kv, vv);
