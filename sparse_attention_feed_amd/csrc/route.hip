@@ -168,11 +168,21 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
       hi[ax] = max(hi[ax], __shfl_xor(hi[ax], o, 64));
     }
   const int4* cent = reinterpret_cast<const int4*>(a.cent);
-  // pass 1: the bound T
+  // pass 1: the bound T (eight centroid loads in flight per lane, not one round trip per step)
   uint32_t lmin = 0xFFFFFFFFu;
-  for (int c = a.kv_lo + l; c < a.kv_hi; c += 64) {
-    const int4 e = cent[c];
-    lmin = min(lmin, box_dmax(e.x, e.y, e.z, lo, hi));
+  {
+    int c = a.kv_lo + l;
+    for (; c + 7 * 64 < a.kv_hi; c += 8 * 64) {
+      int4 e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = cent[c + 64 * j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lmin = min(lmin, box_dmax(e[j].x, e[j].y, e[j].z, lo, hi));
+    }
+    for (; c < a.kv_hi; c += 64) {
+      const int4 e = cent[c];
+      lmin = min(lmin, box_dmax(e.x, e.y, e.z, lo, hi));
+    }
   }
   int rank = 0;
   for (int i = 0; i < 64; ++i) {
@@ -192,19 +202,18 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
     bi[x] = -1;
   }
   int c = a.kv_lo;
+  // the next step's centroid is loaded one step ahead (lanes past the end load the last one)
+  int4 e_nx = make_int4(0, 0, 0, 0);
+  if (a.kv_hi > a.kv_lo) e_nx = cent[min(c + l, a.kv_hi - 1)];
   while (c < a.kv_hi) {
     int n = 0;
     // fill the chunk: up to PCH survivors (64 centroids per step; stop before a step could overflow)
     for (; c < a.kv_hi && n + 64 <= PCH; c += 64) {
       const int cc = c + l;
-      bool keep = false;
-      uint32_t dm = 0u;
-      int4 e = make_int4(0, 0, 0, 0);
-      if (cc < a.kv_hi) {
-        e = cent[cc];
-        dm = box_dmin(e.x, e.y, e.z, lo, hi);
-        keep = dm <= T;
-      }
+      const int4 e = e_nx;
+      e_nx = cent[min(cc + 64, a.kv_hi - 1)];
+      const uint32_t dm = box_dmin(e.x, e.y, e.z, lo, hi);
+      const bool keep = cc < a.kv_hi && dm <= T;
       const unsigned long long m = __builtin_amdgcn_ballot_w64(keep);
       if (keep) {
         const int pos = n + __builtin_popcountll(m & ((1ull << l) - 1ull));
