@@ -302,7 +302,15 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
           uint32_t best = 0xFFFFFFFFu;
           const int mc = a.blk_cnt[bb];
           const int2* mp = reinterpret_cast<const int2*>(a.lat) + (size_t)bb * a.cap;
-          for (int t = 0; t < mc; ++t) best = min(best, dist2(uxy, uz, mp[t]));
+          int t = 0;
+          for (; t + 8 <= mc; t += 8) {        // eight member loads in flight, then their d2
+            int2 m[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m[j] = mp[t + j];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) best = min(best, dist2(uxy, uz, m[j]));
+          }
+          for (; t < mc; ++t) best = min(best, dist2(uxy, uz, mp[t]));
           topk_insert<K>(bd, bk, bi, best, a.blk_key[bb], bb);
         }
     }
