@@ -413,6 +413,12 @@ def main():
             "traffic": measured_traffic(dominant, args.config),
         },
         "kernels_ms": {kk: round(vv, 4) for kk, vv in kern_ms.items()},
+        # geometric routing depends only on the token points, so a 24-layer model routes once per
+        # instance: the step with its routing time spread over 24 layers (context, not `value`)
+        "routing_amortised_24_layers": (
+            {"ms_per_step": round(ms_step - kern_ms["route_geometric"] * 23 / 24, 4),
+             "tokens_per_s": round(n_tok / ((ms_step - kern_ms["route_geometric"] * 23 / 24) * 1e-3), 1)}
+            if "route_geometric" in kern_ms else None),
         "algorithmic_gflop": {kk: round(vv / 1e9, 2) for kk, vv in fl.items()},
         "branch_breakdown": breakdown,
         "cpu_baseline": cpu,
