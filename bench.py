@@ -132,7 +132,10 @@ def setup_geometric(w, S, torch, dev):
         ]
 
     def flops():
-        return algorithmic_flops(w, ws["sel"].cpu().numpy())
+        out = algorithmic_flops(w, ws["sel"].cpu().numpy())
+        # grouped-query score routing: the compressed pass (for the lse) and the group scores
+        out["route_scores_gqa"] = out["cmp"] + 2 * w.head_dim * w.n_qh * int(w.blk_cnt.sum()) * w.n_blk
+        return out
 
     def branch(bits):
         nb = bin(bits).count("1")
@@ -169,6 +172,14 @@ def setup_geometric(w, S, torch, dev):
         vgeom = torch.empty(w.n_blk * 8 + w.n_slots * 2, dtype=torch.int32, device=dev)
         fns["route_views"] = lambda: S.route_geometric_views(L, pts, w.top_k, n_vol, vp_d, cb_d, cell_size=8, radius=1,
                                                              sel=vsel, centroids=vcent, geom=vgeom, want_d2=False)
+    # score routing in grouped-query form, the alternative to geometric routing: the compressed
+    # pass that gives every (token, head) its lse, then the top-k blocks by summed group probability
+    if w.dtype == "bf16" and w.top_k <= 64:
+        lse = torch.empty((w.n_slots, w.n_qh), dtype=torch.float32, device=dev)
+        ssel = torch.empty((w.n_slots, w.n_kvh, w.top_k), dtype=torch.int32, device=dev)
+        fns["route_scores_gqa"] = lambda: (
+            S.attn_fwd(L, S.BR_CMP, q, k_cmp=ws["k_cmp"], v_cmp=ws["v_cmp"], lse=lse, out=ws["out"]),
+            S.route_scores_topk(L, q, ws["k_cmp"], lse, w.top_k, sel=ssel))
     # the volume block table from the workload's SDF sampled on a (side + 1)^3 lattice
     if "tau" in w.meta:
         side = int(w.meta["vol_side"])
@@ -312,8 +323,8 @@ def main():
 
     fl = flops_fn()
     # the dominant kernel's branches: routing runs in its own kernel, and the forced-range variant
-    # is a separate breakdown item, not part of the timed step
-    dom_flops = sum(v for kk, v in fl.items() if kk not in ("route", "sel_forced_ref_frame"))
+    # and the score routing are separate breakdown items, not part of the timed step
+    dom_flops = sum(v for kk, v in fl.items() if kk not in ("route", "sel_forced_ref_frame", "route_scores_gqa"))
     achieved = dom_flops / (kern_ms[dominant] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     log("step %.3f ms; %s; %s %.1f TFLOP/s" % (ms_step, ", ".join("%s %.3f" % kv for kv in kern_ms.items()),

@@ -357,7 +357,14 @@ __global__ __launch_bounds__(256) void score_route_kernel(ScoreRouteArgs a) {
     qf.v = *reinterpret_cast<const decltype(qf.v)*>(qp);
   }
   const float c2 = a.scale * kLog2e;
-  const float lse2 = a.lse[(size_t)row * a.n_qh + j * GRP + r] * kLog2e;
+  // S = Q K^T per 16-key group: lane (r, g) gets heads 4g .. 4g+3 of key 16 kt + r, so the group
+  // sum over the 16 heads is three adds in the lane and two exchanges across lane groups
+  f32x4 nlse2;
+  {
+    const f32x4 ls = *reinterpret_cast<const f32x4*>(a.lse + (size_t)row * a.n_qh + j * GRP + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nlse2[i] = -ls[i] * kLog2e;
+  }
   float bv[K];
   uint32_t bk[K];
   int bi[K];
@@ -368,39 +375,36 @@ __global__ __launch_bounds__(256) void score_route_kernel(ScoreRouteArgs a) {
     bi[x] = -1;
   }
   const int kstride = a.n_kvh * HD;
-  const int own_kt = r >> 2, own_i = r & 3;   // the key of each 64-key step this lane ranks
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.n_blk; k0 += 64) {
-    float red[4][4];
+  // K fragments of a 64-key step (keys past the end read the last key; they are never ranked),
+  // loaded one step ahead of their use
+  auto load_step = [&](int k0, Frag8<T> (&kf)[4], uint32_t& bkey) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const int key = k0 + 16 * kt + r;
-      Frag8<T> kf;
-      if (key < a.n_blk)
-        kf.v = *reinterpret_cast<const decltype(kf.v)*>(kc + (size_t)key * kstride + j * HD + 8 * g);
-      else
-        kf.v = decltype(kf.v){};
-      f32x4 s = mma16(kf, qf, z);      // lane: head r, keys k0 + 16kt + 4g + i
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2));
-        // sum over the 16 heads of the group = the 16 lanes of this row
-        p += __shfl_xor(p, 1, 64);
-        p += __shfl_xor(p, 2, 64);
-        p += __shfl_xor(p, 4, 64);
-        p += __shfl_xor(p, 8, 64);
-        red[kt][i] = p;
-      }
+      const int key = min(k0 + 16 * kt + r, a.n_blk - 1);
+      kf[kt].v = *reinterpret_cast<const decltype(kf[kt].v)*>(kc + (size_t)key * kstride + j * HD + 8 * g);
     }
-    float val = red[0][0];
+    bkey = a.blk_key[min(k0 + 16 * g + r, a.n_blk - 1)];   // the key this lane ranks
+  };
+  Frag8<T> kcur[4], knext[4];
+  uint32_t bkcur, bknext = 0u;
+  load_step(0, kcur, bkcur);
+  for (int k0 = 0; k0 < a.n_blk; k0 += 64) {
+    if (k0 + 64 < a.n_blk) load_step(k0 + 64, knext, bknext);
+    float val = 0.f;                   // the group importance of key k0 + 16 g + r (this lane ranks it)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt) {
+      const f32x4 s = mma16(qf, kcur[kt], z);   // lane: heads 4g + i, key k0 + 16 kt + r
+      float p = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (kt == own_kt && i == own_i) val = red[kt][i];
-    const int idx = k0 + 16 * own_kt + 4 * g + own_i;
+      for (int i = 0; i < 4; ++i) p += __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, nlse2[i]));
+      p += __shfl_xor(p, 16, 64);
+      p += __shfl_xor(p, 32, 64);
+      val = kt == g ? p : val;
+    }
+    const int idx = k0 + 16 * g + r;
     if (idx < a.n_blk) {
-      const uint32_t key = a.blk_key[idx];
+      const uint32_t key = bkcur;
       if (better(val, key, bv[K - 1], bk[K - 1])) {
 #pragma unroll
         for (int x = K - 1; x > 0; --x) {
@@ -423,6 +427,9 @@ __global__ __launch_bounds__(256) void score_route_kernel(ScoreRouteArgs a) {
         }
       }
     }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) kcur[kt] = knext[kt];
+    bkcur = bknext;
   }
   // merge the 64 per-lane lists: top_k rounds of a wave arg-best over the list heads
   for (int x = 0; x < a.top_k; ++x) {
