@@ -7,7 +7,12 @@ method's arithmetic.
 
 Every function is written from the pages' statement of the method, in the plainest form: explicit
 loops over query rows and blocks, numpy for the small per-row vector products, float64 throughout
-(inputs are first widened exactly from their float32 / bfloat16 values).
+(inputs are first widened exactly from their float32 / bfloat16 values).  The active-voxel rule and
+the view projection are float64 too: a device that decides them in float32 can differ only where
+the float64 value lies within its rounding error of a threshold or a cell edge, and the tests
+count and leave out exactly those cases.  check_route_geometric is a vectorised whole-table check
+of a routing result against route_geometric's definition (test infrastructure for full-size
+tables); every function here is pinned by tests/test_oracle*.py.
 
 Sources (cited by page title and section; no page prints code or worked numbers):
   [LSRM-cn]  hyper.ai summary of "LSRM" (arXiv 2604.05182), section 方法 (Method):
@@ -170,39 +175,44 @@ def _morton3_u(x, y, z):
     return code
 
 
-def voxel_activity(sdf, N, tau):
+def voxel_activity(sdf, N, tau, return_values=False):
     """Active voxels of an N^3 grid over [-1, 1]^3, [LSRM-cn] eq. M^vol: voxel (i, j, k) is active iff
     over its 4^3 sub-sample points min |s_t| <= tau or (min s_t) (max s_t) <= 0, with
     s_t = Trilinear(sdf; p_t) (the dense stage's decoder taken as the identity on an SDF volume).
 
     sdf [G][G][G] (z, y, x) holds values at the lattice points -1 + 2 g / (G - 1).  Sub-sample m of an
-    axis (m = 4 i + a) sits at grid coordinate u = (2m + 1)(G - 1) / (8N).  The decision is taken in
-    float32 in this order (the device's precision): u by one rounded division; cell g0 = floor(u)
-    (at most G - 2) and fraction f = u - g0; lerp(a, b, f) = a + f (b - a), rounded after every
-    operation, along x, then y, then z.  Returns bool [N][N][N] (z, y, x)."""
-    f32 = np.float32
-    sdf = np.asarray(sdf, dtype=f32)
+    axis (m = 4 i + a, a < 4) sits at the centre of its quarter of the voxel, -1 + (2m + 1) / (4N),
+    i.e. at lattice coordinate u = (2m + 1)(G - 1) / (8N).  Trilinear interpolation in the lattice
+    cell holding u: linear interpolation a + f (b - a) along x, then y, then z (exact on a constant
+    field and at the lattice points); everything in float64, and tau is taken as given.
+    Returns bool [N][N][N] (z, y, x); with return_values also the float64 per-voxel min |s|, min s
+    and max s over the sub-samples (for callers that bound another precision's decision)."""
+    sdf = np.asarray(sdf, dtype=np.float64)
     G = sdf.shape[0]
     m = np.arange(4 * N, dtype=np.int64)
-    u = ((2 * m + 1) * (G - 1)).astype(f32) / f32(8 * N)
+    u = (2 * m + 1) * (G - 1) / (8.0 * N)                # exact rational, one float64 rounding
     g0 = np.minimum(np.floor(u).astype(np.int64), G - 2)
-    fr = (u - g0.astype(f32)).astype(f32)
+    fr = u - g0
 
     def lerp(a, b, t):
-        return (a + (t * (b - a)).astype(f32)).astype(f32)
+        return a + t * (b - a)
 
+    # the interpolation is separable: along x for every lattice row, then y, then z
+    ax = lerp(sdf[:, :, g0], sdf[:, :, g0 + 1], fr[None, None, :])             # [G][G][4N]
+    ay = lerp(ax[:, g0, :], ax[:, g0 + 1, :], fr[None, :, None])               # [G][4N][4N]
     act = np.zeros((N, N, N), dtype=bool)
+    mabs = np.zeros((N, N, N))
+    mins = np.zeros((N, N, N))
+    maxs = np.zeros((N, N, N))
     for k in range(N):                                 # one z-slab of voxels (4 sub-sample planes)
         mz = np.arange(4 * k, 4 * k + 4)
-        zz, yy, xx = np.meshgrid(mz, np.arange(4 * N), np.arange(4 * N), indexing="ij")
-        x0, y0, z0 = g0[xx], g0[yy], g0[zz]
-        fx, fy, fz = fr[xx], fr[yy], fr[zz]
-        v = lambda a, b, c: sdf[z0 + c, y0 + b, x0 + a]     # noqa: E731
-        s = lerp(lerp(lerp(v(0, 0, 0), v(1, 0, 0), fx), lerp(v(0, 1, 0), v(1, 1, 0), fx), fy),
-                 lerp(lerp(v(0, 0, 1), v(1, 0, 1), fx), lerp(v(0, 1, 1), v(1, 1, 1), fx), fy), fz)
+        s = lerp(ay[g0[mz]], ay[g0[mz] + 1], fr[mz][:, None, None])              # [4][4N][4N]
         s = s.reshape(4, N, 4, N, 4).transpose(1, 3, 0, 2, 4).reshape(N, N, 64)   # [j][i][64 samples]
-        mn, mx = s.min(axis=2), s.max(axis=2)
-        act[k] = (np.abs(s).min(axis=2) <= f32(tau)) | ((mn * mx).astype(f32) <= 0)
+        mn, mx, ma = s.min(axis=2), s.max(axis=2), np.abs(s).min(axis=2)
+        act[k] = (ma <= tau) | ((mn <= 0) & (mx >= 0))     # (min s)(max s) <= 0, as a sign test
+        mabs[k], mins[k], maxs[k] = ma, mn, mx
+    if return_values:
+        return act, mabs, mins, maxs
     return act
 
 
@@ -279,6 +289,61 @@ def route_geometric(pts, blk_cnt, blk_key, cap, top_k, rows=None):
         sel[i, :kk] = order
         dd[i, :kk] = d2[order]
     return sel, dd
+
+
+def check_route_geometric(pts, blk_cnt, blk_key, cap, sel, d2, rows=None, chunk=2048):
+    """Whole-table check of a geometric routing result (rows of sel / d2 for the slots `rows`,
+    default every slot) against the definition of route_geometric, vectorised so that it covers
+    every row of a full-size table:
+      * padding rows hold -1 / 0xFFFFFFFF throughout;
+      * a valid row lists kk = min(top_k, n_blk) block indices in [0, n_blk), then -1 / 0xFFFFFFFF;
+      * each listed d2 is the exact integer squared distance from the token's lattice point to the
+        block centroid;
+      * the listed (d2, blk_key) pairs strictly ascend (so they are distinct);
+      * exactly kk - 1 blocks of all n_blk have a (d2, blk_key) pair smaller than the last listed
+        one, so the listed blocks are the kk smallest: the unique top-k of the total order.
+    Returns the number of rows that fail (0 for a correct table) and the first failing slots."""
+    import torch
+    blk_cnt = np.asarray(blk_cnt)
+    n_blk = blk_cnt.shape[0]
+    S = n_blk * cap
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    sel = np.asarray(sel).astype(np.int64)
+    d2 = np.asarray(d2).astype(np.int64)
+    top_k = sel.shape[1]
+    kk = min(top_k, n_blk)
+    valid = valid_mask(blk_cnt, cap)[rows]
+    cen = torch.from_numpy(block_centroids(pts, blk_cnt, cap))                        # [n_blk, 3]
+    u = torch.from_numpy(lattice_coords(np.asarray(pts)[rows]))                        # [R, 3]
+    key = torch.from_numpy(np.asarray(blk_key, dtype=np.int64))
+    tsel = torch.from_numpy(sel)
+    td2 = torch.from_numpy(d2)
+    bad = torch.zeros(rows.shape[0], dtype=torch.bool)
+    # padding rows and the tails of valid rows
+    tail_ok = (tsel[:, kk:] == -1).all(1) & (td2[:, kk:] == 0xFFFFFFFF).all(1)
+    pad_ok = (tsel == -1).all(1) & (td2 == 0xFFFFFFFF).all(1)
+    tv = torch.from_numpy(valid)
+    bad |= ~tv & ~pad_ok
+    bad |= tv & ~tail_ok
+    head = tsel[:, :kk]
+    in_range = ((head >= 0) & (head < n_blk)).all(1)
+    bad |= tv & ~in_range
+    for lo in range(0, rows.shape[0], chunk):
+        hi = min(lo + chunk, rows.shape[0])
+        v = tv[lo:hi] & in_range[lo:hi]
+        if not bool(v.any()):
+            continue
+        h = head[lo:hi].clamp(0, n_blk - 1)
+        dall = ((u[lo:hi, None, :] - cen[None, :, :]) ** 2).sum(2)                    # [r, n_blk]
+        listed = torch.gather(dall, 1, h)                                               # exact d2 of the list
+        rk_all = dall * (1 << 32) + key[None, :]
+        rk = listed * (1 << 32) + key[h]
+        ok = (listed == td2[lo:hi, :kk]).all(1)
+        ok &= (rk[:, 1:] > rk[:, :-1]).all(1) if kk > 1 else torch.ones_like(ok)
+        ok &= (rk_all < rk[:, -1:]).sum(1) == kk - 1
+        bad[lo:hi] |= v & ~ok
+    nbad = int(bad.sum())
+    return nbad, rows[bad.numpy()][:10]
 
 
 # ----------------------------------------------------------------------------------------------
@@ -435,7 +500,9 @@ def nsa_forward(w, rows=None, return_parts=False, forced=None):
     compress K and V (and Q for block-granular queries), route, run the branches listed in
     w.branches and combine them with the sigmoid gates (channel c = c-th listed branch).
     Geometric routing ([LSRM-cn]) is per token and shared by all heads; score routing ([Speed3R])
-    with one query head per KV head is per (query block, head) from the pooled queries."""
+    with one query head per KV head is per (query block, head) from the pooled queries; score
+    routing with several query heads per KV head is per (token, KV group) from the summed group
+    probabilities, with the compressed branch's lse."""
     cap = w.blk_cap
     S = w.n_slots
     rows = np.arange(S) if rows is None else np.asarray(rows)
@@ -450,14 +517,22 @@ def nsa_forward(w, rows=None, return_parts=False, forced=None):
         sel = np.full((S, w.top_k), -1, dtype=np.int32)
         sel[rows] = sel_rows
         q_gran_sel = "token"
-    else:
-        if w.n_qh != w.n_kvh:
-            raise NotImplementedError("whole-layer score routing is defined here for Hq == Hkv")
-        # routing rows are per query block; only the blocks holding the requested rows are needed
+    elif w.n_qh == w.n_kvh:
+        # [Speed3R] 2.1: routing rows are per query block, from the pooled queries; only the blocks
+        # holding the requested rows are needed
         need = np.unique(rows // cap)
         sel = np.full((w.n_blk, w.n_kvh, w.top_k), -1, dtype=np.int32)
         sel[need], _ = route_scores(parts["q_cmp"][need], k_cmp, w.blk_key, w.scale, w.top_k)
         q_gran_sel = "block"
+    else:
+        # [LSRM-cn] "standard NSA" selection under grouped-query attention: per token and KV group,
+        # the blocks with the largest summed softmax probability of the group's heads against the
+        # compressed keys; the normalisers are the compressed branch's lse for the same rows
+        _, lse_rows = attn_branch(CMP, w.q, k_cmp, v_cmp, w.blk_cnt, cap, w.scale, rows=rows)
+        ok = valid_mask(w.blk_cnt, cap)[rows]
+        sel = np.full((S, w.n_kvh, w.top_k), -1, dtype=np.int32)
+        sel[rows], _ = route_scores(w.q[rows], k_cmp, w.blk_key, w.scale, w.top_k, lse=lse_rows, row_valid=ok)
+        q_gran_sel = "token"
     parts["sel"] = sel
     outs = []
     for name in w.branches:
@@ -485,15 +560,17 @@ def nsa_forward(w, rows=None, return_parts=False, forced=None):
 # routing with image blocks found through the views
 # ----------------------------------------------------------------------------------------------
 
+def project_coord(p, proj_row):
+    """Continuous patch coordinate of point p along one image axis of a view: the affine map
+    A0 p0 + A1 p1 + A2 p2 + A3 (an orthographic camera), in float64 on the given float32 values."""
+    a = np.asarray(proj_row, dtype=np.float64)
+    x = np.asarray(p, dtype=np.float64)
+    return float(a[0] * x[0] + a[1] * x[1] + a[2] * x[2] + a[3])
+
+
 def project_cell(p, proj_row, cell):
-    """Cell coordinate of point p along one image axis: the patch coordinate
-    ((A0 p0 + A1 p1) + A2 p2) + A3, each operation rounded to float32 in that order, divided by
-    the cell size (a power of two, so exact) and floored."""
-    f32 = np.float32
-    x = f32(f32(f32(proj_row[0]) * f32(p[0])) + f32(f32(proj_row[1]) * f32(p[1])))
-    x = f32(x + f32(f32(proj_row[2]) * f32(p[2])))
-    x = f32(x + f32(proj_row[3]))
-    return int(math.floor(float(x) / cell))     # cells far outside the grid all give empty windows
+    """Cell coordinate of point p along one image axis: floor(patch coordinate / cell size)."""
+    return int(math.floor(project_coord(p, proj_row) / cell))  # cells far outside the grid give empty windows
 
 
 def route_geometric_views(pts, blk_cnt, blk_key, cap, top_k, n_vol_blk, view_proj, cell_blk, cell, radius,

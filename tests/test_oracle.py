@@ -413,7 +413,7 @@ def test_volume_ramp_hand_fixture():
 def test_volume_constant_sdf():
     g = np.full((3, 3, 3), 0.3, dtype=np.float32)
     assert not O.voxel_activity(g, 8, 0.2).any()
-    assert O.voxel_activity(g, 8, 0.3).all()
+    assert O.voxel_activity(g, 8, float(np.float32(0.3))).all()       # tau equal to the stored value
     assert O.voxel_activity(np.zeros((3, 3, 3), np.float32), 8, 0.0).all()       # s = 0: min * max <= 0
 
 
@@ -424,7 +424,9 @@ def _subsample_coords(N):
 
 def test_volume_linear_sdf_matches_closed_form():
     """Trilinear interpolation reproduces a linear SDF, so activity follows from the analytic values
-    at the sub-samples (cases within 1e-5 of the threshold or of zero are not asserted)."""
+    at the sub-samples.  The oracle computes in float64 on the float32 lattice, whose values carry
+    the float32 rounding of the linear function (below 1e-7 here), so only voxels within 1e-6 of
+    the threshold or of zero are left out; their count is reported and must be tiny."""
     G, N, tau = 5, 8, 0.07
     a = np.array([0.6, -0.3, 0.2])
     c0 = 0.013
@@ -438,8 +440,9 @@ def test_volume_linear_sdf_matches_closed_form():
     s = s.reshape(N, 4, N, 4, N, 4).transpose(0, 2, 4, 1, 3, 5).reshape(N, N, N, 64)
     want = (np.abs(s).min(axis=3) <= tau) | (s.min(axis=3) * s.max(axis=3) <= 0)
     margin = np.minimum(np.abs(np.abs(s).min(axis=3) - tau), np.abs(s).min(axis=3))
-    ok = margin > 1e-5
-    assert ok.mean() > 0.95
+    ok = margin > 1e-6
+    print("linear SDF: %d of %d voxels within 1e-6 of a threshold" % ((~ok).sum(), ok.size))
+    assert ok.mean() > 0.999
     np.testing.assert_array_equal(act[ok], want[ok])
 
 

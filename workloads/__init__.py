@@ -5,7 +5,8 @@ random q/k/v/gate tensors.  It holds none of the method's arithmetic (no pooling
 attention or gating) so that the CPU oracle and the GPU path stay independent of each other.
 
 Workload shapes follow the LSRM pages (hyper.ai summary of arXiv 2604.05182, section "方法"):
-volume tokens on a voxel grid activated near the object surface (eq. M^vol), image tokens from
+volume tokens on a voxel grid near the object surface (here a plain band around the surface of an
+analytic SDF, sized to the target count), image tokens from
 foreground patches of several views, grouped-query attention with 32 query heads over 2 KV heads
 of dimension 32, and spatial blocks of 64 tokens.  The score-routed long-sequence shape follows the
 Speed3R page (gist.science summary of arXiv 2603.08055, section 2.1): 4x4-pooled multi-view grids.
@@ -120,7 +121,8 @@ class Workload:
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.head_dim)
+        """Softmax scale: 1/sqrt(D), unless the input names another in meta['scale']."""
+        return float(self.meta.get("scale", 1.0 / math.sqrt(self.head_dim)))
 
     def valid_mask(self) -> np.ndarray:
         slot = np.arange(self.n_slots)
@@ -163,39 +165,18 @@ def _voxel_centres(idx: np.ndarray, side: int) -> np.ndarray:
     return (-1.0 + (2.0 * idx.astype(np.float64) + 1.0) / side).astype(np.float32)
 
 
-def _active_voxels(side: int, sdf, target: int, prefilter: float) -> tuple:
-    """Activation rule of eq. M^vol (LSRM, section 方法): a voxel is active iff the minimum |s| over
-    its 4^3 sub-samples is <= tau or the samples change sign.  tau is chosen as the smallest value
-    reaching `target` active voxels.  sdf takes voxel-unit coordinates [n,3] and returns [n]."""
+def _active_voxels(side: int, sdf, target: int) -> tuple:
+    """The `target` voxels whose centres lie nearest the surface: a band |sdf(centre)| <= tau, with
+    tau the target-th smallest |sdf| over the voxel centres (ties by voxel index), so the count is
+    exact.  A plain surface band for shaping the input geometry; the method's own activation rule
+    is not applied here.  sdf takes voxel-unit coordinates [n,3] and returns [n]."""
     g = np.arange(side, dtype=np.float64) + 0.5
     zz, yy, xx = np.meshgrid(g, g, g, indexing="ij")
     centres = np.stack([xx.ravel(), yy.ravel(), zz.ravel()], axis=1)
-    s_c = sdf(centres)
-    cand = np.nonzero(np.abs(s_c) <= prefilter)[0]
-    off = (np.arange(4, dtype=np.float64) + 0.5) / 4.0 - 0.5
-    oz, oy, ox = np.meshgrid(off, off, off, indexing="ij")
-    offs = np.stack([ox.ravel(), oy.ravel(), oz.ravel()], axis=1)      # [64, 3]
-    minabs = np.empty(cand.shape[0])
-    cross = np.empty(cand.shape[0], dtype=bool)
-    chunk = 65536
-    for s in range(0, cand.shape[0], chunk):
-        c = centres[cand[s:s + chunk]]
-        p = (c[:, None, :] + offs[None, :, :]).reshape(-1, 3)
-        st = sdf(p).reshape(-1, 64)
-        minabs[s:s + chunk] = np.abs(st).min(axis=1)
-        cross[s:s + chunk] = st.min(axis=1) * st.max(axis=1) <= 0
-    n_cross = int(cross.sum())
-    rest = np.sort(minabs[~cross])
-    need = target - n_cross
-    if need <= 0:
-        tau = 0.0
-    else:
-        if need > rest.shape[0]:
-            raise ValueError("prefilter too small for the requested active count")
-        tau = float(rest[need - 1])
-    if tau + 1.0 > prefilter:
-        raise ValueError("prefilter too small for tau=%g" % tau)
-    active = cand[cross | (minabs <= tau)]
+    a = np.abs(sdf(centres))
+    order = np.argsort(a, kind="stable")
+    active = np.sort(order[:target])
+    tau = float(a[order[target - 1]])
     ix = active % side
     iy = (active // side) % side
     iz = active // (side * side)
@@ -365,13 +346,13 @@ def _lsrm_geometric(name, seed, dtype, vol_side, vol_shape, vol_target, n_views,
     elif vol_shape == "sphere":
         cen = np.full(3, half) + rng.uniform(-2.0, 2.0, size=3)
         rad = rng.uniform(0.80, 0.90) * half
-        vox, tau = _active_voxels(vol_side, _sphere_sdf(cen, rad), vol_target, prefilter=16.0)
+        vox, tau = _active_voxels(vol_side, _sphere_sdf(cen, rad), vol_target)
         sph_c = -1.0 + 2.0 * cen / vol_side
         sph_r = rad / half
         meta.update(tau=tau, sphere_centre=cen.tolist(), sphere_radius=rad)
     elif vol_shape == "sphere_torus":
         ph = rng.uniform(0.0, 2.0 * math.pi, size=3)
-        vox, tau = _active_voxels(vol_side, _sphere_torus_sdf(vol_side, ph), vol_target, prefilter=16.0)
+        vox, tau = _active_voxels(vol_side, _sphere_torus_sdf(vol_side, ph), vol_target)
         sph_c = np.zeros(3)
         sph_r = 0.62
         meta.update(tau=tau, sdf_phases=ph.tolist())
