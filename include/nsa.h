@@ -3,8 +3,9 @@
  *
  * C ABI.  Every pointer argument is a DEVICE pointer unless it is marked "host".  Every call only
  * validates its arguments on the host and enqueues kernels on the caller's stream: NSA_OK means
- * "enqueued", not "finished".  The library never allocates, frees or synchronises, keeps no
- * per-call state, and is safe to call from several host threads.  The caller owns every buffer.
+ * "enqueued", not "finished".  The library never allocates, frees or synchronises (apart from the
+ * opt-in debug check below), keeps no per-call state, and is safe to call from several host
+ * threads.  The caller owns every buffer.
  *
  * Status convention for every call:
  *   NSA_ERR_INVALID      a null pointer, a non-positive size, inconsistent sizes (e.g. n_qh not a
@@ -25,7 +26,11 @@
  * Padding slots are never read as keys or queries; every output row of a padding slot is written
  * as 0 (attention, gate), -1 (routing indices) or -inf (lse).
  * Device-side preconditions (not checked on the host): 1 <= blk_cnt[b] <= blk_cap; blk_key values
- * are unique; points lie in [-1, 1]; routing indices are -1 or in [0, n_blk).
+ * are unique; points lie in [-1, 1]; routing indices are -1 or in [0, n_blk).  With the environment
+ * variable NSA_DEBUG_CHECKS=1, every call that takes a layout first copies blk_cnt to the host
+ * (synchronising the device) and returns NSA_ERR_INVALID if a count lies outside 1..blk_cap.
+ * Alignment: every q, k, v, q_cmp, k_cmp, v_cmp, o and lse pointer must be 16-byte aligned
+ * (NSA_ERR_UNSUPPORTED otherwise): the kernels read them with 16-byte vector loads.
  */
 #ifndef NSA_H
 #define NSA_H

@@ -99,10 +99,28 @@ def _dtype(t):
     raise ValueError("unsupported dtype %s" % t.dtype)
 
 
-class BlockLayout:
-    """Block-major token layout: blk_cnt / blk_key device tensors plus the head shape."""
+def validate_layout(blk_cnt, blk_key, blk_cap):
+    """Host-side check of the layout preconditions the kernels assume without checking:
+    1 <= blk_cnt[b] <= blk_cap and unique blk_key values.  Copies the tensors to the host (which
+    synchronises a device); raises ValueError naming the first violation."""
+    cnt = blk_cnt.detach().cpu().to(torch.int64)
+    bad = torch.nonzero((cnt < 1) | (cnt > int(blk_cap))).flatten()
+    if bad.numel():
+        b = int(bad[0])
+        raise ValueError("blk_cnt[%d] = %d is outside 1..%d" % (b, int(cnt[b]), int(blk_cap)))
+    if blk_key is not None:
+        key = blk_key.detach().cpu().to(torch.int64) & 0xFFFFFFFF
+        if torch.unique(key).numel() != key.numel():
+            raise ValueError("blk_key values are not unique")
 
-    def __init__(self, blk_cnt, blk_key, blk_cap, n_qh, n_kvh, head_dim, scale=None):
+
+class BlockLayout:
+    """Block-major token layout: blk_cnt / blk_key device tensors plus the head shape.  With
+    validate=True the preconditions are checked on the host first (validate_layout)."""
+
+    def __init__(self, blk_cnt, blk_key, blk_cap, n_qh, n_kvh, head_dim, scale=None, validate=False):
+        if validate:
+            validate_layout(blk_cnt, blk_key, blk_cap)
         self.blk_cnt = blk_cnt
         self.blk_key = blk_key
         self.blk_cap = int(blk_cap)

@@ -32,6 +32,34 @@ nsa_status hip_status(hipError_t e, const char* what) {
   return NSA_OK;
 }
 
+// Every tensor a kernel reads with 16-byte vector loads must start on a 16-byte boundary (NULL is
+// accepted: unused pointers are checked elsewhere).
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Opt-in debug check of the device-side preconditions on blk_cnt (NSA_DEBUG_CHECKS=1): copies the
+// counts to the host, which synchronises the device, and verifies 1 <= blk_cnt[b] <= blk_cap.  Off
+// by default: the library otherwise never synchronises.
+nsa_status debug_check_counts(const nsa_layout* L, const char* fn) {
+  const char* e = getenv("NSA_DEBUG_CHECKS");
+  if (e == nullptr || e[0] != '1') return NSA_OK;
+  int32_t* h = static_cast<int32_t*>(malloc(sizeof(int32_t) * (size_t)L->n_blk));
+  if (h == nullptr) return fail(NSA_ERR_INVALID, "%s: debug check: out of host memory", fn);
+  const hipError_t err = hipMemcpy(h, L->blk_cnt, sizeof(int32_t) * (size_t)L->n_blk, hipMemcpyDeviceToHost);
+  if (err != hipSuccess) {
+    free(h);
+    return fail(NSA_ERR_HIP, "%s: debug check: reading blk_cnt: %s", fn, hipGetErrorString(err));
+  }
+  nsa_status st = NSA_OK;
+  for (int32_t b = 0; b < L->n_blk; ++b) {
+    if (h[b] < 1 || h[b] > L->blk_cap) {
+      st = fail(NSA_ERR_INVALID, "%s: debug check: blk_cnt[%d] = %d is outside 1..%d", fn, b, h[b], L->blk_cap);
+      break;
+    }
+  }
+  free(h);
+  return st;
+}
+
 // Every entry point calls this after validation and before any HIP call.
 #define NSA_FORCED_FAILURE(fn)                                                                 \
   do {                                                                                         \
@@ -49,10 +77,11 @@ nsa_status check_layout(const nsa_layout* L, const char* fn) {
   if (!(L->scale > 0.f) || L->scale > 1e30f) return fail(NSA_ERR_INVALID, "%s: scale must be a positive finite value", fn);
   if (L->blk_cnt == nullptr) return fail(NSA_ERR_INVALID, "%s: blk_cnt is NULL", fn);
   if ((long long)L->n_blk * L->blk_cap > 0x7FFFFFFFLL) return fail(NSA_ERR_INVALID, "%s: too many slots", fn);
-  return NSA_OK;
+  return debug_check_counts(L, fn);
 }
 
 bool dtype_ok(nsa_dtype d) { return d == NSA_F32 || d == NSA_BF16; }
+
 
 }  // namespace
 
@@ -221,6 +250,8 @@ nsa_status nsa_route_scores_topk(const nsa_layout* L, nsa_dtype dtype, nsa_qgran
   if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "nsa_route_scores_topk: top_k must be in 1..64");
   const int G = L->n_qh / L->n_kvh;
   if (G > 1 && lse == nullptr) return fail(NSA_ERR_INVALID, "nsa_route_scores_topk: lse is required when n_qh > n_kvh");
+  if (!aligned16(q) || !aligned16(k_cmp) || !aligned16(lse))
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: q, k_cmp and lse must be 16-byte aligned");
   if (G == 1) {
     if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK || dtype != NSA_BF16)
       return fail(NSA_ERR_UNSUPPORTED,
@@ -288,6 +319,9 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
     return fail(NSA_ERR_UNSUPPORTED, "%s: a gate stride needs the grouped-query kernel (head_dim 32)", fn);
   if (lse != nullptr && n_named != 1) return fail(NSA_ERR_INVALID, "%s: lse needs exactly one branch", fn);
   if (o == nullptr || q == nullptr) return fail(NSA_ERR_INVALID, "%s: q and o must be non-NULL", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_cmp) || !aligned16(k_cmp) ||
+      !aligned16(v_cmp) || !aligned16(o))
+    return fail(NSA_ERR_UNSUPPORTED, "%s: q, k, v, q_cmp, k_cmp, v_cmp and o must be 16-byte aligned", fn);
   if ((branches & (NSA_BR_SEL | NSA_BR_LOC)) && (k == nullptr || v == nullptr))
     return fail(NSA_ERR_INVALID, "%s: SEL and LOC need k and v", fn);
   if ((branches & NSA_BR_CMP) && (k_cmp == nullptr || v_cmp == nullptr))
@@ -450,6 +484,8 @@ nsa_status dense_gated_xattn_fwd(nsa_dtype dtype, int32_t n_tok, int32_t n_x, in
   if (!(scale > 0.f) || scale > 1e30f) return fail(NSA_ERR_INVALID, "dense_gated_xattn_fwd: bad scale");
   if (q == nullptr || k == nullptr || v == nullptr || gate_logits == nullptr || o == nullptr)
     return fail(NSA_ERR_INVALID, "dense_gated_xattn_fwd: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(NSA_ERR_UNSUPPORTED, "dense_gated_xattn_fwd: q, k and v must be 16-byte aligned");
   if (head_dim != 32 || n_qh / n_kvh != 16)
     return fail(NSA_ERR_UNSUPPORTED, "dense_gated_xattn_fwd: compiled for head_dim 32, 16 query heads per KV head");
   NSA_FORCED_FAILURE("dense_gated_xattn_fwd");

@@ -102,8 +102,10 @@ def test_forced_all_blocks_is_dense_attention():
 
 def test_forced_layer_full_size_sampled():
     """The whole score-routed layer at full size with the reference frame forced: pooled Q/K/V, score
-    routing, gated compressed + selected branches, sampled tokens against the oracle's branches on
-    the GPU's routing rows and pooled values (inputs of the attention call)."""
+    routing, gated compressed + selected branches.  Sampled tokens against the oracle's layer on the
+    oracle's own pooled values (rounded to bf16) and routing rows, for the (token, head) pairs whose
+    routing row the GPU chose identically (near-ties may order differently: checked in the
+    score-routing tests)."""
     import sparse_attention_feed_amd as S
     w = wl("speed3r")
     d = to_dev(w)
@@ -119,9 +121,15 @@ def test_forced_layer_full_size_sampled():
     torch.cuda.synchronize()
     rng = np.random.default_rng(12)
     toks = np.sort(rng.choice(w.valid_slots(), 48, replace=False))
-    qch, kch, vch, selh = host(qc), host(kc), host(vc), host(sel)
-    o_cmp, _ = O.attn_branch(O.CMP, qch, kch, vch, w.blk_cnt, w.blk_cap, w.scale, q_gran="block", rows=toks)
-    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=selh, q_gran="block",
+    qr, kr, vr = (rounded(O.pool_blocks(x, w.blk_cnt, w.blk_cap), "bf16") for x in (w.q, w.k, w.v))
+    blocks = np.unique(toks // w.blk_cap)
+    sel_o = np.full((w.n_blk, w.n_kvh, w.top_k), -1, dtype=np.int32)
+    sel_o[blocks], _ = O.route_scores(qr[blocks], kr, w.blk_key, w.scale, w.top_k)
+    o_cmp, _ = O.attn_branch(O.CMP, qr, kr, vr, w.blk_cnt, w.blk_cap, w.scale, q_gran="block", rows=toks)
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel_o, q_gran="block",
                              rows=toks, forced=fr)
     ref = O.gate_combine([o_cmp, o_sel], w.gates[toks])
-    assert max_err(host(o)[toks], ref) <= 2e-2
+    same = np.all(host(sel)[toks // w.blk_cap] == sel_o[toks // w.blk_cap], axis=2)
+    assert same.mean() >= 0.8, same.mean()
+    diff = np.abs(host(o)[toks] - ref).max(axis=2)
+    assert diff[same].max() <= 2e-2

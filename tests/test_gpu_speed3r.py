@@ -48,7 +48,7 @@ def check_eps_ties(got, ref_sel, imp, k, eps_rel):
                 continue
             kth = np.sort(imp[r, h])[::-1][k - 1]
             for b in set(g_row.tolist()) ^ set(r_row.tolist()):
-                assert abs(imp[r, h, b] - kth) <= eps_rel * abs(kth) + 1e-3, (r, h, b)
+                assert abs(imp[r, h, b] - kth) <= eps_rel * abs(kth), (r, h, b)
     return exact / (R * H)
 
 
@@ -192,6 +192,11 @@ def test_fused_layer_block_rows():
 
 
 def test_full_size_sampled():
+    """The whole layer at full size (25,600 blocks).  Independent of the GPU's intermediate results:
+    pooling is compared element-wise with the oracle's on every block; routing is checked on 200
+    sampled block rows against the oracle's routing of the oracle's own pooled values (rounded to
+    bf16); the layer output on sampled tokens is compared with the oracle's layer on its own pooled
+    values and routing, for the (token, head) pairs whose routing row the GPU chose identically."""
     import sparse_attention_feed_amd as S
     say("generate speed3r")
     w = wl("speed3r")
@@ -205,20 +210,30 @@ def test_full_size_sampled():
     o = S.attn_fwd(L, S.BR_CMP | S.BR_SEL, d["q"], d["k"], d["v"], q_cmp=qc, k_cmp=kc, v_cmp=vc, sel=sel,
                    top_k=w.top_k, sel_groups=w.n_kvh, gates=d["gates"], q_gran=S.Q_BLOCK)
     torch.cuda.synchronize()
+    qr, kr, vr = pooled(w)                                  # the oracle's pooling, rounded to bf16
+    for got, ref in ((qc, qr), (kc, kr), (vc, vr)):
+        # fp32 accumulation then one bf16 rounding against the rounded fp64 mean: at most one bf16
+        # ulp apart (2^-7 of the larger magnitude), plus the fp32 accumulation error near zero
+        g = host(got)
+        assert np.all(np.abs(g - ref) <= 2.0 ** -7 * np.maximum(np.abs(g), np.abs(ref)) + 1e-6), "pooling"
     rng = np.random.default_rng(11)
-    # routing: sampled block rows against the oracle on the GPU's own pooled values (rounded bf16)
-    qch, kch = host(qc), host(kc)
-    rows = np.sort(rng.choice(w.n_blk, 24, replace=False))
-    ref_sel, imp = O.route_scores(qch[rows], kch, w.blk_key, w.scale, w.top_k)
-    frac = check_eps_ties(host(sel)[rows], ref_sel, imp, w.top_k, 1e-2)
+    rows = np.sort(rng.choice(w.n_blk, 200, replace=False))
+    ref_sel, imp = O.route_scores(qr[rows], kr, w.blk_key, w.scale, w.top_k)
+    selh = host(sel)
+    frac = check_eps_ties(selh[rows], ref_sel, imp, w.top_k, 1e-2)
+    print("speed3r routing: %.3f of sampled block rows exact" % frac, flush=True)
     assert frac >= 0.8, frac
-    # attention on sampled tokens, using the GPU routing rows (an input of the attention call)
+    # the layer on sampled tokens: the oracle's pooled values and routing rows
     vs = w.valid_slots()
     toks = np.sort(rng.choice(vs, 64, replace=False))
-    vch = host(vc)
-    selh = host(sel)
-    o_cmp, _ = O.attn_branch(O.CMP, qch, kch, vch, w.blk_cnt, w.blk_cap, w.scale, q_gran="block", rows=toks)
-    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=selh, q_gran="block",
+    blocks = np.unique(toks // w.blk_cap)
+    sel_o = np.full((w.n_blk, w.n_kvh, w.top_k), -1, dtype=np.int32)
+    sel_o[blocks], _ = O.route_scores(qr[blocks], kr, w.blk_key, w.scale, w.top_k)
+    o_cmp, _ = O.attn_branch(O.CMP, qr, kr, vr, w.blk_cnt, w.blk_cap, w.scale, q_gran="block", rows=toks)
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel_o, q_gran="block",
                              rows=toks)
     ref = O.gate_combine([o_cmp, o_sel], w.gates[toks])
-    assert max_err(host(o)[toks], ref) <= 2e-2
+    same = np.all(selh[toks // w.blk_cap] == sel_o[toks // w.blk_cap], axis=2)        # [tokens, H]
+    assert same.mean() >= 0.8, same.mean()
+    diff = np.abs(host(o)[toks] - ref).max(axis=2)
+    assert diff[same].max() <= 2e-2

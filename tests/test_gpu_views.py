@@ -1,6 +1,7 @@
 """GPU parity of geometric routing with the image blocks found through the views (LSRM pages,
 section 方法, routing paragraph): selected blocks and their distances bit-exact against the oracle
-on the same fp32 points and cameras."""
+on the same fp32 points and cameras, except for rows whose projection lies within the float32
+evaluation error of a cell edge (the oracle projects in float64), which are counted and left out."""
 import numpy as np
 import pytest
 import torch
@@ -30,10 +31,29 @@ def _gpu_views(w, n_vol, proj, cell_blk, cell, radius):
     return sel.cpu().numpy(), d2.cpu().numpy().view(np.uint32)
 
 
+def near_cell_edge(pts, proj, cell):
+    """Rows whose projection into some view lies within the float32 evaluation error of a cell
+    edge: the device evaluates the affine map ((A0 p0 + A1 p1) + A2 p2) + A3 with every operation
+    rounded to float32 (at most six roundings, each <= 2^-24 of a partial sum bounded by
+    sum |A_i p_i| + |A3|), the oracle in float64; only there may the two pick different cells."""
+    p = np.asarray(pts, dtype=np.float64)
+    A = np.asarray(proj, dtype=np.float64)                              # [V, 2, 4]
+    x = np.einsum("rc,vac->rva", p, A[:, :, :3]) + A[None, :, :, 3]      # [R, V, 2]
+    mag = np.einsum("rc,vac->rva", np.abs(p), np.abs(A[:, :, :3])) + np.abs(A[None, :, :, 3])
+    E = 2.0 * 6.0 * mag * 2.0 ** -24
+    d = np.abs(x - cell * np.round(x / cell))
+    return np.any(d <= E, axis=(1, 2))
+
+
 def _check(w, n_vol, proj, cell_blk, cell, radius, rows=None):
     say("route views", w.name, "n_vol", n_vol, "views", proj.shape[0], "radius", radius)
     sel, d2 = _gpu_views(w, n_vol, proj, cell_blk, cell, radius)
     rows = np.arange(w.n_slots) if rows is None else rows
+    edge = near_cell_edge(w.pts[rows], proj, cell) & w.valid_mask()[rows]
+    print("route views %s: %d of %d rows project within the fp32 error of a cell edge (not compared)"
+          % (w.name, edge.sum(), len(rows)), flush=True)
+    assert edge.mean() < 0.01
+    rows = rows[~edge]
     ref, ref_d2 = O.route_geometric_views(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k, n_vol, proj, cell_blk,
                                           cell, radius, rows=rows)
     np.testing.assert_array_equal(sel[rows], ref)
@@ -56,7 +76,7 @@ def test_route_views_full_size_sampled():
     w = wl("large")
     proj, cell_blk = W.view_cameras(w)
     n_vol = int((w.blk_type == 0).sum())
-    rows = np.sort(np.random.default_rng(9).choice(w.valid_slots(), 300, replace=False))
+    rows = np.sort(np.random.default_rng(9).choice(w.valid_slots(), 2000, replace=False))
     _check(w, n_vol, proj, cell_blk, 8, 1, rows=rows)
 
 

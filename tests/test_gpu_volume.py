@@ -1,6 +1,13 @@
 """GPU parity of the active-voxel selection and the volume block table (LSRM pages, section 方法,
-eq. M^vol and the block paragraph): counts, keys, token points and the block count bit-exact
-against the oracle, which takes the same fp32 decision in the same operation order."""
+eq. M^vol and the block paragraph).
+
+The oracle takes the decision in float64; the device in float32 with a fixed operation order.  A
+voxel whose float64 sub-sample values lie within the float32 evaluation's error bound of the
+threshold tau (or of zero, for the sign test) may legitimately decide differently: such voxels are
+counted and reported, every other voxel must agree exactly.  When no voxel differs, the whole block
+table (counts, keys, token points, block count) must equal the oracle's bit for bit; the GPU table
+must in any case satisfy the grouping rules (one 4^3 cell per block named by its Morton key, keys
+ascending, tokens in local Morton order, float32 voxel centres, zero padding)."""
 import ctypes
 import json
 import os
@@ -26,14 +33,75 @@ def _gpu(sdf, N, tau, max_blk=None):
     return nb, cnt.cpu().numpy(), key.cpu().numpy().view(np.uint32), pts.cpu().numpy()
 
 
-def _check(sdf, N, tau):
+def fp32_error_bound(sdf):
+    """Bound on |s_fp32 - s| for the device's trilinear sample (three nested lerps a + f (b - a),
+    each operation rounded to float32, the fraction f carrying the rounding of one division of
+    size <= G): per lerp at most (2G + 5) M 2^-24 with M = max |sdf|; three levels, doubled."""
+    G = sdf.shape[0]
+    M = float(np.abs(sdf.astype(np.float64)).max())
+    return 6.0 * (2 * G + 5) * max(M, 1e-30) * 2.0 ** -24
+
+
+def certain_voxels(mabs, mn, mx, tau, E):
+    """Voxels whose decision cannot change under an evaluation error below E."""
+    tau_true = mabs < tau - E
+    tau_false = mabs > tau + E
+    signs_sure = mabs > E
+    sign_true = signs_sure & (mn <= 0) & (mx >= 0)
+    return tau_true | sign_true | (tau_false & signs_sure)
+
+
+def _morton3_decode(code):
+    x = y = z = 0
+    for b in range(10):
+        x |= ((code >> (3 * b)) & 1) << b
+        y |= ((code >> (3 * b + 1)) & 1) << b
+        z |= ((code >> (3 * b + 2)) & 1) << b
+    return x, y, z
+
+
+def gpu_table_active(N, nb, cnt, key, pts):
+    """Check the grouping rules of a device block table; return its active voxels [z][y][x]."""
+    act = np.zeros((N, N, N), dtype=bool)
+    assert np.all((cnt >= 1) & (cnt <= 64))
+    assert np.all(np.diff(key.astype(np.int64)) > 0)
+    f32 = np.float32
+    for b in range(nb):
+        p = pts[b * 64: b * 64 + cnt[b]].astype(np.float64)
+        idx = np.rint((p * N + (N - 1)) / 2.0).astype(np.int64)
+        assert np.all((idx >= 0) & (idx < N))
+        cen = ((2 * idx + 1).astype(f32) - f32(N)) / f32(N)
+        np.testing.assert_array_equal(cen.astype(f32).view(np.uint32), pts[b * 64: b * 64 + cnt[b]].view(np.uint32))
+        cx, cy, cz = _morton3_decode(int(key[b]))
+        assert np.all(idx[:, 0] >> 2 == cx) and np.all(idx[:, 1] >> 2 == cy) and np.all(idx[:, 2] >> 2 == cz)
+        local = W.morton3(idx[:, 0] & 3, idx[:, 1] & 3, idx[:, 2] & 3).astype(np.int64)
+        assert np.all(np.diff(local) > 0)
+        act[idx[:, 2], idx[:, 1], idx[:, 0]] = True
+        assert np.all(pts[b * 64 + cnt[b]: (b + 1) * 64] == 0)
+    return act
+
+
+def _check(sdf, N, tau, require_exact=False):
+    tau = float(np.float32(tau))          # the device takes tau in float32; the oracle the same number
     say("volume blocks", "G=%d" % sdf.shape[0], "N=%d" % N, "tau=%r" % tau)
-    cnt, key, pts = O.volume_block_table(sdf, N, tau)
+    act, mabs, mn, mx = O.voxel_activity(sdf, N, tau, return_values=True)
+    E = fp32_error_bound(sdf)
+    sure = certain_voxels(mabs, mn, mx, tau, E)
     nb, gc, gk, gp = _gpu(sdf, N, tau)
-    assert nb == cnt.shape[0]
-    np.testing.assert_array_equal(gc, cnt)
-    np.testing.assert_array_equal(gk, key)
-    np.testing.assert_array_equal(gp.view(np.uint32), pts.view(np.uint32))     # bit-exact, padding 0
+    gact = gpu_table_active(N, nb, gc, gk, gp)
+    n_unsure = int((~sure).sum())
+    n_diff = int((gact != act).sum())
+    print("volume G=%d N=%d: %d voxels within the fp32 bound %.3g of a threshold, %d decided differently"
+          % (sdf.shape[0], N, n_unsure, E, n_diff), flush=True)
+    np.testing.assert_array_equal(gact[sure], act[sure])
+    if require_exact:
+        assert n_diff == 0
+    if n_diff == 0:
+        cnt, key, pts = O.volume_block_table(sdf, N, tau)
+        assert nb == cnt.shape[0]
+        np.testing.assert_array_equal(gc, cnt)
+        np.testing.assert_array_equal(gk, key)
+        np.testing.assert_array_equal(gp.view(np.uint32), pts.view(np.uint32))     # bit-exact, padding 0
     return nb
 
 
@@ -56,14 +124,14 @@ def test_volume_ramp_hand_fixture_gpu():
     assert nb == 1 and gc.tolist() == fx["blk_cnt"] and gk.tolist() == fx["blk_key"]
     np.testing.assert_array_equal(gp[:3], np.array(fx["first_points"], dtype=np.float32))
     assert np.all(gp[fx["blk_cnt"][0]:] == 0)
-    _check(sdf, fx["N"], fx["tau"])
+    _check(sdf, fx["N"], fx["tau"], require_exact=True)
 
 
 def test_volume_empty_and_full():
     g = np.full((3, 3, 3), 0.3, dtype=np.float32)
-    assert _check(g, 8, 0.2) == 0                         # no active voxel: zero blocks
-    assert _check(g, 8, 0.3) == 8                         # every voxel active: 8 full blocks
-    assert _check(np.zeros((2, 2, 2), np.float32), 4, 0.0) == 1
+    assert _check(g, 8, 0.2, require_exact=True) == 0     # no active voxel: zero blocks
+    assert _check(g, 8, 0.3, require_exact=True) == 8     # every voxel active: 8 full blocks
+    assert _check(np.zeros((2, 2, 2), np.float32), 4, 0.0, require_exact=True) == 1
 
 
 @pytest.mark.parametrize("case", ["linear", "random9", "random3_coarse", "sphere33", "sphere_offcentre",
@@ -93,7 +161,8 @@ def test_volume_large_small_workload_lattice():
 
 
 def test_volume_full_size_large_lattice():
-    """The 128^3 volume of the large sparse stage (SDF lattice 129^3): the whole table bit-exact."""
+    """The 128^3 volume of the large sparse stage (SDF lattice 129^3): every voxel outside the fp32
+    band decided as the oracle decides, and the table bit-exact when no voxel differs."""
     w = W.make("large")
     lat, tau = W.sdf_lattice(w, 129)
     nb = _check(lat, 128, tau)
@@ -104,7 +173,9 @@ def test_volume_max_blk_truncates_and_reports():
     import sparse_attention_feed_amd as S
     rng = np.random.default_rng(np.random.PCG64(78))
     sdf = rng.standard_normal((9, 9, 9)).astype(np.float32)
-    N, tau = 16, 0.05
+    N, tau = 16, float(np.float32(0.05))
+    _, mabs, mn, mx = O.voxel_activity(sdf, N, tau, return_values=True)
+    assert certain_voxels(mabs, mn, mx, tau, fp32_error_bound(sdf)).all()    # no voxel near a threshold
     cnt, key, pts = O.volume_block_table(sdf, N, tau)
     nb_all = cnt.shape[0]
     cap = nb_all // 2
@@ -144,7 +215,10 @@ def test_volume_workspace_reuse():
     ws = S.volume_workspace(N)
     for G, tau in ((9, 0.3), (5, 0.01)):
         sdf = rng.standard_normal((G, G, G)).astype(np.float32)
+        tau = float(np.float32(tau))
         say("volume workspace reuse", G, tau)
+        _, mabs, mn, mx = O.voxel_activity(sdf, N, tau, return_values=True)
+        assert certain_voxels(mabs, mn, mx, tau, fp32_error_bound(sdf)).all()
         cnt, key, pts = O.volume_block_table(sdf, N, tau)
         nb, gc, gk, gp = S.build_volume_blocks(torch.from_numpy(sdf).to("cuda:0"), N, tau, workspace=ws)
         assert nb == cnt.shape[0]

@@ -13,7 +13,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nsa.h")
 LIB = os.path.join(ROOT, "sparse_attention_feed_amd", "libnsa.so")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libnsa.so not built")
+
+
+def test_library_is_built():
+    """The boundary tests below need the library; a missing build is a failure, not a skip."""
+    assert os.path.exists(LIB), "libnsa.so is not built: run __graft_entry__.build()"
 
 
 def declared_functions():
@@ -189,6 +193,11 @@ def test_other_calls_validate(S, monkeypatch):
     assert lib.nsa_route_geometric(ctypes.byref(layout(S, blk_key=None)), FAKE, 4, FAKE, FAKE, None, None) == -1
     assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE, None, 4, FAKE, None) == -1  # lse needed
     assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 1, FAKE, FAKE, FAKE, 4, FAKE, None) == -2
+    # 16-byte alignment of the vector-loaded operands
+    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE, FAKE + 4, 4, FAKE, None) == -2
+    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE + 8, FAKE, FAKE, 4, FAKE, None) == -2
+    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE + 2, FAKE, 4, FAKE, None) == -2
+    assert lib.dense_gated_xattn_fwd(1, 100, 50, 32, 2, 32, 0.17, FAKE + 8, FAKE, FAKE, FAKE, FAKE, None) == -2
     arr = (ctypes.c_void_p * 2)(FAKE, None)
     assert lib.nsa_gate_combine(1, 10, 32, 32, 2, arr, FAKE, FAKE, None) == -1
     assert lib.nsa_gate_combine(1, 10, 32, 32, 9, arr, FAKE, FAKE, None) == -1
@@ -248,3 +257,22 @@ def test_build_is_hip_only():
     """The package has no CPU fallback: it exposes only the library wrappers."""
     src = open(os.path.join(ROOT, "sparse_attention_feed_amd", "__init__.py")).read()
     assert "import oracle" not in src and "from oracle" not in src
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "k_cmp", "v_cmp", "o"])
+def test_attn_alignment(S, field):
+    assert attn(S, layout(S), **{field: FAKE + 8}) == -2
+    assert "16-byte aligned" in S.lib.nsa_last_error().decode()
+
+
+def test_host_layout_validation():
+    """The binding's host-side check of the preconditions the kernels take on trust."""
+    import torch
+    import sparse_attention_feed_amd as S
+    S.validate_layout(torch.tensor([1, 64, 7], dtype=torch.int32), torch.tensor([3, 9, 1], dtype=torch.int32), 64)
+    with pytest.raises(ValueError, match="blk_cnt\\[1\\] = 65"):
+        S.validate_layout(torch.tensor([1, 65], dtype=torch.int32), None, 64)
+    with pytest.raises(ValueError, match="blk_cnt\\[0\\] = 0"):
+        S.validate_layout(torch.tensor([0, 5], dtype=torch.int32), None, 64)
+    with pytest.raises(ValueError, match="not unique"):
+        S.validate_layout(torch.tensor([1, 2], dtype=torch.int32), torch.tensor([4, 4], dtype=torch.int32), 8)
