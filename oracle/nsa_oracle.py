@@ -313,8 +313,8 @@ def check_route_geometric(pts, blk_cnt, blk_key, cap, sel, d2, rows=None, chunk=
     top_k = sel.shape[1]
     kk = min(top_k, n_blk)
     valid = valid_mask(blk_cnt, cap)[rows]
-    cen = torch.from_numpy(block_centroids(pts, blk_cnt, cap))                        # [n_blk, 3]
-    u = torch.from_numpy(lattice_coords(np.asarray(pts)[rows]))                        # [R, 3]
+    cen = torch.from_numpy(block_centroids(pts, blk_cnt, cap).astype(np.int32))      # [n_blk, 3]
+    u = torch.from_numpy(lattice_coords(np.asarray(pts)[rows]).astype(np.int32))      # [R, 3]
     key = torch.from_numpy(np.asarray(blk_key, dtype=np.int64))
     tsel = torch.from_numpy(sel)
     td2 = torch.from_numpy(d2)
@@ -328,19 +328,29 @@ def check_route_geometric(pts, blk_cnt, blk_key, cap, sel, d2, rows=None, chunk=
     head = tsel[:, :kk]
     in_range = ((head >= 0) & (head < n_blk)).all(1)
     bad |= tv & ~in_range
+    key32 = (key - (1 << 31)).to(torch.int32)          # order-preserving shift of the uint32 keys
     for lo in range(0, rows.shape[0], chunk):
         hi = min(lo + chunk, rows.shape[0])
         v = tv[lo:hi] & in_range[lo:hi]
         if not bool(v.any()):
             continue
         h = head[lo:hi].clamp(0, n_blk - 1)
-        dall = ((u[lo:hi, None, :] - cen[None, :, :]) ** 2).sum(2)                    # [r, n_blk]
-        listed = torch.gather(dall, 1, h)                                               # exact d2 of the list
-        rk_all = dall * (1 << 32) + key[None, :]
-        rk = listed * (1 << 32) + key[h]
+        # exact squared distances to every centroid, int32 (each < 2^28)
+        dall = u[lo:hi, 0:1] - cen[None, :, 0]
+        dall.mul_(dall)
+        for ax in (1, 2):
+            t = u[lo:hi, ax:ax + 1] - cen[None, :, ax]
+            dall.add_(t.mul_(t))
+        listed = torch.gather(dall, 1, h).to(torch.int64)                               # exact d2 of the list
+        lkey = key[h]
         ok = (listed == td2[lo:hi, :kk]).all(1)
-        ok &= (rk[:, 1:] > rk[:, :-1]).all(1) if kk > 1 else torch.ones_like(ok)
-        ok &= (rk_all < rk[:, -1:]).sum(1) == kk - 1
+        if kk > 1:
+            ok &= ((listed[:, 1:] > listed[:, :-1]) |
+                   ((listed[:, 1:] == listed[:, :-1]) & (lkey[:, 1:] > lkey[:, :-1]))).all(1)
+        dk = listed[:, -1:].to(torch.int32)
+        kk32 = key32[h[:, -1:]]
+        better = (dall < dk) | ((dall == dk) & (key32[None, :] < kk32))
+        ok &= better.sum(1) == kk - 1
         bad[lo:hi] |= v & ~ok
     nbad = int(bad.sum())
     return nbad, rows[bad.numpy()][:10]

@@ -367,15 +367,14 @@ def test_score_routing_full_size_sampled(name, top_k):
 
 
 def test_gqa_score_routed_layer():
-    """The grouped-query score-routed layer end to end: pooled K/V, the compressed branch's lse,
-    score routing per (token, KV group), and the gated compressed + selected + local branches with
-    per-group routing rows, against the oracle's whole layer (nsa_forward with score routing).
-    Where fp32 scores order near-tied blocks differently the routing rows differ (checked against
-    epsilon ties above); outputs are compared on the (token, group) pairs whose rows agree."""
-    import copy
+    """The grouped-query score-routed layer end to end on the GPU (pooled K/V, the compressed
+    branch's lse, score routing per (token, KV group), the gated compressed + selected + local
+    branches with per-group routing rows) against the oracle's steps of nsa_forward's score-routed
+    layer, with the pooled values rounded to bf16 where the GPU layer stores them.  Routing: every
+    row agrees with the oracle's up to epsilon ties (against the oracle's own lse, while the GPU
+    routes with its own); outputs are compared on the (token, group) pairs whose rows agree."""
     import sparse_attention_feed_amd as S
-    w = copy.copy(wl("stage2_small"))
-    w.routing = "scores"
+    w = wl("stage2_small")
     d = to_dev(w)
     L = d["layout"]
     say("gqa score-routed layer", w.name)
@@ -387,11 +386,27 @@ def test_gqa_score_routed_layer():
     o = S.attn_fwd(L, S.BR_CMP | S.BR_SEL | S.BR_LOC, d["q"], d["k"], d["v"], k_cmp=kc, v_cmp=vc, sel=sel,
                    top_k=w.top_k, sel_groups=w.n_kvh, gates=d["gates"])
     torch.cuda.synchronize()
-    ref, parts = O.nsa_forward(w, return_parts=True)
+    kr = rounded(O.pool_blocks(w.k, w.blk_cnt, w.blk_cap), w.dtype).astype(np.float64)
+    vr = rounded(O.pool_blocks(w.v, w.blk_cnt, w.blk_cap), w.dtype).astype(np.float64)
+    vs = w.valid_slots()
+    o_cmp, lse_o = O.attn_branch(O.CMP, w.q, kr, vr, w.blk_cnt, w.blk_cap, w.scale)
+    ref_sel = np.full((w.n_slots, w.n_kvh, w.top_k), -1, dtype=np.int32)
+    ref_sel[vs], imp = O.route_scores(w.q[vs], kr, w.blk_key, w.scale, w.top_k, lse=lse_o[vs])
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=ref_sel)
+    o_loc, _ = O.attn_branch(O.LOC, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale)
+    ref = O.gate_combine([o_cmp, o_sel, o_loc], w.gates)
     got_sel = host(sel)
     vm = w.valid_mask()
-    same = np.all(got_sel == parts["sel"], axis=2) & vm[:, None]          # [S, Hkv]
-    assert same[vm].mean() > 0.9, same[vm].mean()
+    for i, s_ in enumerate(vs):
+        for j in range(w.n_kvh):
+            if np.array_equal(got_sel[s_, j], ref_sel[s_, j]):
+                continue
+            kth = np.sort(imp[i, j])[::-1][w.top_k - 1]
+            for b in set(got_sel[s_, j].tolist()) ^ set(ref_sel[s_, j].tolist()):
+                assert abs(imp[i, j, b] - kth) <= 1e-2 * kth, (s_, j, b)
+    same = np.all(got_sel == ref_sel, axis=2) & vm[:, None]                # [S, Hkv]
+    print("gqa score-routed layer: %.3f of (token, group) rows exact" % same[vm].mean(), flush=True)
+    assert same[vm].mean() > 0.85, same[vm].mean()
     G = w.n_qh // w.n_kvh
     diff = np.abs(host(o) - ref).max(axis=2).reshape(w.n_slots, w.n_kvh, G).max(axis=2)
     assert diff[same].max() <= tol(w), diff[same].max()
