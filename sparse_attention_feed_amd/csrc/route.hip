@@ -6,10 +6,7 @@
 // per axis, block centroid rounded half-up, squared distance < 2^28 in 32-bit integers; ranking is
 // the total order (d2, blk_key).
 //
-// Score routing ("standard NSA" selection the LSRM pages compare with; Speed3R page, section 2.1):
-// importance of a pooled block for a query token and KV group = the group's summed softmax
-// probability against the compressed keys, computed tile by tile with MFMA and reduced to a top-k
-// per lane, then merged across the wave.
+// (Score routing in grouped-query form is in route_scores.hip.)
 #include "common.h"
 #include "kernels.h"
 
@@ -328,161 +325,11 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// score routing, grouped-query form (16 query heads per KV head, head dim 32)
-// ---------------------------------------------------------------------------------------------
-
-__device__ __forceinline__ bool better(float v, uint32_t k, float v2, uint32_t k2) {
-  return v > v2 || (v == v2 && k < k2);
-}
-
-template <typename T, int K>
-__global__ __launch_bounds__(256) void score_route_kernel(ScoreRouteArgs a) {
-  constexpr int HD = 32, GRP = 16;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int l = lane_id(), r = l & 15, g = l >> 4;
-  const int row = wave / a.n_kvh, j = wave % a.n_kvh;
-  if (row >= a.n_rows) return;
-  int32_t* so = a.sel + ((size_t)row * a.n_kvh + j) * a.top_k;
-  const bool valid = (row % a.cap) < a.blk_cnt[row / a.cap];
-  if (!valid) {
-    for (int x = l; x < a.top_k; x += 64) so[x] = -1;
-    return;
-  }
-  const T* q = reinterpret_cast<const T*>(a.q);
-  const T* kc = reinterpret_cast<const T*>(a.k_cmp);
-  Frag8<T> qf;
-  {
-    const T* qp = q + ((size_t)row * a.n_qh + j * GRP + r) * HD + 8 * g;
-    qf.v = *reinterpret_cast<const decltype(qf.v)*>(qp);
-  }
-  const float c2 = a.scale * kLog2e;
-  // S = Q K^T per 16-key group: lane (r, g) gets heads 4g .. 4g+3 of key 16 kt + r, so the group
-  // sum over the 16 heads is three adds in the lane and two exchanges across lane groups
-  f32x4 nlse2;
-  {
-    const f32x4 ls = *reinterpret_cast<const f32x4*>(a.lse + (size_t)row * a.n_qh + j * GRP + 4 * g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) nlse2[i] = -ls[i] * kLog2e;
-  }
-  float bv[K];
-  uint32_t bk[K];
-  int bi[K];
-#pragma unroll
-  for (int x = 0; x < K; ++x) {
-    bv[x] = -INFINITY;
-    bk[x] = 0xFFFFFFFFu;
-    bi[x] = -1;
-  }
-  const int kstride = a.n_kvh * HD;
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  // K fragments of a 64-key step (keys past the end read the last key; they are never ranked),
-  // loaded one step ahead of their use
-  auto load_step = [&](int k0, Frag8<T> (&kf)[4], uint32_t& bkey) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = min(k0 + 16 * kt + r, a.n_blk - 1);
-      kf[kt].v = *reinterpret_cast<const decltype(kf[kt].v)*>(kc + (size_t)key * kstride + j * HD + 8 * g);
-    }
-    bkey = a.blk_key[min(k0 + 16 * g + r, a.n_blk - 1)];   // the key this lane ranks
-  };
-  Frag8<T> kcur[4], knext[4];
-  uint32_t bkcur, bknext = 0u;
-  load_step(0, kcur, bkcur);
-  for (int k0 = 0; k0 < a.n_blk; k0 += 64) {
-    if (k0 + 64 < a.n_blk) load_step(k0 + 64, knext, bknext);
-    float val = 0.f;                   // the group importance of key k0 + 16 g + r (this lane ranks it)
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const f32x4 s = mma16(qf, kcur[kt], z);   // lane: heads 4g + i, key k0 + 16 kt + r
-      float p = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p += __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, nlse2[i]));
-      p += __shfl_xor(p, 16, 64);
-      p += __shfl_xor(p, 32, 64);
-      val = kt == g ? p : val;
-    }
-    const int idx = k0 + 16 * g + r;
-    if (idx < a.n_blk) {
-      const uint32_t key = bkcur;
-      if (better(val, key, bv[K - 1], bk[K - 1])) {
-#pragma unroll
-        for (int x = K - 1; x > 0; --x) {
-          const bool bp = better(val, key, bv[x - 1], bk[x - 1]);
-          const bool bc = better(val, key, bv[x], bk[x]);
-          if (bp) {
-            bv[x] = bv[x - 1];
-            bk[x] = bk[x - 1];
-            bi[x] = bi[x - 1];
-          } else if (bc) {
-            bv[x] = val;
-            bk[x] = key;
-            bi[x] = idx;
-          }
-        }
-        if (better(val, key, bv[0], bk[0])) {
-          bv[0] = val;
-          bk[0] = key;
-          bi[0] = idx;
-        }
-      }
-    }
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) kcur[kt] = knext[kt];
-    bkcur = bknext;
-  }
-  // merge the 64 per-lane lists: top_k rounds of a wave arg-best over the list heads
-  for (int x = 0; x < a.top_k; ++x) {
-    float v = bv[0];
-    uint32_t k = bk[0];
-    int src = l;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float v2 = __shfl_xor(v, o, 64);
-      const uint32_t k2 = __shfl_xor(k, o, 64);
-      const int s2 = __shfl_xor(src, o, 64);
-      if (better(v2, k2, v, k)) {
-        v = v2;
-        k = k2;
-        src = s2;
-      }
-    }
-    const int win = __shfl(bi[0], src, 64);
-    if (l == 0) so[x] = (v == -INFINITY) ? -1 : win;
-    if (l == src) {
-#pragma unroll
-      for (int y = 0; y < K - 1; ++y) {
-        bv[y] = bv[y + 1];
-        bk[y] = bk[y + 1];
-        bi[y] = bi[y + 1];
-      }
-      bv[K - 1] = -INFINITY;
-      bk[K - 1] = 0xFFFFFFFFu;
-      bi[K - 1] = -1;
-    }
-  }
-}
-
 template <int K>
 hipError_t launch_route_k(const RouteArgs& a, hipStream_t s) {
   if (a.n_qblk == 0) return hipSuccess;
   hipLaunchKernelGGL(route_kernel<K>, dim3(a.n_qblk), dim3(64), 0, s, a);
   return hipGetLastError();
-}
-
-template <typename T, int K>
-hipError_t launch_score_k(const ScoreRouteArgs& a, hipStream_t s) {
-  const long long waves = (long long)a.n_rows * a.n_kvh;
-  hipLaunchKernelGGL((score_route_kernel<T, K>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_score_t(const ScoreRouteArgs& a, hipStream_t s) {
-  if (a.top_k <= 8) return launch_score_k<T, 8>(a, s);
-  if (a.top_k <= 16) return launch_score_k<T, 16>(a, s);
-  if (a.top_k <= 32) return launch_score_k<T, 32>(a, s);
-  return launch_score_k<T, 64>(a, s);
 }
 
 }  // namespace
@@ -497,10 +344,6 @@ hipError_t launch_route_geometric(const RouteArgs& a, hipStream_t s) {
   if (a.top_k <= 16) return launch_route_k<16>(a, s);
   if (a.top_k <= 32) return launch_route_k<32>(a, s);
   return launch_route_k<64>(a, s);
-}
-
-hipError_t launch_route_scores(int is_bf16, const ScoreRouteArgs& a, hipStream_t s) {
-  return is_bf16 ? launch_score_t<bf16>(a, s) : launch_score_t<float>(a, s);
 }
 
 }  // namespace nsa
