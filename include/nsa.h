@@ -150,6 +150,20 @@ nsa_status nsa_route_geometric(const nsa_layout* layout, const float* pts, int32
                                hipStream_t stream);
 
 /*
+ * nsa_route_geometric for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same routing, with the
+ * centroid workspace taken from a fixed array inside the library (65,536 blocks x 4 int32 = 1 MiB
+ * per device, held until the process ends) instead of a caller buffer.  The call allocates
+ * nothing.  Every call on one device shares that device's array and rewrites the centroids of
+ * blocks [0, n_blk) before reading them, so nothing carries over from an earlier call; calls that
+ * overlap in time on one device (two streams, two host threads) race on the array and must not be
+ * issued.  n_blk > 65536 returns NSA_ERR_UNSUPPORTED; other arguments and results are those of
+ * nsa_route_geometric.
+ */
+nsa_status nsa_route_geometric_noalloc(const nsa_layout* layout, const float* pts, int32_t top_k,
+                                       int32_t* sel, uint32_t* sel_d2, hipStream_t stream);
+
+/*
  * Geometric routing with the image blocks found through the views (LSRM pages, section 方法,
  * routing paragraph: for image blocks the query point is projected into every input view, nearby
  * image blocks are gathered per view and ranked by their smallest 3D distance to the query; volume

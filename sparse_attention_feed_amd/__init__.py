@@ -24,7 +24,7 @@ Q_TOKEN, Q_BLOCK = 0, 1
 EXPORTS = ("nsa_build_volume_blocks", "nsa_pool_blocks", "nsa_pool_blocks_resblock", "nsa_route_geometric",
            "nsa_route_geometric_range", "nsa_route_geometric_views", "nsa_attn_fwd_range", "nsa_route_scores_topk", "nsa_attn_fwd",
            "nsa_attn_fwd_forced",
-           "nsa_gate_combine", "dense_gated_xattn_fwd", "nsa_last_error")
+           "nsa_gate_combine", "dense_gated_xattn_fwd", "nsa_route_geometric_noalloc", "nsa_last_error")
 
 
 class NsaError(RuntimeError):
@@ -51,6 +51,7 @@ def _load():
         "nsa_pool_blocks": [LP, I, I, P, P, P],
         "nsa_pool_blocks_resblock": [LP, I, I, P, P, P, P, P, P, P],
         "nsa_route_geometric": [LP, P, I, P, P, P, P],
+        "nsa_route_geometric_noalloc": [LP, P, I, P, P, P],
         "nsa_route_geometric_range": [LP, P, I, I, I, I, I, P, P, P, P],
         "nsa_route_geometric_views": [LP, P, I, I, I, P, P, I, I, I, P, P, P, P, P],
         "nsa_attn_fwd_range": [LP, I, U, I, I, I, I, P, P, P, P, P, P, I, I, P, I, P, P, P],

@@ -185,6 +185,38 @@ nsa_status nsa_route_geometric(const nsa_layout* L, const float* pts, int32_t to
   return route_geometric("nsa_route_geometric", L, pts, top_k, 0, n, 0, n, centroids, sel, sel_d2, stream);
 }
 
+nsa_status nsa_route_geometric_noalloc(const nsa_layout* L, const float* pts, int32_t top_k, int32_t* sel,
+                                       uint32_t* sel_d2, hipStream_t stream) {
+  const char* fn = "nsa_route_geometric_noalloc";
+  nsa_status st = check_layout(L, fn);
+  if (st != NSA_OK) return st;
+  if (pts == nullptr || sel == nullptr || L->blk_key == nullptr)
+    return fail(NSA_ERR_INVALID, "%s: pts, sel and blk_key must be non-NULL", fn);
+  if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "%s: top_k must be in 1..64 (got %d)", fn, top_k);
+  if (L->n_blk > nsa::kScratchMaxBlocks)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: n_blk %d exceeds the fixed centroid array (%d blocks)", fn, L->n_blk,
+                nsa::kScratchMaxBlocks);
+  NSA_FORCED_FAILURE(fn);
+  int32_t* cent = nullptr;
+  nsa_status hs = hip_status(nsa::route_scratch_centroids(&cent), fn);
+  if (hs != NSA_OK) return hs;
+  nsa::RouteArgs a{};
+  a.q_blk0 = 0;
+  a.n_qblk = L->n_blk;
+  a.kv_lo = 0;
+  a.kv_hi = L->n_blk;
+  a.pts = pts;
+  a.blk_cnt = L->blk_cnt;
+  a.blk_key = L->blk_key;
+  a.cent = cent;
+  a.sel = sel;
+  a.sel_d2 = sel_d2;
+  a.n_blk = L->n_blk;
+  a.cap = L->blk_cap;
+  a.top_k = top_k;
+  return hip_status(nsa::launch_route_geometric(a, stream), fn);
+}
+
 nsa_status nsa_route_geometric_views(const nsa_layout* L, const float* pts, int32_t top_k, int32_t n_vol_blk,
                                      int32_t n_views, const float* view_proj, const int32_t* cell_blk,
                                      int32_t n_cell, int32_t cell_size, int32_t radius, int32_t* centroids,

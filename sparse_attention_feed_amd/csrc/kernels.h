@@ -106,6 +106,10 @@ hipError_t launch_build_volume_blocks(const float* sdf, int G, int N, float tau,
                                       unsigned long long* cell_mask, int* cell_block, int* n_blk, int32_t* blk_cnt,
                                       uint32_t* blk_key, float* pts, hipStream_t s);
 hipError_t launch_route_geometric(const RouteArgs& a, hipStream_t s);
+constexpr int kScratchMaxBlocks = 65536;   // blocks of the allocation-free routing entry point
+// Device address of the library's fixed centroid array on the current device (looked up once per
+// device, then cached); kScratchMaxBlocks x 4 int32.
+hipError_t route_scratch_centroids(int32_t** out);
 hipError_t launch_route_scores(int is_bf16, const ScoreRouteArgs& a, hipStream_t s);
 hipError_t launch_gate(int is_bf16, int n_rows, int n_qh, int head_dim, int n_branch,
                        const void* const* o_branch, const void* gates, void* o, hipStream_t s);

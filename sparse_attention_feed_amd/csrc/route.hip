@@ -7,6 +7,8 @@
 // the total order (d2, blk_key).
 //
 // (Score routing in grouped-query form is in route_scores.hip.)
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -345,5 +347,36 @@ hipError_t launch_route_geometric(const RouteArgs& a, hipStream_t s) {
   if (a.top_k <= 32) return launch_route_k<32>(a, s);
   return launch_route_k<64>(a, s);
 }
+
+// ---------------------------------------------------------------------------------------------
+// the routing centroids in a fixed device array, for callers that cannot allocate
+// ---------------------------------------------------------------------------------------------
+
+namespace {
+// [kScratchMaxBlocks][4] int32 centroids (1 MiB), one copy per device for the life of the process
+static __device__ __align__(256) int32_t scratch[kScratchMaxBlocks * 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t route_scratch_centroids(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // the array's device address on the current device: the host-side name is not one
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 
 }  // namespace nsa

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 13
+    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 14
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -276,3 +276,17 @@ def test_host_layout_validation():
         S.validate_layout(torch.tensor([0, 5], dtype=torch.int32), None, 64)
     with pytest.raises(ValueError, match="not unique"):
         S.validate_layout(torch.tensor([1, 2], dtype=torch.int32), torch.tensor([4, 4], dtype=torch.int32), 8)
+
+
+def test_noalloc_routing_validation(S, monkeypatch):
+    """The allocation-free routing call validates like nsa_route_geometric and refuses layouts
+    beyond its fixed centroid array before any device work."""
+    r = S.lib.nsa_route_geometric_noalloc
+    assert r(ctypes.byref(layout(S, n_blk=65537, blk_cap=1)), FAKE, 4, FAKE, None, None) == -2
+    assert "65536" in S.lib.nsa_last_error().decode()
+    assert r(ctypes.byref(layout(S)), FAKE, 0, FAKE, None, None) == -1
+    assert r(ctypes.byref(layout(S)), None, 4, FAKE, None, None) == -1
+    assert r(ctypes.byref(layout(S)), FAKE, 4, None, None, None) == -1
+    assert r(ctypes.byref(layout(S, blk_key=None)), FAKE, 4, FAKE, None, None) == -1
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    assert r(ctypes.byref(layout(S, n_blk=65536, blk_cap=1)), FAKE, 4, FAKE, None, None) == -3
