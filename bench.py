@@ -7,8 +7,9 @@ copied to HBM before timing.
 
 Prints ONE JSON line.  Besides the throughput it reports, for the dominant kernel (the fused
 attention), achieved algorithmic TFLOP/s against the bf16 MFMA peak, the per-kernel times measured
-with HIP events on the launch stream, per-branch throughput, and the fp64 CPU oracle timed on a
-bounded sample of the same workload.
+with HIP events on the launch stream, per-branch throughput, the fp64 CPU oracle timed on the
+host's cores on a bounded sample of the same workload, and the same step measurements for the
+other four workloads (stage2, speed3r, dense, tiny) with fewer steps.
 """
 import argparse
 import json
@@ -76,34 +77,84 @@ def measured_traffic(kernel, config):
         return None
 
 
-def cpu_baseline(w, budget_s):
-    """fp64 oracle on a bounded sample of query rows of the same workload, one thread: a probe call
-    of 16 rows, then calls sized from the last one's time per row until the budget is spent (each
-    call also pays the oracle's per-call pooling and centroids, so the sizes grow call by call)."""
-    from threadpoolctl import threadpool_limits
+_CPU_W = None     # the workload the CPU-baseline workers read (inherited at fork)
+_CPU_POOLED = None
+
+
+def _oracle_rows(rows):
+    """The oracle's layer on a chunk of query rows with the pooled K/V computed once beforehand:
+    the same oracle functions that nsa_forward composes (routing, the branches, the gate)."""
     import oracle as O
-    rng = np.random.default_rng(123)
-    if hasattr(w, "n_x"):
-        vs = np.arange(w.n_tok)
-        run = lambda rows: O.dense_gated_xattn(w.q, w.k, w.v, w.n_x, w.gates, w.scale, rows=rows)  # noqa: E731
-    else:
-        vs = w.valid_slots()
-        run = lambda rows: O.nsa_forward(w, rows=rows)  # noqa: E731
+    from threadpoolctl import threadpool_limits
+    w = _CPU_W
+    t0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        n_call, t_sum, n_sum, calls = 16, 0.0, 0, 0
-        while True:
-            rows = np.sort(rng.choice(vs, n_call, replace=False))
-            t0 = time.perf_counter()
-            run(rows)
-            t = time.perf_counter() - t0
-            t_sum, n_sum, calls = t_sum + t, n_sum + n_call, calls + 1
-            left = budget_s - t_sum
-            if left <= 0.1 * budget_s or calls == 4 or n_call >= min(4096, len(vs)):
-                break
-            n_call = int(min(4096, len(vs), max(16, left / (t / n_call))))
-    return {"value": round(n_sum / t_sum, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d random query tokens of the same workload in %d calls, %.1f s; every call also "
-                      "pools all blocks and computes all block centroids" % (n_sum, calls, t_sum)}
+        if hasattr(w, "n_x"):
+            O.dense_gated_xattn(w.q, w.k, w.v, w.n_x, w.gates, w.scale, rows=rows)
+        elif w.routing == "scores":
+            O.nsa_forward(w, rows=rows)
+        else:
+            k_cmp, v_cmp = _CPU_POOLED
+            sel_rows, _ = O.route_geometric(w.pts, w.blk_cnt, w.blk_key, w.blk_cap, w.top_k, rows=rows)
+            sel = np.full((w.n_slots, w.top_k), -1, dtype=np.int32)
+            sel[rows] = sel_rows
+            outs = []
+            for name in w.branches:
+                br = O.BRANCH_NAMES[name]
+                if br == O.CMP:
+                    oc, _ = O.attn_branch(O.CMP, w.q, k_cmp, v_cmp, w.blk_cnt, w.blk_cap, w.scale, rows=rows)
+                elif br == O.SEL:
+                    oc, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel, rows=rows)
+                else:
+                    oc, _ = O.attn_branch(O.LOC, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, rows=rows)
+                outs.append(oc)
+            O.gate_combine(outs, w.gates[rows])
+    return len(rows), time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle on the host's cores: worker processes (one per core of this process's
+    affinity, at most 16, each single-threaded) run chunks of randomly sampled query rows of the
+    same workload until the time budget is spent.  Geometric workloads pool K and V once first
+    (timed, and included in the extrapolated whole-layer rate).  Runs before any GPU work."""
+    import concurrent.futures
+    import multiprocessing
+    global _CPU_W, _CPU_POOLED
+    import oracle as O
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    rng = np.random.default_rng(123)
+    vs = np.arange(w.n_tok) if hasattr(w, "n_x") else w.valid_slots()
+    n_all = len(vs)
+    _CPU_W = w
+    t_setup = 0.0
+    if not hasattr(w, "n_x") and w.routing != "scores":
+        t0 = time.perf_counter()
+        _CPU_POOLED = (O.pool_blocks(w.k, w.blk_cnt, w.blk_cap), O.pool_blocks(w.v, w.blk_cnt, w.blk_cap))
+        t_setup = time.perf_counter() - t0
+    # a probe chunk in this process sizes the chunks for the budget
+    probe = np.sort(rng.choice(vs, min(8, n_all), replace=False))
+    n_p, t_p = _oracle_rows(probe)
+    per_row = t_p / n_p
+    chunk = int(max(4, min(2048, 0.1 * budget_s / per_row)))
+    n_chunks = max(cores, int(budget_s * cores / (per_row * chunk)))
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.perf_counter()
+    done_rows = 0
+    with concurrent.futures.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        futs = [ex.submit(_oracle_rows, np.sort(rng.choice(vs, min(chunk, n_all), replace=False)))
+                for _ in range(n_chunks)]
+        for f in concurrent.futures.as_completed(futs):
+            done_rows += f.result()[0]
+    wall = time.perf_counter() - t0
+    rate = done_rows / wall
+    whole = n_all / (t_setup + n_all / rate)
+    desc = ("%d random query tokens of the same workload in %d chunks on %d worker processes, %.1f s wall"
+            % (done_rows, n_chunks, cores, wall))
+    if t_setup:
+        desc += ("; K/V pooling once %.1f s, included in value (whole-layer rate %.1f tokens/s = %d tokens / "
+                 "(pooling + tokens / %.1f tokens/s))" % (t_setup, whole, n_all, rate))
+    return {"value": round(whole, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "rows_per_s": round(rate, 2), "sample": desc}
 
 
 def setup_geometric(w, S, torch, dev):
@@ -259,34 +310,24 @@ def setup_dense(w, S, torch, dev):
     return stages, flops, {}, "dense_gated_xattn"
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="large")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-breakdown", action="store_true")
-    ap.add_argument("--calib-copy", action="store_true",
-                    help="after the timed region, copy 1 GiB device to device twice: the reference kernel "
-                         "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: libnsa has no multi-GPU path (the NSA layer would shard "
-              "whole blocks across GPUs and all-gather the pooled K/V).", file=sys.stderr)
-        sys.exit(2)
+def describe(name, w, dense):
+    if name == "large":
+        return ("large: 128^3 volume (%d active surface voxels) + 16 views x 128^2 at 50%% foreground (%d), "
+                "32q/2kv heads, D=32, 64-token blocks, top-%d geometric routing + local + compressed, "
+                "3-way sigmoid gate" % (w.n_vol_tokens, w.n_img_tokens, w.top_k))
+    if dense:
+        return "%s: stage-1 dense gated self/cross attention, %d tokens (%d volume), 32q/2kv, D=32" % (
+            name, w.n_tok, w.n_x)
+    return "%s: %d tokens, %d blocks of %d, %dq/%dkv heads, D=%d, top-%d %s routing" % (
+        name, w.n_valid, w.n_blk, w.blk_cap, w.n_qh, w.n_kvh, w.head_dim, w.top_k, w.routing)
 
-    import torch
-    import sparse_attention_feed_amd as S
+
+def run_config(name, w, steps, warmup, breakdown_on, torch, S, dev):
+    """Time `steps` layer steps of workload w (after `warmup` untimed ones) with HIP events on the
+    launch stream; optionally time the per-branch and next-row items.  Returns a result dict."""
     import workloads as W
-
-    t0 = time.time()
-    w = W.make(args.config)
     dense = isinstance(w, W.DenseWorkload)
     n_tok = w.n_tok if dense else w.n_valid
-    log("workload %s: %d tokens (%.1fs)" % (args.config, n_tok, time.time() - t0))
-    dev = "cuda:0"
     if dense:
         stages_fn, flops_fn, branches, dominant = setup_dense(w, S, torch, dev)
     elif w.routing == "scores":
@@ -304,21 +345,21 @@ def main():
         if ev is not None:
             ev[len(stages)].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    kern_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, (name, _) in enumerate(stages)}
+    ms_step = total_ms / steps
+    kern_ms = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, (nm, _) in enumerate(stages)}
     value = n_tok / (ms_step * 1e-3)
 
     fl = flops_fn()
@@ -327,13 +368,13 @@ def main():
     dom_flops = sum(v for kk, v in fl.items() if kk not in ("route", "sel_forced_ref_frame", "route_scores_gqa"))
     achieved = dom_flops / (kern_ms[dominant] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    log("step %.3f ms; %s; %s %.1f TFLOP/s" % (ms_step, ", ".join("%s %.3f" % kv for kv in kern_ms.items()),
-                                              dominant, achieved))
+    log("%s: step %.3f ms; %s; %s %.1f TFLOP/s" % (name, ms_step, ", ".join("%s %.3f" % kv for kv in kern_ms.items()),
+                                                  dominant, achieved))
 
     breakdown = None
-    if branches and not args.no_breakdown:
+    if branches and breakdown_on:
         breakdown = {}
-        for name, fn in branches.items():
+        for bname, fn in branches.items():
             for _ in range(2):
                 fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -344,77 +385,46 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
-            if name == "pool_kv_resblock":
+            if bname == "pool_kv_resblock":
                 # K and V: 4*D^2 FLOP per valid token and KV head (two D x D products)
                 f = 2 * 4 * w.head_dim * w.head_dim * w.n_kvh * int(w.blk_cnt.sum())
-                breakdown[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2)}
+                breakdown[bname] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2)}
                 continue
-            if name == "route_views":
-                breakdown[name] = {"ms": round(ms, 4)}
+            if bname == "route_views":
+                breakdown[bname] = {"ms": round(ms, 4)}
                 continue
-            if name == "split_layer":
-                n_tok = int(w.blk_cnt.sum())
-                breakdown[name] = {"ms": round(ms, 4), "tokens_per_s": round(n_tok / (ms * 1e-3), 1)}
+            if bname == "split_layer":
+                nt = int(w.blk_cnt.sum())
+                breakdown[bname] = {"ms": round(ms, 4), "tokens_per_s": round(nt / (ms * 1e-3), 1)}
                 continue
-            if name == "volume_blocks":
+            if bname == "volume_blocks":
                 # 64 trilinear SDF samples per voxel of the side^3 grid
                 side = int(w.meta["vol_side"])
                 nb = int(fn()["n_blk"].item())
-                breakdown[name] = {"ms": round(ms, 4), "n_blk": nb,
-                                   "gvoxel_per_s": round(side ** 3 / (ms * 1e-3) / 1e9, 3)}
+                breakdown[bname] = {"ms": round(ms, 4), "n_blk": nb,
+                                    "gvoxel_per_s": round(side ** 3 / (ms * 1e-3) / 1e9, 3)}
                 continue
-            if name == "gate_combine_unfused":
+            if bname == "gate_combine_unfused":
                 # bytes: three branch outputs and the gate logits read, the output written
                 esz = 2 if w.dtype == "bf16" else 4
                 nbytes = (4 * w.n_slots * w.n_qh * w.head_dim + w.n_slots * w.n_qh * 3) * esz
-                breakdown[name] = {"ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                                   "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                breakdown[bname] = {"ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
                 continue
-            f = sum(fl[p] for p in name.split("+"))
-            breakdown[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 1),
-                               "mfma_frac": round(f / (ms * 1e-3) / 1e12 / peak, 4)}
+            f = sum(fl[p] for p in bname.split("+"))
+            breakdown[bname] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 1),
+                                "mfma_frac": round(f / (ms * 1e-3) / 1e12 / peak, 4)}
         step()
         torch.cuda.synchronize()
 
-    if args.calib_copy:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    cpu = None
-    if not args.no_cpu:
-        log("timing the fp64 oracle on a bounded sample (~%.0f s)" % args.cpu_seconds)
-        cpu = cpu_baseline(w, args.cpu_seconds)
-
-    if args.config == "large":
-        desc = ("large: 128^3 volume (%d active surface voxels) + 16 views x 128^2 at 50%% foreground (%d), "
-                "32q/2kv heads, D=32, 64-token blocks, top-%d geometric routing + local + compressed, "
-                "3-way sigmoid gate" % (w.n_vol_tokens, w.n_img_tokens, w.top_k))
-    elif dense:
-        desc = "%s: stage-1 dense gated self/cross attention, %d tokens (%d volume), 32q/2kv, D=32" % (
-            args.config, w.n_tok, w.n_x)
-    else:
-        desc = "%s: %d tokens, %d blocks of %d, %dq/%dkv heads, D=%d, top-%d %s routing" % (
-            args.config, w.n_valid, w.n_blk, w.blk_cap, w.n_qh, w.n_kvh, w.head_dim, w.top_k, w.routing)
-    cfg = {"workload": desc, "n_tokens": n_tok, "n_qh": w.n_qh, "n_kvh": w.n_kvh, "head_dim": w.head_dim}
+    cfg = {"workload": describe(name, w, dense), "n_tokens": n_tok, "n_qh": w.n_qh, "n_kvh": w.n_kvh,
+           "head_dim": w.head_dim}
     if not dense:
         cfg.update(n_blk=w.n_blk, blk_cap=w.blk_cap, top_k=w.top_k)
-    rec = {
-        "metric": METRIC,
+    return {
         "value": round(value, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; token geometry and head shapes of the pages' workloads)",
         "config": cfg,
         "roofline": {
             "kernel": dominant,
@@ -423,7 +433,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(dominant, args.config),
+            "traffic": measured_traffic(dominant, name),
         },
         "kernels_ms": {kk: round(vv, 4) for kk, vv in kern_ms.items()},
         # geometric routing depends only on the token points, so a 24-layer model routes once per
@@ -434,7 +444,99 @@ def main():
             if "route_geometric" in kern_ms else None),
         "algorithmic_gflop": {kk: round(vv / 1e9, 2) for kk, vv in fl.items()},
         "branch_breakdown": breakdown,
+    }
+
+
+# the other workloads, timed after the headline one with fewer steps
+OTHER_CONFIGS = ("stage2", "speed3r", "dense", "tiny")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="large")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="time the headline workload only")
+    ap.add_argument("--config-steps", type=int, default=5, help="timed steps of each other workload")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed region, copy 1 GiB device to device twice: the reference kernel "
+                         "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: libnsa has no multi-GPU path (the NSA layer would shard "
+              "whole blocks across GPUs and all-gather the pooled K/V).", file=sys.stderr)
+        sys.exit(2)
+
+    import workloads as W
+
+    t0 = time.time()
+    w = W.make(args.config)
+    log("workload %s (%.1fs)" % (args.config, time.time() - t0))
+    # the CPU oracle first, in forked worker processes, before anything touches the GPU
+    cpu = None
+    if not args.no_cpu:
+        log("timing the fp64 oracle on a bounded sample (~%.0f s)" % args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log("oracle: %.1f tokens/s on %d cores" % (cpu["value"], cpu["cores"]))
+
+    import torch
+    import sparse_attention_feed_amd as S
+    dev = "cuda:0"
+    head = run_config(args.config, w, args.steps, args.warmup, not args.no_breakdown, torch, S, dev)
+
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    others = None
+    if not args.no_configs:
+        others = {}
+        del w
+        torch.cuda.empty_cache()
+        for name in OTHER_CONFIGS:
+            if name == args.config:
+                continue
+            t0 = time.time()
+            wo = W.make(name)
+            log("workload %s (%.1fs)" % (name, time.time() - t0))
+            r = run_config(name, wo, args.config_steps, 2, False, torch, S, dev)
+            others[name] = {"ms_per_step": r["ms_per_step"], "tokens_per_s": r["value"], "dtype": r["dtype"],
+                            "workload": r["config"]["workload"], "kernels_ms": r["kernels_ms"],
+                            "dominant": {kk: r["roofline"][kk] for kk in ("kernel", "achieved", "peak", "unit",
+                                                                          "frac")}}
+            del wo
+            torch.cuda.empty_cache()
+
+    rec = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic (seeded; token geometry and head shapes of the pages' workloads)",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "kernels_ms": head["kernels_ms"],
+        "routing_amortised_24_layers": head["routing_amortised_24_layers"],
+        "algorithmic_gflop": head["algorithmic_gflop"],
+        "branch_breakdown": head["branch_breakdown"],
         "cpu_baseline": cpu,
+        "gpu_over_oracle": round(head["value"] / cpu["value"], 1) if cpu else None,
+        "other_configs": others,
     }
     print(json.dumps(rec), flush=True)
 
