@@ -447,6 +447,58 @@ def run_config(name, w, steps, warmup, breakdown_on, torch, S, dev):
     }
 
 
+PROBES = {0: ("exp", 8, 0), 1: ("mfma", 0, 8), 2: ("mfma+exp", 16, 8), 3: ("fma", 8, 0), 4: ("mfma+fma", 32, 8),
+          5: ("tile_pass", 0, 0)}
+
+
+def run_probes():
+    """Instruction-rate microbenchmarks (libnsa_probe.so): SIMD cycles per instruction (or per loop
+    iteration for the mixes) from the shader clock, at 1, 2 and 4 waves per SIMD, and the attention
+    kernel's own token pass on register-resident tiles (its compute ceiling)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_feed_amd", "libnsa_probe.so"))
+    lib.nsa_probe_run.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
+    lib.nsa_probe_run.restype = ctypes.c_int
+    props = torch.cuda.get_device_properties(0)
+    n_cu = props.multi_processor_count
+    stream = torch.cuda.current_stream()
+    out = {"n_cu": n_cu, "device": props.name, "probes": []}
+    for which, (name, n_valu, n_mfma) in PROBES.items():
+        for k in ((1, 2) if which == 5 else (1, 2, 4)):
+            iters = 2000 if which == 5 else 20000
+            sink = torch.empty(n_cu * 256 * k, dtype=torch.float32, device="cuda")
+            cyc = torch.empty(n_cu * 4 * k, dtype=torch.int64, device="cuda")
+            run = lambda: lib.nsa_probe_run(which, k, n_cu, iters, sink.data_ptr(), cyc.data_ptr(),  # noqa: E731
+                                            ctypes.c_void_p(stream.cuda_stream))
+            assert run() == 0
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert run() == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            c = float(cyc.float().median().item())
+            rec = {"probe": name, "waves_per_simd": k, "iters": iters, "ms": round(ms, 4),
+                   "cycles_per_wave": c, "clock_ghz": round(c / (ms * 1e6), 3)}
+            per_iter = c / (iters * k)                     # SIMD cycles per loop iteration
+            if which == 5:
+                passes = 8
+                rec["simd_cycles_per_token_pass"] = round(per_iter / passes, 1)
+                flop = n_cu * 4 * k * iters * passes * 131072
+                rec["tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+                rec["frac_of_bf16_peak"] = round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+            elif n_mfma and n_valu:
+                rec["simd_cycles_per_iteration"] = round(per_iter, 1)
+                rec["instructions_per_iteration"] = {"mfma": n_mfma, "valu": n_valu}
+            else:
+                rec["simd_cycles_per_instruction"] = round(per_iter / (n_valu or n_mfma), 2)
+            log(json.dumps(rec))
+            out["probes"].append(rec)
+    return out
+
+
 # the other workloads, timed after the headline one with fewer steps
 OTHER_CONFIGS = ("stage2", "speed3r", "dense", "tiny")
 
@@ -462,6 +514,8 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="time the headline workload only")
     ap.add_argument("--config-steps", type=int, default=5, help="timed steps of each other workload")
+    ap.add_argument("--probes", action="store_true",
+                    help="run the instruction-rate microbenchmarks instead of the layer benchmark")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, copy 1 GiB device to device twice: the reference kernel "
                          "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes")
@@ -470,6 +524,10 @@ def main():
         print("bench.py measures one GPU only: libnsa has no multi-GPU path (the NSA layer would shard "
               "whole blocks across GPUs and all-gather the pooled K/V).", file=sys.stderr)
         sys.exit(2)
+
+    if args.probes:
+        print(json.dumps(run_probes()), flush=True)
+        return
 
     import workloads as W
 
