@@ -246,7 +246,7 @@ nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_
  *   lse: NULL, or (single branch only) float32 [rows][n_qh] natural-log partition function,
  *        rows = n_blk for CMP with NSA_Q_BLOCK, else S; -inf on padding rows and empty key sets.
  * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16 with NSA_Q_TOKEN (n_blk <= 65536 when SEL
- * is named); and (D, G) = (64, 1) for NSA_BF16 with NSA_Q_BLOCK, branches CMP and SEL, blk_cap in
+ * is named; n_blk * blk_cap * n_qh * max(32, gate_stride) < 2^31, row offsets being 32-bit); and (D, G) = (64, 1) for NSA_BF16 with NSA_Q_BLOCK, branches CMP and SEL, blk_cap in
  * {1, 2, 4, 8, 16} (the compressed branch's gated result is written to o in bf16 and the selected
  * branch adds to it).  top_k <= 64.  Accumulation is fp32; bf16 probabilities feed the value product.
  */
@@ -312,7 +312,8 @@ nsa_status nsa_gate_combine(nsa_dtype dtype, int32_t n_rows, int32_t n_qh, int32
  *         + sigmoid(g[t][h][1]) * Attn(q_t; keys of the other type),
  * an empty key set contributing 0.  q [n_tok][n_qh][D]; k, v [n_tok][n_kvh][D];
  * gate_logits [n_tok][n_qh][2]; o [n_tok][n_qh][D].  0 <= n_x <= n_tok.
- * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16.
+ * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16, n_tok * n_qh * 32 < 2^31
+ * (NSA_ERR_UNSUPPORTED otherwise: row offsets are 32-bit).
  */
 nsa_status dense_gated_xattn_fwd(nsa_dtype dtype, int32_t n_tok, int32_t n_x, int32_t n_qh,
                                  int32_t n_kvh, int32_t head_dim, float scale, const void* q,

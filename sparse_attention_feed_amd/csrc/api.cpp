@@ -411,6 +411,9 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   if (L->head_dim != 32 || L->n_qh / L->n_kvh != 16 || q_gran != NSA_Q_TOKEN)
     return fail(NSA_ERR_UNSUPPORTED, "%s: compiled for head_dim 32, 16 query heads per KV head, NSA_Q_TOKEN "
                                      "(or head_dim 64, one query head per KV head, NSA_Q_BLOCK)", fn);
+  // the grouped-query kernels index rows of q, o, gate_logits, lse and sel in 32-bit arithmetic
+  if ((long long)L->n_blk * L->blk_cap * L->n_qh * (gate_stride > 32 ? gate_stride : 32) > 0x7FFFFFFFLL)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: n_blk * blk_cap * n_qh * max(32, gate_stride) must be < 2^31", fn);
   nsa::AttnArgs a;
   a.q = q;
   a.k = k;
@@ -520,6 +523,8 @@ nsa_status dense_gated_xattn_fwd(nsa_dtype dtype, int32_t n_tok, int32_t n_x, in
     return fail(NSA_ERR_UNSUPPORTED, "dense_gated_xattn_fwd: q, k and v must be 16-byte aligned");
   if (head_dim != 32 || n_qh / n_kvh != 16)
     return fail(NSA_ERR_UNSUPPORTED, "dense_gated_xattn_fwd: compiled for head_dim 32, 16 query heads per KV head");
+  if ((long long)n_tok * n_qh * 32 > 0x7FFFFFFFLL)   // rows of q, o and gate_logits are indexed in 32 bits
+    return fail(NSA_ERR_UNSUPPORTED, "dense_gated_xattn_fwd: n_tok * n_qh * 32 must be < 2^31");
   NSA_FORCED_FAILURE("dense_gated_xattn_fwd");
   nsa::DenseArgs a;
   a.q = q;

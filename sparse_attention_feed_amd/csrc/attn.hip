@@ -60,8 +60,8 @@ template <typename T, int NT> struct Stager {
         bool isv = c >= CH;
         int cc = isv ? c - CH : c;
         int key = cc / CPR, part = cc % CPR;
-        if (key < nk)
-          r[i] = *reinterpret_cast<const uint4*>((isv ? vb : kb) + (size_t)key * stride + part * E);
+        if (key < nk)   // 32-bit offset within the tile: key < TILE, so key * stride fits
+          r[i] = *reinterpret_cast<const uint4*>((isv ? vb : kb) + (key * stride + part * E));
         else
           r[i] = make_uint4(0u, 0u, 0u, 0u);
       }
@@ -78,7 +78,7 @@ template <typename T, int NT> struct Stager {
         bool isv = c >= CH;
         int cc = isv ? c - CH : c;
         int key = min(cc / CPR, max(nk - 1, 0)), part = cc % CPR;
-        r[i] = *reinterpret_cast<const uint4*>((isv ? vb : kb) + (size_t)key * stride + part * E);
+        r[i] = *reinterpret_cast<const uint4*>((isv ? vb : kb) + (key * stride + part * E));
       }
     }
   }
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     Frag8<T> raw[TPW];   // every slot of the block has a query row (padding rows are never used)
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
-      raw[t] = load_q8(q + ((size_t)(b * cap + min(s0 + t * WAVES + w, cap - 1)) * a.n_qh + hh) * HD + 8 * g);
+      raw[t] = load_q8(q + ((b * cap + min(s0 + t * WAVES + w, cap - 1)) * a.n_qh + hh) * HD + 8 * g);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) qf[t] = make_qf<T>(raw[t], c2, t < n_valid);
   }
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     if (a.gates) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const size_t row = (size_t)(b * cap + min(s0 + t * WAVES + w, cap - 1));
+        const int row = b * cap + min(s0 + t * WAVES + w, cap - 1);
         gl[t] = reinterpret_cast<const T*>(a.gates)[(row * a.n_qh + hh) * a.n_gch + ch];
       }
     }
@@ -448,12 +448,12 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     for (int t = 0; t < TPW; ++t) {
       const int slot = s0 + t * WAVES + w;
       if (!(valid & (1u << t))) continue;
-      const size_t row = (size_t)(b * cap + slot);
+      const int row = b * cap + slot;
       const float wgt = a.gates ? sigmoidf_(to_f32(gl[t])) : 1.f;
       float* lp = a.lse ? a.lse + row * a.n_qh + hh : nullptr;
       f32x4 res[2];
       tok_finish(st[t], res, wgt, lp);
-      float* ol = out_lds + ((size_t)(slot - s0) * GRP + r) * HD + 4 * g;
+      float* ol = out_lds + ((slot - s0) * GRP + r) * HD + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         f32x4 acc = res[dt];
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < MAXE; ++i) {
       const int e = threadIdx.x + i * NT;
-      eblk[i] = e < cnt_p * kk ? a.sel[((size_t)(b * cap + s0 + e / kk) * a.sel_groups + grp) * kk + e % kk] : -1;
+      eblk[i] = e < cnt_p * kk ? a.sel[((b * cap + s0 + e / kk) * a.sel_groups + grp) * kk + e % kk] : -1;
     }
 #pragma unroll
     for (int i = 0; i < MAXE; ++i) ecnt[i] = (eblk[i] >= 0 && eblk[i] < a.n_blk) ? a.blk_cnt[eblk[i]] : 0;
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   for (int t = 0; t < TPW; ++t) {
     const int slot = s0 + t * WAVES + w;
     if (slot >= cap || slot < cnt) continue;
-    const size_t row = (size_t)(b * cap + slot);
+    const int row = b * cap + slot;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       T* dst = o + (row * a.n_qh + hh) * HD + 16 * dt + 4 * g;
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
     Frag8<T> raw[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
-      raw[t] = load_q8(q + ((size_t)min(qb * SLOTS + t * WAVES + w, a.n_tok - 1) * a.n_qh + hh) * HD + 8 * g);
+      raw[t] = load_q8(q + (min(qb * SLOTS + t * WAVES + w, a.n_tok - 1) * a.n_qh + hh) * HD + 8 * g);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) qf[t] = make_qf<T>(raw[t], c2, t < n_valid);
   }
@@ -664,7 +664,7 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
     for (int t = 0; t < TPW; ++t) {
       const int tok = min(qb * SLOTS + t * WAVES + w, a.n_tok - 1);
       const int ch = ((tok < a.n_x) == (ph == 0)) ? 0 : 1;
-      gl[t] = gp[((size_t)tok * a.n_qh + hh) * 2 + ch];
+      gl[t] = gp[(tok * a.n_qh + hh) * 2 + ch];
     }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
       const float wgt = sigmoidf_(to_f32(gl[t]));
       f32x4 res[2];
       tok_finish(st[t], res, wgt, nullptr);
-      float* ol = out_lds + ((size_t)slot * GRP + r) * HD + 4 * g;
+      float* ol = out_lds + (slot * GRP + r) * HD + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         if (ph == 0) {
@@ -684,7 +684,7 @@ __global__ __launch_bounds__(WAVES * 64) void dense_xattn_kernel(DenseArgs a) {
           f32x4 acc = res[dt];
           if constexpr (kOutLds) acc += *reinterpret_cast<const f32x4*>(ol + 16 * dt);
           else acc += out_reg[kOutLds ? 0 : t][dt];
-          T* dst = o + ((size_t)tok * a.n_qh + hh) * HD + 16 * dt + 4 * g;
+          T* dst = o + (tok * a.n_qh + hh) * HD + 16 * dt + 4 * g;
 #pragma unroll
           for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(acc[i]);
         }
