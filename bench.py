@@ -257,11 +257,9 @@ def setup_speed3r(w, S, torch, dev):
         return [
             ("pool_qkv", lambda: (S.pool_blocks(L, q, ws["q_cmp"]), S.pool_blocks(L, k, ws["k_cmp"]),
                                   S.pool_blocks(L, v, ws["v_cmp"]))),
-            ("route_scores", lambda: S.route_scores_topk(L, ws["q_cmp"], ws["k_cmp"], None, w.top_k,
-                                                          q_gran=S.Q_BLOCK, sel=ws["sel"])),
-            ("attn_fused", lambda: S.attn_fwd(L, S.BR_CMP | S.BR_SEL, q, k, v, q_cmp=ws["q_cmp"], k_cmp=ws["k_cmp"],
-                                              v_cmp=ws["v_cmp"], sel=ws["sel"], top_k=w.top_k, sel_groups=w.n_kvh,
-                                              gates=g, out=ws["out"], q_gran=S.Q_BLOCK)),
+            # the routing comes out of the compressed branch's own pass (nsa_attn_fwd_scores_routed)
+            ("attn_routed", lambda: S.attn_fwd_scores_routed(L, q, k, v, ws["q_cmp"], ws["k_cmp"], ws["v_cmp"],
+                                                             w.top_k, g, out=ws["out"], sel=ws["sel"])),
         ]
 
     def flops():
@@ -286,13 +284,17 @@ def setup_speed3r(w, S, torch, dev):
                                   sel=ws["sel"], top_k=w.top_k, sel_groups=w.n_kvh, gates=gg, out=ws["out"],
                                   q_gran=S.Q_BLOCK)
 
-    fns = {"cmp": branch(S.BR_CMP), "sel": branch(S.BR_SEL)}
+    fns = {"cmp": branch(S.BR_CMP), "sel": branch(S.BR_SEL),
+           # the two-call sequence the fused pass replaces: stand-alone routing, then both branches
+           "route": lambda: S.route_scores_topk(L, ws["q_cmp"], ws["k_cmp"], None, w.top_k, q_gran=S.Q_BLOCK,
+                                                sel=ws["sel"]),
+           "cmp+sel": branch(S.BR_CMP | S.BR_SEL)}
     if fr[1] > fr[0]:
         # the variant with a reference frame: its blocks are attended by every query
         fns["sel_forced_ref_frame"] = lambda: S.attn_fwd(
             L, S.BR_SEL, q, k, v, sel=ws["sel"], top_k=w.top_k, sel_groups=w.n_kvh, out=ws["out"],
             q_gran=S.Q_BLOCK, forced=fr)
-    return stages, flops, fns, "attn_fused"
+    return stages, flops, fns, "attn_routed"
 
 
 def setup_dense(w, S, torch, dev):

@@ -257,6 +257,26 @@ nsa_status nsa_attn_fwd(const nsa_layout* layout, nsa_dtype dtype, uint32_t bran
                         const void* gate_logits, void* o, float* lse, hipStream_t stream);
 
 /*
+ * The compressed and selected branches with block queries, routed by the compressed branch's own
+ * scores in the same pass (Speed3R page, section 2.1: every query block picks, per head, the
+ * top-k key blocks by its pooled scores, and its tokens attend those blocks).  Equals
+ * nsa_route_scores_topk(layout, dtype, NSA_Q_BLOCK, q_cmp, k_cmp, NULL, top_k, sel) followed by
+ * nsa_attn_fwd(layout, dtype, NSA_BR_CMP | NSA_BR_SEL, NSA_Q_BLOCK, q, k, v, q_cmp, k_cmp, v_cmp,
+ * sel, top_k, n_kvh, gate_logits, o, NULL): sel receives the same routing rows
+ * [n_blk][n_kvh][top_k] (descending by score, ties to the smaller blk_key, -1 past the last
+ * block), while the compressed branch's logits are formed in fp32 from the raw pooled queries
+ * (rather than from bf16 queries pre-scaled by scale * log2(e)), so o agrees with the two-call
+ * sequence to rounding.  gate_logits [S][n_qh][2] (channel 0 compressed, 1 selected), bf16.
+ * Supported (NSA_ERR_UNSUPPORTED otherwise): n_qh == n_kvh, head_dim 64, NSA_BF16, blk_cap in
+ * {1, 2, 4, 8, 16}, top_k <= 32.  sel and o must not overlap any input.
+ */
+nsa_status nsa_attn_fwd_scores_routed(const nsa_layout* layout, nsa_dtype dtype, const void* q,
+                                      const void* k, const void* v, const void* q_cmp,
+                                      const void* k_cmp, const void* v_cmp, int32_t top_k,
+                                      const void* gate_logits, void* o, int32_t* sel,
+                                      hipStream_t stream);
+
+/*
  * nsa_attn_fwd with a forced block range in the selected branch (Speed3R page, section 2.2: in the
  * variant for a model with a reference frame, that frame's tokens are always attended, whatever the
  * routing picks).  SEL's key set for every row becomes the valid tokens of the union of the routed

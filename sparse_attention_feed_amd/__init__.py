@@ -23,7 +23,7 @@ BR_CMP, BR_SEL, BR_LOC = 1, 2, 4
 Q_TOKEN, Q_BLOCK = 0, 1
 EXPORTS = ("nsa_build_volume_blocks", "nsa_pool_blocks", "nsa_pool_blocks_resblock", "nsa_route_geometric",
            "nsa_route_geometric_range", "nsa_route_geometric_views", "nsa_attn_fwd_range", "nsa_route_scores_topk", "nsa_attn_fwd",
-           "nsa_attn_fwd_forced",
+           "nsa_attn_fwd_forced", "nsa_attn_fwd_scores_routed",
            "nsa_gate_combine", "dense_gated_xattn_fwd", "nsa_route_geometric_noalloc", "nsa_last_error")
 
 
@@ -58,6 +58,7 @@ def _load():
         "nsa_route_scores_topk": [LP, I, I, P, P, P, I, P, P],
         "nsa_attn_fwd": [LP, I, U, I, P, P, P, P, P, P, P, I, I, P, P, P, P],
         "nsa_attn_fwd_forced": [LP, I, U, I, P, P, P, P, P, P, P, I, I, I, I, P, P, P, P],
+        "nsa_attn_fwd_scores_routed": [LP, I, P, P, P, P, P, P, I, P, P, P, P],
         "nsa_gate_combine": [I, I, I, I, I, ctypes.POINTER(ctypes.c_void_p), P, P, P],
         "dense_gated_xattn_fwd": [I, I, I, I, I, I, F, P, P, P, P, P, P],
     }
@@ -310,6 +311,18 @@ def attn_fwd(layout: BlockLayout, branches, q, k=None, v=None, q_cmp=None, k_cmp
                                   _ptr(k), _ptr(v), _ptr(k_cmp), _ptr(v_cmp), _ptr(sel), int(top_k), int(sel_groups),
                                   gp, gs, _ptr(out), _ptr(lse), _stream()))
     return out
+
+
+def attn_fwd_scores_routed(layout: BlockLayout, q, k, v, q_cmp, k_cmp, v_cmp, top_k, gates, out=None, sel=None):
+    """Compressed + selected branches with block queries, the routing taken from the compressed
+    pass's own scores (nsa_attn_fwd_scores_routed).  Returns (out, sel [n_blk, n_kvh, top_k])."""
+    if out is None:
+        out = torch.empty_like(q)
+    if sel is None:
+        sel = torch.empty((layout.n_blk, layout.n_kvh, top_k), dtype=torch.int32, device=q.device)
+    _check(lib.nsa_attn_fwd_scores_routed(layout.c, _dtype(q), _ptr(q), _ptr(k), _ptr(v), _ptr(q_cmp), _ptr(k_cmp),
+                                          _ptr(v_cmp), int(top_k), _ptr(gates), _ptr(out), _ptr(sel), _stream()))
+    return out, sel
 
 
 def gate_combine(outs, gates, out=None):

@@ -486,6 +486,55 @@ nsa_status nsa_attn_fwd_range(const nsa_layout* L, nsa_dtype dtype, uint32_t bra
                   stream);
 }
 
+nsa_status nsa_attn_fwd_scores_routed(const nsa_layout* L, nsa_dtype dtype, const void* q, const void* k,
+                                      const void* v, const void* q_cmp, const void* k_cmp, const void* v_cmp,
+                                      int32_t top_k, const void* gate_logits, void* o, int32_t* sel,
+                                      hipStream_t stream) {
+  const char* fn = "nsa_attn_fwd_scores_routed";
+  nsa_status st = check_layout(L, fn);
+  if (st != NSA_OK) return st;
+  if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "%s: unknown dtype", fn);
+  if (q == nullptr || k == nullptr || v == nullptr || q_cmp == nullptr || k_cmp == nullptr || v_cmp == nullptr ||
+      gate_logits == nullptr || o == nullptr || sel == nullptr || L->blk_key == nullptr)
+    return fail(NSA_ERR_INVALID, "%s: q, k, v, q_cmp, k_cmp, v_cmp, gate_logits, o, sel and blk_key must be non-NULL", fn);
+  if (top_k < 1 || top_k > 64) return fail(NSA_ERR_INVALID, "%s: top_k must be in 1..64 (got %d)", fn, top_k);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_cmp) || !aligned16(k_cmp) || !aligned16(v_cmp) ||
+      !aligned16(o))
+    return fail(NSA_ERR_UNSUPPORTED, "%s: q, k, v, q_cmp, k_cmp, v_cmp and o must be 16-byte aligned", fn);
+  if (L->n_qh != L->n_kvh || L->head_dim != 64 || dtype != NSA_BF16 || L->blk_cap > 16 || 64 % L->blk_cap != 0 ||
+      top_k > 32)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: compiled for one query head per KV head, head_dim 64, bf16, blk_cap in "
+                                     "{1, 2, 4, 8, 16} and top_k <= 32", fn);
+  NSA_FORCED_FAILURE(fn);
+  nsa::G1Args g{};
+  g.q = q;
+  g.k = k;
+  g.v = v;
+  g.q_cmp = q_cmp;
+  g.k_cmp = k_cmp;
+  g.v_cmp = v_cmp;
+  g.sel = sel;
+  g.blk_cnt = L->blk_cnt;
+  g.blk_key = L->blk_key;
+  g.gates = gate_logits;
+  g.o = o;
+  g.lse = nullptr;
+  g.n_blk = L->n_blk;
+  g.cap = L->blk_cap;
+  g.n_qh = L->n_qh;
+  g.n_kvh = L->n_kvh;
+  g.top_k = top_k;
+  g.sel_groups = L->n_kvh;
+  g.n_gch = 2;
+  g.ch_cmp = 0;
+  g.ch_sel = 1;
+  g.scale = L->scale;
+  g.branches = NSA_BR_CMP | NSA_BR_SEL;
+  g.f_lo = 0;
+  g.f_hi = 0;
+  return hip_status(nsa::launch_attn_g1_routed(g, stream), fn);
+}
+
 nsa_status nsa_gate_combine(nsa_dtype dtype, int32_t n_rows, int32_t n_qh, int32_t head_dim, int32_t n_branch,
                             const void* const* o_branch, const void* gate_logits, void* o, hipStream_t stream) {
   if (!dtype_ok(dtype)) return fail(NSA_ERR_INVALID, "nsa_gate_combine: unknown dtype");

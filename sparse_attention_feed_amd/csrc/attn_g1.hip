@@ -562,6 +562,196 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// compressed branch and routing in one pass (block queries)
+// ---------------------------------------------------------------------------------------------
+//
+// The compressed branch and the routing of the selected branch read the same scores, pooled Q
+// against pooled K (Speed3R page, section 2.1: the blocks are picked from the compressed
+// attention's scores; with one query head per KV head the probability order is the score order).
+// This kernel forms S^T = K Q^T once per tile from the raw pooled queries, ranks it for the
+// routing with the products and ranking key of route_g1_kernel (so the routing rows are the same),
+// and feeds scale * log2(e) * S to the compressed branch's online softmax.
+//
+// A row's running top-K list is spread over its four lanes: lane group g holds ranks
+// [gE, gE + E) in descending order (K = 4E), so the row's K-th best key, the bound a score must
+// reach to be a candidate, is lane group 3's last entry.  A candidate enters in one step of all
+// four lane groups: a group whose last entry the candidate beats takes the candidate, or, when the
+// candidate also beats the previous group's last entry, that entry (which the previous group
+// pushes out); a bounded sorted insert of that value keeps every group sorted and the list exact.
+// Each round inserts one pending candidate per row, from the row's lowest lane group that has one.
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = __shfl((uint32_t)v, src, 64), hi = __shfl((uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int E, int CGF>
+__global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
+  static_assert(CW * 64 == KT * 8, "one 16-byte piece of K and of V per thread");
+  __shared__ TileG1 tb[2];
+  __shared__ uint32_t keys_lds[2][KT];
+  __shared__ f32x4 sc_lds[CW][4][64];        // one column group's tile scores per wave, slot-major
+  constexpr int ROWS = CW * CGF * 16;
+  const int n_rowgrp = (a.n_blk + ROWS - 1) / ROWS;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = wg / n_rowgrp, rg = wg % n_rowgrp;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), r = l & 15, g = l >> 4;
+  const int stride = a.n_kvh * DG;
+  const bf16* qc = reinterpret_cast<const bf16*>(a.q_cmp);
+  const bf16* kb = reinterpret_cast<const bf16*>(a.k_cmp) + h * DG;
+  const bf16* vb = reinterpret_cast<const bf16*>(a.v_cmp) + h * DG;
+  const float c2 = a.scale * kLog2e;
+
+  QG1 q[CGF];
+  StateG1 st[CGF];
+  TopList<E> lst[CGF];
+  float thr[CGF];
+  int row_of[CGF];
+#pragma unroll
+  for (int c = 0; c < CGF; ++c) {
+    row_of[c] = (rg * CW * CGF + w * CGF + c) * 16 + r;
+    q[c] = load_q_row(qc + ((size_t)row_of[c] * a.n_qh + h) * DG, row_of[c] < a.n_blk);   // raw
+    state_init(st[c]);
+    toplist_init(lst[c]);
+    thr[c] = -INFINITY;
+  }
+  const int ntiles = (a.n_blk + KT - 1) / KT;
+  // staging as in cmp_g1_kernel, plus the tile's 64 ranking keys (threads < 64)
+  const int s_key = tid >> 3, s_part = tid & 7;
+  auto fetch = [&](int u, uint4& kv, uint4& vv, uint32_t& bkey) {
+    const size_t off = (size_t)min(u * KT + s_key, a.n_blk - 1) * stride + s_part * 8;
+    kv = *reinterpret_cast<const uint4*>(kb + off);
+    vv = *reinterpret_cast<const uint4*>(vb + off);
+    bkey = a.blk_key[min(u * KT + (tid & (KT - 1)), a.n_blk - 1)];
+  };
+  auto store = [&](int buf, const uint4& kv, const uint4& vv, uint32_t bkey) {
+    TileG1& t = tb[buf];
+    *reinterpret_cast<uint4*>(&t.k[s_key][s_part * 8]) = kv;
+    const uint32_t wd[4] = {vv.x, vv.y, vv.z, vv.w};
+    const int pos = vt_pos_g1(s_key);
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      t.vt[s_part * 8 + x][pos] = __builtin_bit_cast(bf16, (uint16_t)(wd[x >> 1] >> (16 * (x & 1))));
+    if (tid < KT) keys_lds[buf][tid] = bkey;
+  };
+  uint4 kv, vv;
+  uint32_t bkey;
+  fetch(0, kv, vv, bkey);
+  store(0, kv, vv, bkey);
+  __syncthreads();
+  for (int u = 0; u < ntiles; ++u) {
+    const int cur = u & 1;
+    if (u + 1 < ntiles) fetch(u + 1, kv, vv, bkey);
+    TileFragsG1 f;
+    load_frags_g1(tb[cur], f);
+    const int nk = min(KT, a.n_blk - u * KT);
+    uint32_t vmask = 0xFFFFu;                 // slot j = 4*kt + i holds key 16*kt + 4*g + i
+    if (nk < KT) {
+      vmask = 0u;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) vmask |= (16 * (j >> 2) + 4 * g + (j & 3) < nk) ? (1u << j) : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < CGF; ++c) {
+      f32x4 s[4];
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[kt] = mma16(f.k[kt][1], q[c].h[1], mma16(f.k[kt][0], q[c].h[0], z));
+      // ---- routing: candidates reach the row's K-th best score ----
+      uint32_t m = 0u;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m |= (s[j >> 2][j & 3] >= thr[c]) ? (1u << j) : 0u;
+      m &= vmask;
+      if (row_of[c] >= a.n_blk) m = 0u;       // rows past the end rank nothing
+      if (__builtin_amdgcn_ballot_w64(m != 0u) != 0ull) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sc_lds[w][kt][l] = s[kt];
+        for (;;) {
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(m != 0u);
+          if (bal == 0ull) break;
+          const uint32_t rowbits = (uint32_t)((bal >> r) & 1ull) | (uint32_t)((bal >> (r + 15)) & 2ull) |
+                                   (uint32_t)((bal >> (r + 30)) & 4ull) | (uint32_t)((bal >> (r + 45)) & 8ull);
+          const int gs = rowbits != 0u ? __builtin_ctz(rowbits) : g;
+          uint64_t ck = 0ull;
+          int ci = -1;
+          if (rowbits != 0u && g == gs) {
+            const int j = __builtin_ctz(m);
+            m &= m - 1u;
+            const float v = reinterpret_cast<const float*>(&sc_lds[w][j >> 2][l])[j & 3];
+            const int key = 16 * (j >> 2) + 4 * g + (j & 3);
+            if (v >= thr[c]) {
+              ck = rank_key(v, keys_lds[cur][key]);
+              ci = u * KT + key;
+            }
+          }
+          const int src = r + 16 * gs;
+          ck = shfl_u64(ck, src);
+          ci = __shfl(ci, src, 64);
+          const uint64_t pk = shfl_u64(lst[c].key[E - 1], (l + 48) & 63);   // previous group's last
+          const int pi = __shfl(lst[c].idx[E - 1], (l + 48) & 63, 64);
+          const bool push = g > 0 && ck > pk;
+          toplist_insert(lst[c], push ? pk : ck, push ? pi : ci);
+          thr[c] = unord_f32((uint32_t)(shfl_u64(lst[c].key[E - 1], r + 48) >> 32));
+        }
+      }
+      // ---- compressed branch: base-2 logits relative to the running reference max ----
+      f32x4 x[4];
+      if (nk == KT) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[kt][i] = __builtin_fmaf(s[kt][i], c2, -st[c].mc);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            x[kt][i] = ((vmask >> (4 * kt + i)) & 1u) ? __builtin_fmaf(s[kt][i], c2, -st[c].mc) : -INFINITY;
+      }
+      softmax_pv_g1(st[c], x, f);
+    }
+    // every wave finished tile u - 1 (the previous barrier), so buffer cur ^ 1 is free
+    if (u + 1 < ntiles) store(cur ^ 1, kv, vv, bkey);
+    __syncthreads();
+  }
+  // finish: normalise, gate per token, give the block's pooled result to each of its tokens; the
+  // routing row is the list itself (lane group g holds ranks gE .. gE + E - 1)
+  bf16* o = reinterpret_cast<bf16*>(a.o);
+  const bf16* gp = reinterpret_cast<const bf16*>(a.gates);
+  int32_t* sel = const_cast<int32_t*>(a.sel);
+#pragma unroll
+  for (int c = 0; c < CGF; ++c) {
+    const int b = row_of[c];
+    const float lsum = rows_sum(st[c].l);
+    if (b >= a.n_blk) continue;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int rank = g * E + e;
+      if (rank < a.top_k) sel[((size_t)b * a.n_kvh + h) * a.top_k + rank] = lst[c].key[e] == 0ull ? -1 : lst[c].idx[e];
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int cnt = a.blk_cnt[b];
+    for (int t = 0; t < a.cap; ++t) {
+      const size_t row = (size_t)b * a.cap + t;
+      float wgt = 0.f;
+      if (t < cnt) wgt = gp ? sigmoidf_((float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_cmp]) * inv : inv;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        bf16x4* dst = reinterpret_cast<bf16x4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
+        *dst = __builtin_convertvector(st[c].acc[dt] * wgt, bf16x4);
+      }
+    }
+  }
+}
+
+template <int E, int CGF>
+hipError_t launch_cmp_route_g1_k(const G1Args& a, hipStream_t s) {
+  const int n_rowgrp = (a.n_blk + CW * CGF * 16 - 1) / (CW * CGF * 16);
+  hipLaunchKernelGGL((cmp_route_g1_kernel<E, CGF>), dim3(n_rowgrp * a.n_kvh), dim3(CW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
 // selected branch with block routing rows: one wave per (query block, head)
 // ---------------------------------------------------------------------------------------------
 
@@ -667,6 +857,18 @@ hipError_t launch_route_g1(const G1Args& a, hipStream_t s) {
   if (a.top_k <= 16) return launch_route_g1_k<16, 2>(a, s);
   if (a.top_k <= 32) return launch_route_g1_k<32, 1>(a, s);
   return launch_route_g1_k<64, 1>(a, s);
+}
+
+hipError_t launch_attn_g1_routed(const G1Args& a0, hipStream_t s) {
+  G1Args a = a0;
+  hipError_t e;
+  if (a.top_k <= 8) e = launch_cmp_route_g1_k<2, 2>(a, s);
+  else if (a.top_k <= 16) e = launch_cmp_route_g1_k<4, 2>(a, s);
+  else e = launch_cmp_route_g1_k<8, 1>(a, s);
+  if (e != hipSuccess) return e;
+  a.accumulate = 1;
+  hipLaunchKernelGGL(sel_g1_kernel<0>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_g1(const G1Args& a0, hipStream_t s) {

@@ -237,3 +237,85 @@ def test_full_size_sampled():
     assert same.mean() >= 0.8, same.mean()
     diff = np.abs(host(o)[toks] - ref).max(axis=2)
     assert diff[same].max() <= 2e-2
+
+
+def _routed_case(w, qc=None, kc=None):
+    """Both paths on the same device inputs: the fused compressed+routing pass and the two-call
+    sequence (routing, then the compressed and selected branches)."""
+    import sparse_attention_feed_amd as S
+    d = to_dev(w)
+    L = d["layout"]
+    qd = S.pool_blocks(L, d["q"]) if qc is None else dev(qc)
+    kd = S.pool_blocks(L, d["k"]) if kc is None else dev(kc)
+    vd = S.pool_blocks(L, d["v"])
+    o_f, sel_f = S.attn_fwd_scores_routed(L, d["q"], d["k"], d["v"], qd, kd, vd, w.top_k, d["gates"])
+    sel_2 = S.route_scores_topk(L, qd, kd, None, w.top_k, q_gran=S.Q_BLOCK)
+    o_2 = S.attn_fwd(L, S.BR_CMP | S.BR_SEL, d["q"], d["k"], d["v"], q_cmp=qd, k_cmp=kd, v_cmp=vd, sel=sel_2,
+                     top_k=w.top_k, sel_groups=w.n_kvh, gates=d["gates"], q_gran=S.Q_BLOCK)
+    torch.cuda.synchronize()
+    return host(o_f), host(sel_f), host(o_2), host(sel_2), host(qd), host(kd), host(vd)
+
+
+@pytest.mark.parametrize("n_blk,k,seed", [(200, 16, 1), (130, 5, 2), (77, 32, 3), (10, 16, 4), (1, 8, 5),
+                                          (64, 24, 6)])
+def test_scores_routed_equals_two_calls(n_blk, k, seed):
+    """The fused pass picks the same routing rows as nsa_route_scores_topk (the same products and
+    ranking key: bit-identical), and its layer output agrees with the two-call sequence and with the
+    oracle's steps on the same pooled values.  Ragged counts, ragged last key tile, fewer blocks
+    than k (tail of -1), each list size (k <= 8, 16, 32)."""
+    rng = np.random.default_rng(seed)
+    cnt = rng.integers(1, 17, size=n_blk)
+    w = W.custom_block_workload(90 + seed, cnt, 16, 16, 16, 64, "bf16", k, routing="scores", q_gran="block",
+                                branches=("cmp", "sel"), n_gate=2)
+    say("scores_routed", n_blk, k)
+    o_f, sel_f, o_2, sel_2, qc, kc, vc = _routed_case(w)
+    np.testing.assert_array_equal(sel_f, sel_2)
+    vm = w.valid_mask()
+    assert np.all(o_f[~vm] == 0)
+    assert max_err(o_f[vm], o_2[vm]) <= 2e-2
+    # the oracle's steps on the device's pooled values and routing rows
+    o_cmp, _ = O.attn_branch(O.CMP, qc, kc, vc, w.blk_cnt, w.blk_cap, w.scale, q_gran="block")
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel_f, q_gran="block")
+    ref = O.gate_combine([o_cmp, o_sel], w.gates)
+    assert max_err(o_f[vm], ref[vm]) <= 2e-2
+
+
+def test_scores_routed_exact_on_integer_inputs():
+    """Small-integer pooled queries and keys: every score is exact in fp32, so the fused routing
+    equals the oracle's ranking bit for bit, ties (resolved by blk_key) included."""
+    w = wl("speed3r_small")
+    rng = np.random.default_rng(8)
+    qc = rng.integers(-2, 3, size=(w.n_blk, w.n_qh, w.head_dim)).astype(np.float32)
+    kc = rng.integers(-2, 3, size=(w.n_blk, w.n_kvh, w.head_dim)).astype(np.float32)
+    say("scores_routed integer")
+    o_f, sel_f, o_2, sel_2, _, _, _ = _routed_case(w, qc, kc)
+    ref_sel, _ = O.route_scores(qc, kc, w.blk_key, w.scale, w.top_k)
+    np.testing.assert_array_equal(sel_f, ref_sel)
+    np.testing.assert_array_equal(sel_2, ref_sel)
+
+
+def test_scores_routed_full_size():
+    """Full size (25,600 blocks, top-16): the fused pass's routing rows equal the two-call routing on
+    every row, and the layer output matches the two-call output on every valid token and the
+    oracle's layer (its own pooling and routing) on sampled tokens whose rows agree."""
+    say("generate speed3r")
+    w = wl("speed3r")
+    say("scores_routed full", w.n_blk)
+    o_f, sel_f, o_2, sel_2, _, _, _ = _routed_case(w)
+    np.testing.assert_array_equal(sel_f, sel_2)
+    vm = w.valid_mask()
+    assert max_err(o_f[vm], o_2[vm]) <= 2e-2
+    qr, kr, vr = pooled(w)
+    rng = np.random.default_rng(12)
+    toks = np.sort(rng.choice(w.valid_slots(), 48, replace=False))
+    blocks = np.unique(toks // w.blk_cap)
+    sel_o = np.full((w.n_blk, w.n_kvh, w.top_k), -1, dtype=np.int32)
+    sel_o[blocks], _ = O.route_scores(qr[blocks], kr, w.blk_key, w.scale, w.top_k)
+    o_cmp, _ = O.attn_branch(O.CMP, qr, kr, vr, w.blk_cnt, w.blk_cap, w.scale, q_gran="block", rows=toks)
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel_o, q_gran="block",
+                             rows=toks)
+    ref = O.gate_combine([o_cmp, o_sel], w.gates[toks])
+    same = np.all(sel_f[toks // w.blk_cap] == sel_o[toks // w.blk_cap], axis=2)
+    assert same.mean() >= 0.8, same.mean()
+    diff = np.abs(o_f[toks] - ref).max(axis=2)
+    assert diff[same].max() <= 2e-2

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 14
+    assert "nsa_attn_fwd" in names and "dense_gated_xattn_fwd" in names and len(names) == 15
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -290,3 +290,29 @@ def test_noalloc_routing_validation(S, monkeypatch):
     assert r(ctypes.byref(layout(S, blk_key=None)), FAKE, 4, FAKE, None, None) == -1
     monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
     assert r(ctypes.byref(layout(S, n_blk=65536, blk_cap=1)), FAKE, 4, FAKE, None, None) == -3
+
+
+def test_scores_routed_validation(S, monkeypatch):
+    """nsa_attn_fwd_scores_routed: argument checks and the supported set, before any device work."""
+    f = S.lib.nsa_attn_fwd_scores_routed
+    g1 = dict(n_blk=64, blk_cap=16, n_qh=16, n_kvh=16, head_dim=64, scale=0.125)
+
+    def call(L, top_k=16, dtype=1, gates=FAKE, sel=FAKE, q_cmp=FAKE):
+        return f(ctypes.byref(L), dtype, FAKE, FAKE, FAKE, q_cmp, FAKE, FAKE, top_k, gates, FAKE, sel, None)
+
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    assert call(layout(S, **g1)) == -3                           # valid: reaches the launch
+    assert call(layout(S, **g1), top_k=32) == -3
+    assert call(layout(S, **g1), top_k=0) == -1
+    assert call(layout(S, **g1), top_k=33) == -2                 # compiled lists hold at most 32
+    assert "top_k <= 32" in S.lib.nsa_last_error().decode()
+    assert call(layout(S, **g1), gates=None) == -1
+    assert call(layout(S, **g1), sel=None) == -1
+    assert call(layout(S, **g1), q_cmp=None) == -1
+    assert call(layout(S, **dict(g1, blk_key=None))) == -1
+    assert call(layout(S, **g1), dtype=0) == -2                  # f32: bf16 only
+    assert call(layout(S, **dict(g1, blk_cap=32))) == -2
+    assert call(layout(S, **dict(g1, blk_cap=12))) == -2
+    assert call(layout(S)) == -2                                 # grouped-query layout
+    assert f(ctypes.byref(layout(S, **g1)), 1, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
+             None) == -2                                         # misaligned q
