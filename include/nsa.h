@@ -246,9 +246,11 @@ nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_
  *   lse: NULL, or (single branch only) float32 [rows][n_qh] natural-log partition function,
  *        rows = n_blk for CMP with NSA_Q_BLOCK, else S; -inf on padding rows and empty key sets.
  * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16 with NSA_Q_TOKEN (n_blk <= 65536 when SEL
- * is named; n_blk * blk_cap * n_qh * max(32, gate_stride) < 2^31, row offsets being 32-bit); and (D, G) = (64, 1) for NSA_BF16 with NSA_Q_BLOCK, branches CMP and SEL, blk_cap in
- * {1, 2, 4, 8, 16} (the compressed branch's gated result is written to o in bf16 and the selected
- * branch adds to it).  top_k <= 64.  Accumulation is fp32; bf16 probabilities feed the value product.
+ * is named; n_blk * blk_cap * n_qh * max(32, gate_stride) < 2^31, row offsets being 32-bit); and
+ * (D, G) = (64, 1) for NSA_BF16 with NSA_Q_BLOCK (pooled queries in the compressed branch, token
+ * queries in the selected and local ones), blk_cap in {1, 2, 4, 8, 16}: each named branch runs in
+ * its own launch, the first writing its gated result to o in bf16 and the later ones adding to it.
+ * top_k <= 64.  Accumulation is fp32; bf16 probabilities feed the value product.
  */
 nsa_status nsa_attn_fwd(const nsa_layout* layout, nsa_dtype dtype, uint32_t branches,
                         nsa_qgran q_gran, const void* q, const void* k, const void* v,

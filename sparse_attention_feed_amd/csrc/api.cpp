@@ -369,11 +369,10 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   }
   if (L->n_qh == L->n_kvh) {
     // one query head per KV head (score-routed, block-granular layout)
-    if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK || dtype != NSA_BF16 || (branches & NSA_BR_LOC) ||
-        L->blk_cap > 16 || 64 % L->blk_cap != 0)
+    if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK || dtype != NSA_BF16 || L->blk_cap > 16 || 64 % L->blk_cap != 0)
       return fail(NSA_ERR_UNSUPPORTED,
                   "%s: with one query head per KV head the compiled kernels take head_dim 64, NSA_Q_BLOCK, "
-                  "bf16, the CMP and SEL branches and blk_cap in {1, 2, 4, 8, 16}", fn);
+                  "bf16 and blk_cap in {1, 2, 4, 8, 16}", fn);
     if (!whole) return fail(NSA_ERR_UNSUPPORTED, "%s: block ranges need the grouped-query kernel (head_dim 32)", fn);
     if (f_hi - f_lo > nsa::kMaxForcedBlocks)
       return fail(NSA_ERR_UNSUPPORTED, "%s: at most %d forced blocks", fn, nsa::kMaxForcedBlocks);
@@ -400,6 +399,7 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
     g.n_gch = n_named;
     g.ch_cmp = 0;
     g.ch_sel = (branches & NSA_BR_CMP) ? 1 : 0;
+    g.ch_loc = g.ch_sel + ((branches & NSA_BR_SEL) ? 1 : 0);
     g.scale = L->scale;
     g.branches = branches;
     g.f_lo = f_lo;
@@ -528,6 +528,7 @@ nsa_status nsa_attn_fwd_scores_routed(const nsa_layout* L, nsa_dtype dtype, cons
   g.n_gch = 2;
   g.ch_cmp = 0;
   g.ch_sel = 1;
+  g.ch_loc = 2;
   g.scale = L->scale;
   g.branches = NSA_BR_CMP | NSA_BR_SEL;
   g.f_lo = 0;

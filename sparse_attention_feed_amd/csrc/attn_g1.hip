@@ -773,12 +773,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 ? 1 :
   const float c2 = a.scale * kLog2e;
   // lane x < top_k holds entry x of this block's routing row for head h; -1, out-of-range and
   // repeated entries count no keys; the valid tokens of the rest are packed one after another
+  // (local branch: the one entry is the block itself)
   const int grp = a.sel_groups == 1 ? 0 : h;
-  const int32_t* srow = a.sel + ((size_t)b * a.sel_groups + grp) * a.top_k;
-  const int sb = l < a.top_k ? srow[l] : -1;
+  const int n_ent = a.local ? 1 : a.top_k;
+  const int sb = a.local ? (l == 0 ? b : -1) : (l < a.top_k ? a.sel[((size_t)b * a.sel_groups + grp) * a.top_k + l] : -1);
   const int nf = NF > 0 ? a.f_hi - a.f_lo : 0;
   bool keep = sb >= 0 && sb < a.n_blk && !(sb >= a.f_lo && sb - a.f_lo < nf);   // forced blocks come below
-  for (int y = 0; y < a.top_k; ++y) {
+  for (int y = 0; y < n_ent; ++y) {
     const int sy = __builtin_amdgcn_readlane(sb, y);
     keep = keep && !(y < l && sy == sb);
   }
@@ -881,10 +882,21 @@ hipError_t launch_attn_g1(const G1Args& a0, hipStream_t s) {
   }
   if (a.branches & 2) {
     a.accumulate = (a.branches & 1) ? 1 : 0;
+    a.local = 0;
     if (a.f_hi > a.f_lo)
       hipLaunchKernelGGL(sel_g1_kernel<kMaxForcedBlocks>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
     else
       hipLaunchKernelGGL(sel_g1_kernel<0>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.branches & 4) {
+    // local branch: the selected branch's kernel with the block's own block as its one entry
+    a.accumulate = (a.branches & 3) ? 1 : 0;
+    a.local = 1;
+    a.ch_sel = a.ch_loc;
+    a.f_lo = a.f_hi = 0;
+    hipLaunchKernelGGL(sel_g1_kernel<0>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;

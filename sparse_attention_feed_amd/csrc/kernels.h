@@ -82,10 +82,11 @@ struct G1Args {
   const void* gates;    // nullable
   void* o;
   float* lse;           // nullable
-  int n_blk, cap, n_qh, n_kvh, top_k, sel_groups, n_gch, ch_cmp, ch_sel;
+  int n_blk, cap, n_qh, n_kvh, top_k, sel_groups, n_gch, ch_cmp, ch_sel, ch_loc;
   float scale;
   uint32_t branches;
-  int accumulate;       // selected branch adds to o (the compressed branch wrote it first)
+  int accumulate;       // selected/local branch adds to o (an earlier branch wrote it first)
+  int local;            // sel_g1_kernel: the key set is the query block's own block (local branch)
   int f_lo, f_hi;       // blocks [f_lo, f_hi) are always in the selected branch's key set
 };
 

@@ -100,7 +100,7 @@ def test_score_routing_edge_sizes(n_blk, k):
     np.testing.assert_array_equal(host(sel), ref_sel)
 
 
-@pytest.mark.parametrize("branch", ["cmp", "sel"])
+@pytest.mark.parametrize("branch", ["cmp", "sel", "loc"])
 def test_single_branch_block_rows(branch):
     import sparse_attention_feed_amd as S
     w = wl("speed3r_small")
@@ -110,7 +110,7 @@ def test_single_branch_block_rows(branch):
     rows = w.n_blk if branch == "cmp" else w.n_slots
     lse = torch.empty((rows, w.n_qh), dtype=torch.float32, device="cuda")
     say("attn_g1", branch)
-    bit = S.BR_CMP if branch == "cmp" else S.BR_SEL
+    bit = {"cmp": S.BR_CMP, "sel": S.BR_SEL, "loc": S.BR_LOC}[branch]
     o = S.attn_fwd(d["layout"], bit, d["q"], d["k"], d["v"], q_cmp=dev(qc), k_cmp=dev(kc), v_cmp=dev(vc),
                    sel=torch.from_numpy(sel).cuda(), top_k=w.top_k, sel_groups=w.n_kvh, lse=lse, q_gran=S.Q_BLOCK)
     torch.cuda.synchronize()
@@ -124,8 +124,11 @@ def test_single_branch_block_rows(branch):
         gl = host(lse)
         assert max_err(gl, ref_lse_rows) <= lse_bound(w, qc, kc)
     else:
-        ref, ref_lse = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel,
-                                     q_gran="block")
+        if branch == "sel":
+            ref, ref_lse = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel,
+                                         q_gran="block")
+        else:
+            ref, ref_lse = O.attn_branch(O.LOC, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale)
         vm = w.valid_mask()
         gl = host(lse)
         assert np.all(np.isneginf(gl[~vm]))
@@ -319,3 +322,32 @@ def test_scores_routed_full_size():
     assert same.mean() >= 0.8, same.mean()
     diff = np.abs(o_f[toks] - ref).max(axis=2)
     assert diff[same].max() <= 2e-2
+
+
+def test_three_branch_layer_block_rows():
+    """The score-routed layout with all three branches gated (the local branch runs after the
+    compressed and selected ones and adds to o): against the oracle's three branches on the
+    device's pooled values and routing rows, ragged block counts."""
+    import sparse_attention_feed_amd as S
+    rng = np.random.default_rng(21)
+    n_blk = 70
+    cnt = rng.integers(1, 17, size=n_blk)
+    w = W.custom_block_workload(121, cnt, 16, 16, 16, 64, "bf16", 8, routing="scores", q_gran="block",
+                                branches=("cmp", "sel", "loc"), n_gate=3)
+    d = to_dev(w)
+    L = d["layout"]
+    say("attn_g1 three branches")
+    qd, kd, vd = S.pool_blocks(L, d["q"]), S.pool_blocks(L, d["k"]), S.pool_blocks(L, d["v"])
+    sel = S.route_scores_topk(L, qd, kd, None, w.top_k, q_gran=S.Q_BLOCK)
+    o = S.attn_fwd(L, S.BR_CMP | S.BR_SEL | S.BR_LOC, d["q"], d["k"], d["v"], q_cmp=qd, k_cmp=kd, v_cmp=vd,
+                   sel=sel, top_k=w.top_k, sel_groups=w.n_kvh, gates=d["gates"], q_gran=S.Q_BLOCK)
+    torch.cuda.synchronize()
+    qc, kc, vc, selh = host(qd), host(kd), host(vd), host(sel)
+    o_cmp, _ = O.attn_branch(O.CMP, qc, kc, vc, w.blk_cnt, w.blk_cap, w.scale, q_gran="block")
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=selh, q_gran="block")
+    o_loc, _ = O.attn_branch(O.LOC, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale)
+    ref = O.gate_combine([o_cmp, o_sel, o_loc], w.gates)
+    vm = w.valid_mask()
+    got = host(o)
+    assert max_err(got[vm], ref[vm]) <= 2e-2
+    assert np.all(got[~vm] == 0)

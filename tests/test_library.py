@@ -316,3 +316,14 @@ def test_scores_routed_validation(S, monkeypatch):
     assert call(layout(S)) == -2                                 # grouped-query layout
     assert f(ctypes.byref(layout(S, **g1)), 1, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
              None) == -2                                         # misaligned q
+
+
+def test_score_routed_layout_takes_the_local_branch(S, monkeypatch):
+    """One query head per KV head: the local branch is accepted alone (no routing rows needed) and
+    with the other two; f32 stays unsupported."""
+    g1 = layout(S, n_blk=64, n_qh=16, n_kvh=16, head_dim=64, blk_cap=16)
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    assert attn(S, g1, branches=4, q_gran=1, sel=None, gates=None, q_cmp=FAKE) == -3
+    assert attn(S, g1, branches=7, q_gran=1, q_cmp=FAKE) == -3
+    assert attn(S, g1, branches=5, q_gran=1, q_cmp=FAKE, sel=None) == -3
+    assert attn(S, g1, branches=4, q_gran=1, dtype=0, sel=None, gates=None) == -2
