@@ -691,8 +691,10 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
           const int pi = __shfl(lst[c].idx[E - 1], (l + 48) & 63, 64);
           const bool push = g > 0 && ck > pk;
           toplist_insert(lst[c], push ? pk : ck, push ? pi : ci);
-          thr[c] = unord_f32((uint32_t)(shfl_u64(lst[c].key[E - 1], r + 48) >> 32));
         }
+        // the bound moves once per tile: a candidate that no longer beats the k-th best is only
+        // dropped by the insert, so a stale bound inside the rounds changes no result
+        thr[c] = unord_f32((uint32_t)(shfl_u64(lst[c].key[E - 1], r + 48) >> 32));
       }
       // ---- compressed branch: base-2 logits relative to the running reference max ----
       f32x4 x[4];
@@ -771,6 +773,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 ? 1 :
   const bf16* kb = reinterpret_cast<const bf16*>(a.k) + h * DG;
   const bf16* vb = reinterpret_cast<const bf16*>(a.v) + h * DG;
   const float c2 = a.scale * kLog2e;
+  // loads that do not depend on the routing row are issued first, so their round trips overlap
+  // the row's: the token's query, its gate logit and (accumulating) the output written before
+  const bool valid = r < cnt;
+  const size_t row = (size_t)b * cap + min(r, cap - 1);
+  const QG1 qq = load_q_row(q + (row * a.n_qh + h) * DG, valid, c2);
+  bf16* o = reinterpret_cast<bf16*>(a.o);
+  const bf16* gp = reinterpret_cast<const bf16*>(a.gates);
+  const float glog = (gp && valid) ? (float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_sel] : 0.f;
+  bf16x4 prev[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    prev[dt] = bf16x4{};
+    if (a.accumulate && valid) prev[dt] = *reinterpret_cast<const bf16x4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
+  }
   // lane x < top_k holds entry x of this block's routing row for head h; -1, out-of-range and
   // repeated entries count no keys; the valid tokens of the rest are packed one after another
   // (local branch: the one entry is the block itself)
@@ -804,7 +820,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 ? 1 :
   __syncthreads();
   StateG1 st;
   state_init(st);
-  const QG1 qq = load_q_row(q + ((size_t)(b * cap + r) * a.n_qh + h) * DG, r < cnt, c2);
   RowsG1 pre;
   if (ntiles > 0) gather_rows_g1(pre, kb, vb, stride, keys_lds, l);
   for (int u = 0; u < ntiles; ++u) {
@@ -823,21 +838,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 ? 1 :
   }
   const float lsum = rows_sum(st.l);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  bf16* o = reinterpret_cast<bf16*>(a.o);
-  const bf16* gp = reinterpret_cast<const bf16*>(a.gates);
   if (r < cap) {
-    const size_t row = (size_t)b * cap + r;
-    if (a.lse && g == 0) a.lse[row * a.n_qh + h] = (r < cnt && lsum > 0.f) ? (st.mc + __log2f(lsum)) * kLn2 : -INFINITY;
-    const bool valid = r < cnt;
-    const float wgt = valid ? (gp ? sigmoidf_((float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_sel]) * inv : inv) : 0.f;
+    if (a.lse && g == 0) a.lse[row * a.n_qh + h] = (valid && lsum > 0.f) ? (st.mc + __log2f(lsum)) * kLn2 : -INFINITY;
+    const float wgt = valid ? (gp ? sigmoidf_(glog) * inv : inv) : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       bf16x4* dst = reinterpret_cast<bf16x4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
       f32x4 v = st.acc[dt] * wgt;
       if (a.accumulate && valid) {
-        const bf16x4 prev = *dst;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += (float)prev[i];
+        for (int i = 0; i < 4; ++i) v[i] += (float)prev[dt][i];
       }
       *dst = __builtin_convertvector(v, bf16x4);
     }
