@@ -579,6 +579,12 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
 // candidate also beats the previous group's last entry, that entry (which the previous group
 // pushes out); a bounded sorted insert of that value keeps every group sorted and the list exact.
 // Each round inserts one pending candidate per row, from the row's lowest lane group that has one.
+//
+// The first tiles would make nearly every key a candidate.  A short first sweep over the first
+// eighth of the key tiles (scores only) gives each row a lower bound T0 on its k-th best score:
+// lane (r, g) keeps the 2E largest of its per-tile maxima there, each the best of 16 keys no other
+// lane or tile sees, so the k-th largest of the row's 2k kept values is at most the row's k-th best
+// score; the running bound starts at T0.
 
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   const uint32_t lo = __shfl((uint32_t)v, src, 64), hi = __shfl((uint32_t)(v >> 32), src, 64);
@@ -605,7 +611,7 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
   QG1 q[CGF];
   StateG1 st[CGF];
   TopList<E> lst[CGF];
-  float thr[CGF];
+  float thr[CGF], t0[CGF];
   int row_of[CGF];
 #pragma unroll
   for (int c = 0; c < CGF; ++c) {
@@ -613,9 +619,80 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
     q[c] = load_q_row(qc + ((size_t)row_of[c] * a.n_qh + h) * DG, row_of[c] < a.n_blk);   // raw
     state_init(st[c]);
     toplist_init(lst[c]);
-    thr[c] = -INFINITY;
   }
   const int ntiles = (a.n_blk + KT - 1) / KT;
+  // ---- first sweep: the bound T0 from the first eighth of the key tiles (K only) ----
+  {
+    constexpr int E2 = 2 * E;
+    const int n1 = max(1, ntiles / 8);
+    const int k_key = tid >> 3, k_part = tid & 7;
+    auto fetch_k = [&](int u) {
+      return *reinterpret_cast<const uint4*>(kb + (size_t)min(u * KT + k_key, a.n_blk - 1) * stride + k_part * 8);
+    };
+    float top[CGF][E2];
+#pragma unroll
+    for (int c = 0; c < CGF; ++c)
+#pragma unroll
+      for (int e = 0; e < E2; ++e) top[c][e] = -INFINITY;
+    uint4 kn = fetch_k(0);
+    *reinterpret_cast<uint4*>(&tb[0].k[k_key][k_part * 8]) = kn;
+    __syncthreads();
+    for (int u = 0; u < n1; ++u) {
+      const int cur = u & 1;
+      if (u + 1 < n1) kn = fetch_k(u + 1);
+      Frag8<bf16> kf[4][2];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) kf[kt][hh] = ld8(&tb[cur].k[16 * kt + r][32 * hh + 8 * g]);
+      const int nk = min(KT, a.n_blk - u * KT);
+#pragma unroll
+      for (int c = 0; c < CGF; ++c) {
+        f32x4 sc[4];
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sc[kt] = mma16(kf[kt][1], q[c].h[1], mma16(kf[kt][0], q[c].h[0], z));
+        if (nk < KT) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            sc[j >> 2][j & 3] = (16 * (j >> 2) + 4 * g + (j & 3) < nk) ? sc[j >> 2][j & 3] : -INFINITY;
+        }
+        const float lm = fmaxf(fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3]))),
+                               fmaxf(fmaxf(fmaxf(sc[2][0], sc[2][1]), fmaxf(sc[2][2], sc[2][3])),
+                                     fmaxf(fmaxf(sc[3][0], sc[3][1]), fmaxf(sc[3][2], sc[3][3]))));
+        // bounded insert into the descending list: entry e becomes the median of its old value,
+        // its predecessor's and lm
+#pragma unroll
+        for (int e = E2 - 1; e > 0; --e) top[c][e] = __builtin_amdgcn_fmed3f(top[c][e - 1], top[c][e], lm);
+        top[c][0] = fmaxf(top[c][0], lm);
+      }
+      if (u + 1 < n1) *reinterpret_cast<uint4*>(&tb[cur ^ 1].k[k_key][k_part * 8]) = kn;
+      __syncthreads();
+    }
+    // T0 = the k-th largest of the row's 4 * E2 kept maxima: k rounds, each popping the largest
+    // head among the row's four lanes (the lowest lane group on equal heads)
+#pragma unroll
+    for (int c = 0; c < CGF; ++c) {
+      float kth = -INFINITY;
+      for (int i = 0; i < 4 * E; ++i) {
+        const float hd = top[c][0];
+        float m = fmaxf(hd, __shfl_xor(hd, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(hd == m);
+        const uint32_t rowbits = (uint32_t)((bal >> r) & 1ull) | (uint32_t)((bal >> (r + 15)) & 2ull) |
+                                 (uint32_t)((bal >> (r + 30)) & 4ull) | (uint32_t)((bal >> (r + 45)) & 8ull);
+        if (g == __builtin_ctz(rowbits | 16u)) {
+#pragma unroll
+          for (int e = 0; e < E2 - 1; ++e) top[c][e] = top[c][e + 1];
+          top[c][E2 - 1] = -INFINITY;
+        }
+        kth = m;
+      }
+      t0[c] = kth;
+      thr[c] = kth;
+    }
+  }
   // staging as in cmp_g1_kernel, plus the tile's 64 ranking keys (threads < 64)
   const int s_key = tid >> 3, s_part = tid & 7;
   auto fetch = [&](int u, uint4& kv, uint4& vv, uint32_t& bkey) {
@@ -694,7 +771,7 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
         }
         // the bound moves once per tile: a candidate that no longer beats the k-th best is only
         // dropped by the insert, so a stale bound inside the rounds changes no result
-        thr[c] = unord_f32((uint32_t)(shfl_u64(lst[c].key[E - 1], r + 48) >> 32));
+        thr[c] = fmaxf(t0[c], unord_f32((uint32_t)(shfl_u64(lst[c].key[E - 1], r + 48) >> 32)));
       }
       // ---- compressed branch: base-2 logits relative to the running reference max ----
       f32x4 x[4];
