@@ -327,3 +327,17 @@ def test_score_routed_layout_takes_the_local_branch(S, monkeypatch):
     assert attn(S, g1, branches=7, q_gran=1, q_cmp=FAKE) == -3
     assert attn(S, g1, branches=5, q_gran=1, q_cmp=FAKE, sel=None) == -3
     assert attn(S, g1, branches=4, q_gran=1, dtype=0, sel=None, gates=None) == -2
+
+
+def test_row_offsets_fit_32_bits(S, monkeypatch):
+    """The grouped-query and dense kernels index rows in 32 bits: sizes past 2^31 elements are
+    refused before any launch, sizes just inside reach it."""
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    big = layout(S, n_blk=32768, blk_cap=64)          # 32768 * 64 * 32 * 32 = 2^31
+    assert attn(S, big, branches=1, sel=None, gates=None) == -2
+    assert "2^31" in S.lib.nsa_last_error().decode()
+    ok = layout(S, n_blk=32767, blk_cap=64)
+    assert attn(S, ok, branches=1, sel=None, gates=None) == -3
+    lib = S.lib
+    assert lib.dense_gated_xattn_fwd(1, 1 << 21, 0, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert lib.dense_gated_xattn_fwd(1, (1 << 21) - 1, 0, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
