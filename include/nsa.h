@@ -218,7 +218,7 @@ nsa_status nsa_route_geometric_range(const nsa_layout* layout, const float* pts,
  *   k_cmp [n_blk][n_kvh][D];  lse [rows][n_qh] float32 natural-log partition function of the
  *   compressed branch (required iff G > 1);  sel [rows][n_kvh][top_k] int32.
  * Supported: (D, G) = (32, 16) with q_gran TOKEN (bf16 or f32, n_blk <= 65536), and (64, 1) with
- * q_gran BLOCK (bf16); 1 <= top_k <= 64.
+ * q_gran BLOCK (bf16 or f32; scores are fp32 products of the stored rows); 1 <= top_k <= 64.
  */
 nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_qgran q_gran,
                                  const void* q, const void* k_cmp, const float* lse,
@@ -247,10 +247,11 @@ nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_
  *        rows = n_blk for CMP with NSA_Q_BLOCK, else S; -inf on padding rows and empty key sets.
  * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16 with NSA_Q_TOKEN (n_blk <= 65536 when SEL
  * is named; n_blk * blk_cap * n_qh * max(32, gate_stride) < 2^31, row offsets being 32-bit); and
- * (D, G) = (64, 1) for NSA_BF16 with NSA_Q_BLOCK (pooled queries in the compressed branch, token
- * queries in the selected and local ones), blk_cap in {1, 2, 4, 8, 16}: each named branch runs in
- * its own launch, the first writing its gated result to o in bf16 and the later ones adding to it.
- * top_k <= 64.  Accumulation is fp32; bf16 probabilities feed the value product.
+ * (D, G) = (64, 1) for NSA_F32 and NSA_BF16 with NSA_Q_BLOCK (pooled queries in the compressed
+ * branch, token queries in the selected and local ones), blk_cap in {1, 2, 4, 8, 16}: each named
+ * branch runs in its own launch, the first writing its gated result to o in `dtype` and the later
+ * ones adding to it.  top_k <= 64.  Accumulation is fp32; with bf16 inputs bf16 probabilities feed
+ * the value product, with fp32 inputs fp32 ones.
  */
 nsa_status nsa_attn_fwd(const nsa_layout* layout, nsa_dtype dtype, uint32_t branches,
                         nsa_qgran q_gran, const void* q, const void* k, const void* v,
@@ -268,8 +269,10 @@ nsa_status nsa_attn_fwd(const nsa_layout* layout, nsa_dtype dtype, uint32_t bran
  * [n_blk][n_kvh][top_k] (descending by score, ties to the smaller blk_key, -1 past the last
  * block), while the compressed branch's logits are formed in fp32 from the raw pooled queries
  * (rather than from bf16 queries pre-scaled by scale * log2(e)), so o agrees with the two-call
- * sequence to rounding.  gate_logits [S][n_qh][2] (channel 0 compressed, 1 selected), bf16.
- * Supported (NSA_ERR_UNSUPPORTED otherwise): n_qh == n_kvh, head_dim 64, NSA_BF16, blk_cap in
+ * sequence to rounding.  gate_logits [S][n_qh][2] (channel 0 compressed, 1 selected), in `dtype`.
+ * With NSA_F32 the routing runs as its own pass before the two branches (exactly the two-call
+ * sequence); with NSA_BF16 it shares the compressed branch's pass.
+ * Supported (NSA_ERR_UNSUPPORTED otherwise): n_qh == n_kvh, head_dim 64, blk_cap in
  * {1, 2, 4, 8, 16}, top_k <= 32.  sel and o must not overlap any input.
  */
 nsa_status nsa_attn_fwd_scores_routed(const nsa_layout* layout, nsa_dtype dtype, const void* q,

@@ -285,10 +285,10 @@ nsa_status nsa_route_scores_topk(const nsa_layout* L, nsa_dtype dtype, nsa_qgran
   if (!aligned16(q) || !aligned16(k_cmp) || !aligned16(lse))
     return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: q, k_cmp and lse must be 16-byte aligned");
   if (G == 1) {
-    if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK || dtype != NSA_BF16)
+    if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK)
       return fail(NSA_ERR_UNSUPPORTED,
-                  "nsa_route_scores_topk: with one query head per KV head the compiled kernel takes head_dim 64, "
-                  "NSA_Q_BLOCK rows and bf16");
+                  "nsa_route_scores_topk: with one query head per KV head the compiled kernel takes head_dim 64 "
+                  "and NSA_Q_BLOCK rows");
     NSA_FORCED_FAILURE("nsa_route_scores_topk");
     nsa::G1Args g{};
     g.q_cmp = q;
@@ -302,7 +302,7 @@ nsa_status nsa_route_scores_topk(const nsa_layout* L, nsa_dtype dtype, nsa_qgran
     g.n_kvh = L->n_kvh;
     g.top_k = top_k;
     g.scale = L->scale;
-    return hip_status(nsa::launch_route_g1(g, stream), "nsa_route_scores_topk");
+    return hip_status(nsa::launch_route_g1(dtype == NSA_BF16, g, stream), "nsa_route_scores_topk");
   }
   if (L->head_dim != 32 || G != 16 || q_gran != NSA_Q_TOKEN)
     return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: compiled for head_dim 32, 16 query heads per KV head, per-token rows");
@@ -369,10 +369,10 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   }
   if (L->n_qh == L->n_kvh) {
     // one query head per KV head (score-routed, block-granular layout)
-    if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK || dtype != NSA_BF16 || L->blk_cap > 16 || 64 % L->blk_cap != 0)
+    if (L->head_dim != 64 || q_gran != NSA_Q_BLOCK || L->blk_cap > 16 || 64 % L->blk_cap != 0)
       return fail(NSA_ERR_UNSUPPORTED,
-                  "%s: with one query head per KV head the compiled kernels take head_dim 64, NSA_Q_BLOCK, "
-                  "bf16 and blk_cap in {1, 2, 4, 8, 16}", fn);
+                  "%s: with one query head per KV head the compiled kernels take head_dim 64, NSA_Q_BLOCK "
+                  "and blk_cap in {1, 2, 4, 8, 16}", fn);
     if (!whole) return fail(NSA_ERR_UNSUPPORTED, "%s: block ranges need the grouped-query kernel (head_dim 32)", fn);
     if (f_hi - f_lo > nsa::kMaxForcedBlocks)
       return fail(NSA_ERR_UNSUPPORTED, "%s: at most %d forced blocks", fn, nsa::kMaxForcedBlocks);
@@ -404,7 +404,7 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
     g.branches = branches;
     g.f_lo = f_lo;
     g.f_hi = f_hi;
-    return hip_status(nsa::launch_attn_g1(g, stream), fn);
+    return hip_status(nsa::launch_attn_g1(dtype == NSA_BF16, g, stream), fn);
   }
   if (forced)
     return fail(NSA_ERR_UNSUPPORTED, "%s: a forced block range needs the one-head-per-KV-head kernels (head_dim 64)", fn);
@@ -501,9 +501,8 @@ nsa_status nsa_attn_fwd_scores_routed(const nsa_layout* L, nsa_dtype dtype, cons
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_cmp) || !aligned16(k_cmp) || !aligned16(v_cmp) ||
       !aligned16(o))
     return fail(NSA_ERR_UNSUPPORTED, "%s: q, k, v, q_cmp, k_cmp, v_cmp and o must be 16-byte aligned", fn);
-  if (L->n_qh != L->n_kvh || L->head_dim != 64 || dtype != NSA_BF16 || L->blk_cap > 16 || 64 % L->blk_cap != 0 ||
-      top_k > 32)
-    return fail(NSA_ERR_UNSUPPORTED, "%s: compiled for one query head per KV head, head_dim 64, bf16, blk_cap in "
+  if (L->n_qh != L->n_kvh || L->head_dim != 64 || L->blk_cap > 16 || 64 % L->blk_cap != 0 || top_k > 32)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: compiled for one query head per KV head, head_dim 64, blk_cap in "
                                      "{1, 2, 4, 8, 16} and top_k <= 32", fn);
   NSA_FORCED_FAILURE(fn);
   nsa::G1Args g{};
@@ -533,7 +532,7 @@ nsa_status nsa_attn_fwd_scores_routed(const nsa_layout* L, nsa_dtype dtype, cons
   g.branches = NSA_BR_CMP | NSA_BR_SEL;
   g.f_lo = 0;
   g.f_hi = 0;
-  return hip_status(nsa::launch_attn_g1_routed(g, stream), fn);
+  return hip_status(nsa::launch_attn_g1_routed(dtype == NSA_BF16, g, stream), fn);
 }
 
 nsa_status nsa_gate_combine(nsa_dtype dtype, int32_t n_rows, int32_t n_qh, int32_t head_dim, int32_t n_branch,

@@ -8,6 +8,10 @@
 // one head (16 pooled blocks in the compressed branch and routing, the up to 16 tokens of one block
 // in the selected branch).  With D = 64 a 16-key step takes two MFMAs (d halves) and the value
 // product four 16-row d tiles.  Lane l then holds query row l%16 and keys 16*kt + 4*(l/16) + i.
+//
+// The kernels are templated on the element type of q, k, v and o.  fp32 inputs take eight
+// v_mfma_f32_16x16x4f32 per bf16 instruction on the same lane data, keep the probabilities in fp32
+// for the value product, and move each row piece of eight elements as 32 bytes instead of 16.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,9 +22,10 @@ constexpr int KT = 64;      // keys per tile
 constexpr int DG = 64;      // head dim of these kernels
 constexpr int KP = 72;      // LDS row stride (elements) of K and V^T tiles
 
+template <typename T>
 struct TileG1 {
-  bf16 k[KT][KP];           // K rows
-  bf16 vt[DG][KP];          // V^T with the key order permuted as in vt_pos_g1
+  T k[KT][KP];              // K rows
+  T vt[DG][KP];             // V^T with the key order permuted as in vt_pos_g1
 };
 
 // Column of V^T holding key `key`: lane group g of a 32-key product step reads keys
@@ -31,102 +36,153 @@ __device__ __forceinline__ int vt_pos_g1(int key) {
   return 32 * c + 8 * (rr >> 2) + 4 * hi + (rr & 3);
 }
 
-__device__ __forceinline__ Frag8<bf16> ld8(const bf16* p) {
-  Frag8<bf16> f;
-  f.v = *reinterpret_cast<const bf16x8*>(p);
-  return f;
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Eight consecutive elements of a row as one thread moves them: one 16-byte word of bf16, two of
+// fp32 (kept as raw words, so no unpacking stands between a load and its use).
+template <typename T> struct Oct;
+template <> struct Oct<bf16> { uint4 a; };
+template <> struct Oct<float> { uint4 a, b; };
+
+__device__ __forceinline__ Oct<bf16> load_oct(const bf16* p) { return {*reinterpret_cast<const uint4*>(p)}; }
+__device__ __forceinline__ Oct<float> load_oct(const float* p) {
+  const uint4* s = reinterpret_cast<const uint4*>(p);
+  return {s[0], s[1]};
+}
+__device__ __forceinline__ void store_oct(bf16* p, const Oct<bf16>& o) { *reinterpret_cast<uint4*>(p) = o.a; }
+__device__ __forceinline__ void store_oct(float* p, const Oct<float>& o) {
+  uint4* d = reinterpret_cast<uint4*>(p);
+  d[0] = o.a;
+  d[1] = o.b;
+}
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+// element x (< 8) of an eight-element piece
+__device__ __forceinline__ bf16 oct_elem(const Oct<bf16>& o, int x) {
+  return __builtin_bit_cast(bf16, (uint16_t)(word(o.a, x >> 1) >> (16 * (x & 1))));
+}
+__device__ __forceinline__ float oct_elem(const Oct<float>& o, int x) { return __uint_as_float(word(x < 4 ? o.a : o.b, x & 3)); }
+
+// Four consecutive output elements
+template <typename T> struct V4;
+template <> struct V4<bf16> { typedef bf16x4 t; };
+template <> struct V4<float> { typedef f32x4 t; };
 
 // Query fragments (two d halves) of one row: B operand of S^T.  With c2 != 1 every element is
 // multiplied by c2 = scale * log2(e) in fp32 and rounded once to bf16, so S^T comes out in base-2
 // logit units (the routing kernel keeps the raw query: c2 = 1).
-struct QG1 { Frag8<bf16> h[2]; };
+// (with fp32 inputs the product is formed in fp32, no rounding beyond it)
+template <typename T>
+struct QG1 { Frag8<T> h[2]; };
 
-__device__ __forceinline__ QG1 load_q_row(const bf16* row, bool valid, float c2 = 1.f) {
-  QG1 q;
+template <typename T>
+__device__ __forceinline__ QG1<T> load_q_row(const T* row, bool valid, float c2 = 1.f) {
+  QG1<T> q;
   const int g = lane_id() >> 4;
   if (valid) {
-    q.h[0] = ld8(row + 8 * g);
-    q.h[1] = ld8(row + 32 + 8 * g);
+    q.h[0] = load_frag(row + 8 * g);
+    q.h[1] = load_frag(row + 32 + 8 * g);
     if (c2 != 1.f) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q.h[hh].v[e] = (bf16)((float)q.h[hh].v[e] * c2);
+        for (int e = 0; e < 8; ++e) q.h[hh].v[e] = (T)((float)q.h[hh].v[e] * c2);
     }
   } else {
-    q.h[0].v = bf16x8{};
-    q.h[1].v = bf16x8{};
+    q.h[0].v = decltype(q.h[0].v){};
+    q.h[1].v = decltype(q.h[1].v){};
   }
   return q;
 }
 
 // K and V^T fragments of a staged tile.
+template <typename T>
 struct TileFragsG1 {
-  Frag8<bf16> k[4][2];      // [key tile][d half]
-  Frag8<bf16> v[4][2];      // [d tile][key chunk]
+  Frag8<T> k[4][2];         // [key tile][d half]
+  Frag8<T> v[4][2];         // [d tile][key chunk]
 };
 
-__device__ __forceinline__ void load_frags_g1(const TileG1& t, TileFragsG1& f) {
+template <typename T>
+__device__ __forceinline__ void load_frags_g1(const TileG1<T>& t, TileFragsG1<T>& f) {
   const int l = lane_id(), r = l & 15, g = l >> 4;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) f.k[kt][h] = ld8(&t.k[16 * kt + r][32 * h + 8 * g]);
+    for (int h = 0; h < 2; ++h) f.k[kt][h] = load_frag(&t.k[16 * kt + r][32 * h + 8 * g]);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) f.v[dt][c] = ld8(&t.vt[16 * dt + r][32 * c + 8 * g]);
+    for (int c = 0; c < 2; ++c) f.v[dt][c] = load_frag(&t.vt[16 * dt + r][32 * c + 8 * g]);
 }
 
 // Raw scores S^T = K Q^T (+ seed) for one column group.
-__device__ __forceinline__ void scores_g1(const TileFragsG1& f, const QG1& q, const f32x4 (&seed)[4], f32x4 (&s)[4]) {
+template <typename T>
+__device__ __forceinline__ void scores_g1(const TileFragsG1<T>& f, const QG1<T>& q, const f32x4 (&seed)[4],
+                                          f32x4 (&s)[4]) {
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) s[kt] = mma16(f.k[kt][1], q.h[1], mma16(f.k[kt][0], q.h[0], seed[kt]));
 }
 
-// One wave's share of a gathered 64-key tile: chunk tid + 64 i (i < 8) of the 512 16-byte chunks
-// of K and the same chunk of V.  All sixteen loads are issued before any is used, so a tile costs one
-// memory round trip, and the next tile's gather runs during the current tile's compute.  Padding
-// keys (row -1) read row 0: their scores are masked to -inf, so they weigh nothing.
+// One wave's share of a gathered 64-key tile: chunk tid + 64 i (i < NCH) of the 16-byte chunks of
+// K and the same chunk of V (512 each in bf16, 1024 in fp32).  All loads are issued before any is
+// used, so a tile costs one memory round trip, and the next tile's gather runs during the current
+// tile's compute.  Padding keys (row -1) read row 0: their scores are masked to -inf, so they weigh
+// nothing.
 // (vector types, not arrays: an array carried across the tile loop was placed in scratch memory)
 typedef uint32_t u32x32 __attribute__((ext_vector_type(32)));
-struct RowsG1 { u32x32 k, v; };
+typedef uint32_t u32x64 __attribute__((ext_vector_type(64)));
+template <typename T> struct RowsG1;
+template <> struct RowsG1<bf16> { u32x32 k, v; };
+template <> struct RowsG1<float> { u32x64 k, v; };
 
-__device__ __forceinline__ void put4(u32x32& d, int i, uint4 x) {
+template <typename T> struct ChunkG1 {
+  static constexpr int EPC = 16 / sizeof(T);     // elements per 16-byte chunk
+  static constexpr int CPK = DG / EPC;           // chunks per key row
+  static constexpr int NCH = KT * CPK / 64;      // chunks per thread
+};
+
+template <typename V>
+__device__ __forceinline__ void put4(V& d, int i, uint4 x) {
   d[4 * i] = x.x;
   d[4 * i + 1] = x.y;
   d[4 * i + 2] = x.z;
   d[4 * i + 3] = x.w;
 }
 
-__device__ __forceinline__ void gather_rows_g1(RowsG1& g, const bf16* kb, const bf16* vb, int stride,
+// element x of chunk i of a gathered row piece
+template <typename V>
+__device__ __forceinline__ bf16 chunk_elem(const V& d, int i, int x, bf16) {
+  return __builtin_bit_cast(bf16, (uint16_t)(d[4 * i + (x >> 1)] >> (16 * (x & 1))));
+}
+template <typename V>
+__device__ __forceinline__ float chunk_elem(const V& d, int i, int x, float) { return __uint_as_float(d[4 * i + x]); }
+
+template <typename T>
+__device__ __forceinline__ void gather_rows_g1(RowsG1<T>& g, const T* kb, const T* vb, int stride,
                                                const int* rows /* LDS [64] */, int tid) {
+  typedef ChunkG1<T> C;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < C::NCH; ++i) {
     const int cc = tid + i * 64;
-    const int key = cc >> 3, part = cc & 7;
-    const size_t off = (size_t)max(rows[key], 0) * stride + part * 8;
+    const int key = cc / C::CPK, part = cc % C::CPK;
+    const size_t off = (size_t)max(rows[key], 0) * stride + part * C::EPC;
     put4(g.k, i, *reinterpret_cast<const uint4*>(kb + off));
     put4(g.v, i, *reinterpret_cast<const uint4*>(vb + off));
   }
 }
 
-__device__ __forceinline__ void store_rows_g1(TileG1& t, const RowsG1& g, int tid) {
+template <typename T>
+__device__ __forceinline__ void store_rows_g1(TileG1<T>& t, const RowsG1<T>& g, int tid) {
+  typedef ChunkG1<T> C;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < C::NCH; ++i) {
     const int cc = tid + i * 64;
-    const int key = cc >> 3, part = cc & 7;
-    *reinterpret_cast<uint4*>(&t.k[key][part * 8]) = make_uint4(g.k[4 * i], g.k[4 * i + 1], g.k[4 * i + 2], g.k[4 * i + 3]);
-    // the eight bf16 values by shifts
-    const uint32_t wd[4] = {g.v[4 * i], g.v[4 * i + 1], g.v[4 * i + 2], g.v[4 * i + 3]};
+    const int key = cc / C::CPK, part = cc % C::CPK;
+    *reinterpret_cast<uint4*>(&t.k[key][part * C::EPC]) =
+        make_uint4(g.k[4 * i], g.k[4 * i + 1], g.k[4 * i + 2], g.k[4 * i + 3]);
     const int pos = vt_pos_g1(key);
 #pragma unroll
-    for (int x = 0; x < 8; ++x)
-      t.vt[part * 8 + x][pos] = __builtin_bit_cast(bf16, (uint16_t)(wd[x >> 1] >> (16 * (x & 1))));
+    for (int x = 0; x < C::EPC; ++x) t.vt[part * C::EPC + x][pos] = chunk_elem(g.v, i, x, T());
   }
 }
 
@@ -181,10 +237,25 @@ __device__ __forceinline__ float exp_pack_g1(const f32x4 (&x)[4], Frag8<bf16> (&
   return lt;
 }
 
+// fp32: the probabilities enter the value product unrounded
+__device__ __forceinline__ float exp_pack_g1(const f32x4 (&x)[4], Frag8<float> (&pf)[2]) {
+  float lt = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(x[2 * h + (e >> 2)][e & 3]);
+      pf[h].v[e] = p;
+      lt += p;
+    }
+  return lt;
+}
+
 // One tile: x = S^T - mc (padding keys -inf) from scores_g1; probabilities rounded to bf16 for the
-// value product.
-__device__ __forceinline__ void softmax_pv_g1(StateG1& st, f32x4 (&x)[4], const TileFragsG1& f) {
-  Frag8<bf16> pf[2];
+// value product (bf16 inputs).
+template <typename T>
+__device__ __forceinline__ void softmax_pv_g1(StateG1& st, f32x4 (&x)[4], const TileFragsG1<T>& f) {
+  Frag8<T> pf[2];
   float lt = exp_pack_g1(x, pf);
   if (__builtin_amdgcn_ballot_w64(!(lt <= kStaleLimitG1) || !(st.l + lt >= kTinyMassG1)) != 0) {
     float mx = -INFINITY;
@@ -240,22 +311,26 @@ __device__ __forceinline__ void mask_seed(int nk, f32x4 (&cm)[4]) {
 // ---------------------------------------------------------------------------------------------
 
 constexpr int CW = 8;       // waves per workgroup
-constexpr int CG = 2;       // column groups (16 rows each) per wave
+// column groups (16 rows each) per wave: two in bf16; one in fp32, whose fragments take twice the
+// registers
+template <typename T> struct CmpGroups { static constexpr int value = sizeof(T) == 2 ? 2 : 1; };
 
+template <typename T>
 __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
-  static_assert(CW * 64 == KT * 8, "one 16-byte piece of K and of V per thread");
-  __shared__ TileG1 tb[2];
+  static_assert(CW * 64 == KT * 8, "one eight-element piece of K and of V per thread");
+  constexpr int CG = CmpGroups<T>::value;
+  __shared__ TileG1<T> tb[2];
   const int n_rowgrp = (a.n_blk + CW * CG * 16 - 1) / (CW * CG * 16);
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int h = wg / n_rowgrp, rg = wg % n_rowgrp;
   const int w = threadIdx.x >> 6, l = lane_id(), r = l & 15, g = l >> 4;
   const int stride = a.n_kvh * DG;
-  const bf16* qc = reinterpret_cast<const bf16*>(a.q_cmp);
-  const bf16* kb = reinterpret_cast<const bf16*>(a.k_cmp) + h * DG;
-  const bf16* vb = reinterpret_cast<const bf16*>(a.v_cmp) + h * DG;
+  const T* qc = reinterpret_cast<const T*>(a.q_cmp);
+  const T* kb = reinterpret_cast<const T*>(a.k_cmp) + h * DG;
+  const T* vb = reinterpret_cast<const T*>(a.v_cmp) + h * DG;
   const float c2 = a.scale * kLog2e;
 
-  QG1 q[CG];
+  QG1<T> q[CG];
   StateG1 st[CG];
   int row_of[CG];
 #pragma unroll
@@ -266,32 +341,30 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
     state_init(st[c]);
   }
   const int ntiles = (a.n_blk + KT - 1) / KT;
-  // staging: thread t copies the 16-byte piece (key t / 8, part t % 8) of both K and V; the next
-  // tile's loads are issued before the current tile's compute
+  // staging: thread t copies the eight-element piece (key t / 8, part t % 8) of both K and V; the
+  // next tile's loads are issued before the current tile's compute
   const int s_key = threadIdx.x >> 3, s_part = threadIdx.x & 7;
   // (no branch around the loads and no unpacking before the store: either would make the next
   // tile's load wait at once; keys past the end repeat the last row, masked out of the scores)
-  auto fetch = [&](int u, uint4& kv, uint4& vv) {
+  auto fetch = [&](int u, Oct<T>& kv, Oct<T>& vv) {
     const size_t off = (size_t)min(u * KT + s_key, a.n_blk - 1) * stride + s_part * 8;
-    kv = *reinterpret_cast<const uint4*>(kb + off);
-    vv = *reinterpret_cast<const uint4*>(vb + off);
+    kv = load_oct(kb + off);
+    vv = load_oct(vb + off);
   };
-  auto store = [&](TileG1& t, const uint4& kv, const uint4& vv) {
-    *reinterpret_cast<uint4*>(&t.k[s_key][s_part * 8]) = kv;
-    const uint32_t wd[4] = {vv.x, vv.y, vv.z, vv.w};
+  auto store = [&](TileG1<T>& t, const Oct<T>& kv, const Oct<T>& vv) {
+    store_oct(&t.k[s_key][s_part * 8], kv);
     const int pos = vt_pos_g1(s_key);
 #pragma unroll
-    for (int x = 0; x < 8; ++x)
-      t.vt[s_part * 8 + x][pos] = __builtin_bit_cast(bf16, (uint16_t)(wd[x >> 1] >> (16 * (x & 1))));
+    for (int x = 0; x < 8; ++x) t.vt[s_part * 8 + x][pos] = oct_elem(vv, x);
   };
-  uint4 kv, vv;
+  Oct<T> kv, vv;
   fetch(0, kv, vv);
   store(tb[0], kv, vv);
   __syncthreads();
   for (int u = 0; u < ntiles; ++u) {
     const int cur = u & 1;
     if (u + 1 < ntiles) fetch(u + 1, kv, vv);
-    TileFragsG1 f;
+    TileFragsG1<T> f;
     load_frags_g1(tb[cur], f);
     const int nk = min(KT, a.n_blk - u * KT);
     const bool full = nk == KT;
@@ -309,8 +382,9 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
     __syncthreads();
   }
   // finish: normalise, gate per token, give the block's pooled result to each of its tokens
-  bf16* o = reinterpret_cast<bf16*>(a.o);
-  const bf16* gp = reinterpret_cast<const bf16*>(a.gates);
+  T* o = reinterpret_cast<T*>(a.o);
+  const T* gp = reinterpret_cast<const T*>(a.gates);
+  typedef typename V4<T>::t v4;
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
     const int b = row_of[c];
@@ -325,8 +399,8 @@ __global__ __launch_bounds__(CW * 64) void cmp_g1_kernel(G1Args a) {
       if (t < cnt) wgt = gp ? sigmoidf_((float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_cmp]) * inv : inv;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        bf16x4* dst = reinterpret_cast<bf16x4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
-        *dst = __builtin_convertvector(st[c].acc[dt] * wgt, bf16x4);
+        v4* dst = reinterpret_cast<v4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
+        *dst = __builtin_convertvector(st[c].acc[dt] * wgt, v4);
       }
     }
   }
@@ -411,9 +485,9 @@ __device__ __forceinline__ float row_threshold(const TopList<K>& t) {
   return unord_f32((uint32_t)(b >> 32));
 }
 
-template <int K, int CG>
+template <typename T, int K, int CG>
 __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
-  __shared__ bf16 kt_lds[2][KT][KP];
+  __shared__ T kt_lds[2][KT][KP];
   __shared__ uint32_t keys_lds[2][KT];
   __shared__ f32x4 sc_lds[RW][4][64];      // one column group's tile scores per wave, slot-major
   const int rows_per_wg = RW * CG * 16;
@@ -422,10 +496,10 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
   const int h = wg / n_rowgrp, rg = wg % n_rowgrp;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), r = l & 15, g = l >> 4;
   const int stride = a.n_kvh * DG;
-  const bf16* qc = reinterpret_cast<const bf16*>(a.q_cmp);
-  const bf16* kb = reinterpret_cast<const bf16*>(a.k_cmp) + h * DG;
+  const T* qc = reinterpret_cast<const T*>(a.q_cmp);
+  const T* kb = reinterpret_cast<const T*>(a.k_cmp) + h * DG;
 
-  QG1 q[CG];
+  QG1<T> q[CG];
   TopList<K> lst[CG];
   float thr[CG];
   int row_of[CG];
@@ -457,20 +531,21 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
     thr[c] = row_threshold(lst[c]);
   };
   const int ntiles = (a.n_blk + KT - 1) / KT;
-  // staging: thread t copies 16 bytes (key t / 8, piece t % 8) of the K tile; threads < 64 the keys
+  // staging: thread t copies eight elements (key t / 8, piece t % 8) of the K tile; threads < 64
+  // the keys
   const int s_key = tid >> 3, s_part = tid & 7;
-  auto fetch = [&](int u, uint4& kv, uint32_t& bkey) {
+  auto fetch = [&](int u, Oct<T>& kv, uint32_t& bkey) {
     const int key = u * KT + s_key;
-    kv = make_uint4(0u, 0u, 0u, 0u);
-    if (key < a.n_blk) kv = *reinterpret_cast<const uint4*>(kb + (size_t)key * stride + s_part * 8);
+    kv = Oct<T>{};
+    if (key < a.n_blk) kv = load_oct(kb + (size_t)key * stride + s_part * 8);
     const int kk = u * KT + tid;
     bkey = (tid < KT && kk < a.n_blk) ? a.blk_key[kk] : 0u;
   };
-  auto store = [&](int buf, const uint4& kv, uint32_t bkey) {
-    *reinterpret_cast<uint4*>(&kt_lds[buf][s_key][s_part * 8]) = kv;
+  auto store = [&](int buf, const Oct<T>& kv, uint32_t bkey) {
+    store_oct(&kt_lds[buf][s_key][s_part * 8], kv);
     if (tid < KT) keys_lds[buf][tid] = bkey;
   };
-  uint4 kv;
+  Oct<T> kv;
   uint32_t bkey;
   fetch(0, kv, bkey);
   store(0, kv, bkey);
@@ -478,11 +553,11 @@ __global__ __launch_bounds__(RW * 64) void route_g1_kernel(G1Args a) {
   for (int u = 0; u < ntiles; ++u) {
     const int cur = u & 1;
     if (u + 1 < ntiles) fetch(u + 1, kv, bkey);
-    Frag8<bf16> kf[4][2];
+    Frag8<T> kf[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) kf[kt][hh] = ld8(&kt_lds[cur][16 * kt + r][32 * hh + 8 * g]);
+      for (int hh = 0; hh < 2; ++hh) kf[kt][hh] = load_frag(&kt_lds[cur][16 * kt + r][32 * hh + 8 * g]);
     const int nk = min(KT, a.n_blk - u * KT);
     uint32_t vmask = 0xFFFFu;                 // slot j = 4*kt + i holds key 16*kt + 4*g + i
     if (nk < KT) {
@@ -591,10 +666,10 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-template <int E, int CGF>
+template <typename T, int E, int CGF>
 __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
-  static_assert(CW * 64 == KT * 8, "one 16-byte piece of K and of V per thread");
-  __shared__ TileG1 tb[2];
+  static_assert(CW * 64 == KT * 8, "one eight-element piece of K and of V per thread");
+  __shared__ TileG1<T> tb[2];
   __shared__ uint32_t keys_lds[2][KT];
   __shared__ f32x4 sc_lds[CW][4][64];        // one column group's tile scores per wave, slot-major
   constexpr int ROWS = CW * CGF * 16;
@@ -603,12 +678,12 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
   const int h = wg / n_rowgrp, rg = wg % n_rowgrp;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), r = l & 15, g = l >> 4;
   const int stride = a.n_kvh * DG;
-  const bf16* qc = reinterpret_cast<const bf16*>(a.q_cmp);
-  const bf16* kb = reinterpret_cast<const bf16*>(a.k_cmp) + h * DG;
-  const bf16* vb = reinterpret_cast<const bf16*>(a.v_cmp) + h * DG;
+  const T* qc = reinterpret_cast<const T*>(a.q_cmp);
+  const T* kb = reinterpret_cast<const T*>(a.k_cmp) + h * DG;
+  const T* vb = reinterpret_cast<const T*>(a.v_cmp) + h * DG;
   const float c2 = a.scale * kLog2e;
 
-  QG1 q[CGF];
+  QG1<T> q[CGF];
   StateG1 st[CGF];
   TopList<E> lst[CGF];
   float thr[CGF], t0[CGF];
@@ -626,25 +701,23 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
     constexpr int E2 = 2 * E;
     const int n1 = max(1, ntiles / 8);
     const int k_key = tid >> 3, k_part = tid & 7;
-    auto fetch_k = [&](int u) {
-      return *reinterpret_cast<const uint4*>(kb + (size_t)min(u * KT + k_key, a.n_blk - 1) * stride + k_part * 8);
-    };
+    auto fetch_k = [&](int u) { return load_oct(kb + (size_t)min(u * KT + k_key, a.n_blk - 1) * stride + k_part * 8); };
     float top[CGF][E2];
 #pragma unroll
     for (int c = 0; c < CGF; ++c)
 #pragma unroll
       for (int e = 0; e < E2; ++e) top[c][e] = -INFINITY;
-    uint4 kn = fetch_k(0);
-    *reinterpret_cast<uint4*>(&tb[0].k[k_key][k_part * 8]) = kn;
+    Oct<T> kn = fetch_k(0);
+    store_oct(&tb[0].k[k_key][k_part * 8], kn);
     __syncthreads();
     for (int u = 0; u < n1; ++u) {
       const int cur = u & 1;
       if (u + 1 < n1) kn = fetch_k(u + 1);
-      Frag8<bf16> kf[4][2];
+      Frag8<T> kf[4][2];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) kf[kt][hh] = ld8(&tb[cur].k[16 * kt + r][32 * hh + 8 * g]);
+        for (int hh = 0; hh < 2; ++hh) kf[kt][hh] = load_frag(&tb[cur].k[16 * kt + r][32 * hh + 8 * g]);
       const int nk = min(KT, a.n_blk - u * KT);
 #pragma unroll
       for (int c = 0; c < CGF; ++c) {
@@ -667,7 +740,7 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
         for (int e = E2 - 1; e > 0; --e) top[c][e] = __builtin_amdgcn_fmed3f(top[c][e - 1], top[c][e], lm);
         top[c][0] = fmaxf(top[c][0], lm);
       }
-      if (u + 1 < n1) *reinterpret_cast<uint4*>(&tb[cur ^ 1].k[k_key][k_part * 8]) = kn;
+      if (u + 1 < n1) store_oct(&tb[cur ^ 1].k[k_key][k_part * 8], kn);
       __syncthreads();
     }
     // T0 = the k-th largest of the row's 4 * E2 kept maxima: k rounds, each popping the largest
@@ -695,23 +768,21 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
   }
   // staging as in cmp_g1_kernel, plus the tile's 64 ranking keys (threads < 64)
   const int s_key = tid >> 3, s_part = tid & 7;
-  auto fetch = [&](int u, uint4& kv, uint4& vv, uint32_t& bkey) {
+  auto fetch = [&](int u, Oct<T>& kv, Oct<T>& vv, uint32_t& bkey) {
     const size_t off = (size_t)min(u * KT + s_key, a.n_blk - 1) * stride + s_part * 8;
-    kv = *reinterpret_cast<const uint4*>(kb + off);
-    vv = *reinterpret_cast<const uint4*>(vb + off);
+    kv = load_oct(kb + off);
+    vv = load_oct(vb + off);
     bkey = a.blk_key[min(u * KT + (tid & (KT - 1)), a.n_blk - 1)];
   };
-  auto store = [&](int buf, const uint4& kv, const uint4& vv, uint32_t bkey) {
-    TileG1& t = tb[buf];
-    *reinterpret_cast<uint4*>(&t.k[s_key][s_part * 8]) = kv;
-    const uint32_t wd[4] = {vv.x, vv.y, vv.z, vv.w};
+  auto store = [&](int buf, const Oct<T>& kv, const Oct<T>& vv, uint32_t bkey) {
+    TileG1<T>& t = tb[buf];
+    store_oct(&t.k[s_key][s_part * 8], kv);
     const int pos = vt_pos_g1(s_key);
 #pragma unroll
-    for (int x = 0; x < 8; ++x)
-      t.vt[s_part * 8 + x][pos] = __builtin_bit_cast(bf16, (uint16_t)(wd[x >> 1] >> (16 * (x & 1))));
+    for (int x = 0; x < 8; ++x) t.vt[s_part * 8 + x][pos] = oct_elem(vv, x);
     if (tid < KT) keys_lds[buf][tid] = bkey;
   };
-  uint4 kv, vv;
+  Oct<T> kv, vv;
   uint32_t bkey;
   fetch(0, kv, vv, bkey);
   store(0, kv, vv, bkey);
@@ -719,7 +790,7 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
   for (int u = 0; u < ntiles; ++u) {
     const int cur = u & 1;
     if (u + 1 < ntiles) fetch(u + 1, kv, vv, bkey);
-    TileFragsG1 f;
+    TileFragsG1<T> f;
     load_frags_g1(tb[cur], f);
     const int nk = min(KT, a.n_blk - u * KT);
     uint32_t vmask = 0xFFFFu;                 // slot j = 4*kt + i holds key 16*kt + 4*g + i
@@ -795,8 +866,9 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
   }
   // finish: normalise, gate per token, give the block's pooled result to each of its tokens; the
   // routing row is the list itself (lane group g holds ranks gE .. gE + E - 1)
-  bf16* o = reinterpret_cast<bf16*>(a.o);
-  const bf16* gp = reinterpret_cast<const bf16*>(a.gates);
+  T* o = reinterpret_cast<T*>(a.o);
+  const T* gp = reinterpret_cast<const T*>(a.gates);
+  typedef typename V4<T>::t v4;
   int32_t* sel = const_cast<int32_t*>(a.sel);
 #pragma unroll
   for (int c = 0; c < CGF; ++c) {
@@ -816,17 +888,17 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
       if (t < cnt) wgt = gp ? sigmoidf_((float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_cmp]) * inv : inv;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        bf16x4* dst = reinterpret_cast<bf16x4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
-        *dst = __builtin_convertvector(st[c].acc[dt] * wgt, bf16x4);
+        v4* dst = reinterpret_cast<v4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
+        *dst = __builtin_convertvector(st[c].acc[dt] * wgt, v4);
       }
     }
   }
 }
 
-template <int E, int CGF>
+template <typename T, int E, int CGF>
 hipError_t launch_cmp_route_g1_k(const G1Args& a, hipStream_t s) {
   const int n_rowgrp = (a.n_blk + CW * CGF * 16 - 1) / (CW * CGF * 16);
-  hipLaunchKernelGGL((cmp_route_g1_kernel<E, CGF>), dim3(n_rowgrp * a.n_kvh), dim3(CW * 64), 0, s, a);
+  hipLaunchKernelGGL((cmp_route_g1_kernel<T, E, CGF>), dim3(n_rowgrp * a.n_kvh), dim3(CW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -836,33 +908,35 @@ hipError_t launch_cmp_route_g1_k(const G1Args& a, hipStream_t s) {
 
 // NF: capacity for forced blocks (0: the forced range is ignored, and the key list stays small)
 // Two waves per SIMD (at most 256 registers each) where LDS allows eight workgroups per CU; the
-// forced variant's key list allows four.
-template <int NF>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 ? 1 : 2))) void sel_g1_kernel(G1Args a) {
-  __shared__ TileG1 tb;
+// forced variant's key list allows four, and the fp32 tile (twice the LDS and registers) fewer.
+template <typename T, int NF>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 || sizeof(T) == 4 ? 1 : 2)))
+void sel_g1_kernel(G1Args a) {
+  __shared__ TileG1<T> tb;
   __shared__ int keys_lds[(64 + NF) * 16 + KT];   // source rows of the selected valid tokens, packed
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int b = wg / a.n_kvh, h = wg % a.n_kvh;
   const int l = lane_id(), r = l & 15, g = l >> 4;
   const int cap = a.cap, cnt = a.blk_cnt[b];
   const int stride = a.n_kvh * DG;
-  const bf16* q = reinterpret_cast<const bf16*>(a.q);
-  const bf16* kb = reinterpret_cast<const bf16*>(a.k) + h * DG;
-  const bf16* vb = reinterpret_cast<const bf16*>(a.v) + h * DG;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* kb = reinterpret_cast<const T*>(a.k) + h * DG;
+  const T* vb = reinterpret_cast<const T*>(a.v) + h * DG;
   const float c2 = a.scale * kLog2e;
   // loads that do not depend on the routing row are issued first, so their round trips overlap
   // the row's: the token's query, its gate logit and (accumulating) the output written before
   const bool valid = r < cnt;
   const size_t row = (size_t)b * cap + min(r, cap - 1);
-  const QG1 qq = load_q_row(q + (row * a.n_qh + h) * DG, valid, c2);
-  bf16* o = reinterpret_cast<bf16*>(a.o);
-  const bf16* gp = reinterpret_cast<const bf16*>(a.gates);
+  const QG1<T> qq = load_q_row(q + (row * a.n_qh + h) * DG, valid, c2);
+  T* o = reinterpret_cast<T*>(a.o);
+  const T* gp = reinterpret_cast<const T*>(a.gates);
   const float glog = (gp && valid) ? (float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_sel] : 0.f;
-  bf16x4 prev[4];
+  typedef typename V4<T>::t v4;
+  v4 prev[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
-    prev[dt] = bf16x4{};
-    if (a.accumulate && valid) prev[dt] = *reinterpret_cast<const bf16x4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
+    prev[dt] = v4{};
+    if (a.accumulate && valid) prev[dt] = *reinterpret_cast<const v4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
   }
   // lane x < top_k holds entry x of this block's routing row for head h; -1, out-of-range and
   // repeated entries count no keys; the valid tokens of the rest are packed one after another
@@ -897,13 +971,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 ? 1 :
   __syncthreads();
   StateG1 st;
   state_init(st);
-  RowsG1 pre;
+  RowsG1<T> pre;
   if (ntiles > 0) gather_rows_g1(pre, kb, vb, stride, keys_lds, l);
   for (int u = 0; u < ntiles; ++u) {
     store_rows_g1(tb, pre, l);
     __syncthreads();
     if (u + 1 < ntiles) gather_rows_g1(pre, kb, vb, stride, keys_lds + (u + 1) * KT, l);
-    TileFragsG1 f;
+    TileFragsG1<T> f;
     load_frags_g1(tb, f);
     const int nk = min(KT, total - u * KT);
     f32x4 cm[4], seed[4], x[4];
@@ -920,50 +994,54 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 ? 1 :
     const float wgt = valid ? (gp ? sigmoidf_(glog) * inv : inv) : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      bf16x4* dst = reinterpret_cast<bf16x4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
+      v4* dst = reinterpret_cast<v4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
       f32x4 v = st.acc[dt] * wgt;
       if (a.accumulate && valid) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] += (float)prev[dt][i];
       }
-      *dst = __builtin_convertvector(v, bf16x4);
+      *dst = __builtin_convertvector(v, v4);
     }
   }
 }
 
-template <int K, int CG>
+template <typename T, int K, int CG>
 hipError_t launch_route_g1_k(const G1Args& a, hipStream_t s) {
   const int n_rowgrp = (a.n_blk + RW * CG * 16 - 1) / (RW * CG * 16);
-  hipLaunchKernelGGL((route_g1_kernel<K, CG>), dim3(n_rowgrp * a.n_kvh), dim3(RW * 64), 0, s, a);
+  hipLaunchKernelGGL((route_g1_kernel<T, K, CG>), dim3(n_rowgrp * a.n_kvh), dim3(RW * 64), 0, s, a);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_route_g1(const G1Args& a, hipStream_t s) {
-  if (a.top_k <= 8) return launch_route_g1_k<8, 2>(a, s);
-  if (a.top_k <= 16) return launch_route_g1_k<16, 2>(a, s);
-  if (a.top_k <= 32) return launch_route_g1_k<32, 1>(a, s);
-  return launch_route_g1_k<64, 1>(a, s);
+// fp32 takes one column group per wave throughout: its query fragments and key tile take twice the
+// registers of bf16 ones
+template <typename T>
+hipError_t launch_route_g1_t(const G1Args& a, hipStream_t s) {
+  constexpr int C2 = sizeof(T) == 2 ? 2 : 1;
+  if (a.top_k <= 8) return launch_route_g1_k<T, 8, C2>(a, s);
+  if (a.top_k <= 16) return launch_route_g1_k<T, 16, C2>(a, s);
+  if (a.top_k <= 32) return launch_route_g1_k<T, 32, 1>(a, s);
+  return launch_route_g1_k<T, 64, 1>(a, s);
 }
 
-hipError_t launch_attn_g1_routed(const G1Args& a0, hipStream_t s) {
+hipError_t launch_attn_g1_routed_bf16(const G1Args& a0, hipStream_t s) {
   G1Args a = a0;
   hipError_t e;
-  if (a.top_k <= 8) e = launch_cmp_route_g1_k<2, 2>(a, s);
-  else if (a.top_k <= 16) e = launch_cmp_route_g1_k<4, 2>(a, s);
-  else e = launch_cmp_route_g1_k<8, 1>(a, s);
+  if (a.top_k <= 8) e = launch_cmp_route_g1_k<bf16, 2, 2>(a, s);
+  else if (a.top_k <= 16) e = launch_cmp_route_g1_k<bf16, 4, 2>(a, s);
+  else e = launch_cmp_route_g1_k<bf16, 8, 1>(a, s);
   if (e != hipSuccess) return e;
   a.accumulate = 1;
-  hipLaunchKernelGGL(sel_g1_kernel<0>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((sel_g1_kernel<bf16, 0>), dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_g1(const G1Args& a0, hipStream_t s) {
+template <typename T>
+hipError_t launch_attn_g1_t(const G1Args& a0, hipStream_t s) {
   G1Args a = a0;
   if (a.branches & 1) {
+    constexpr int CG = CmpGroups<T>::value;
     const int n_rowgrp = (a.n_blk + CW * CG * 16 - 1) / (CW * CG * 16);
-    hipLaunchKernelGGL(cmp_g1_kernel, dim3(n_rowgrp * a.n_kvh), dim3(CW * 64), 0, s, a);
+    hipLaunchKernelGGL(cmp_g1_kernel<T>, dim3(n_rowgrp * a.n_kvh), dim3(CW * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -971,9 +1049,9 @@ hipError_t launch_attn_g1(const G1Args& a0, hipStream_t s) {
     a.accumulate = (a.branches & 1) ? 1 : 0;
     a.local = 0;
     if (a.f_hi > a.f_lo)
-      hipLaunchKernelGGL(sel_g1_kernel<kMaxForcedBlocks>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+      hipLaunchKernelGGL((sel_g1_kernel<T, kMaxForcedBlocks>), dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
     else
-      hipLaunchKernelGGL(sel_g1_kernel<0>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+      hipLaunchKernelGGL((sel_g1_kernel<T, 0>), dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -983,10 +1061,29 @@ hipError_t launch_attn_g1(const G1Args& a0, hipStream_t s) {
     a.local = 1;
     a.ch_sel = a.ch_loc;
     a.f_lo = a.f_hi = 0;
-    hipLaunchKernelGGL(sel_g1_kernel<0>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((sel_g1_kernel<T, 0>), dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_route_g1(int is_bf16, const G1Args& a, hipStream_t s) {
+  return is_bf16 ? launch_route_g1_t<bf16>(a, s) : launch_route_g1_t<float>(a, s);
+}
+
+hipError_t launch_attn_g1_routed(int is_bf16, const G1Args& a, hipStream_t s) {
+  if (is_bf16) return launch_attn_g1_routed_bf16(a, s);
+  // fp32: the routing pass, then the compressed and selected branches (the fused pass's ranked lists
+  // next to fp32 tiles exceed the registers of two waves per SIMD); the same rows and outputs
+  hipError_t e = launch_route_g1_t<float>(a, s);
+  if (e != hipSuccess) return e;
+  return launch_attn_g1_t<float>(a, s);
+}
+
+hipError_t launch_attn_g1(int is_bf16, const G1Args& a, hipStream_t s) {
+  return is_bf16 ? launch_attn_g1_t<bf16>(a, s) : launch_attn_g1_t<float>(a, s);
 }
 
 }  // namespace nsa

@@ -68,7 +68,7 @@ struct ScoreRouteArgs {
   float scale;
 };
 
-// One query head per KV head, head dim 64, block-granular queries and routing rows (bf16).
+// One query head per KV head, head dim 64, block-granular queries and routing rows (bf16 or fp32).
 struct G1Args {
   const void* q;        // [S][n_qh][64] token queries (selected branch)
   const void* k;        // [S][n_kvh][64]
@@ -91,10 +91,10 @@ struct G1Args {
 };
 
 constexpr int kMaxForcedBlocks = 192;   // longest forced range of the selected branch (blk_cap <= 16)
-hipError_t launch_route_g1(const G1Args& a, hipStream_t s);
-hipError_t launch_attn_g1(const G1Args& a, hipStream_t s);
+hipError_t launch_route_g1(int is_bf16, const G1Args& a, hipStream_t s);
+hipError_t launch_attn_g1(int is_bf16, const G1Args& a, hipStream_t s);
 // compressed branch with the routing of its scores (sel is written), then the selected branch
-hipError_t launch_attn_g1_routed(const G1Args& a, hipStream_t s);
+hipError_t launch_attn_g1_routed(int is_bf16, const G1Args& a, hipStream_t s);
 
 size_t attn_lds_bytes(int is_bf16, const AttnArgs& a);
 hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s);

@@ -224,6 +224,10 @@ def test_other_calls_validate(S, monkeypatch):
     assert lib.nsa_pool_blocks_resblock(ctypes.byref(L), 1, 2, FAKE, w, w, w, w, FAKE, None) == -3
     assert lib.nsa_route_geometric(ctypes.byref(L), FAKE, 4, FAKE, FAKE, None, None) == -3
     assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE, FAKE, 4, FAKE, None) == -3
+    g1 = layout(S, n_blk=64, n_qh=16, n_kvh=16, head_dim=64, blk_cap=16)
+    for dt in (0, 1):                                            # block rows, f32 and bf16
+        assert lib.nsa_route_scores_topk(ctypes.byref(g1), dt, 1, FAKE, FAKE, None, 16, FAKE, None) == -3
+    assert lib.nsa_route_scores_topk(ctypes.byref(g1), 0, 0, FAKE, FAKE, None, 16, FAKE, None) == -2
     arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
     assert lib.nsa_gate_combine(1, 10, 32, 32, 2, arr, FAKE, FAKE, None) == -3
     assert lib.dense_gated_xattn_fwd(1, 100, 50, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
@@ -310,7 +314,8 @@ def test_scores_routed_validation(S, monkeypatch):
     assert call(layout(S, **g1), sel=None) == -1
     assert call(layout(S, **g1), q_cmp=None) == -1
     assert call(layout(S, **dict(g1, blk_key=None))) == -1
-    assert call(layout(S, **g1), dtype=0) == -2                  # f32: bf16 only
+    assert call(layout(S, **g1), dtype=0) == -3                  # f32: routing pass, then the branches
+    assert call(layout(S, **g1), dtype=2) == -1                  # unknown dtype
     assert call(layout(S, **dict(g1, blk_cap=32))) == -2
     assert call(layout(S, **dict(g1, blk_cap=12))) == -2
     assert call(layout(S)) == -2                                 # grouped-query layout
@@ -320,13 +325,15 @@ def test_scores_routed_validation(S, monkeypatch):
 
 def test_score_routed_layout_takes_the_local_branch(S, monkeypatch):
     """One query head per KV head: the local branch is accepted alone (no routing rows needed) and
-    with the other two; f32 stays unsupported."""
+    with the other two, in bf16 and in f32."""
     g1 = layout(S, n_blk=64, n_qh=16, n_kvh=16, head_dim=64, blk_cap=16)
     monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
     assert attn(S, g1, branches=4, q_gran=1, sel=None, gates=None, q_cmp=FAKE) == -3
     assert attn(S, g1, branches=7, q_gran=1, q_cmp=FAKE) == -3
     assert attn(S, g1, branches=5, q_gran=1, q_cmp=FAKE, sel=None) == -3
-    assert attn(S, g1, branches=4, q_gran=1, dtype=0, sel=None, gates=None) == -2
+    assert attn(S, g1, branches=4, q_gran=1, dtype=0, sel=None, gates=None) == -3
+    assert attn(S, g1, branches=7, q_gran=1, dtype=0, q_cmp=FAKE) == -3
+    assert attn(S, g1, branches=4, q_gran=0, dtype=0, sel=None, gates=None) == -2      # token rows
 
 
 def test_row_offsets_fit_32_bits(S, monkeypatch):
