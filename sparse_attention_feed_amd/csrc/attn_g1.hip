@@ -906,14 +906,29 @@ hipError_t launch_cmp_route_g1_k(const G1Args& a, hipStream_t s) {
 // selected branch with block routing rows: one wave per (query block, head)
 // ---------------------------------------------------------------------------------------------
 
-// NF: capacity for forced blocks (0: the forced range is ignored, and the key list stays small)
+// Append the valid token slots of lane l's block `blk` (when `on`) to a packed key list after its
+// first `total` entries, in lane order; returns the new length.
+__device__ __forceinline__ int pack_block_tokens(int* keys, int total, int blk, bool on, const int32_t* blk_cnt,
+                                                 int cap) {
+  const int l = lane_id();
+  const int c = on ? blk_cnt[blk] : 0;
+  int inc = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (l >= o) inc += y;
+  }
+  for (int t = 0; t < c; ++t) keys[total + inc - c + t] = blk * cap + t;
+  return total + __builtin_amdgcn_readlane(inc, 63);
+}
+
 // Two waves per SIMD (at most 256 registers each) where LDS allows eight workgroups per CU; the
-// forced variant's key list allows four, and the fp32 tile (twice the LDS and registers) fewer.
-template <typename T, int NF>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NF > 0 || sizeof(T) == 4 ? 1 : 2)))
+// fp32 tile (twice the LDS and registers) allows fewer.
+template <typename T>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 1 : 2)))
 void sel_g1_kernel(G1Args a) {
   __shared__ TileG1<T> tb;
-  __shared__ int keys_lds[(64 + NF) * 16 + KT];   // source rows of the selected valid tokens, packed
+  __shared__ int keys_lds[64 * 16 + KT];          // source rows of the selected valid tokens, packed
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int b = wg / a.n_kvh, h = wg % a.n_kvh;
   const int l = lane_id(), r = l & 15, g = l >> 4;
@@ -944,28 +959,12 @@ void sel_g1_kernel(G1Args a) {
   const int grp = a.sel_groups == 1 ? 0 : h;
   const int n_ent = a.local ? 1 : a.top_k;
   const int sb = a.local ? (l == 0 ? b : -1) : (l < a.top_k ? a.sel[((size_t)b * a.sel_groups + grp) * a.top_k + l] : -1);
-  const int nf = NF > 0 ? a.f_hi - a.f_lo : 0;
-  bool keep = sb >= 0 && sb < a.n_blk && !(sb >= a.f_lo && sb - a.f_lo < nf);   // forced blocks come below
+  bool keep = sb >= 0 && sb < a.n_blk;
   for (int y = 0; y < n_ent; ++y) {
     const int sy = __builtin_amdgcn_readlane(sb, y);
     keep = keep && !(y < l && sy == sb);
   }
-  int total = 0;
-  // the routed blocks, then the forced range 64 blocks at a time, packed one after another
-  for (int f0 = -64; f0 < nf; f0 += 64) {
-    const int fb = a.f_lo + f0 + l;                          // forced block of this lane (f0 >= 0)
-    const int blk = f0 < 0 ? sb : fb;
-    const bool on = f0 < 0 ? keep : (f0 + l < nf);
-    const int c = on ? a.blk_cnt[blk] : 0;
-    int inc = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o, 64);
-      if (l >= o) inc += y;
-    }
-    for (int t = 0; t < c; ++t) keys_lds[total + inc - c + t] = blk * cap + t;
-    total += __builtin_amdgcn_readlane(inc, 63);
-  }
+  const int total = pack_block_tokens(keys_lds, 0, sb, keep, a.blk_cnt, cap);
   const int ntiles = (total + KT - 1) / KT;
   for (int i = total + l; i < ntiles * KT; i += 64) keys_lds[i] = -1;
   __syncthreads();
@@ -1005,6 +1004,131 @@ void sel_g1_kernel(G1Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// selected branch with a forced block range: NQ query blocks of one head per wave
+// ---------------------------------------------------------------------------------------------
+//
+// The forced range (Speed3R page, section 2.2: the reference frame's tokens, attended by every
+// query) is the same key set for every query block, and fetching it is most of the branch's cost
+// when each (block, head) wave gathers it alone.  A wave here serves NQ consecutive query blocks
+// of one head: it runs each block over the block's routed blocks outside the range, one block
+// after the other (as sel_g1_kernel does), then gathers the range's valid tokens once per tile for
+// all NQ blocks, each tile continuing every block's online softmax.  The key set of a block is the
+// same union as before (each block once), only taken in another order.
+
+// query blocks per wave: the most that keep the kernel free of scratch at one wave per SIMD (bf16:
+// 8.3, 7.5 and 7.1 ms for 4, 5 and 6 blocks at the speed3r shape with the reference frame forced,
+// where one block per wave took 20.5 ms)
+template <typename T> struct ForcedGroup { static constexpr int value = sizeof(T) == 2 ? 6 : 2; };
+
+template <typename T, int NQ>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void sel_forced_g1_kernel(G1Args a) {
+  __shared__ TileG1<T> tb;
+  // packed source rows: one block's routed keys (at most 64 * 16), later the range's
+  __shared__ int keys_lds[kMaxForcedBlocks * 16 + KT];
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bg = wg / a.n_kvh, h = wg % a.n_kvh;
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const int cap = a.cap;
+  const int stride = a.n_kvh * DG;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* kb = reinterpret_cast<const T*>(a.k) + h * DG;
+  const T* vb = reinterpret_cast<const T*>(a.v) + h * DG;
+  const float c2 = a.scale * kLog2e;
+  T* o = reinterpret_cast<T*>(a.o);
+  const T* gp = reinterpret_cast<const T*>(a.gates);
+  typedef typename V4<T>::t v4;
+  const int grp = a.sel_groups == 1 ? 0 : h;
+  const int nf = a.f_hi - a.f_lo;
+  // every block's query (blocks past the end: none valid)
+  QG1<T> qq[NQ];
+  StateG1 st[NQ];
+  int cnt[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int b = bg * NQ + j;
+    cnt[j] = b < a.n_blk ? a.blk_cnt[b] : 0;
+    const size_t row = (size_t)min(b, a.n_blk - 1) * cap + min(r, cap - 1);
+    qq[j] = load_q_row(q + (row * a.n_qh + h) * DG, r < cnt[j], c2);
+    state_init(st[j]);
+  }
+  // one tile loop over keys_lds[0, total): gathered one tile ahead; blocks j with use[j] attend it
+  auto attend = [&](int total, const bool (&use)[NQ]) {
+    const int ntiles = (total + KT - 1) / KT;
+    for (int i = total + l; i < ntiles * KT; i += 64) keys_lds[i] = -1;
+    __syncthreads();
+    RowsG1<T> pre;
+    if (ntiles > 0) gather_rows_g1(pre, kb, vb, stride, keys_lds, l);
+    for (int u = 0; u < ntiles; ++u) {
+      store_rows_g1(tb, pre, l);
+      __syncthreads();
+      if (u + 1 < ntiles) gather_rows_g1(pre, kb, vb, stride, keys_lds + (u + 1) * KT, l);
+      TileFragsG1<T> f;
+      load_frags_g1(tb, f);
+      const int nk = min(KT, total - u * KT);
+      f32x4 cm[4];
+      if (nk < KT) mask_seed(nk, cm);
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        if (!use[j]) continue;
+        f32x4 seed[4], x[4];
+        row_seed(st[j], nk == KT, cm, seed);
+        scores_g1(f, qq[j], seed, x);
+        softmax_pv_g1(st[j], x, f);
+      }
+      __syncthreads();
+    }
+  };
+  // each block's routed blocks outside the range (lane x < top_k: entry x; -1, out-of-range and
+  // repeated entries count no keys)
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int b = bg * NQ + j;
+    if (b >= a.n_blk) break;
+    const int sb = l < a.top_k ? a.sel[((size_t)b * a.sel_groups + grp) * a.top_k + l] : -1;
+    bool keep = sb >= 0 && sb < a.n_blk && !(sb >= a.f_lo && sb - a.f_lo < nf);
+    for (int y = 0; y < a.top_k; ++y) {
+      const int sy = __builtin_amdgcn_readlane(sb, y);
+      keep = keep && !(y < l && sy == sb);
+    }
+    bool use[NQ];
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) use[x] = x == j;
+    attend(pack_block_tokens(keys_lds, 0, sb, keep, a.blk_cnt, cap), use);
+  }
+  // the range's valid tokens, 64 blocks per packing step, shared by all NQ blocks
+  {
+    int total = 0;
+    for (int f0 = 0; f0 < nf; f0 += 64)
+      total = pack_block_tokens(keys_lds, total, a.f_lo + f0 + l, f0 + l < nf, a.blk_cnt, cap);
+    bool use[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) use[j] = cnt[j] > 0;
+    attend(total, use);
+  }
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int b = bg * NQ + j;
+    if (b >= a.n_blk) break;
+    const float lsum = rows_sum(st[j].l);
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const bool valid = r < cnt[j];
+    const size_t row = (size_t)b * cap + min(r, cap - 1);
+    if (r < cap) {
+      if (a.lse && g == 0) a.lse[row * a.n_qh + h] = (valid && lsum > 0.f) ? (st[j].mc + __log2f(lsum)) * kLn2 : -INFINITY;
+      const float glog = (gp && valid) ? (float)gp[(row * a.n_qh + h) * a.n_gch + a.ch_sel] : 0.f;
+      const float wgt = valid ? (gp ? sigmoidf_(glog) * inv : inv) : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        v4* dst = reinterpret_cast<v4*>(o + (row * a.n_qh + h) * DG + 16 * dt + 4 * g);
+        f32x4 v = st[j].acc[dt] * wgt;
+        if (a.accumulate && valid) v += __builtin_convertvector(*dst, f32x4);
+        *dst = __builtin_convertvector(v, v4);
+      }
+    }
+  }
+}
+
 template <typename T, int K, int CG>
 hipError_t launch_route_g1_k(const G1Args& a, hipStream_t s) {
   const int n_rowgrp = (a.n_blk + RW * CG * 16 - 1) / (RW * CG * 16);
@@ -1031,7 +1155,7 @@ hipError_t launch_attn_g1_routed_bf16(const G1Args& a0, hipStream_t s) {
   else e = launch_cmp_route_g1_k<bf16, 8, 1>(a, s);
   if (e != hipSuccess) return e;
   a.accumulate = 1;
-  hipLaunchKernelGGL((sel_g1_kernel<bf16, 0>), dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(sel_g1_kernel<bf16>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1048,10 +1172,12 @@ hipError_t launch_attn_g1_t(const G1Args& a0, hipStream_t s) {
   if (a.branches & 2) {
     a.accumulate = (a.branches & 1) ? 1 : 0;
     a.local = 0;
-    if (a.f_hi > a.f_lo)
-      hipLaunchKernelGGL((sel_g1_kernel<T, kMaxForcedBlocks>), dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
-    else
-      hipLaunchKernelGGL((sel_g1_kernel<T, 0>), dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+    if (a.f_hi > a.f_lo) {
+      constexpr int NQ = ForcedGroup<T>::value;
+      hipLaunchKernelGGL((sel_forced_g1_kernel<T, NQ>), dim3((a.n_blk + NQ - 1) / NQ * a.n_kvh), dim3(64), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(sel_g1_kernel<T>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1061,7 +1187,7 @@ hipError_t launch_attn_g1_t(const G1Args& a0, hipStream_t s) {
     a.local = 1;
     a.ch_sel = a.ch_loc;
     a.f_lo = a.f_hi = 0;
-    hipLaunchKernelGGL((sel_g1_kernel<T, 0>), dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(sel_g1_kernel<T>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -53,13 +53,13 @@ def test_reference_frame_selected_branch():
     assert max_err(gl[vm], ref_lse[vm]) <= lse_bound(w, w.q, w.k)
 
 
-@pytest.mark.parametrize("lo,hi,k", [(0, 90, 16), (13, 147, 40), (60, 61, 8), (0, 0, 16)])
-def test_forced_range_with_repeats_and_gaps(lo, hi, k):
+@pytest.mark.parametrize("lo,hi,k,n_blk", [(0, 90, 16, 152), (13, 147, 40, 151), (60, 61, 8, 153), (0, 0, 16, 150)])
+def test_forced_range_with_repeats_and_gaps(lo, hi, k, n_blk):
     """Ragged block counts; routing rows with repeats, -1 and entries inside the forced range; forced
-    ranges that start at 0, start mid-sequence, hold a single block, or are empty."""
+    ranges that start at 0, start mid-sequence, hold a single block, or are empty; block counts that
+    leave the forced kernel's last wave (six query blocks per wave) with two, one or three blocks."""
     import sparse_attention_feed_amd as S
     rng = np.random.default_rng(lo + 3 * hi + k)
-    n_blk = 150
     cnt = rng.integers(1, 17, size=n_blk)
     w = W.custom_block_workload(90 + k, cnt, 16, 16, 16, 64, "bf16", k, routing="scores", q_gran="block",
                                 branches=("cmp", "sel"))

@@ -107,12 +107,13 @@ def test_f32_single_branch(branch):
     assert np.all(got[~vm] == 0)
 
 
-@pytest.mark.parametrize("lo,hi,k", [(0, 0, 40), (13, 147, 16), (60, 61, 8)])
-def test_f32_selected_rows_repeats_gaps_forced(lo, hi, k):
+@pytest.mark.parametrize("lo,hi,k,n_blk", [(0, 0, 40, 150), (13, 147, 16, 151), (60, 61, 8, 149)])
+def test_f32_selected_rows_repeats_gaps_forced(lo, hi, k, n_blk):
     """Routing rows with repeated entries, -1 and whole empty rows; k = 40 packs several 64-key tiles;
-    forced ranges that span the sequence or hold one block."""
+    forced ranges that span the sequence or hold one block; block counts that leave the last wave of
+    the forced kernel (two query blocks per wave in fp32) with one block."""
     import sparse_attention_feed_amd as S
-    w = case(5 + k, 150, k)
+    w = case(5 + k, n_blk, k)
     d = to_dev(w)
     rng = np.random.default_rng(lo + hi + k)
     sel = rng.integers(-1, w.n_blk, size=(w.n_blk, H, k)).astype(np.int32)
