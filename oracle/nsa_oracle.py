@@ -512,7 +512,8 @@ def nsa_forward(w, rows=None, return_parts=False, forced=None):
     Geometric routing ([LSRM-cn]) is per token and shared by all heads; score routing ([Speed3R])
     with one query head per KV head is per (query block, head) from the pooled queries; score
     routing with several query heads per KV head is per (token, KV group) from the summed group
-    probabilities, with the compressed branch's lse."""
+    probabilities, with the compressed branch's lse, or per (query block, KV group) from the pooled
+    queries when w.q_gran is 'block'."""
     cap = w.blk_cap
     S = w.n_slots
     rows = np.arange(S) if rows is None else np.asarray(rows)
@@ -533,6 +534,15 @@ def nsa_forward(w, rows=None, return_parts=False, forced=None):
         need = np.unique(rows // cap)
         sel = np.full((w.n_blk, w.n_kvh, w.top_k), -1, dtype=np.int32)
         sel[need], _ = route_scores(parts["q_cmp"][need], k_cmp, w.blk_key, w.scale, w.top_k)
+        q_gran_sel = "block"
+    elif w.q_gran == "block":
+        # grouped-query score routing with pooled query rows: per (query block, KV group), the blocks
+        # with the largest summed softmax probability of the group's heads for the block's pooled
+        # query, normalised by that pooled row's compressed-branch lse
+        need = np.unique(rows // cap)
+        lse_b = np.stack([attend(parts["q_cmp"][b], k_cmp, v_cmp, w.scale)[1] for b in need])
+        sel = np.full((w.n_blk, w.n_kvh, w.top_k), -1, dtype=np.int32)
+        sel[need], _ = route_scores(parts["q_cmp"][need], k_cmp, w.blk_key, w.scale, w.top_k, lse=lse_b)
         q_gran_sel = "block"
     else:
         # [LSRM-cn] "standard NSA" selection under grouped-query attention: per token and KV group,

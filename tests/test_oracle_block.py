@@ -243,6 +243,60 @@ def test_nsa_forward_gqa_scores_all_blocks_is_dense():
     np.testing.assert_allclose(o[vs], sdpa(w.q[vs], w.k[vs], w.v[vs], w.scale), rtol=0, atol=1e-12)
 
 
+def _gqa_block_case(seed=44, top_k=3):
+    return W.custom_block_workload(seed, [5, 8, 1, 3, 8, 6, 2, 7], 8, 4, 2, 8, "f32", top_k, routing="scores",
+                                   q_gran="block", branches=("cmp", "sel", "loc"))
+
+
+def test_nsa_forward_gqa_block_queries_against_torch():
+    """Grouped-query attention with pooled query rows: routing per (query block, KV group) by the
+    torch softmax ranking of the torch-pooled query, the compressed branch as torch attention of
+    that pooled query given to each valid token, the selected branch per token over its block's
+    row, the local branch per token."""
+    w = _gqa_block_case()
+    o, parts = O.nsa_forward(w, return_parts=True)
+    qc = torch_pool(w.q, w.blk_cnt, w.blk_cap)
+    kc = torch_pool(w.k, w.blk_cnt, w.blk_cap)
+    vc = torch_pool(w.v, w.blk_cnt, w.blk_cap)
+    G = w.n_qh // w.n_kvh
+    k = torch.from_numpy(kc).repeat_interleave(G, dim=1)
+    p = torch.softmax(w.scale * torch.einsum("rhd,bhd->rhb", torch.from_numpy(qc), k), dim=2)
+    imp = p.reshape(w.n_blk, w.n_kvh, G, -1).sum(2).numpy()            # [n_blk, Hkv, n_blk]
+    ocmp = sdpa(qc, kc, vc, w.scale)                                    # [n_blk, Hq, D]
+    g = 1.0 / (1.0 + np.exp(-w.gates.astype(np.float64)))
+    assert parts["sel"].shape == (w.n_blk, w.n_kvh, w.top_k)
+    for b in range(w.n_blk):
+        for j in range(w.n_kvh):
+            order = sorted(range(w.n_blk), key=lambda x: (-imp[b, j, x], int(w.blk_key[x])))[:w.top_k]
+            assert parts["sel"][b, j].tolist() == order
+    for s in w.valid_slots():
+        b = s // w.blk_cap
+        own = np.arange(b * w.blk_cap, b * w.blk_cap + w.blk_cnt[b])
+        oloc = sdpa(w.q[s:s + 1], w.k[own], w.v[own], w.scale)[0]
+        for j in range(w.n_kvh):
+            blocks = sorted(parts["sel"][b, j].tolist())
+            ks = np.concatenate([np.arange(x * w.blk_cap, x * w.blk_cap + w.blk_cnt[x]) for x in blocks])
+            hs = slice(j * G, (j + 1) * G)
+            osel = sdpa(w.q[s:s + 1, hs], w.k[ks][:, j:j + 1], w.v[ks][:, j:j + 1], w.scale)[0]
+            ref = g[s, hs, 0:1] * ocmp[b, hs] + g[s, hs, 1:2] * osel + g[s, hs, 2:3] * oloc[hs]
+            np.testing.assert_allclose(o[s, hs], ref, rtol=0, atol=1e-13)
+    assert np.all(o[~w.valid_mask()] == 0)
+
+
+def test_nsa_forward_gqa_block_equals_token_rows_when_queries_repeat():
+    """When every token of a block carries the same query, the pooled query is that query, so
+    block-granular rows give exactly the per-token layer (routing rows repeated per token)."""
+    w = _gqa_block_case(seed=45)
+    for b in range(w.n_blk):
+        w.q[b * w.blk_cap:(b + 1) * w.blk_cap] = w.q[b * w.blk_cap]
+    ob, pb = O.nsa_forward(w, return_parts=True)
+    w.q_gran = "token"
+    ot, pt = O.nsa_forward(w, return_parts=True)
+    np.testing.assert_allclose(ob, ot, rtol=0, atol=1e-14)
+    vs = w.valid_slots()
+    np.testing.assert_array_equal(pt["sel"][vs], pb["sel"][vs // w.blk_cap])
+
+
 # ---------------------------------------------------------------------------------------------
 # the whole-table geometric routing checker
 # ---------------------------------------------------------------------------------------------
