@@ -214,10 +214,12 @@ nsa_status nsa_route_geometric_range(const nsa_layout* layout, const float* pts,
  *   G == 1: importance of block b for (row r, head h) is <q[r][h], k_cmp[b][h]>.
  * Blocks are ranked by descending importance, ties by ascending blk_key.
  *   q_gran NSA_Q_TOKEN: rows = S, q [S][n_qh][D] (padding rows get -1)
- *   q_gran NSA_Q_BLOCK: rows = n_blk, q is the pooled query [n_blk][n_qh][D]
+ *   q_gran NSA_Q_BLOCK: rows = n_blk, q is the pooled query [n_blk][n_qh][D] (with G > 1, lse is
+ *   then the pooled rows' compressed-branch lse, as nsa_attn_fwd returns it for CMP with
+ *   NSA_Q_BLOCK)
  *   k_cmp [n_blk][n_kvh][D];  lse [rows][n_qh] float32 natural-log partition function of the
  *   compressed branch (required iff G > 1);  sel [rows][n_kvh][top_k] int32.
- * Supported: (D, G) = (32, 16) with q_gran TOKEN (bf16 or f32, n_blk <= 65536), and (64, 1) with
+ * Supported: (D, G) = (32, 16) with either q_gran (bf16 or f32, n_blk <= 65536), and (64, 1) with
  * q_gran BLOCK (bf16 or f32; scores are fp32 products of the stored rows); 1 <= top_k <= 64.
  */
 nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_qgran q_gran,
@@ -245,8 +247,11 @@ nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_
  *   k_cmp, v_cmp [n_blk][n_kvh][D] (CMP); unused pointers may be NULL.  o [S][n_qh][D].
  *   lse: NULL, or (single branch only) float32 [rows][n_qh] natural-log partition function,
  *        rows = n_blk for CMP with NSA_Q_BLOCK, else S; -inf on padding rows and empty key sets.
- * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16 with NSA_Q_TOKEN (n_blk <= 65536 when SEL
- * is named; n_blk * blk_cap * n_qh * max(32, gate_stride) < 2^31, row offsets being 32-bit); and
+ * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16 (n_blk <= 65536 when SEL is named;
+ * n_blk * blk_cap * n_qh * max(32, gate_stride) < 2^31, row offsets being 32-bit).  With NSA_Q_BLOCK
+ * the selected and local branches run first in the fused kernel (token queries, the block's
+ * routing row for every token) and the compressed branch of the pooled queries then adds each
+ * block's gated result to its tokens (o is rounded to `dtype` in between).  And
  * (D, G) = (64, 1) for NSA_F32 and NSA_BF16 with NSA_Q_BLOCK (pooled queries in the compressed
  * branch, token queries in the selected and local ones), blk_cap in {1, 2, 4, 8, 16}: each named
  * branch runs in its own launch, the first writing its gated result to o in `dtype` and the later

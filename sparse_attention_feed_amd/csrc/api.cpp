@@ -304,8 +304,8 @@ nsa_status nsa_route_scores_topk(const nsa_layout* L, nsa_dtype dtype, nsa_qgran
     g.scale = L->scale;
     return hip_status(nsa::launch_route_g1(dtype == NSA_BF16, g, stream), "nsa_route_scores_topk");
   }
-  if (L->head_dim != 32 || G != 16 || q_gran != NSA_Q_TOKEN)
-    return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: compiled for head_dim 32, 16 query heads per KV head, per-token rows");
+  if (L->head_dim != 32 || G != 16)
+    return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: compiled for head_dim 32 with 16 query heads per KV head");
   if (L->n_blk > 65536) return fail(NSA_ERR_UNSUPPORTED, "nsa_route_scores_topk: n_blk must be <= 65536");
   NSA_FORCED_FAILURE("nsa_route_scores_topk");
   nsa::ScoreRouteArgs a;
@@ -315,9 +315,11 @@ nsa_status nsa_route_scores_topk(const nsa_layout* L, nsa_dtype dtype, nsa_qgran
   a.blk_cnt = L->blk_cnt;
   a.blk_key = L->blk_key;
   a.sel = sel;
-  a.n_rows = L->n_blk * L->blk_cap;
+  // NSA_Q_BLOCK: the pooled rows, 64 per workgroup
+  a.dense_rows = q_gran == NSA_Q_BLOCK ? 1 : 0;
+  a.n_rows = a.dense_rows ? L->n_blk : L->n_blk * L->blk_cap;
   a.n_blk = L->n_blk;
-  a.cap = L->blk_cap;
+  a.cap = a.dense_rows ? 64 : L->blk_cap;
   a.n_qh = L->n_qh;
   a.n_kvh = L->n_kvh;
   a.top_k = top_k;
@@ -408,9 +410,11 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   }
   if (forced)
     return fail(NSA_ERR_UNSUPPORTED, "%s: a forced block range needs the one-head-per-KV-head kernels (head_dim 64)", fn);
-  if (L->head_dim != 32 || L->n_qh / L->n_kvh != 16 || q_gran != NSA_Q_TOKEN)
-    return fail(NSA_ERR_UNSUPPORTED, "%s: compiled for head_dim 32, 16 query heads per KV head, NSA_Q_TOKEN "
-                                     "(or head_dim 64, one query head per KV head, NSA_Q_BLOCK)", fn);
+  if (L->head_dim != 32 || L->n_qh / L->n_kvh != 16)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: compiled for head_dim 32 with 16 query heads per KV head (or head_dim 64 "
+                                     "with one query head per KV head and NSA_Q_BLOCK)", fn);
+  if (q_gran == NSA_Q_BLOCK && !whole)
+    return fail(NSA_ERR_UNSUPPORTED, "%s: block ranges take per-token query rows (NSA_Q_TOKEN)", fn);
   // the grouped-query kernels index rows of q, o, gate_logits, lse and sel in 32-bit arithmetic
   if ((long long)L->n_blk * L->blk_cap * L->n_qh * (gate_stride > 32 ? gate_stride : 32) > 0x7FFFFFFFLL)
     return fail(NSA_ERR_UNSUPPORTED, "%s: n_blk * blk_cap * n_qh * max(32, gate_stride) must be < 2^31", fn);
@@ -435,8 +439,10 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   a.scale = L->scale;
   a.branches = branches;
   a.n_words = (L->n_blk + 31) / 32;
+  a.sel_per_block = q_gran == NSA_Q_BLOCK ? 1 : 0;
   {
-    long long u = (long long)L->blk_cap * (a.top_k > 0 ? a.top_k : 1);
+    // distinct selected blocks of one query block: one routing row per slot, or one per block
+    long long u = (long long)(a.sel_per_block ? 1 : L->blk_cap) * (a.top_k > 0 ? a.top_k : 1);
     a.u_cap = (int)(u < L->n_blk ? u : L->n_blk);
   }
   // Test hook (NSA_TEST_RING_STALL=1): the selected branch's tile ring waits for one count more
@@ -454,7 +460,24 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   const size_t lds = nsa::attn_lds_bytes(dtype == NSA_BF16, a);
   if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "%s: LDS need %zu bytes exceeds 160 KiB", fn, lds);
   NSA_FORCED_FAILURE(fn);
-  return hip_status(nsa::launch_attn(dtype == NSA_BF16, a, stream), fn);
+  if (q_gran == NSA_Q_TOKEN) return hip_status(nsa::launch_attn(dtype == NSA_BF16, a, stream), fn);
+  // block rows: the selected and local branches (token queries, the block's routing row) in the
+  // fused kernel, reading the gate channels after the compressed one; then the compressed branch
+  // of the pooled queries, adding each block's gated result to its tokens
+  const uint32_t rest = branches & (NSA_BR_SEL | NSA_BR_LOC);
+  const bool has_cmp = (branches & NSA_BR_CMP) != 0;
+  if (rest) {
+    nsa::AttnArgs f = a;
+    f.branches = rest;
+    if (gate_logits != nullptr && has_cmp)
+      f.gates = static_cast<const char*>(gate_logits) + (dtype == NSA_BF16 ? 2 : 4);
+    hipError_t e = nsa::launch_attn(dtype == NSA_BF16, f, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  if (!has_cmp) return NSA_OK;
+  nsa::AttnArgs c = a;
+  c.q = q_cmp;
+  return hip_status(nsa::launch_cmp_pooled(dtype == NSA_BF16, c, rest ? 1 : 0, 0, stream), fn);
 }
 
 nsa_status nsa_attn_fwd(const nsa_layout* L, nsa_dtype dtype, uint32_t branches, nsa_qgran q_gran,

@@ -501,11 +501,14 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     // rows) and their blocks' token counts, all loads issued at once: a loop of dependent loads
     // would pay one memory round trip per entry, exposed with one workgroup per CU
     constexpr int MAXE = (64 * 64 + NT - 1) / NT;   // rows <= 64, entries per row <= 64
+    // routing row of slot s0 + t: sel_wg + t * sel_tstride (block rows: every slot reads row b)
+    const int sel_tstride = a.sel_per_block ? 0 : a.sel_groups * kk;
+    const int32_t* sel_wg = a.sel + ((size_t)(a.sel_per_block ? b : b * cap + s0) * a.sel_groups + grp) * kk;
     int eblk[MAXE], ecnt[MAXE];
 #pragma unroll
     for (int i = 0; i < MAXE; ++i) {
       const int e = threadIdx.x + i * NT;
-      eblk[i] = e < cnt_p * kk ? a.sel[((b * cap + s0 + e / kk) * a.sel_groups + grp) * kk + e % kk] : -1;
+      eblk[i] = e < cnt_p * kk ? sel_wg[(e / kk) * sel_tstride + e % kk] : -1;
     }
 #pragma unroll
     for (int i = 0; i < MAXE; ++i) ecnt[i] = (eblk[i] >= 0 && eblk[i] < a.n_blk) ? a.blk_cnt[eblk[i]] : 0;
@@ -605,6 +608,78 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
       for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(0.f);
     }
     if (a.lse && g == 0) a.lse[row * a.n_qh + hh] = -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// compressed branch of pooled queries (block-granular query rows)
+// ---------------------------------------------------------------------------------------------
+//
+// The rows are the pooled queries [n_blk][n_qh][D], SLOTS of them per workgroup in storage order,
+// each with its KV group's 16 heads; the tile loop over every pooled key block is the fused
+// kernel's compressed phase.  Each block's result is then given to every valid token of the block,
+// with that token's gate, added to what o holds (accumulate) or written with zeros on padding
+// slots.  Speed3R page, section 2.1: the compression branch attends with block-pooled queries.
+
+template <typename T, int WAVES, int TPW>
+__global__ __launch_bounds__(WAVES * 64) void cmp_pooled_kernel(AttnArgs a, int accumulate, int gate_ch) {
+  constexpr int NT = WAVES * 64;
+  constexpr int SLOTS = WAVES * TPW;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  TileBuf<T>* buf = reinterpret_cast<TileBuf<T>*>(smem);
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int rg = wg / a.n_kvh, j = wg % a.n_kvh;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  const int hh = j * GRP + r;
+  const int kvs = a.n_kvh * HD;
+  const float c2 = a.scale * kLog2e;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  // pooled row t of wave w: rg * SLOTS + t * WAVES + w; this workgroup's rows are [0, rem)
+  const int rem = a.n_blk - rg * SLOTS;
+  const int n_valid = rem > w ? min(TPW, (rem - w + WAVES - 1) / WAVES) : 0;
+  QF<T> qf[TPW];
+  {
+    Frag8<T> raw[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      raw[t] = load_q8(q + ((size_t)(rg * SLOTS + min(t * WAVES + w, rem - 1)) * a.n_qh + hh) * HD + 8 * g);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) qf[t] = make_qf<T>(raw[t], c2, t < n_valid);
+  }
+  TokState st[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) tok_init(st[t]);
+  RangeSrc<T> src;
+  src.base = reinterpret_cast<const T*>(a.k_cmp) + j * HD;
+  src.vbase = reinterpret_cast<const T*>(a.v_cmp) + j * HD;
+  src.stride = kvs;
+  src.lo = 0;
+  src.hi = a.n_blk;
+  AllPart part{n_valid};
+  run_tiles<T, NT, TPW>(buf, src, (a.n_blk + TILE - 1) / TILE, part, st, qf);
+  T* o = reinterpret_cast<T*>(a.o);
+  const T* gp = reinterpret_cast<const T*>(a.gates);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (t >= n_valid) continue;
+    const int b = rg * SLOTS + t * WAVES + w;
+    f32x4 res[2];
+    tok_finish(st[t], res, 1.f, a.lse ? a.lse + (size_t)b * a.n_qh + hh : nullptr);
+    const int cnt = a.blk_cnt[b];
+    for (int sl = 0; sl < a.cap; ++sl) {
+      const size_t row = (size_t)b * a.cap + sl;
+      T* dst = o + (row * a.n_qh + hh) * HD + 4 * g;
+      if (sl >= cnt && accumulate) continue;
+      const float wgt = sl >= cnt ? 0.f : (gp ? sigmoidf_(to_f32(gp[(row * a.n_qh + hh) * a.n_gch + gate_ch])) : 1.f);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float prev = accumulate ? to_f32(dst[16 * dt + i]) : 0.f;
+          dst[16 * dt + i] = from_f32<T>(prev + wgt * res[dt][i]);
+        }
+    }
   }
 }
 
@@ -729,6 +804,15 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
 }
 
 template <typename T>
+hipError_t launch_cmp_pooled_t(const AttnArgs& a, int accumulate, int gate_ch, hipStream_t s) {
+  constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
+  const size_t lds = 2 * sizeof(TileBuf<T>);
+  const int nwg = ((a.n_blk + WAVES * TPW - 1) / (WAVES * TPW)) * a.n_kvh;
+  hipLaunchKernelGGL((cmp_pooled_kernel<T, WAVES, TPW>), dim3(nwg), dim3(NT), lds, s, a, accumulate, gate_ch);
+  return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_dense_t(const DenseArgs& a, hipStream_t s) {
   constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
   constexpr int SLOTS = WAVES * TPW;
@@ -751,6 +835,10 @@ size_t attn_lds_bytes(int is_bf16, const AttnArgs& a) {
 
 hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s) {
   return is_bf16 ? launch_attn_t<bf16>(a, s) : launch_attn_t<float>(a, s);
+}
+
+hipError_t launch_cmp_pooled(int is_bf16, const AttnArgs& a, int accumulate, int gate_ch, hipStream_t s) {
+  return is_bf16 ? launch_cmp_pooled_t<bf16>(a, accumulate, gate_ch, s) : launch_cmp_pooled_t<float>(a, accumulate, gate_ch, s);
 }
 
 hipError_t launch_dense(int is_bf16, const DenseArgs& a, hipStream_t s) {

@@ -27,6 +27,7 @@ struct AttnArgs {
   int ring_stall;      // test hook: extra count the ring waits for (0 in normal use)
   int q_blk0, n_qblk;  // query blocks [q_blk0, q_blk0 + n_qblk)
   int kv_lo, kv_hi;    // key blocks of the compressed and local branches: [kv_lo, kv_hi)
+  int sel_per_block;   // routing rows are per query block ([n_blk][sel_groups][top_k]), not per slot
 };
 
 struct DenseArgs {
@@ -66,6 +67,7 @@ struct ScoreRouteArgs {
   int32_t* sel;
   int n_rows, n_blk, cap, n_qh, n_kvh, top_k;
   float scale;
+  int dense_rows;       // rows are n_rows pooled rows, 64 per workgroup (cap = 64), not token slots
 };
 
 // One query head per KV head, head dim 64, block-granular queries and routing rows (bf16 or fp32).
@@ -98,6 +100,10 @@ hipError_t launch_attn_g1_routed(int is_bf16, const G1Args& a, hipStream_t s);
 
 size_t attn_lds_bytes(int is_bf16, const AttnArgs& a);
 hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s);
+// compressed branch of pooled queries (a.q = [n_blk][n_qh][D]), each block's result given to its
+// valid tokens: o = (accumulate ? o : 0) + sigmoid(gates[.., gate_ch]) * result (no gate when
+// a.gates is NULL), padding slots 0 when not accumulating; lse [n_blk][n_qh] when a.lse is set
+hipError_t launch_cmp_pooled(int is_bf16, const AttnArgs& a, int accumulate, int gate_ch, hipStream_t s);
 hipError_t launch_dense(int is_bf16, const DenseArgs& a, hipStream_t s);
 hipError_t launch_pool(int is_bf16, const void* x, void* x_cmp, const int32_t* blk_cnt, int n_blk,
                        int cap, int n_heads, int head_dim, hipStream_t s);

@@ -7,7 +7,8 @@
 // (importance descending, blk_key ascending).
 //
 // Work decomposition: one workgroup per (query block, KV group), 8 waves x 8 tokens, as the fused
-// attention kernel.  Tiles of 64 pooled keys are staged once in LDS and serve all 64 tokens.
+// attention kernel.  With pooled query rows (one per block) the rows are taken 64 at a time in
+// storage order instead.  Tiles of 64 pooled keys are staged once in LDS and serve all 64 tokens.
 // Per (token, tile), with S = Q K^T on v_mfma_f32_16x16x32 (A = the token's 16 pre-scaled query
 // rows, B = 16 keys): lane (r, g) gets heads 4g..4g+3 of key 16 kt + r, and the accumulator seed
 // -lse_h log2(e) makes the MFMA output the exponent itself.  The head sum is three adds in the lane
@@ -144,17 +145,19 @@ __global__ __launch_bounds__(RWAVES * 64) void score_route_gqa_kernel(ScoreRoute
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int cap = a.cap;
   const int j = wg % a.n_kvh, b = wg / a.n_kvh;
-  const int cnt = a.blk_cnt[b];
+  // rows [b * cap, b * cap + cnt): a storage block's valid slots, or (dense rows, cap = 64) the
+  // next 64 pooled rows
+  const int cnt = a.dense_rows ? min(cap, a.n_rows - b * cap) : a.blk_cnt[b];
   const int w = threadIdx.x >> 6, l = lane_id(), r = l & 15, g = l >> 4;
   const int n_valid = cnt > w ? min(RTPW, (cnt - w + RWAVES - 1) / RWAVES) : 0;   // tokens t < n_valid
   const int kk = min(a.top_k, a.n_blk);
   const float c2 = a.scale * kLog2e;
   const T* q = reinterpret_cast<const T*>(a.q);
 
-  // padding slots of the block: rows of -1
+  // padding slots of the block: rows of -1 (dense rows have none)
   for (int t = 0; t < RTPW; ++t) {
     const int slot = t * RWAVES + w;
-    if (slot < cap && slot >= cnt) {
+    if (slot < cap && slot >= cnt && !a.dense_rows) {
       int32_t* so = a.sel + ((size_t)(b * cap + slot) * a.n_kvh + j) * a.top_k;
       for (int x = l; x < a.top_k; x += 64) so[x] = -1;
     }
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(RWAVES * 64) void score_route_gqa_kernel(ScoreRoute
     f32x4 ls[RTPW];
 #pragma unroll
     for (int t = 0; t < RTPW; ++t) {
-      const size_t row = (size_t)b * cap + min(t * RWAVES + w, cap - 1);
+      const size_t row = (size_t)b * cap + min(t * RWAVES + w, cnt - 1);
       if constexpr (sizeof(T) == 2) {
         raw[t].v = *reinterpret_cast<const bf16x8*>(q + (row * a.n_qh + j * RGRP + r) * RHD + 8 * g);
       } else {
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(RWAVES * 64) void score_route_gqa_kernel(ScoreRoute
 template <typename T, int RCAP>
 hipError_t launch_cap(const ScoreRouteArgs& a, hipStream_t s) {
   const size_t lds = 2 * sizeof(RTile<T>) + (size_t)RWAVES * RTPW * RCAP * sizeof(Cand);
-  const int nwg = a.n_blk * a.n_kvh;
+  const int nwg = (a.dense_rows ? (a.n_rows + RT - 1) / RT : a.n_blk) * a.n_kvh;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_route_gqa_kernel<T, RCAP>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -192,7 +192,7 @@ def test_other_calls_validate(S, monkeypatch):
     assert lib.nsa_route_geometric(ctypes.byref(L), None, 4, FAKE, FAKE, None, None) == -1
     assert lib.nsa_route_geometric(ctypes.byref(layout(S, blk_key=None)), FAKE, 4, FAKE, FAKE, None, None) == -1
     assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE, None, 4, FAKE, None) == -1  # lse needed
-    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 1, FAKE, FAKE, FAKE, 4, FAKE, None) == -2
+    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 2, FAKE, FAKE, FAKE, 4, FAKE, None) == -1  # bad q_gran
     # 16-byte alignment of the vector-loaded operands
     assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE, FAKE + 4, 4, FAKE, None) == -2
     assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE + 8, FAKE, FAKE, 4, FAKE, None) == -2
@@ -224,6 +224,8 @@ def test_other_calls_validate(S, monkeypatch):
     assert lib.nsa_pool_blocks_resblock(ctypes.byref(L), 1, 2, FAKE, w, w, w, w, FAKE, None) == -3
     assert lib.nsa_route_geometric(ctypes.byref(L), FAKE, 4, FAKE, FAKE, None, None) == -3
     assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 0, FAKE, FAKE, FAKE, 4, FAKE, None) == -3
+    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 1, FAKE, FAKE, FAKE, 4, FAKE, None) == -3  # pooled rows
+    assert lib.nsa_route_scores_topk(ctypes.byref(L), 1, 1, FAKE, FAKE, None, 4, FAKE, None) == -1  # lse needed
     g1 = layout(S, n_blk=64, n_qh=16, n_kvh=16, head_dim=64, blk_cap=16)
     for dt in (0, 1):                                            # block rows, f32 and bf16
         assert lib.nsa_route_scores_topk(ctypes.byref(g1), dt, 1, FAKE, FAKE, None, 16, FAKE, None) == -3
@@ -348,3 +350,18 @@ def test_row_offsets_fit_32_bits(S, monkeypatch):
     lib = S.lib
     assert lib.dense_gated_xattn_fwd(1, 1 << 21, 0, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
     assert lib.dense_gated_xattn_fwd(1, (1 << 21) - 1, 0, 32, 2, 32, 0.17, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
+
+
+def test_grouped_query_block_rows(S, monkeypatch):
+    """Grouped-query layout with pooled query rows (NSA_Q_BLOCK): every branch combination reaches
+    the launch; the compressed branch needs q_cmp; block ranges keep per-token rows."""
+    monkeypatch.setenv("NSA_FORCE_HIP_ERROR", "1")
+    L = layout(S)
+    for br in (1, 2, 4, 3, 5, 6, 7):
+        kw = dict(branches=br, q_gran=1, q_cmp=FAKE)
+        if br in (1, 2, 4):
+            kw["gates"] = None
+        assert attn(S, L, **kw) == -3, br
+    assert attn(S, L, branches=1, q_gran=1, q_cmp=None, gates=None) == -1
+    lse = FAKE
+    assert attn(S, L, branches=1, q_gran=1, q_cmp=FAKE, gates=None, lse=lse) == -3
