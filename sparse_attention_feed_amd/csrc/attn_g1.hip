@@ -129,16 +129,20 @@ __device__ __forceinline__ void scores_g1(const TileFragsG1<T>& f, const QG1<T>&
 // tile's compute.  Padding keys (row -1) read row 0: their scores are masked to -inf, so they weigh
 // nothing.
 // (vector types, not arrays: an array carried across the tile loop was placed in scratch memory)
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x32 __attribute__((ext_vector_type(32)));
 typedef uint32_t u32x64 __attribute__((ext_vector_type(64)));
-template <typename T> struct RowsG1;
-template <> struct RowsG1<bf16> { u32x32 k, v; };
-template <> struct RowsG1<float> { u32x64 k, v; };
+// a thread's share of a tile gathered by NTH threads
+template <typename T, int NTH> struct RowsG1;
+template <> struct RowsG1<bf16, 64> { u32x32 k, v; };
+template <> struct RowsG1<float, 64> { u32x64 k, v; };
+template <> struct RowsG1<bf16, 128> { u32x16 k, v; };
+template <> struct RowsG1<float, 128> { u32x32 k, v; };
 
-template <typename T> struct ChunkG1 {
+template <typename T, int NTH = 64> struct ChunkG1 {
   static constexpr int EPC = 16 / sizeof(T);     // elements per 16-byte chunk
   static constexpr int CPK = DG / EPC;           // chunks per key row
-  static constexpr int NCH = KT * CPK / 64;      // chunks per thread
+  static constexpr int NCH = KT * CPK / NTH;     // chunks per thread
 };
 
 template <typename V>
@@ -157,13 +161,13 @@ __device__ __forceinline__ bf16 chunk_elem(const V& d, int i, int x, bf16) {
 template <typename V>
 __device__ __forceinline__ float chunk_elem(const V& d, int i, int x, float) { return __uint_as_float(d[4 * i + x]); }
 
-template <typename T>
-__device__ __forceinline__ void gather_rows_g1(RowsG1<T>& g, const T* kb, const T* vb, int stride,
+template <int NTH, typename T>
+__device__ __forceinline__ void gather_rows_g1(RowsG1<T, NTH>& g, const T* kb, const T* vb, int stride,
                                                const int* rows /* LDS [64] */, int tid) {
-  typedef ChunkG1<T> C;
+  typedef ChunkG1<T, NTH> C;
 #pragma unroll
   for (int i = 0; i < C::NCH; ++i) {
-    const int cc = tid + i * 64;
+    const int cc = tid + i * NTH;
     const int key = cc / C::CPK, part = cc % C::CPK;
     const size_t off = (size_t)max(rows[key], 0) * stride + part * C::EPC;
     put4(g.k, i, *reinterpret_cast<const uint4*>(kb + off));
@@ -171,12 +175,12 @@ __device__ __forceinline__ void gather_rows_g1(RowsG1<T>& g, const T* kb, const 
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void store_rows_g1(TileG1<T>& t, const RowsG1<T>& g, int tid) {
-  typedef ChunkG1<T> C;
+template <int NTH, typename T>
+__device__ __forceinline__ void store_rows_g1(TileG1<T>& t, const RowsG1<T, NTH>& g, int tid) {
+  typedef ChunkG1<T, NTH> C;
 #pragma unroll
   for (int i = 0; i < C::NCH; ++i) {
-    const int cc = tid + i * 64;
+    const int cc = tid + i * NTH;
     const int key = cc / C::CPK, part = cc % C::CPK;
     *reinterpret_cast<uint4*>(&t.k[key][part * C::EPC]) =
         make_uint4(g.k[4 * i], g.k[4 * i + 1], g.k[4 * i + 2], g.k[4 * i + 3]);
@@ -970,12 +974,12 @@ void sel_g1_kernel(G1Args a) {
   __syncthreads();
   StateG1 st;
   state_init(st);
-  RowsG1<T> pre;
-  if (ntiles > 0) gather_rows_g1(pre, kb, vb, stride, keys_lds, l);
+  RowsG1<T, 64> pre;
+  if (ntiles > 0) gather_rows_g1<64>(pre, kb, vb, stride, keys_lds, l);
   for (int u = 0; u < ntiles; ++u) {
-    store_rows_g1(tb, pre, l);
+    store_rows_g1<64>(tb, pre, l);
     __syncthreads();
-    if (u + 1 < ntiles) gather_rows_g1(pre, kb, vb, stride, keys_lds + (u + 1) * KT, l);
+    if (u + 1 < ntiles) gather_rows_g1<64>(pre, kb, vb, stride, keys_lds + (u + 1) * KT, l);
     TileFragsG1<T> f;
     load_frags_g1(tb, f);
     const int nk = min(KT, total - u * KT);
@@ -1017,18 +1021,33 @@ void sel_g1_kernel(G1Args a) {
 // same union as before (each block once), only taken in another order.
 
 // query blocks per wave: the most that keep the kernel free of scratch at one wave per SIMD (bf16:
-// 8.3, 7.5 and 7.1 ms for 4, 5 and 6 blocks at the speed3r shape with the reference frame forced,
-// where one block per wave took 20.5 ms)
+// 8.3, 7.5 and 7.1 ms for 4, 5 and 6 blocks, one wave per workgroup, at the speed3r shape with the
+// reference frame forced, where one block per wave took 20.5 ms)
 template <typename T> struct ForcedGroup { static constexpr int value = sizeof(T) == 2 ? 6 : 2; };
+// waves per workgroup: FW * NQ query blocks share each gathered range tile (7.12 -> 6.80 ms for
+// FW = 1 -> 2 at the same shape; the range's gather is then no longer what bounds the kernel)
+constexpr int FW = 2;
+
+// Wave-local ordering of LDS accesses (a wave's own LDS operations complete in issue order).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <typename T, int NQ>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void sel_forced_g1_kernel(G1Args a) {
-  __shared__ TileG1<T> tb;
-  // packed source rows: one block's routed keys (at most 64 * 16), later the range's
-  __shared__ int keys_lds[kMaxForcedBlocks * 16 + KT];
+__global__ __launch_bounds__(FW * 64) __attribute__((amdgpu_waves_per_eu(1))) void sel_forced_g1_kernel(G1Args a) {
+  // wave w's tile and key list for its blocks' routed parts; the FW tiles then double-buffer the
+  // shared range
+  __shared__ TileG1<T> tb[FW];
+  __shared__ int keys_w[FW][64 * 16 + KT];
+  __shared__ int keys_f[kMaxForcedBlocks * 16 + KT];
+  __shared__ int f_total;
+  static_assert(FW == 2, "the range's tiles are double-buffered in the FW wave tiles");
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bg = wg / a.n_kvh, h = wg % a.n_kvh;
-  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), r = l & 15, g = l >> 4;
+  const int b0 = (bg * FW + w) * NQ;               // this wave's first query block
   const int cap = a.cap;
   const int stride = a.n_kvh * DG;
   const T* q = reinterpret_cast<const T*>(a.q);
@@ -1046,44 +1065,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void se
   int cnt[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    const int b = bg * NQ + j;
+    const int b = b0 + j;
     cnt[j] = b < a.n_blk ? a.blk_cnt[b] : 0;
     const size_t row = (size_t)min(b, a.n_blk - 1) * cap + min(r, cap - 1);
     qq[j] = load_q_row(q + (row * a.n_qh + h) * DG, r < cnt[j], c2);
     state_init(st[j]);
   }
-  // one tile loop over keys_lds[0, total): gathered one tile ahead; blocks j with use[j] attend it
-  auto attend = [&](int total, const bool (&use)[NQ]) {
-    const int ntiles = (total + KT - 1) / KT;
-    for (int i = total + l; i < ntiles * KT; i += 64) keys_lds[i] = -1;
-    __syncthreads();
-    RowsG1<T> pre;
-    if (ntiles > 0) gather_rows_g1(pre, kb, vb, stride, keys_lds, l);
-    for (int u = 0; u < ntiles; ++u) {
-      store_rows_g1(tb, pre, l);
-      __syncthreads();
-      if (u + 1 < ntiles) gather_rows_g1(pre, kb, vb, stride, keys_lds + (u + 1) * KT, l);
-      TileFragsG1<T> f;
-      load_frags_g1(tb, f);
-      const int nk = min(KT, total - u * KT);
-      f32x4 cm[4];
-      if (nk < KT) mask_seed(nk, cm);
-#pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        if (!use[j]) continue;
-        f32x4 seed[4], x[4];
-        row_seed(st[j], nk == KT, cm, seed);
-        scores_g1(f, qq[j], seed, x);
-        softmax_pv_g1(st[j], x, f);
-      }
-      __syncthreads();
-    }
-  };
   // each block's routed blocks outside the range (lane x < top_k: entry x; -1, out-of-range and
-  // repeated entries count no keys)
+  // repeated entries count no keys), in the wave's own tile: no workgroup barrier, since the
+  // waves' tile counts differ
+  TileG1<T>& tw = tb[w];
+  int* kw = keys_w[w];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    const int b = bg * NQ + j;
+    const int b = b0 + j;
     if (b >= a.n_blk) break;
     const int sb = l < a.top_k ? a.sel[((size_t)b * a.sel_groups + grp) * a.top_k + l] : -1;
     bool keep = sb >= 0 && sb < a.n_blk && !(sb >= a.f_lo && sb - a.f_lo < nf);
@@ -1091,24 +1086,65 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void se
       const int sy = __builtin_amdgcn_readlane(sb, y);
       keep = keep && !(y < l && sy == sb);
     }
-    bool use[NQ];
-#pragma unroll
-    for (int x = 0; x < NQ; ++x) use[x] = x == j;
-    attend(pack_block_tokens(keys_lds, 0, sb, keep, a.blk_cnt, cap), use);
+    const int total = pack_block_tokens(kw, 0, sb, keep, a.blk_cnt, cap);
+    const int ntiles = (total + KT - 1) / KT;
+    for (int i = total + l; i < ntiles * KT; i += 64) kw[i] = -1;
+    wave_sync();
+    RowsG1<T, 64> pre;
+    if (ntiles > 0) gather_rows_g1<64>(pre, kb, vb, stride, kw, l);
+    for (int u = 0; u < ntiles; ++u) {
+      store_rows_g1<64>(tw, pre, l);
+      wave_sync();
+      if (u + 1 < ntiles) gather_rows_g1<64>(pre, kb, vb, stride, kw + (u + 1) * KT, l);
+      TileFragsG1<T> f;
+      load_frags_g1(tw, f);
+      const int nk = min(KT, total - u * KT);
+      f32x4 cm[4], seed[4], x[4];
+      if (nk < KT) mask_seed(nk, cm);
+      row_seed(st[j], nk == KT, cm, seed);
+      scores_g1(f, qq[j], seed, x);
+      softmax_pv_g1(st[j], x, f);
+      wave_sync();
+    }
   }
-  // the range's valid tokens, 64 blocks per packing step, shared by all NQ blocks
-  {
+  // the range's valid tokens (64 blocks per packing step), each tile gathered once by the whole
+  // workgroup for its FW * NQ blocks
+  __syncthreads();
+  if (w == 0) {
     int total = 0;
     for (int f0 = 0; f0 < nf; f0 += 64)
-      total = pack_block_tokens(keys_lds, total, a.f_lo + f0 + l, f0 + l < nf, a.blk_cnt, cap);
-    bool use[NQ];
+      total = pack_block_tokens(keys_f, total, a.f_lo + f0 + l, f0 + l < nf, a.blk_cnt, cap);
+    const int nt = (total + KT - 1) / KT;
+    for (int i = total + l; i < nt * KT; i += 64) keys_f[i] = -1;
+    if (l == 0) f_total = total;
+  }
+  __syncthreads();
+  const int total_f = f_total;
+  const int nft = (total_f + KT - 1) / KT;
+  RowsG1<T, FW * 64> pf;
+  if (nft > 0) gather_rows_g1<FW * 64>(pf, kb, vb, stride, keys_f, tid);
+  for (int u = 0; u < nft; ++u) {
+    // buffer u & 1 was last read in tile u - 2, before every wave passed the previous barrier
+    store_rows_g1<FW * 64>(tb[u & 1], pf, tid);
+    __syncthreads();
+    if (u + 1 < nft) gather_rows_g1<FW * 64>(pf, kb, vb, stride, keys_f + (u + 1) * KT, tid);
+    TileFragsG1<T> f;
+    load_frags_g1(tb[u & 1], f);
+    const int nk = min(KT, total_f - u * KT);
+    f32x4 cm[4];
+    if (nk < KT) mask_seed(nk, cm);
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) use[j] = cnt[j] > 0;
-    attend(total, use);
+    for (int j = 0; j < NQ; ++j) {
+      if (cnt[j] == 0) continue;
+      f32x4 seed[4], x[4];
+      row_seed(st[j], nk == KT, cm, seed);
+      scores_g1(f, qq[j], seed, x);
+      softmax_pv_g1(st[j], x, f);
+    }
   }
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    const int b = bg * NQ + j;
+    const int b = b0 + j;
     if (b >= a.n_blk) break;
     const float lsum = rows_sum(st[j].l);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
@@ -1173,8 +1209,9 @@ hipError_t launch_attn_g1_t(const G1Args& a0, hipStream_t s) {
     a.accumulate = (a.branches & 1) ? 1 : 0;
     a.local = 0;
     if (a.f_hi > a.f_lo) {
-      constexpr int NQ = ForcedGroup<T>::value;
-      hipLaunchKernelGGL((sel_forced_g1_kernel<T, NQ>), dim3((a.n_blk + NQ - 1) / NQ * a.n_kvh), dim3(64), 0, s, a);
+      constexpr int NB = ForcedGroup<T>::value * FW;   // query blocks per workgroup
+      hipLaunchKernelGGL((sel_forced_g1_kernel<T, ForcedGroup<T>::value>), dim3((a.n_blk + NB - 1) / NB * a.n_kvh),
+                         dim3(FW * 64), 0, s, a);
     } else {
       hipLaunchKernelGGL(sel_g1_kernel<T>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
     }
