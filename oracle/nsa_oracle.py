@@ -291,6 +291,65 @@ def route_geometric(pts, blk_cnt, blk_key, cap, top_k, rows=None):
     return sel, dd
 
 
+def check_route_scores(q_rows, k_cmp, blk_key, sel, eps_rel, chunk=1024):
+    """Whole-table check of score-routing rows with one query head per KV head ([Speed3R] 2.1: per
+    (query block, head), the top_k key blocks by the compressed score <q_rh, k_bh>; route_scores is
+    the definition), vectorised so that it covers every row of a full-size table.  The scores here
+    are float64 products of the given rows; a device that ranks float32 products of the same stored
+    values may order blocks whose scores lie within eps = eps_rel * |k-th best score| either way.
+    A row (r, h) passes when:
+      * it lists kk = min(top_k, n_blk) distinct blocks in [0, n_blk), then -1;
+      * every listed block scores at least the k-th best score minus eps;
+      * no unlisted block scores more than the lowest listed score plus eps;
+      * consecutive listed scores never rise by more than eps (descending order up to eps).
+    Returns (rows failing, rows equal to the exact ranking by (score descending, blk_key
+    ascending), the first failing (row, head) pairs)."""
+    import torch
+    q = torch.from_numpy(np.asarray(q_rows, dtype=np.float64))          # [R, H, D]
+    k = torch.from_numpy(np.asarray(k_cmp, dtype=np.float64))           # [n_blk, H, D]
+    key = torch.from_numpy(np.asarray(blk_key, dtype=np.int64))
+    sel_t = torch.from_numpy(np.asarray(sel).astype(np.int64))          # [R, H, top_k]
+    R, H, _ = q.shape
+    n_blk = k.shape[0]
+    top_k = sel_t.shape[2]
+    kk = min(top_k, n_blk)
+    n_bad, n_exact, first = 0, 0, []
+    for h in range(H):
+        kh = k[:, h, :].T.contiguous()                                  # [D, n_blk]
+        for lo in range(0, R, chunk):
+            hi = min(lo + chunk, R)
+            s = q[lo:hi, h, :] @ kh                                     # [c, n_blk] scores
+            row = sel_t[lo:hi, h, :]
+            head = row[:, :kk]
+            ok = (row[:, kk:] == -1).all(1) & ((head >= 0) & (head < n_blk)).all(1)
+            hc = head.clamp(0, n_blk - 1)
+            if kk > 1:
+                srt = torch.sort(hc, dim=1).values
+                ok &= (srt[:, 1:] != srt[:, :-1]).all(1)
+            # the exact ranking: the best kk + 8 by score, equal scores ordered by blk_key
+            m = min(kk + 8, n_blk)
+            vals, idx = torch.topk(s, m, dim=1)
+            o1 = torch.argsort(key[idx], dim=1, stable=True)
+            idx1, v1 = torch.gather(idx, 1, o1), torch.gather(vals, 1, o1)
+            ref = torch.gather(idx1, 1, torch.argsort(-v1, dim=1, stable=True))[:, :kk]
+            kth = vals[:, kk - 1]
+            # rows whose k-th score is tied beyond those m: rank the whole row
+            for i in torch.nonzero((vals[:, m - 1] == kth) & (m < n_blk)).flatten().tolist():
+                ref[i] = torch.from_numpy(np.lexsort((key.numpy(), -s[i].numpy()))[:kk])
+            eps = eps_rel * kth.abs()
+            ls = torch.gather(s, 1, hc)                                  # the listed blocks' scores
+            ok &= (ls >= (kth - eps)[:, None]).all(1)
+            unl = s.scatter(1, hc, float("-inf")).max(1).values if kk < n_blk else torch.full_like(kth, -np.inf)
+            ok &= unl <= ls.min(1).values + eps
+            if kk > 1:
+                ok &= (ls[:, 1:] <= ls[:, :-1] + eps[:, None]).all(1)
+            n_exact += int(((ref == head).all(1) & ok).sum())
+            bad = torch.nonzero(~ok).flatten()
+            n_bad += int(bad.numel())
+            first += [(lo + int(i), h) for i in bad[:max(0, 8 - len(first))]]
+    return n_bad, n_exact, first
+
+
 def check_route_geometric(pts, blk_cnt, blk_key, cap, sel, d2, rows=None, chunk=2048):
     """Whole-table check of a geometric routing result (rows of sel / d2 for the slots `rows`,
     default every slot) against the definition of route_geometric, vectorised so that it covers

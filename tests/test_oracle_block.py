@@ -298,6 +298,72 @@ def test_nsa_forward_gqa_block_equals_token_rows_when_queries_repeat():
 
 
 # ---------------------------------------------------------------------------------------------
+# the whole-table score routing checker (one query head per KV head)
+# ---------------------------------------------------------------------------------------------
+
+def _score_case(seed, n_blk=300, rows=48, heads=3, d=16, integer=False):
+    rng = np.random.default_rng(seed)
+    if integer:
+        q = rng.integers(-1, 2, size=(rows, heads, d)).astype(np.float64)
+        k = rng.integers(-1, 2, size=(n_blk, heads, d)).astype(np.float64)
+    else:
+        q = rng.standard_normal((rows, heads, d))
+        k = rng.standard_normal((n_blk, heads, d))
+    key = rng.permutation(np.arange(n_blk, dtype=np.uint32) * 5 + 1)
+    return q, k, key
+
+
+@pytest.mark.parametrize("case", ["random", "integer_ties", "k_beyond"])
+def test_score_checker_accepts_the_definition(case):
+    q, k, key = _score_case(61, integer=case == "integer_ties", n_blk=5 if case == "k_beyond" else 300)
+    top_k = 8
+    sel, _ = O.route_scores(q, k, key, 1.0, top_k)
+    n_bad, n_exact, _ = O.check_route_scores(q, k, key, sel, 1e-6, chunk=7)
+    assert n_bad == 0 and n_exact == q.shape[0] * q.shape[1]
+
+
+def test_score_checker_tolerates_only_near_ties():
+    """Two adjacent entries swapped pass (not as exact) when their scores lie within eps of each
+    other, and fail when they do not."""
+    q, k, key = _score_case(62)
+    sel, imp = O.route_scores(q, k, key, 1.0, 8)
+    r, h = 5, 1
+    s = imp[r, h]
+    a, b = sel[r, h, 3], sel[r, h, 4]
+    gap = (s[a] - s[b]) / abs(s[sel[r, h, 7]])
+    sel[r, h, [3, 4]] = sel[r, h, [4, 3]]
+    n_bad, n_exact, _ = O.check_route_scores(q, k, key, sel, 2 * gap)
+    assert n_bad == 0 and n_exact == q.shape[0] * q.shape[1] - 1
+    n_bad, _, first = O.check_route_scores(q, k, key, sel, gap / 2)
+    assert n_bad == 1 and first == [(r, h)]
+
+
+@pytest.mark.parametrize("mistake", ["swap_ends", "worse_block", "duplicate", "out_of_range", "tail", "skip_best"])
+def test_score_checker_rejects_planted_mistakes(mistake):
+    q, k, key = _score_case(63, n_blk=6 if mistake == "tail" else 300)
+    top_k = 8
+    sel, imp = O.route_scores(q, k, key, 1.0, top_k)
+    r, h = 7, 2
+    s = imp[r, h]
+    if mistake == "swap_ends":
+        sel[r, h, [0, 5]] = sel[r, h, [5, 0]]
+    elif mistake == "worse_block":
+        sel[r, h, -1] = int(np.argmin(s))
+    elif mistake == "duplicate":
+        sel[r, h, 4] = sel[r, h, 3]
+    elif mistake == "out_of_range":
+        sel[r, h, 2] = k.shape[0]
+    elif mistake == "tail":                    # k beyond the block count: the tail stays -1
+        assert top_k > k.shape[0]
+        sel[r, h, -1] = int(sel[r, h, 0])
+    elif mistake == "skip_best":               # the best block left out, the rest moved up
+        sel[r, h, :-1] = sel[r, h, 1:].copy()
+        sel[r, h, -1] = int(np.argsort(-s, kind="stable")[top_k])
+    n_bad, _, first = O.check_route_scores(q, k, key, sel, 1e-6, chunk=5)
+    assert n_bad == 1 and first == [(r, h)]
+
+
+# ---------------------------------------------------------------------------------------------
 # the whole-table geometric routing checker
 # ---------------------------------------------------------------------------------------------
 
