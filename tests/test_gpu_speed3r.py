@@ -242,6 +242,29 @@ def test_full_size_sampled():
     assert diff[same].max() <= 2e-2
 
 
+def test_full_size_routing_every_row():
+    """Every one of the 409,600 (query block, head) routing rows of the full workload, as the fused
+    pass (the benchmark's call) picks them from the device's own pooling, against the oracle's
+    definition on the oracle's own pooled values (rounded to bf16): a vectorised whole-table check
+    (listed blocks distinct, none below the k-th best score minus eps, no unlisted block above the
+    lowest listed plus eps, descending up to eps; eps = 1e-2 of the k-th score, reading R21)."""
+    import sparse_attention_feed_amd as S
+    say("generate speed3r")
+    w = wl("speed3r")
+    d = to_dev(w)
+    L = d["layout"]
+    say("routing every row", w.n_blk, w.n_kvh)
+    qd, kd, vd = S.pool_blocks(L, d["q"]), S.pool_blocks(L, d["k"]), S.pool_blocks(L, d["v"])
+    _, sel = S.attn_fwd_scores_routed(L, d["q"], d["k"], d["v"], qd, kd, vd, w.top_k, d["gates"])
+    torch.cuda.synchronize()
+    qr, kr, _ = pooled(w)
+    n_bad, n_exact, first = O.check_route_scores(qr, kr, w.blk_key, host(sel), 1e-2)
+    print("speed3r routing, every row: %d failing, %.4f exact" % (n_bad, n_exact / (w.n_blk * w.n_kvh)),
+          flush=True)
+    assert n_bad == 0, first
+    assert n_exact / (w.n_blk * w.n_kvh) >= 0.99        # every row exact when measured
+
+
 def _routed_case(w, qc=None, kc=None):
     """Both paths on the same device inputs: the fused compressed+routing pass and the two-call
     sequence (routing, then the compressed and selected branches)."""
