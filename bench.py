@@ -498,6 +498,23 @@ def run_probes():
                 rec["simd_cycles_per_instruction"] = round(per_iter / (n_valu or n_mfma), 2)
             log(json.dumps(rec))
             out["probes"].append(rec)
+    # HBM: a 4 GiB device-to-device copy (torch's copy kernel), read + write bytes over event time
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    rec = {"probe": "hbm_copy", "bytes_moved": 2 * 4 * n, "ms": round(ms, 4),
+           "gbs": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1)}
+    log(json.dumps(rec))
+    out["probes"].append(rec)
     return out
 
 
