@@ -821,6 +821,10 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
         for (;;) {
           const uint64_t bal = __builtin_amdgcn_ballot_w64(m != 0u);
           if (bal == 0ull) break;
+          // the previous group's last entry does not depend on this round's candidate: its
+          // cross-lane reads go out first, together with the candidate's score and key reads
+          const uint64_t pk = shfl_u64(lst[c].key[E - 1], (l + 48) & 63);
+          const int pi = __shfl(lst[c].idx[E - 1], (l + 48) & 63, 64);
           const uint32_t rowbits = (uint32_t)((bal >> r) & 1ull) | (uint32_t)((bal >> (r + 15)) & 2ull) |
                                    (uint32_t)((bal >> (r + 30)) & 4ull) | (uint32_t)((bal >> (r + 45)) & 8ull);
           const int gs = rowbits != 0u ? __builtin_ctz(rowbits) : g;
@@ -829,18 +833,17 @@ __global__ __launch_bounds__(CW * 64) void cmp_route_g1_kernel(G1Args a) {
           if (rowbits != 0u && g == gs) {
             const int j = __builtin_ctz(m);
             m &= m - 1u;
-            const float v = reinterpret_cast<const float*>(&sc_lds[w][j >> 2][l])[j & 3];
             const int key = 16 * (j >> 2) + 4 * g + (j & 3);
-            if (v >= thr[c]) {
-              ck = rank_key(v, keys_lds[cur][key]);
-              ci = u * KT + key;
-            }
+            const float v = reinterpret_cast<const float*>(&sc_lds[w][j >> 2][l])[j & 3];
+            const uint32_t bk = keys_lds[cur][key];            // read with the score, used if it passes
+            const uint64_t rk = rank_key(v, bk);
+            const bool pass = v >= thr[c];
+            ck = pass ? rk : 0ull;
+            ci = pass ? u * KT + key : -1;
           }
           const int src = r + 16 * gs;
           ck = shfl_u64(ck, src);
           ci = __shfl(ci, src, 64);
-          const uint64_t pk = shfl_u64(lst[c].key[E - 1], (l + 48) & 63);   // previous group's last
-          const int pi = __shfl(lst[c].idx[E - 1], (l + 48) & 63, 64);
           const bool push = g > 0 && ck > pk;
           toplist_insert(lst[c], push ? pk : ck, push ? pi : ci);
         }
