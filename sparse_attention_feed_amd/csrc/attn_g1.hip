@@ -1019,9 +1019,10 @@ void sel_g1_kernel(G1Args a) {
 // query) is the same key set for every query block, and fetching it is most of the branch's cost
 // when each (block, head) wave gathers it alone.  A wave here serves NQ consecutive query blocks
 // of one head: it runs each block over the block's routed blocks outside the range, one block
-// after the other (as sel_g1_kernel does), then gathers the range's valid tokens once per tile for
-// all NQ blocks, each tile continuing every block's online softmax.  The key set of a block is the
-// same union as before (each block once), only taken in another order.
+// after the other (as sel_g1_kernel does); then the FW waves of the workgroup gather the range's
+// valid tokens together, once per tile for all their FW * NQ blocks, each tile continuing every
+// block's online softmax.  Each block's key set is the union of its routed blocks and the range,
+// every block once; only the order in which its keys are visited differs from one packed list.
 
 // query blocks per wave: the most that keep the kernel free of scratch at one wave per SIMD (bf16:
 // 8.3, 7.5 and 7.1 ms for 4, 5 and 6 blocks, one wave per workgroup, at the speed3r shape with the
