@@ -374,3 +374,52 @@ def test_three_branch_layer_block_rows():
     got = host(o)
     assert max_err(got[vm], ref[vm]) <= 2e-2
     assert np.all(got[~vm] == 0)
+
+
+@pytest.mark.parametrize("cap", [1, 4, 8])
+def test_small_block_capacities(cap):
+    """Block capacities below 16 (a 16-row column group of the selected branch then spans one block
+    of cap slots): score routing, the three gated branches, the fused routed entry point and a forced
+    range, each against the oracle on the oracle's pooled values rounded to bf16 (fed to both
+    sides), ragged counts."""
+    import sparse_attention_feed_amd as S
+    rng = np.random.default_rng(200 + cap)
+    n_blk, H, k = 100, 4, 8
+    cnt = rng.integers(1, cap + 1, size=n_blk)
+    w = W.custom_block_workload(210 + cap, cnt, cap, H, H, 64, "bf16", k, routing="scores", q_gran="block",
+                                branches=("cmp", "sel", "loc"), n_gate=3)
+    d = to_dev(w)
+    L = d["layout"]
+    qc, kc, vc = pooled(w)
+    say("small cap", cap)
+    sel = S.route_scores_topk(L, dev(qc), dev(kc), None, k, q_gran=S.Q_BLOCK)
+    torch.cuda.synchronize()
+    ref_sel, imp = O.route_scores(qc, kc, w.blk_key, w.scale, k)
+    assert check_eps_ties(host(sel), ref_sel, imp, k, 1e-2) >= 0.9
+    # the three branches on the oracle's routing rows
+    o = S.attn_fwd(L, S.BR_CMP | S.BR_SEL | S.BR_LOC, d["q"], d["k"], d["v"], q_cmp=dev(qc), k_cmp=dev(kc),
+                   v_cmp=dev(vc), sel=torch.from_numpy(ref_sel).cuda(), top_k=k, sel_groups=H, gates=d["gates"],
+                   q_gran=S.Q_BLOCK)
+    o_cmp, _ = O.attn_branch(O.CMP, qc, kc, vc, w.blk_cnt, w.blk_cap, w.scale, q_gran="block")
+    o_sel, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=ref_sel, q_gran="block")
+    o_loc, _ = O.attn_branch(O.LOC, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale)
+    g3 = d["gates"]
+    # the fused routed entry point (its own routing) against the two calls
+    g2 = g3[:, :, :2].contiguous()
+    o_f, sel_f = S.attn_fwd_scores_routed(L, d["q"], d["k"], d["v"], dev(qc), dev(kc), dev(vc), k, g2)
+    o_2 = S.attn_fwd(L, S.BR_CMP | S.BR_SEL, d["q"], d["k"], d["v"], q_cmp=dev(qc), k_cmp=dev(kc), v_cmp=dev(vc),
+                     sel=sel, top_k=k, sel_groups=H, gates=g2, q_gran=S.Q_BLOCK)
+    # a forced range on the oracle's rows
+    fr = (10, 37)
+    o_fr = S.attn_fwd(L, S.BR_SEL, d["q"], d["k"], d["v"], sel=torch.from_numpy(ref_sel).cuda(), top_k=k,
+                      sel_groups=H, q_gran=S.Q_BLOCK, forced=fr)
+    torch.cuda.synchronize()
+    vm = w.valid_mask()
+    ref = O.gate_combine([o_cmp, o_sel, o_loc], w.gates)
+    assert max_err(host(o)[vm], ref[vm]) <= 2e-2
+    assert np.all(host(o)[~vm] == 0)
+    np.testing.assert_array_equal(host(sel_f), host(sel))
+    assert max_err(host(o_f)[vm], host(o_2)[vm]) <= 2e-2
+    ref_fr, _ = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=ref_sel, q_gran="block",
+                              forced=fr)
+    assert max_err(host(o_fr), ref_fr) <= 2e-2
