@@ -291,62 +291,81 @@ def route_geometric(pts, blk_cnt, blk_key, cap, top_k, rows=None):
     return sel, dd
 
 
-def check_route_scores(q_rows, k_cmp, blk_key, sel, eps_rel, chunk=1024):
-    """Whole-table check of score-routing rows with one query head per KV head ([Speed3R] 2.1: per
-    (query block, head), the top_k key blocks by the compressed score <q_rh, k_bh>; route_scores is
-    the definition), vectorised so that it covers every row of a full-size table.  The scores here
-    are float64 products of the given rows; a device that ranks float32 products of the same stored
-    values may order blocks whose scores lie within eps = eps_rel * |k-th best score| either way.
-    A row (r, h) passes when:
+def check_route_scores(q_rows, k_cmp, blk_key, sel, eps_rel, chunk=1024, scale=None, row_valid=None):
+    """Whole-table check of score-routing rows against the definition of route_scores, vectorised so
+    that it covers every row of a full-size table.
+      * one query head per KV head ([Speed3R] 2.1): the importance of block b for (row r, head h) is
+        the compressed score <q_rh, k_bh>;
+      * several query heads per KV head ([LSRM-cn] "standard NSA" selection): the importance for
+        (row r, KV group j) is the group's summed softmax probability,
+        sum over its heads h of exp(scale <q_rh, k_bj> - lse_rh), where lse_rh is the compressed
+        branch's log-partition function over all blocks (computed here from the same products).
+    Importances are float64 functions of the given rows; a device that ranks float32 values of the
+    same stored inputs may order blocks whose importances lie within eps = eps_rel * |k-th best|
+    either way.  A row (r, j) passes when:
+      * rows with row_valid False hold -1 throughout;
       * it lists kk = min(top_k, n_blk) distinct blocks in [0, n_blk), then -1;
-      * every listed block scores at least the k-th best score minus eps;
-      * no unlisted block scores more than the lowest listed score plus eps;
-      * consecutive listed scores never rise by more than eps (descending order up to eps).
-    Returns (rows failing, rows equal to the exact ranking by (score descending, blk_key
-    ascending), the first failing (row, head) pairs)."""
+      * every listed block's importance is at least the k-th best minus eps;
+      * no unlisted block's importance exceeds the lowest listed one plus eps;
+      * consecutive listed importances never rise by more than eps (descending order up to eps).
+    Returns (valid rows failing, valid rows equal to the exact ranking by (importance descending,
+    blk_key ascending), the first failing (row, group) pairs)."""
     import torch
-    q = torch.from_numpy(np.asarray(q_rows, dtype=np.float64))          # [R, H, D]
-    k = torch.from_numpy(np.asarray(k_cmp, dtype=np.float64))           # [n_blk, H, D]
+    q = torch.from_numpy(np.asarray(q_rows, dtype=np.float64))          # [R, Hq, D]
+    k = torch.from_numpy(np.asarray(k_cmp, dtype=np.float64))           # [n_blk, Hkv, D]
     key = torch.from_numpy(np.asarray(blk_key, dtype=np.int64))
-    sel_t = torch.from_numpy(np.asarray(sel).astype(np.int64))          # [R, H, top_k]
-    R, H, _ = q.shape
-    n_blk = k.shape[0]
+    sel_t = torch.from_numpy(np.asarray(sel).astype(np.int64))          # [R, Hkv, top_k]
+    R, Hq, _ = q.shape
+    n_blk, Hkv, _ = k.shape
+    G = Hq // Hkv
+    if G > 1 and scale is None:
+        raise ValueError("grouped score routing needs the softmax scale")
+    rv = torch.ones(R, dtype=torch.bool) if row_valid is None else torch.from_numpy(np.asarray(row_valid, bool))
     top_k = sel_t.shape[2]
     kk = min(top_k, n_blk)
     n_bad, n_exact, first = 0, 0, []
-    for h in range(H):
-        kh = k[:, h, :].T.contiguous()                                  # [D, n_blk]
+    for j in range(Hkv):
+        kj = k[:, j, :].T.contiguous()                                  # [D, n_blk]
         for lo in range(0, R, chunk):
             hi = min(lo + chunk, R)
-            s = q[lo:hi, h, :] @ kh                                     # [c, n_blk] scores
-            row = sel_t[lo:hi, h, :]
+            if G == 1:
+                s = q[lo:hi, j, :] @ kj                                 # [c, n_blk] scores
+            else:
+                s = torch.zeros((hi - lo, n_blk), dtype=torch.float64)
+                for h in range(j * G, (j + 1) * G):
+                    z = scale * (q[lo:hi, h, :] @ kj)
+                    s += torch.exp(z - torch.logsumexp(z, dim=1, keepdim=True))
+            row = sel_t[lo:hi, j, :]
+            v = rv[lo:hi]
+            pad_ok = (row == -1).all(1)
             head = row[:, :kk]
             ok = (row[:, kk:] == -1).all(1) & ((head >= 0) & (head < n_blk)).all(1)
             hc = head.clamp(0, n_blk - 1)
             if kk > 1:
                 srt = torch.sort(hc, dim=1).values
                 ok &= (srt[:, 1:] != srt[:, :-1]).all(1)
-            # the exact ranking: the best kk + 8 by score, equal scores ordered by blk_key
+            # the exact ranking: the best kk + 8 by importance, equal values ordered by blk_key
             m = min(kk + 8, n_blk)
             vals, idx = torch.topk(s, m, dim=1)
             o1 = torch.argsort(key[idx], dim=1, stable=True)
             idx1, v1 = torch.gather(idx, 1, o1), torch.gather(vals, 1, o1)
             ref = torch.gather(idx1, 1, torch.argsort(-v1, dim=1, stable=True))[:, :kk]
             kth = vals[:, kk - 1]
-            # rows whose k-th score is tied beyond those m: rank the whole row
-            for i in torch.nonzero((vals[:, m - 1] == kth) & (m < n_blk)).flatten().tolist():
+            # rows whose k-th value is tied beyond those m: rank the whole row
+            for i in torch.nonzero((vals[:, m - 1] == kth) & (m < n_blk) & v).flatten().tolist():
                 ref[i] = torch.from_numpy(np.lexsort((key.numpy(), -s[i].numpy()))[:kk])
             eps = eps_rel * kth.abs()
-            ls = torch.gather(s, 1, hc)                                  # the listed blocks' scores
+            ls = torch.gather(s, 1, hc)                                  # the listed blocks' values
             ok &= (ls >= (kth - eps)[:, None]).all(1)
             unl = s.scatter(1, hc, float("-inf")).max(1).values if kk < n_blk else torch.full_like(kth, -np.inf)
             ok &= unl <= ls.min(1).values + eps
             if kk > 1:
                 ok &= (ls[:, 1:] <= ls[:, :-1] + eps[:, None]).all(1)
-            n_exact += int(((ref == head).all(1) & ok).sum())
+            ok = torch.where(v, ok, pad_ok)
+            n_exact += int(((ref == head).all(1) & ok & v).sum())
             bad = torch.nonzero(~ok).flatten()
             n_bad += int(bad.numel())
-            first += [(lo + int(i), h) for i in bad[:max(0, 8 - len(first))]]
+            first += [(lo + int(i), j) for i in bad[:max(0, 8 - len(first))]]
     return n_bad, n_exact, first
 
 

@@ -363,6 +363,47 @@ def test_score_checker_rejects_planted_mistakes(mistake):
     assert n_bad == 1 and first == [(r, h)]
 
 
+def _grouped_score_case(seed, n_blk=120, rows=40, hkv=2, g=4, d=8, top_k=6):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((rows, hkv * g, d))
+    k = rng.standard_normal((n_blk, hkv, d))
+    key = rng.permutation(np.arange(n_blk, dtype=np.uint32) * 3 + 2)
+    scale = 0.35
+    valid = np.ones(rows, dtype=bool)
+    valid[::7] = False
+    # the compressed branch's lse of each row (attention over every pooled block)
+    lse = np.stack([O.attend(q[r], k, k, scale)[1] for r in range(rows)])
+    sel, imp = O.route_scores(q, k, key, scale, top_k, lse=lse, row_valid=valid)
+    return q, k, key, scale, valid, sel, imp
+
+
+@pytest.mark.parametrize("n_blk", [120, 5])
+def test_grouped_score_checker_accepts_the_definition(n_blk):
+    """Several query heads per KV head: the checker's own importances (softmax over all blocks,
+    summed over the group) agree with route_scores fed the compressed branch's lse; padding rows
+    hold -1; k beyond the block count leaves a -1 tail."""
+    q, k, key, scale, valid, sel, _ = _grouped_score_case(64, n_blk=n_blk)
+    n_bad, n_exact, _ = O.check_route_scores(q, k, key, sel, 1e-9, chunk=9, scale=scale, row_valid=valid)
+    assert n_bad == 0 and n_exact == int(valid.sum()) * k.shape[1]
+
+
+@pytest.mark.parametrize("mistake", ["swap_ends", "worse_block", "duplicate", "padding_filled"])
+def test_grouped_score_checker_rejects_planted_mistakes(mistake):
+    q, k, key, scale, valid, sel, imp = _grouped_score_case(65)
+    r, j = 3, 1
+    if mistake == "swap_ends":
+        sel[r, j, [0, 5]] = sel[r, j, [5, 0]]
+    elif mistake == "worse_block":
+        sel[r, j, -1] = int(np.argmin(imp[r, j]))
+    elif mistake == "duplicate":
+        sel[r, j, 2] = sel[r, j, 1]
+    else:
+        r = int(np.nonzero(~valid)[0][1])
+        sel[r, j, 0] = 0
+    n_bad, _, first = O.check_route_scores(q, k, key, sel, 1e-9, chunk=9, scale=scale, row_valid=valid)
+    assert n_bad == 1 and first == [(r, j)]
+
+
 # ---------------------------------------------------------------------------------------------
 # the whole-table geometric routing checker
 # ---------------------------------------------------------------------------------------------
