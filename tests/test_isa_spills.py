@@ -28,7 +28,7 @@ KNOWN_TILE_LOOP_SPILLS = {"route_g1_kernelIDF16bLi64ELi1E", "route_g1_kernelIfLi
 
 def _asm(src, out_dir):
     out = os.path.join(out_dir, os.path.splitext(src)[0] + ".s")
-    cmd = ([nsa_build.HIPCC] + nsa_build.FLAGS + ["-x", "hip", "-S", "--cuda-device-only",
+    cmd = ([nsa_build.HIPCC] + nsa_build.flags_for(src) + ["-x", "hip", "-S", "--cuda-device-only",
                                                   os.path.join(CSRC, src), "-o", out])
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
