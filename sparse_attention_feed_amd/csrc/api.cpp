@@ -440,6 +440,9 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   a.branches = branches;
   a.n_words = (L->n_blk + 31) / 32;
   a.sel_per_block = q_gran == NSA_Q_BLOCK ? 1 : 0;
+  // gate channels in the order CMP, SEL, LOC among the named branches (whatever each launch runs)
+  a.ch_sel = (branches & NSA_BR_CMP) ? 1 : 0;
+  a.ch_loc = n_named - 1;
   {
     // distinct selected blocks of one query block: one routing row per slot, or one per block
     long long u = (long long)(a.sel_per_block ? 1 : L->blk_cap) * (a.top_k > 0 ? a.top_k : 1);
@@ -447,11 +450,15 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   }
   // Test hook (NSA_TEST_RING_STALL=1): the selected branch's tile ring waits for one count more
   // than ever arrives, with a short bound, so the bounded-wait path runs (output NaN, no hang).
+  // It and NSA_SEL_RING=1 keep the selected branch in the fused kernel's tile ring.
+  bool sel_ring;
   {
     const char* e = getenv("NSA_TEST_RING_STALL");
     const bool stall = e != nullptr && e[0] == '1';
     a.ring_spins = stall ? 64 : (1 << 16);
     a.ring_stall = stall ? 1 : 0;
+    const char* f = getenv("NSA_SEL_RING");
+    sel_ring = stall || (f != nullptr && f[0] == '1');
   }
   a.q_blk0 = q_lo;
   a.n_qblk = q_hi - q_lo;
@@ -460,7 +467,23 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   const size_t lds = nsa::attn_lds_bytes(dtype == NSA_BF16, a);
   if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "%s: LDS need %zu bytes exceeds 160 KiB", fn, lds);
   NSA_FORCED_FAILURE(fn);
-  if (q_gran == NSA_Q_TOKEN) return hip_status(nsa::launch_attn(dtype == NSA_BF16, a, stream), fn);
+  if (q_gran == NSA_Q_TOKEN) {
+    // bf16: the selected branch runs in its own kernel of wave-owned token clusters, after the
+    // fused kernel has written the other named branches' gated sum (which it then adds to)
+    if (dtype != NSA_BF16 || !(branches & NSA_BR_SEL) || sel_ring)
+      return hip_status(nsa::launch_attn(dtype == NSA_BF16, a, stream), fn);
+    if (nsa::sel_wave_lds(a) > 160 * 1024)
+      return fail(NSA_ERR_UNSUPPORTED, "%s: LDS need %zu bytes exceeds 160 KiB", fn, nsa::sel_wave_lds(a));
+    const uint32_t rest = branches & (NSA_BR_CMP | NSA_BR_LOC);
+    if (rest) {
+      nsa::AttnArgs f = a;
+      f.branches = rest;
+      f.top_k = 0;
+      hipError_t e = nsa::launch_attn(1, f, stream);
+      if (e != hipSuccess) return hip_status(e, fn);
+    }
+    return hip_status(nsa::launch_sel_wave(a, rest ? 1 : 0, stream), fn);
+  }
   // block rows: the selected and local branches (token queries, the block's routing row) in the
   // fused kernel, reading the gate channels after the compressed one; then the compressed branch
   // of the pooled queries, adding each block's gated result to its tokens
@@ -468,9 +491,7 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   const bool has_cmp = (branches & NSA_BR_CMP) != 0;
   if (rest) {
     nsa::AttnArgs f = a;
-    f.branches = rest;
-    if (gate_logits != nullptr && has_cmp)
-      f.gates = static_cast<const char*>(gate_logits) + (dtype == NSA_BF16 ? 2 : 4);
+    f.branches = rest;   // gate channels stay those of the whole branch set (a.ch_sel, a.ch_loc)
     hipError_t e = nsa::launch_attn(dtype == NSA_BF16, f, stream);
     if (e != hipSuccess) return hip_status(e, fn);
   }

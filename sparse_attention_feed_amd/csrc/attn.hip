@@ -561,7 +561,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     const RingBufs<T> rb{smem, 2 * (int)sizeof(TileBuf<T>) + off_ring};
     run_tiles_ring<T, NT, TPW, R>(rb, ring_ctr, ring_ctr + R, ring_ctr + 2 * R, a.ring_spins, a.ring_stall, src, n_union,
                                   part, st, qf);   // ends with a barrier
-    finish_all((a.branches & 1) ? 1 : 0);
+    finish_all(a.ch_sel);
   }
 
   // ---- local branch: the query's own block ----
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
     AllPart part{n_valid};
     // the own block is a key block only when it lies in the key range (an empty key set adds 0)
     run_tiles<T, NT, TPW>(buf, src, (b >= a.kv_lo && b < a.kv_hi) ? 1 : 0, part, st, qf);
-    finish_all(n_named - 1);
+    finish_all(a.ch_loc);
   }
 
   // ---- compressed branch: every pooled block ----
@@ -608,6 +608,243 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
       for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(0.f);
     }
     if (a.lse && g == 0) a.lse[row * a.n_qh + hh] = -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// selected branch with wave-owned token clusters (bf16, per-token routing rows)
+// ---------------------------------------------------------------------------------------------
+//
+// One wave per (8 consecutive slots of a block, KV head), no workgroup barrier and no shared
+// staging.  Slots are stored in Morton order, so 8 consecutive slots are spatial neighbours whose
+// routing rows largely agree: the wave walks the union of its 8 rows once, in ascending block
+// order, and each block's tile serves the tokens that selected it (LSRM pages, section 方法: the
+// selected active blocks give each query its fine detail).  A tile's K rows are loaded from
+// global memory straight into the MFMA A-operand layout (one 16-byte load per lane and 16-key
+// step).  V^T is formed in registers too: an MFMA of the V rows against a 0/1 selector matrix
+// gives D[key][d] = V[key][d] exactly (one nonzero product per sum, fp32), and the MFMA output
+// layout (lane: four consecutive keys of one column) is the key order in which the softmax hands
+// over its probabilities, so the converted outputs are the V^T fragments as they are.
+// The result is gated and written to o, or added to what o holds (accumulate).
+
+constexpr int SEL_TPW = 8;   // tokens (consecutive slots) per wave
+constexpr int SEL_WPG = 4;   // waves per workgroup (independent)
+constexpr int SEL_MAXE = SEL_TPW;   // routing entries per lane: 8 rows x top_k <= 64 entries / 64 lanes
+
+// LDS bytes of one wave's tables: bitmap and per-word prefix (n_words each), union list and
+// per-block token masks (ucap each).
+__host__ __device__ inline int sel_wave_lds_bytes(int n_words, int ucap) {
+  return ((2 * n_words + 2 * ucap) * 4 + 15) & ~15;
+}
+
+// Orders this wave's LDS accesses (all lanes) before the next ones.  A wave's LDS instructions
+// execute in order, so only compiler reordering has to be stopped.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int wave_exclusive_scan(int x, int& total) {
+  const int l = lane_id();
+  int inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (l >= o) inc += y;
+  }
+  total = __shfl(inc, 63, 64);
+  return inc - x;
+}
+
+struct SelRaw {                 // one tile's K and V rows as loaded: 16 keys per step
+  Frag8<bf16> k[4], v[4];
+};
+
+__global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, int accumulate, int ucap) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const int cap = a.cap;
+  const int nclu = (cap + SEL_TPW - 1) / SEL_TPW;
+  const int n_waves = a.n_qblk * nclu * a.n_kvh;
+  const int wv = xcd_remap(blockIdx.x, gridDim.x) * SEL_WPG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv >= n_waves) return;                     // waves never wait for each other
+  const int c = wv % nclu, j = (wv / nclu) % a.n_kvh;
+  const int b = a.q_blk0 + wv / (nclu * a.n_kvh);
+  const int s0 = c * SEL_TPW;
+  const int cnt = a.blk_cnt[b];
+  const int n_valid = min(max(cnt - s0, 0), SEL_TPW);
+  const int hh = j * GRP + r;
+  const int kvs = a.n_kvh * HD;
+  bf16* o = reinterpret_cast<bf16*>(a.o);
+
+  TokState st[SEL_TPW];
+#pragma unroll
+  for (int t = 0; t < SEL_TPW; ++t) tok_init(st[t]);
+
+  if (n_valid > 0) {
+    // queries of the wave's tokens (padding slots read a valid row of the block; never used)
+    QF<bf16> qf[SEL_TPW];
+    {
+      const bf16* q = reinterpret_cast<const bf16*>(a.q);
+      const float c2 = a.scale * kLog2e;
+      Frag8<bf16> raw[SEL_TPW];
+#pragma unroll
+      for (int t = 0; t < SEL_TPW; ++t)
+        raw[t] = load_q8(q + ((b * cap + s0 + min(t, n_valid - 1)) * a.n_qh + hh) * HD + 8 * g);
+#pragma unroll
+      for (int t = 0; t < SEL_TPW; ++t) qf[t] = make_qf<bf16>(raw[t], c2, t < n_valid);
+    }
+
+    // routing entries of the wave's rows (entry e: row e / top_k, position e % top_k) and their
+    // blocks' token counts, all loads issued at once
+    const int kk = a.top_k;
+    const int grp = a.sel_groups == 1 ? 0 : j;
+    const int ne = n_valid * kk;
+    int eblk[SEL_MAXE], ecnt[SEL_MAXE];
+#pragma unroll
+    for (int i = 0; i < SEL_MAXE; ++i) {
+      const int e = l + 64 * i;
+      const int t = e / kk;
+      eblk[i] = e < ne ? a.sel[((b * cap + s0 + t) * a.sel_groups + grp) * kk + (e - t * kk)] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < SEL_MAXE; ++i) ecnt[i] = (eblk[i] >= 0 && eblk[i] < a.n_blk) ? a.blk_cnt[eblk[i]] : 0;
+
+    // union of the rows in this wave's LDS tables: bitmap, per-word prefix, list, token masks
+    const int nw = a.n_words;
+    unsigned char* tab = smem + (threadIdx.x >> 6) * sel_wave_lds_bytes(nw, ucap);
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(tab);
+    int* wpre = reinterpret_cast<int*>(tab + nw * 4);
+    int* ulist = reinterpret_cast<int*>(tab + nw * 8);
+    uint32_t* umask = reinterpret_cast<uint32_t*>(tab + nw * 8 + ucap * 4);
+    for (int i = l; i < nw; i += 64) bitmap[i] = 0u;
+    wave_lds_order();
+#pragma unroll
+    for (int i = 0; i < SEL_MAXE; ++i)
+      if (eblk[i] >= 0 && eblk[i] < a.n_blk) atomicOr(&bitmap[eblk[i] >> 5], 1u << (eblk[i] & 31));
+    wave_lds_order();
+    const int per = (nw + 63) / 64, w0 = l * per;
+    int mine = 0;
+    for (int i = 0; i < per; ++i)
+      if (w0 + i < nw) mine += __builtin_popcount(bitmap[w0 + i]);
+    int n_union;
+    int base = wave_exclusive_scan(mine, n_union);
+    for (int i = 0; i < per; ++i) {
+      const int wi = w0 + i;
+      if (wi < nw) {
+        wpre[wi] = base;
+        base += __builtin_popcount(bitmap[wi]);
+      }
+    }
+    for (int i = l; i < n_union; i += 64) umask[i] = 0u;
+    wave_lds_order();
+#pragma unroll
+    for (int i = 0; i < SEL_MAXE; ++i) {
+      const int blk = eblk[i];
+      if (blk >= 0 && blk < a.n_blk) {
+        const int wi = blk >> 5;
+        const int u = wpre[wi] + __builtin_popcount(bitmap[wi] & ((1u << (blk & 31)) - 1u));
+        ulist[u] = blk | (ecnt[i] << 16);
+        atomicOr(&umask[u], 1u << ((l + 64 * i) / kk));
+      }
+    }
+    wave_lds_order();
+
+    // 0/1 selectors: sel_d[dt] is B[k][n] = (k == n + 16 dt) in the B-operand layout
+    Frag8<bf16> bsel[2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bsel[dt].v[e] = (8 * g + e == r + 16 * dt) ? (bf16)1.0f : (bf16)0.0f;
+
+    const bf16* kb = reinterpret_cast<const bf16*>(a.k) + j * HD;
+    const bf16* vb = reinterpret_cast<const bf16*>(a.v) + j * HD;
+    // rows past the block's count repeat its last valid row (masked by the -inf seed); the
+    // block's base is wave-uniform and the lane's part a 32-bit offset
+    const unsigned kvs2 = 2u * kvs, goff = 16u * g;   // row stride and the lane's part, in bytes
+    auto load_tile = [&](int u, SelRaw& x) {
+      const int ent = __builtin_amdgcn_readfirstlane(ulist[u]);
+      const int blk = ent & 0xFFFF, last = max((ent >> 16) - 1, 0);
+      const size_t base = (size_t)(blk * cap) * kvs2;
+      const char* kt = reinterpret_cast<const char*>(kb) + base;
+      const char* vt = reinterpret_cast<const char*>(vb) + base;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const unsigned off = __umul24((unsigned)min(16 * q4 + r, last), kvs2) + goff;
+        x.k[q4].v = *reinterpret_cast<const bf16x8*>(kt + off);
+        x.v[q4].v = *reinterpret_cast<const bf16x8*>(vt + off);
+      }
+    };
+    auto step = [&](int u, SelRaw& cur, SelRaw& nxt) {
+      // V^T fragments of tile u: vf[dt][h] takes keys 32h + 4g + i (from 16-key step 2h) and
+      // 32h + 16 + 4g + i (step 2h + 1) of head-dim column 16 dt + r
+      Frag8<bf16> vf[2][2];
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 d0 = mma16(cur.v[2 * h], bsel[dt], zero);
+          const f32x4 d1 = mma16(cur.v[2 * h + 1], bsel[dt], zero);
+          const bf16x2 p0 = __builtin_convertvector((f32x2){d0[0], d0[1]}, bf16x2);
+          const bf16x2 p1 = __builtin_convertvector((f32x2){d0[2], d0[3]}, bf16x2);
+          const bf16x2 p2 = __builtin_convertvector((f32x2){d1[0], d1[1]}, bf16x2);
+          const bf16x2 p3 = __builtin_convertvector((f32x2){d1[2], d1[3]}, bf16x2);
+          vf[dt][h].v = (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+      const int nk = ulist[u] >> 16;
+      const uint32_t pm = __builtin_amdgcn_readfirstlane(umask[u]);
+      if (u + 1 < n_union) load_tile(u + 1, nxt);
+      f32x4 cm[4];
+      if (nk < TILE) tile_mask(nk, cm);
+      tile_masked<bf16, SEL_TPW>(st, qf, pm, cur.k, vf, cm, nk == TILE);
+    };
+    SelRaw ra, rb;
+    if (n_union > 0) load_tile(0, ra);
+    for (int u = 0; u < n_union; u += 2) {
+      step(u, ra, rb);
+      if (u + 1 < n_union) step(u + 1, rb, ra);
+    }
+  }
+
+  // gate, then write or add; padding slots get 0 (write) or are left alone (add)
+  bf16 gl[SEL_TPW];
+  if (a.gates) {
+#pragma unroll
+    for (int t = 0; t < SEL_TPW; ++t) {
+      const int row = b * cap + min(s0 + t, cap - 1);
+      gl[t] = reinterpret_cast<const bf16*>(a.gates)[(row * a.n_qh + hh) * a.n_gch + a.ch_sel];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < SEL_TPW; ++t) {
+    const int slot = s0 + t;
+    if (slot >= cap) continue;
+    const int row = b * cap + slot;
+    bf16x4* dst = reinterpret_cast<bf16x4*>(o + (row * a.n_qh + hh) * HD + 4 * g);
+    if (t >= n_valid) {
+      if (!accumulate) {
+        const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+        dst[0] = z;
+        dst[4] = z;
+      }
+      if (a.lse && g == 0) a.lse[row * a.n_qh + hh] = -INFINITY;
+      continue;
+    }
+    const float wgt = a.gates ? sigmoidf_(to_f32(gl[t])) : 1.f;
+    f32x4 res[2];
+    tok_finish(st[t], res, wgt, a.lse ? a.lse + row * a.n_qh + hh : nullptr);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      f32x4 acc = res[dt];
+      if (accumulate) {
+        const bf16x4 prev = dst[4 * dt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += (float)prev[i];
+      }
+      dst[4 * dt] = (bf16x4){(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+    }
   }
 }
 
@@ -803,6 +1040,11 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+int sel_wave_ucap(const AttnArgs& a) {
+  const long long u = (long long)SEL_TPW * (a.top_k > 0 ? a.top_k : 1);
+  return (int)(u < a.n_blk ? u : a.n_blk);
+}
+
 template <typename T>
 hipError_t launch_cmp_pooled_t(const AttnArgs& a, int accumulate, int gate_ch, hipStream_t s) {
   constexpr int WAVES = Shape<T>::WAVES, TPW = Shape<T>::TPW, NT = WAVES * 64;
@@ -835,6 +1077,25 @@ size_t attn_lds_bytes(int is_bf16, const AttnArgs& a) {
 
 hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s) {
   return is_bf16 ? launch_attn_t<bf16>(a, s) : launch_attn_t<float>(a, s);
+}
+
+size_t sel_wave_lds(const AttnArgs& a) {
+  return (size_t)SEL_WPG * sel_wave_lds_bytes(a.n_words, sel_wave_ucap(a));
+}
+
+hipError_t launch_sel_wave(const AttnArgs& a, int accumulate, hipStream_t s) {
+  const int nclu = (a.cap + SEL_TPW - 1) / SEL_TPW;
+  const long long waves = (long long)a.n_qblk * nclu * a.n_kvh;
+  if (waves == 0) return hipSuccess;
+  const int nwg = (int)((waves + SEL_WPG - 1) / SEL_WPG);
+  const size_t lds = sel_wave_lds(a);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sel_wave_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(sel_wave_kernel, dim3(nwg), dim3(SEL_WPG * 64), lds, s, a, accumulate, sel_wave_ucap(a));
+  return hipGetLastError();
 }
 
 hipError_t launch_cmp_pooled(int is_bf16, const AttnArgs& a, int accumulate, int gate_ch, hipStream_t s) {

@@ -28,6 +28,7 @@ struct AttnArgs {
   int q_blk0, n_qblk;  // query blocks [q_blk0, q_blk0 + n_qblk)
   int kv_lo, kv_hi;    // key blocks of the compressed and local branches: [kv_lo, kv_hi)
   int sel_per_block;   // routing rows are per query block ([n_blk][sel_groups][top_k]), not per slot
+  int ch_sel, ch_loc;  // gate channels of the selected and local branches (the compressed one is 0)
 };
 
 struct DenseArgs {
@@ -100,6 +101,11 @@ hipError_t launch_attn_g1_routed(int is_bf16, const G1Args& a, hipStream_t s);
 
 size_t attn_lds_bytes(int is_bf16, const AttnArgs& a);
 hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s);
+// selected branch (bf16, per-token routing rows) by wave-owned clusters of 8 consecutive slots:
+// o = (accumulate ? o : 0) + sigmoid(gates[.., a.ch_sel]) * result (no gate when a.gates is NULL);
+// padding slots 0 when not accumulating; lse when a.lse is set.  Query blocks [q_blk0, +n_qblk).
+size_t sel_wave_lds(const AttnArgs& a);
+hipError_t launch_sel_wave(const AttnArgs& a, int accumulate, hipStream_t s);
 // compressed branch of pooled queries (a.q = [n_blk][n_qh][D]), each block's result given to its
 // valid tokens: o = (accumulate ? o : 0) + sigmoid(gates[.., gate_ch]) * result (no gate when
 // a.gates is NULL), padding slots 0 when not accumulating; lse [n_blk][n_qh] when a.lse is set

@@ -567,6 +567,39 @@ def test_ring_wait_bound_ends_with_nan(monkeypatch):
     assert max_err(host(o), ref) <= tol(w)
 
 
+@pytest.mark.parametrize("name", ["stage2_small", "k48_cap16", "ragged_cap16"])
+def test_selected_branch_paths_agree(name, monkeypatch):
+    """bf16 token queries take the selected branch to its own kernel (wave-owned token clusters)
+    after the fused kernel's other branches; NSA_SEL_RING=1 keeps it in the fused kernel's tile
+    ring.  Both orders of the same sums meet the oracle, alone and in the gated three-branch layer,
+    and agree with each other to bf16 rounding of the output."""
+    import sparse_attention_feed_amd as S
+    w = get(name)
+    d = to_dev(w)
+    kc, vc, sel, kc_d, vc_d, sel_d = _branch_inputs(w, d)
+    ref_sel = O.attn_branch(O.SEL, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale, sel=sel)[0]
+    ref_outs = [O.attn_branch(O.CMP, w.q, kc.astype(np.float64), vc.astype(np.float64), w.blk_cnt, w.blk_cap,
+                              w.scale)[0], ref_sel,
+                O.attn_branch(O.LOC, w.q, w.k, w.v, w.blk_cnt, w.blk_cap, w.scale)[0]]
+    ref = O.gate_combine(ref_outs, w.gates)
+    res = {}
+    for ring in ("0", "1"):
+        monkeypatch.setenv("NSA_SEL_RING", ring)
+        say("selected branch path", name, "ring", ring)
+        o1 = S.attn_fwd(d["layout"], S.BR_SEL, d["q"], d["k"], d["v"], sel=sel_d, top_k=w.top_k)
+        o3 = S.attn_fwd(d["layout"], 7, d["q"], d["k"], d["v"], k_cmp=kc_d, v_cmp=vc_d, sel=sel_d,
+                        top_k=w.top_k, gates=d["gates"])
+        torch.cuda.synchronize()
+        res[ring] = (host(o1), host(o3))
+        assert max_err(res[ring][0], ref_sel) <= tol(w)
+        assert max_err(res[ring][1], ref) <= tol(w)
+        vm = w.valid_mask()
+        assert np.all(res[ring][0][~vm] == 0) and np.all(res[ring][1][~vm] == 0)
+    monkeypatch.delenv("NSA_SEL_RING")
+    assert max_err(res["0"][0], res["1"][0]) <= 2.0 ** -7
+    assert max_err(res["0"][1], res["1"][1]) <= 2.0 ** -6
+
+
 def test_repeat_runs_bit_identical():
     import sparse_attention_feed_amd as S
     w = wl("large_small")
