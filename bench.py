@@ -5,11 +5,13 @@ K and V, exact geometric routing (top-32 blocks per token), and the fused compre
 local attention with the three-way sigmoid gate.  Inputs are generated on the host (seeded) and
 copied to HBM before timing.
 
-Prints ONE JSON line.  Besides the throughput it reports, for the dominant kernel (the fused
-attention), achieved algorithmic TFLOP/s against the bf16 MFMA peak, the per-kernel times measured
-with HIP events on the launch stream, per-branch throughput, the fp64 CPU oracle timed on the
-host's cores on a bounded sample of the same workload, and the same step measurements for the
-other four workloads (stage2, speed3r, dense, tiny) with fewer steps.
+Prints ONE JSON line.  Besides the throughput it reports, for the dominant stage (the attention
+call: with bf16 inputs the fused compressed + local kernel, then the selected-branch kernel that
+adds its gated result; `roofline.launches` names them), achieved algorithmic TFLOP/s against the
+bf16 MFMA peak, the per-stage times measured with HIP events on the launch stream, per-branch
+throughput, the fp64 CPU oracle timed on the host's cores on a bounded sample of the same workload,
+and the same step measurements for the other four workloads (stage2, speed3r, dense, tiny) with
+fewer steps.
 """
 import argparse
 import json
@@ -55,6 +57,17 @@ def _source_digest():
         with open(os.path.join(ROOT, "sparse_attention_feed_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+# the kernels one call of each timed attention stage launches, in order
+LAUNCHES = {
+    "attn_fused": {"bf16": ["nsa_attn_kernel (compressed + local branches, writes o)",
+                            "sel_wave_kernel (selected branch, adds its gated result to o)"],
+                   "f32": ["nsa_attn_kernel (all three branches)"]},
+    "attn_routed": {"bf16": ["cmp_route_g1_kernel (compressed branch + score routing)",
+                             "sel_g1_kernel (selected branch, adds to o)"]},
+    "dense_gated_xattn": {"bf16": ["dense_xattn_kernel"]},
+}
 
 
 def measured_traffic(kernel, config):
@@ -430,6 +443,7 @@ def run_config(name, w, steps, warmup, breakdown_on, torch, S, dev):
         "config": cfg,
         "roofline": {
             "kernel": dominant,
+            "launches": LAUNCHES.get(dominant, {}).get("bf16" if w.dtype == "bf16" else "f32"),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": peak,

@@ -84,7 +84,8 @@ def spills(tmp_path_factory):
 def test_kernels_found(spills):
     names = " ".join(spills)
     for k in ["nsa_attn_kernel", "dense_xattn_kernel", "route_g1_kernel", "sel_g1_kernel", "sel_forced_g1_kernel",
-              "cmp_g1_kernel", "cmp_route_g1_kernel", "cmp_pooled_kernel", "score_route_gqa_kernel", "route_kernel"]:
+              "cmp_g1_kernel", "cmp_route_g1_kernel", "cmp_pooled_kernel", "score_route_gqa_kernel", "route_kernel",
+              "sel_wave_kernel"]:
         assert k in names, k
 
 
