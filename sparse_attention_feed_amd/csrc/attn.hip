@@ -383,7 +383,9 @@ template <typename T> struct OutInLds { static constexpr bool value = sizeof(T) 
 // tables inside the region the running gated sum takes later, so they cost no LDS.
 template <typename T> struct RingSize { static constexpr int value = sizeof(T) == 2 ? 8 : 4; };
 
-template <typename T, int WAVES, int TPW>
+// kSel: the selected branch's phase is compiled in (launches whose branches include it); without
+// it the compressed and local phases get the registers to themselves.
+template <typename T, int WAVES, int TPW, bool kSel>
 __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr bool kOutLds = OutInLds<T>::value;
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
   };
 
   // ---- selected branch: union of the block's routing rows, streamed once ----
-  if (a.branches & 2) {
+  if (kSel && (a.branches & 2)) {
     // byte offsets from `extra` (kept as offsets so the pointers stay LDS pointers): bitmap,
     // per-word prefix, union list, scan scratch, per-wave token masks, ring buffers 2 .. R-1, and
     // the ring counters ready[R], done[R], broken
@@ -1031,13 +1033,16 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   const int n_part = (a.cap + WAVES * TPW - 1) / (WAVES * TPW);   // workgroups per block and KV head
   const int nwg = a.n_qblk * n_part * a.n_kvh;
   if (nwg == 0) return hipSuccess;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nsa_attn_kernel<T, WAVES, TPW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((nsa_attn_kernel<T, WAVES, TPW>), dim3(nwg), dim3(NT), lds, s, a);
-  return hipGetLastError();
+  auto go = [&](auto kernel) -> hipError_t {
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kernel, dim3(nwg), dim3(NT), lds, s, a);
+    return hipGetLastError();
+  };
+  return (a.branches & 2) ? go(&nsa_attn_kernel<T, WAVES, TPW, true>) : go(&nsa_attn_kernel<T, WAVES, TPW, false>);
 }
 
 int sel_wave_ucap(const AttnArgs& a) {
