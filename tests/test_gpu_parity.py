@@ -41,10 +41,19 @@ def edge(kind):
     if kind == "k64_cap8":
         cnt = np.random.default_rng(11).integers(1, 9, size=90).tolist()
         return W.custom_block_workload(11, cnt, 8, 32, 2, 32, "f32", 64)
+    if kind == "k64_cap8_bf16":   # every lane of the selected-branch wave holds eight routing entries
+        cnt = np.random.default_rng(12).integers(1, 9, size=90).tolist()
+        return W.custom_block_workload(12, cnt, 8, 32, 2, 32, "bf16", 64)
+    if kind == "cap1_bf16":       # one slot per block: one-token clusters, one-key tiles
+        return W.custom_block_workload(13, [1] * 150, 1, 32, 2, 32, "bf16", 12)
+    if kind == "ragged_cap64_bf16":   # partial 8-slot clusters at every block end
+        cnt = np.random.default_rng(14).integers(1, 65, size=40).tolist()
+        return W.custom_block_workload(14, cnt, 64, 32, 2, 32, "bf16", 24)
     raise KeyError(kind)
 
 
-EDGES = ["ragged_cap16", "single_block", "k_beyond_blocks", "lattice_ties", "cnt_one_blocks", "k48_cap16", "k64_cap8"]
+EDGES = ["ragged_cap16", "single_block", "k_beyond_blocks", "lattice_ties", "cnt_one_blocks", "k48_cap16", "k64_cap8",
+         "k64_cap8_bf16", "cap1_bf16", "ragged_cap64_bf16"]
 
 
 def get(name):
@@ -171,7 +180,7 @@ def test_single_branch(name, branch):
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", SMALL + ["ragged_cap16", "k_beyond_blocks", "cnt_one_blocks", "k48_cap16",
-                                          "k64_cap8"])
+                                          "k64_cap8", "k64_cap8_bf16", "cap1_bf16", "ragged_cap64_bf16"])
 def test_fused_layer(name):
     import sparse_attention_feed_amd as S
     w = get(name)
@@ -567,7 +576,8 @@ def test_ring_wait_bound_ends_with_nan(monkeypatch):
     assert max_err(host(o), ref) <= tol(w)
 
 
-@pytest.mark.parametrize("name", ["stage2_small", "k48_cap16", "ragged_cap16"])
+@pytest.mark.parametrize("name", ["stage2_small", "k48_cap16", "ragged_cap16", "k64_cap8_bf16", "cap1_bf16",
+                                  "ragged_cap64_bf16", "k_beyond_blocks", "single_block"])
 def test_selected_branch_paths_agree(name, monkeypatch):
     """bf16 token queries take the selected branch to its own kernel (wave-owned token clusters)
     after the fused kernel's other branches; NSA_SEL_RING=1 keeps it in the fused kernel's tile
