@@ -250,8 +250,9 @@ nsa_status nsa_route_scores_topk(const nsa_layout* layout, nsa_dtype dtype, nsa_
  * Supported: (D, G) = (32, 16) for NSA_F32 and NSA_BF16 (n_blk <= 65536 when SEL is named;
  * n_blk * blk_cap * n_qh * max(32, gate_stride) < 2^31, row offsets being 32-bit).  With NSA_Q_TOKEN
  * and NSA_BF16 the selected branch runs in a second kernel after the fused kernel's other branches
- * and adds its gated result to o (o is rounded to bf16 in between; the environment variable
- * NSA_SEL_RING=1 keeps it in the fused kernel instead).  With NSA_Q_BLOCK
+ * and adds its gated result to o (o is rounded to bf16 in between); without the compressed branch
+ * the local branch runs in that kernel family too, first (the environment variable NSA_SEL_RING=1
+ * keeps every branch in the fused kernel instead).  With NSA_Q_BLOCK
  * the selected and local branches run first in the fused kernel (token queries, the block's
  * routing row for every token) and the compressed branch of the pooled queries then adds each
  * block's gated result to its tokens (o is rounded to `dtype` in between).  And

@@ -468,21 +468,31 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
   if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "%s: LDS need %zu bytes exceeds 160 KiB", fn, lds);
   NSA_FORCED_FAILURE(fn);
   if (q_gran == NSA_Q_TOKEN) {
-    // bf16: the selected branch runs in its own kernel of wave-owned token clusters, after the
-    // fused kernel has written the other named branches' gated sum (which it then adds to)
-    if (dtype != NSA_BF16 || !(branches & NSA_BR_SEL) || sel_ring)
+    // bf16: the local and selected branches run in kernels of wave-owned token clusters, each
+    // adding its gated result to what the launches before it wrote (the compressed branch in the
+    // fused kernel first)
+    if (dtype != NSA_BF16 || !(branches & (NSA_BR_SEL | NSA_BR_LOC)) || sel_ring)
       return hip_status(nsa::launch_attn(dtype == NSA_BF16, a, stream), fn);
     if (nsa::sel_wave_lds(a) > 160 * 1024)
       return fail(NSA_ERR_UNSUPPORTED, "%s: LDS need %zu bytes exceeds 160 KiB", fn, nsa::sel_wave_lds(a));
-    const uint32_t rest = branches & (NSA_BR_CMP | NSA_BR_LOC);
-    if (rest) {
+    // With the compressed branch named, the local branch stays in the fused kernel (its one tile
+    // there costs less than a launch of its own that reads and writes o again); without it, it
+    // runs in the wave kernel's local instantiation.
+    int written = 0;
+    if (branches & NSA_BR_CMP) {
       nsa::AttnArgs f = a;
-      f.branches = rest;
+      f.branches = branches & (NSA_BR_CMP | NSA_BR_LOC);
       f.top_k = 0;
       hipError_t e = nsa::launch_attn(1, f, stream);
       if (e != hipSuccess) return hip_status(e, fn);
+      written = 1;
+    } else if (branches & NSA_BR_LOC) {
+      hipError_t e = nsa::launch_sel_wave(a, 1, written, stream);
+      if (e != hipSuccess) return hip_status(e, fn);
+      written = 1;
     }
-    return hip_status(nsa::launch_sel_wave(a, rest ? 1 : 0, stream), fn);
+    if (!(branches & NSA_BR_SEL)) return NSA_OK;
+    return hip_status(nsa::launch_sel_wave(a, 0, written, stream), fn);
   }
   // block rows: the selected and local branches (token queries, the block's routing row) in the
   // fused kernel, reading the gate channels after the compressed one; then the compressed branch

@@ -663,6 +663,9 @@ struct SelRaw {                 // one tile's K and V rows as loaded: 16 keys pe
   Frag8<bf16> k[4], v[4];
 };
 
+// kLoc: the local branch instead (the query block's own block is the one tile, every valid token
+// takes part; no routing rows are read).
+template <bool kLoc>
 __global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, int accumulate, int ucap) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int l = lane_id(), r = l & 15, g = l >> 4;
@@ -698,6 +701,20 @@ __global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, i
       for (int t = 0; t < SEL_TPW; ++t) qf[t] = make_qf<bf16>(raw[t], c2, t < n_valid);
     }
 
+    const int nw = kLoc ? 0 : a.n_words;
+    unsigned char* tab = smem + (threadIdx.x >> 6) * sel_wave_lds_bytes(nw, ucap);
+    int* ulist = reinterpret_cast<int*>(tab + nw * 8);
+    uint32_t* umask = reinterpret_cast<uint32_t*>(tab + nw * 8 + ucap * 4);
+    int n_union;
+    if constexpr (kLoc) {
+      // the own block, when it lies in the key range (an empty key set adds 0)
+      if (l == 0) {
+        ulist[0] = b | (cnt << 16);
+        umask[0] = (1u << n_valid) - 1u;
+      }
+      n_union = (b >= a.kv_lo && b < a.kv_hi) ? 1 : 0;
+      wave_lds_order();
+    } else {
     // routing entries of the wave's rows (entry e: row e / top_k, position e % top_k) and their
     // blocks' token counts, all loads issued at once
     const int kk = a.top_k;
@@ -714,12 +731,8 @@ __global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, i
     for (int i = 0; i < SEL_MAXE; ++i) ecnt[i] = (eblk[i] >= 0 && eblk[i] < a.n_blk) ? a.blk_cnt[eblk[i]] : 0;
 
     // union of the rows in this wave's LDS tables: bitmap, per-word prefix, list, token masks
-    const int nw = a.n_words;
-    unsigned char* tab = smem + (threadIdx.x >> 6) * sel_wave_lds_bytes(nw, ucap);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(tab);
     int* wpre = reinterpret_cast<int*>(tab + nw * 4);
-    int* ulist = reinterpret_cast<int*>(tab + nw * 8);
-    uint32_t* umask = reinterpret_cast<uint32_t*>(tab + nw * 8 + ucap * 4);
     for (int i = l; i < nw; i += 64) bitmap[i] = 0u;
     wave_lds_order();
 #pragma unroll
@@ -730,7 +743,6 @@ __global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, i
     int mine = 0;
     for (int i = 0; i < per; ++i)
       if (w0 + i < nw) mine += __builtin_popcount(bitmap[w0 + i]);
-    int n_union;
     int base = wave_exclusive_scan(mine, n_union);
     for (int i = 0; i < per; ++i) {
       const int wi = w0 + i;
@@ -752,6 +764,7 @@ __global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, i
       }
     }
     wave_lds_order();
+    }
 
     // 0/1 selectors: sel_d[dt] is B[k][n] = (k == n + 16 dt) in the B-operand layout
     Frag8<bf16> bsel[2];
@@ -816,7 +829,7 @@ __global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, i
 #pragma unroll
     for (int t = 0; t < SEL_TPW; ++t) {
       const int row = b * cap + min(s0 + t, cap - 1);
-      gl[t] = reinterpret_cast<const bf16*>(a.gates)[(row * a.n_qh + hh) * a.n_gch + a.ch_sel];
+      gl[t] = reinterpret_cast<const bf16*>(a.gates)[(row * a.n_qh + hh) * a.n_gch + (kLoc ? a.ch_loc : a.ch_sel)];
     }
   }
 #pragma unroll
@@ -1088,18 +1101,23 @@ size_t sel_wave_lds(const AttnArgs& a) {
   return (size_t)SEL_WPG * sel_wave_lds_bytes(a.n_words, sel_wave_ucap(a));
 }
 
-hipError_t launch_sel_wave(const AttnArgs& a, int accumulate, hipStream_t s) {
+hipError_t launch_sel_wave(const AttnArgs& a, int local, int accumulate, hipStream_t s) {
   const int nclu = (a.cap + SEL_TPW - 1) / SEL_TPW;
   const long long waves = (long long)a.n_qblk * nclu * a.n_kvh;
   if (waves == 0) return hipSuccess;
   const int nwg = (int)((waves + SEL_WPG - 1) / SEL_WPG);
+  if (local) {
+    hipLaunchKernelGGL(sel_wave_kernel<true>, dim3(nwg), dim3(SEL_WPG * 64), (size_t)SEL_WPG * sel_wave_lds_bytes(0, 1),
+                       s, a, accumulate, 1);
+    return hipGetLastError();
+  }
   const size_t lds = sel_wave_lds(a);
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sel_wave_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sel_wave_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(sel_wave_kernel, dim3(nwg), dim3(SEL_WPG * 64), lds, s, a, accumulate, sel_wave_ucap(a));
+  hipLaunchKernelGGL(sel_wave_kernel<false>, dim3(nwg), dim3(SEL_WPG * 64), lds, s, a, accumulate, sel_wave_ucap(a));
   return hipGetLastError();
 }
 

@@ -101,11 +101,13 @@ hipError_t launch_attn_g1_routed(int is_bf16, const G1Args& a, hipStream_t s);
 
 size_t attn_lds_bytes(int is_bf16, const AttnArgs& a);
 hipError_t launch_attn(int is_bf16, const AttnArgs& a, hipStream_t s);
-// selected branch (bf16, per-token routing rows) by wave-owned clusters of 8 consecutive slots:
-// o = (accumulate ? o : 0) + sigmoid(gates[.., a.ch_sel]) * result (no gate when a.gates is NULL);
-// padding slots 0 when not accumulating; lse when a.lse is set.  Query blocks [q_blk0, +n_qblk).
+// selected branch (bf16, per-token routing rows), or with `local` the local branch, by wave-owned
+// clusters of 8 consecutive slots: o = (accumulate ? o : 0) + sigmoid(gates[.., a.ch_sel or
+// a.ch_loc]) * result (no gate when a.gates is NULL); padding slots 0 when not accumulating; lse
+// when a.lse is set.  Query blocks [q_blk0, +n_qblk); the local branch attends the own block only
+// inside [kv_lo, kv_hi).  sel_wave_lds: the selected branch's LDS per workgroup.
 size_t sel_wave_lds(const AttnArgs& a);
-hipError_t launch_sel_wave(const AttnArgs& a, int accumulate, hipStream_t s);
+hipError_t launch_sel_wave(const AttnArgs& a, int local, int accumulate, hipStream_t s);
 // compressed branch of pooled queries (a.q = [n_blk][n_qh][D]), each block's result given to its
 // valid tokens: o = (accumulate ? o : 0) + sigmoid(gates[.., gate_ch]) * result (no gate when
 // a.gates is NULL), padding slots 0 when not accumulating; lse [n_blk][n_qh] when a.lse is set
