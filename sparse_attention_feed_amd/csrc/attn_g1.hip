@@ -935,7 +935,9 @@ template <typename T>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 1 : 2)))
 void sel_g1_kernel(G1Args a) {
   __shared__ TileG1<T> tb;
-  __shared__ int keys_lds[64 * 16 + KT];          // source rows of the selected valid tokens, packed
+  // source rows of the selected valid tokens, packed: (entries x blk_cap + KT) ints, sized at launch
+  // so that eight bf16 workgroups fit a compute unit's LDS at top_k 16 and blk_cap 16
+  extern __shared__ int keys_lds[];
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int b = wg / a.n_kvh, h = wg % a.n_kvh;
   const int l = lane_id(), r = l & 15, g = l >> 4;
@@ -1187,6 +1189,11 @@ hipError_t launch_route_g1_t(const G1Args& a, hipStream_t s) {
   return launch_route_g1_k<T, 64, 1>(a, s);
 }
 
+// dynamic LDS of sel_g1_kernel: the packed key list of one query block's selection
+size_t sel_g1_keys_lds(const G1Args& a) {
+  return (size_t)((a.local ? 1 : a.top_k) * a.cap + KT) * sizeof(int);
+}
+
 hipError_t launch_attn_g1_routed_bf16(const G1Args& a0, hipStream_t s) {
   G1Args a = a0;
   hipError_t e;
@@ -1195,7 +1202,7 @@ hipError_t launch_attn_g1_routed_bf16(const G1Args& a0, hipStream_t s) {
   else e = launch_cmp_route_g1_k<bf16, 8, 1>(a, s);
   if (e != hipSuccess) return e;
   a.accumulate = 1;
-  hipLaunchKernelGGL(sel_g1_kernel<bf16>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(sel_g1_kernel<bf16>, dim3(a.n_blk * a.n_kvh), dim3(64), sel_g1_keys_lds(a), s, a);
   return hipGetLastError();
 }
 
@@ -1217,7 +1224,7 @@ hipError_t launch_attn_g1_t(const G1Args& a0, hipStream_t s) {
       hipLaunchKernelGGL((sel_forced_g1_kernel<T, ForcedGroup<T>::value>), dim3((a.n_blk + NB - 1) / NB * a.n_kvh),
                          dim3(FW * 64), 0, s, a);
     } else {
-      hipLaunchKernelGGL(sel_g1_kernel<T>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+      hipLaunchKernelGGL(sel_g1_kernel<T>, dim3(a.n_blk * a.n_kvh), dim3(64), sel_g1_keys_lds(a), s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1228,7 +1235,7 @@ hipError_t launch_attn_g1_t(const G1Args& a0, hipStream_t s) {
     a.local = 1;
     a.ch_sel = a.ch_loc;
     a.f_lo = a.f_hi = 0;
-    hipLaunchKernelGGL(sel_g1_kernel<T>, dim3(a.n_blk * a.n_kvh), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(sel_g1_kernel<T>, dim3(a.n_blk * a.n_kvh), dim3(64), sel_g1_keys_lds(a), s, a);
     return hipGetLastError();
   }
   return hipSuccess;
