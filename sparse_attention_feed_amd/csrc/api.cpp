@@ -471,7 +471,9 @@ static nsa_status attn_fwd(const char* fn, const nsa_layout* L, nsa_dtype dtype,
     // bf16: the local and selected branches run in kernels of wave-owned token clusters, each
     // adding its gated result to what the launches before it wrote (the compressed branch in the
     // fused kernel first)
-    if (dtype != NSA_BF16 || !(branches & (NSA_BR_SEL | NSA_BR_LOC)) || sel_ring)
+    // (the wave kernels' block lists hold a block index in 16 bits: n_blk <= 65536, which the
+    // selected branch requires anyway; a larger local-only call stays in the fused kernel)
+    if (dtype != NSA_BF16 || !(branches & (NSA_BR_SEL | NSA_BR_LOC)) || sel_ring || L->n_blk > 65536)
       return hip_status(nsa::launch_attn(dtype == NSA_BF16, a, stream), fn);
     if (nsa::sel_wave_lds(a) > 160 * 1024)
       return fail(NSA_ERR_UNSUPPORTED, "%s: LDS need %zu bytes exceeds 160 KiB", fn, nsa::sel_wave_lds(a));
