@@ -537,6 +537,28 @@ def test_layer_at_the_block_limit_sampled():
     assert np.all(host(o)[~w.valid_mask()] == 0)
 
 
+@pytest.mark.parametrize("n_blk", [65536, 65537])
+def test_local_branch_one_token_blocks(n_blk):
+    """Local branch alone over one-token blocks: each token attends only itself, so o equals its
+    own v row for every head of the group, exactly (one key: probability 1), and lse equals
+    scale * <q, k>.  65,536 blocks take the wave-cluster kernel, 65,537 the fused kernel."""
+    import sparse_attention_feed_amd as S
+    w = W.custom_block_workload(16, [1] * n_blk, 1, 32, 2, 32, "bf16", 1)
+    d = to_dev(w)
+    lse = torch.empty((w.n_slots, w.n_qh), dtype=torch.float32, device="cuda")
+    say("local branch, one-token blocks", n_blk)
+    o = S.attn_fwd(d["layout"], S.BR_LOC, d["q"], d["k"], d["v"], lse=lse)
+    torch.cuda.synchronize()
+    grp = w.n_qh // w.n_kvh
+    want = np.repeat(w.v, grp, axis=1)                     # head h reads KV head h // grp
+    np.testing.assert_array_equal(host(o), want)
+    ref_lse = w.scale * np.einsum("shd,shd->sh", w.q.astype(np.float64), np.repeat(w.k, grp, axis=1).astype(np.float64))
+    qn = np.linalg.norm(w.q.astype(np.float64), axis=2).max()
+    kn = np.linalg.norm(w.k.astype(np.float64), axis=2).max()
+    # the probability is rounded to bf16 (|d ln l| <= 1.96e-3) and the pre-scaled query once to bf16
+    assert max_err(host(lse), ref_lse) <= 1.96e-3 + 2.0 ** -9 * w.scale * qn * kn + 1e-4
+
+
 def test_full_size_dense_sampled():
     import sparse_attention_feed_amd as S
     w = W.make("dense")
