@@ -635,8 +635,20 @@ constexpr int SEL_MAXE = SEL_TPW;   // routing entries per lane: 8 rows x top_k 
 
 // LDS bytes of one wave's tables: bitmap and per-word prefix (n_words each), union list and
 // per-block token masks (ucap each).
+constexpr int SEL_VPAD = 40;                          // LDS row stride (elements) of the staged V rows
+constexpr int SEL_VT_BYTES = TILE * SEL_VPAD * 2;      // one wave's staged V tile (bf16)
 __host__ __device__ inline int sel_wave_lds_bytes(int n_words, int ucap) {
-  return ((2 * n_words + 2 * ucap) * 4 + 15) & ~15;
+  return SEL_VT_BYTES + (((2 * n_words + 2 * ucap) * 4 + 15) & ~15);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group, source lane s names
+// 4 consecutive 16-bit elements; result lane i receives, as its element e, element i % 4 of source
+// lane 4e + i / 4.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(reinterpret_cast<const s16x4*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 // Orders this wave's LDS accesses (all lanes) before the next ones.  A wave's LDS instructions
@@ -702,7 +714,9 @@ __global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, i
     }
 
     const int nw = kLoc ? 0 : a.n_words;
-    unsigned char* tab = smem + (threadIdx.x >> 6) * sel_wave_lds_bytes(nw, ucap);
+    unsigned char* vtile = smem + (threadIdx.x >> 6) * sel_wave_lds_bytes(nw, ucap);
+    bf16* vrows = reinterpret_cast<bf16*>(vtile);               // the tile's V rows, row-major
+    unsigned char* tab = vtile + SEL_VT_BYTES;
     int* ulist = reinterpret_cast<int*>(tab + nw * 8);
     uint32_t* umask = reinterpret_cast<uint32_t*>(tab + nw * 8 + ucap * 4);
     int n_union;
@@ -766,13 +780,6 @@ __global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, i
     wave_lds_order();
     }
 
-    // 0/1 selectors: sel_d[dt] is B[k][n] = (k == n + 16 dt) in the B-operand layout
-    Frag8<bf16> bsel[2];
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bsel[dt].v[e] = (8 * g + e == r + 16 * dt) ? (bf16)1.0f : (bf16)0.0f;
-
     const bf16* kb = reinterpret_cast<const bf16*>(a.k) + j * HD;
     const bf16* vb = reinterpret_cast<const bf16*>(a.v) + j * HD;
     // rows past the block's count repeat its last valid row (masked by the -inf seed); the
@@ -792,21 +799,23 @@ __global__ __launch_bounds__(SEL_WPG * 64, 2) void sel_wave_kernel(AttnArgs a, i
       }
     };
     auto step = [&](int u, SelRaw& cur, SelRaw& nxt) {
-      // V^T fragments of tile u: vf[dt][h] takes keys 32h + 4g + i (from 16-key step 2h) and
-      // 32h + 16 + 4g + i (step 2h + 1) of head-dim column 16 dt + r
+      // V^T fragments of tile u: vf[dt][h] takes keys 32h + 4g + i and 32h + 16 + 4g + i (i < 4) of
+      // head-dim column 16 dt + r.  The rows go to the wave's LDS tile as loaded (lane (r, g): key
+      // 16 q4 + r, dims 8g..8g+7); a transposing read in which lane (r, g) names key
+      // 32h + 4g + r / 4 (+ 16), dims 16 dt + 4 (r % 4) .. + 3 returns exactly those four keys of
+      // column 16 dt + r to lane (r, g).
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<bf16x8*>(vrows + (16 * q4 + r) * SEL_VPAD + 8 * g) = cur.v[q4].v;
       Frag8<bf16> vf[2][2];
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const f32x4 d0 = mma16(cur.v[2 * h], bsel[dt], zero);
-          const f32x4 d1 = mma16(cur.v[2 * h + 1], bsel[dt], zero);
-          const bf16x2 p0 = __builtin_convertvector((f32x2){d0[0], d0[1]}, bf16x2);
-          const bf16x2 p1 = __builtin_convertvector((f32x2){d0[2], d0[3]}, bf16x2);
-          const bf16x2 p2 = __builtin_convertvector((f32x2){d1[0], d1[1]}, bf16x2);
-          const bf16x2 p3 = __builtin_convertvector((f32x2){d1[2], d1[3]}, bf16x2);
-          vf[dt][h].v = (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          const bf16* base = vrows + (32 * h + 4 * g + (r >> 2)) * SEL_VPAD + 16 * dt + 4 * (r & 3);
+          const bf16x4 lo = lds_read_tr4(base);
+          const bf16x4 hi = lds_read_tr4(base + 16 * SEL_VPAD);
+          vf[dt][h].v = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
       const int nk = ulist[u] >> 16;
       const uint32_t pm = __builtin_amdgcn_readfirstlane(umask[u]);
