@@ -190,6 +190,58 @@ __device__ __forceinline__ void store_rows_g1(TileG1<T>& t, const RowsG1<T, NTH>
   }
 }
 
+// bf16 tiles of the selected branch: V kept as rows (as gathered) and read back transposed.
+struct TileG1R {
+  bf16 k[KT][KP];           // K rows
+  bf16 v[KT][KP];           // V rows
+};
+template <typename T> struct SelTile { typedef TileG1<T> type; };
+template <> struct SelTile<bf16> { typedef TileG1R type; };
+
+template <int NTH>
+__device__ __forceinline__ void store_rows_g1(TileG1R& t, const RowsG1<bf16, NTH>& g, int tid) {
+  typedef ChunkG1<bf16, NTH> C;
+#pragma unroll
+  for (int i = 0; i < C::NCH; ++i) {
+    const int cc = tid + i * NTH;
+    const int key = cc / C::CPK, part = cc % C::CPK;
+    *reinterpret_cast<uint4*>(&t.k[key][part * C::EPC]) =
+        make_uint4(g.k[4 * i], g.k[4 * i + 1], g.k[4 * i + 2], g.k[4 * i + 3]);
+    *reinterpret_cast<uint4*>(&t.v[key][part * C::EPC]) =
+        make_uint4(g.v[4 * i], g.v[4 * i + 1], g.v[4 * i + 2], g.v[4 * i + 3]);
+  }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, source lane s names
+// 4 consecutive 16-bit elements; result lane i receives, as its element e, element i % 4 of source
+// lane 4e + i / 4.
+__device__ __forceinline__ bf16x4 lds_read_tr4_g1(const bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(reinterpret_cast<const s16x4*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// K fragments as load_frags_g1; V^T fragment [dt][c] (keys 32c + 4g + i and 32c + 16 + 4g + i of
+// column 16 dt + r): lane (r, g) names key 32c + 4g + r / 4 (and + 16), columns 16 dt + 4 (r % 4)
+// .. + 3 of the V rows, and the transposing read returns those four keys of column 16 dt + r.
+__device__ __forceinline__ void load_frags_g1(const TileG1R& t, TileFragsG1<bf16>& f) {
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) f.k[kt][h] = load_frag(&t.k[16 * kt + r][32 * h + 8 * g]);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16* base = &t.v[32 * c + 4 * g + (r >> 2)][16 * dt + 4 * (r & 3)];
+      const bf16x4 lo = lds_read_tr4_g1(base);
+      const bf16x4 hi = lds_read_tr4_g1(base + 16 * KP);
+      f.v[dt][c].v = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+}
+
 // Online softmax state of one column group (16 rows of one head), base-2 units.  The reference
 // maximum mc starts at 0 and may go stale: it enters S^T as the MFMA accumulator seed (-mc), and
 // it moves (with a rescale) only when a lane's probability sum could exceed kStaleLimitG1 or is
@@ -934,7 +986,7 @@ __device__ __forceinline__ int pack_block_tokens(int* keys, int total, int blk, 
 template <typename T>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 1 : 2)))
 void sel_g1_kernel(G1Args a) {
-  __shared__ TileG1<T> tb;
+  __shared__ typename SelTile<T>::type tb;
   // source rows of the selected valid tokens, packed: (entries x blk_cap + KT) ints, sized at launch
   // so that eight bf16 workgroups fit a compute unit's LDS at top_k 16 and blk_cap 16
   extern __shared__ int keys_lds[];
@@ -1045,7 +1097,7 @@ template <typename T, int NQ>
 __global__ __launch_bounds__(FW * 64) __attribute__((amdgpu_waves_per_eu(1))) void sel_forced_g1_kernel(G1Args a) {
   // wave w's tile and key list for its blocks' routed parts; the FW tiles then double-buffer the
   // shared range
-  __shared__ TileG1<T> tb[FW];
+  __shared__ typename SelTile<T>::type tb[FW];
   __shared__ int keys_w[FW][64 * 16 + KT];
   __shared__ int keys_f[kMaxForcedBlocks * 16 + KT];
   __shared__ int f_total;
@@ -1080,7 +1132,7 @@ __global__ __launch_bounds__(FW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   // each block's routed blocks outside the range (lane x < top_k: entry x; -1, out-of-range and
   // repeated entries count no keys), in the wave's own tile: no workgroup barrier, since the
   // waves' tile counts differ
-  TileG1<T>& tw = tb[w];
+  typename SelTile<T>::type& tw = tb[w];
   int* kw = keys_w[w];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
