@@ -623,11 +623,10 @@ __global__ __launch_bounds__(WAVES * 64) void nsa_attn_kernel(AttnArgs a) {
 // order, and each block's tile serves the tokens that selected it (LSRM pages, section 方法: the
 // selected active blocks give each query its fine detail).  A tile's K rows are loaded from
 // global memory straight into the MFMA A-operand layout (one 16-byte load per lane and 16-key
-// step).  V^T is formed in registers too: an MFMA of the V rows against a 0/1 selector matrix
-// gives D[key][d] = V[key][d] exactly (one nonzero product per sum, fp32), and the MFMA output
-// layout (lane: four consecutive keys of one column) is the key order in which the softmax hands
-// over its probabilities, so the converted outputs are the V^T fragments as they are.
-// The result is gated and written to o, or added to what o holds (accumulate).
+// step).  The V rows, loaded the same way, go to a tile in the wave's own LDS as they are and come
+// back as V^T fragments through gfx950's transposing LDS read, in the permuted key order in which
+// the softmax hands over its probabilities.  The result is gated and written to o, or added to
+// what o holds (accumulate).
 
 constexpr int SEL_TPW = 8;   // tokens (consecutive slots) per wave
 constexpr int SEL_WPG = 4;   // waves per workgroup (independent)
