@@ -123,8 +123,35 @@ __global__ __launch_bounds__(MAXT) void probe_kernel(int which, int iters, float
   if (l == 0) cyc[wave] = t1 - t0;
 }
 
+// Lane layout of gfx950's transposing LDS read (ds_read_b64_tr_b16), which the selected-branch
+// kernels use for their V^T fragments: LDS holds lds[i] = i (4096 16-bit values); with pattern 0 lane
+// l names elements 4l .. 4l+3, with pattern 1 elements 64 (l % 16) + 4 (l / 16) .. + 3 (every
+// address inside the 8 KiB array); out[64 * 4 * pattern + 4 l + e] = element e of lane l's result.
+__global__ __launch_bounds__(64) void lds_tr_layout_kernel(short* out) {
+  __shared__ short lds[64 * 64];
+  for (int i = threadIdx.x; i < 64 * 64; i += 64) lds[i] = (short)i;
+  __syncthreads();
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int l = threadIdx.x;
+#pragma unroll
+  for (int pattern = 0; pattern < 2; ++pattern) {
+    const int elem = pattern == 0 ? 4 * l : 64 * (l % 16) + 4 * (l / 16);
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 __attribute__((address_space(3)))*)(reinterpret_cast<s16x4*>(lds + elem)));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[256 * pattern + 4 * l + e] = r[e];
+  }
+}
+
 }  // namespace
 }  // namespace nsa
+
+// The transposing LDS read's lane layout (lds_tr_layout_kernel): out holds 512 int16.
+extern "C" int nsa_probe_lds_tr_layout(short* out, hipStream_t stream) {
+  if (out == nullptr) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(nsa::lds_tr_layout_kernel, dim3(1), dim3(64), 0, stream, out);
+  return (int)hipGetLastError();
+}
 
 // Runs probe `which` with `waves_per_simd` waves on each SIMD of `n_cu` compute units, `iters`
 // loop iterations.  sink: n_cu * 256 * waves_per_simd floats; cycles: n_cu * 4 * waves_per_simd
